@@ -1,0 +1,13 @@
+"""fp64 CPU oracle of the ZONOS2 MoE feed-forward layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check of the graft
+entry module and the CPU-baseline leg of the bench may import, call or run
+anything in this package.  The HIP library never uses it and shares no code,
+constant or table with it; the two meet only through the seeded inputs of the
+``synth`` package.
+"""
+
+from .moe_oracle import (  # noqa: F401
+    rmsnorm, router_scores, select_topk, gates, histogram, permutation,
+    silu, swiglu_expert, combine, oracle_forward, MARGIN_TOL,
+)

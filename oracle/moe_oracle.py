@@ -1,0 +1,224 @@
+"""fp64 CPU oracle of one ZONOS2 MoE feed-forward layer (plain NumPy).
+
+TEST INFRASTRUCTURE ONLY: imported by tests, by the smoke check and by the
+bench's CPU-baseline leg; never by the library.
+
+What the layer computes (sources: the ZONOS2 Technical Report as summarised
+on the audio-paper-digest page, section "Method overview and architecture",
+item 5 (MoE backbone: RMSNorm-normalised input, 16 experts, top-1 routing,
+top-2 in the last MoE layer) and item 6 (a per-expert bias vector b_l kept
+for load balancing); the mlsanity index page of the report, "Builds on"
+list (RMSNorm, GLU variants, auxiliary-loss-free load balancing); the
+telknet.cc article, section 2.1 (a router scores experts from the hidden
+state and TopK keeps a few of them)):
+
+  O1  x_t   = g * h_t / sqrt(mean_i h_{t,i}^2 + eps)              RMSNorm
+  O2  z_t   = W_r x_t ;  s_t = z_t + b                          router, biased scores
+  O3  sel_t = the k experts with the largest s_t, in descending order of s,
+              an exact tie going to the lower expert index
+  O4  gate  : k = 1  -> softmax(z_t)[sel]   (full softmax of the unbiased logits)
+              k >= 2 -> softmax of z_t restricted to the selected experts
+  O5  c_e   = #{(t, j) : sel_{t,j} = e};  offsets = exclusive prefix sum of c
+  O6  assignments a = t*k + j sorted stably by expert:
+              gather[p] = token of slot p, scatter[a] = slot of assignment a
+  O7  y_p   = W_down[e] (SiLU(W_gate[e] u) * (W_up[e] u)),  u = x_{gather[p]}
+  O8  out_t = sum_{j<k} gate_{t,j} * y_{scatter[t*k+j]}       (no residual)
+
+Readings where the pages are silent (each is listed in the design doc):
+the bias only steers selection and never enters a gate; the layer returns
+the FFN output without the residual; no capacity limit and no dropped
+tokens; no shared expert; a linear router (no EDA smoothing).
+
+Every floating-point step runs in float64 on the exact values of the inputs
+(bf16 inputs are widened exactly).  Nothing is rounded.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# Tokens whose top-k decision has a margin below this (absolute, on the biased
+# scores) may legitimately route either way in finite precision.
+MARGIN_TOL = 1e-3
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# O1 -------------------------------------------------------------------------
+def rmsnorm(H, g, eps: float) -> np.ndarray:
+    """RMSNorm of each row of H (the normalisation the digest's item 5 applies
+    to the backbone input; defined in the RMSNorm paper of the index page's
+    "Builds on" list): x = g * h / sqrt(mean(h^2) + eps)."""
+    H = _f64(H)
+    g = _f64(g)
+    ms = np.mean(H * H, axis=-1, keepdims=True)
+    return (H / np.sqrt(ms + float(eps))) * g
+
+
+# O2 -------------------------------------------------------------------------
+def router_scores(X, Wr, b):
+    """Linear router: logits z = X W_r^T and selection scores s = z + b
+    (digest item 6: the per-expert bias b_l; index page: auxiliary-loss-free
+    balancing, where the bias shifts which experts are chosen)."""
+    z = _f64(X) @ _f64(Wr).T
+    s = z + _f64(b)[None, :]
+    return z, s
+
+
+# O3 -------------------------------------------------------------------------
+def select_topk(s, k: int):
+    """Top-k experts per row of s (digest item 5: top-1, or top-2 in the last
+    MoE layer), in descending score order; exact ties go to the lower index.
+
+    Returns (sel [T,k] int32, margin [T] float64) where margin is the smallest
+    gap between consecutive sorted scores s_(i) - s_(i+1) for i = 1..min(k, E-1):
+    the amount by which the decision (set and order) could flip.
+    """
+    s = _f64(s)
+    T, E = s.shape
+    if not 1 <= k <= E:
+        raise ValueError("top-k needs 1 <= k <= E")
+    # argsort of -s with a stable sort keeps equal scores in index order.
+    order = np.argsort(-s, axis=1, kind="stable")
+    sel = order[:, :k].astype(np.int32)
+    ranked = np.take_along_axis(s, order, axis=1)
+    m = min(k, E - 1)
+    if m == 0:
+        margin = np.full(T, np.inf)
+    else:
+        margin = np.min(ranked[:, :m] - ranked[:, 1:m + 1], axis=1)
+    return sel, margin
+
+
+# O4 -------------------------------------------------------------------------
+def gates(z, sel) -> np.ndarray:
+    """Gate weights from the unbiased logits z.
+
+    k = 1: the softmax probability of the chosen expert over all E experts.
+    k >= 2: softmax over the chosen experts only (the pair is renormalised).
+    """
+    z = _f64(z)
+    sel = np.asarray(sel)
+    k = sel.shape[1]
+    if k == 1:
+        zmax = np.max(z, axis=1, keepdims=True)
+        ez = np.exp(z - zmax)
+        p = ez / np.sum(ez, axis=1, keepdims=True)
+        return np.take_along_axis(p, sel.astype(np.int64), axis=1)
+    zs = np.take_along_axis(z, sel.astype(np.int64), axis=1)
+    zmax = np.max(zs, axis=1, keepdims=True)
+    ez = np.exp(zs - zmax)
+    return ez / np.sum(ez, axis=1, keepdims=True)
+
+
+# O5 -------------------------------------------------------------------------
+def histogram(sel, E: int):
+    """Assignments per expert and their exclusive prefix sum (offsets[E] = T*k)."""
+    flat = np.asarray(sel).reshape(-1).astype(np.int64)
+    counts = np.bincount(flat, minlength=E).astype(np.int32)
+    offsets = np.zeros(E + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    return counts, offsets
+
+
+# O6 -------------------------------------------------------------------------
+def permutation(sel):
+    """Stable counting sort of the assignments a = t*k + j by expert.
+
+    gather[p]  = token whose row fills expert-ordered slot p;
+    scatter[a] = slot that holds assignment a.
+    Within one expert, slots follow increasing a (hence increasing token).
+    """
+    sel = np.asarray(sel)
+    k = sel.shape[1]
+    flat = sel.reshape(-1)
+    perm = np.argsort(flat, kind="stable")
+    gather = (perm // k).astype(np.int32)
+    scatter = np.empty_like(perm)
+    scatter[perm] = np.arange(perm.size)
+    return gather, scatter.astype(np.int32)
+
+
+# O7 -------------------------------------------------------------------------
+def silu(v):
+    """SiLU(v) = v / (1 + exp(-v))."""
+    v = _f64(v)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def swiglu_expert(Wg, Wu, Wd, U) -> np.ndarray:
+    """SwiGLU expert on the rows of U (GLU-variants paper, index page's
+    "Builds on" list): y = W_down (SiLU(W_gate u) * (W_up u))."""
+    U = _f64(U)
+    G = U @ _f64(Wg).T
+    V = U @ _f64(Wu).T
+    return (silu(G) * V) @ _f64(Wd).T
+
+
+# O8 -------------------------------------------------------------------------
+def combine(Y, gate, scatter, k: int) -> np.ndarray:
+    """out_t = sum over j of gate[t, j] * Y[scatter[t*k + j]], in j order."""
+    gate = _f64(gate)
+    T = gate.shape[0]
+    Y = _f64(Y)
+    out = np.zeros((T, Y.shape[1]))
+    sc = np.asarray(scatter).reshape(T, k)
+    for j in range(k):
+        out += gate[:, j:j + 1] * Y[sc[:, j]]
+    return out
+
+
+# whole layer ----------------------------------------------------------------
+def oracle_forward(vals: dict, k: int | None = None, forced_sel=None, tokens=None,
+                   eps: float | None = None) -> dict:
+    """Run O1-O8 on exact input values (a dict as from ``synth.values_f32``).
+
+    forced_sel : optional [T,k] expert ids that replace O3's choice (so the
+                 expert path can be checked on the device's own routing).
+    tokens     : optional token indices; the output is then computed for
+                 those rows only (routing and permutation are always full).
+    Returns a dict with x, z, s, sel, margin, gate, counts, offsets, gather,
+    scatter and out (float64; rows of ``tokens`` when given).
+    """
+    cfg = vals.get("cfg")
+    if k is None:
+        k = cfg.k
+    if eps is None:
+        eps = cfg.eps
+    H = vals["hidden"]
+    E = np.asarray(vals["w_router"]).shape[0]
+    x = rmsnorm(H, vals["gain"], eps)
+    z, s = router_scores(x, vals["w_router"], vals["bias"])
+    sel_o, margin = select_topk(s, k)
+    sel = sel_o if forced_sel is None else np.asarray(forced_sel, np.int32).reshape(-1, k)
+    gate = gates(z, sel)
+    counts, offsets = histogram(sel, E)
+    gather, scatter = permutation(sel)
+
+    T = x.shape[0]
+    tok = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
+    need = np.zeros(T * k, bool)
+    for j in range(k):
+        need[tok * k + j] = True
+    slots_needed = np.sort(scatter[need])
+    Y = np.zeros((T * k, x.shape[1]))
+    Wg, Wu, Wd = vals["w_gate"], vals["w_up"], vals["w_down"]
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        ps = slots_needed[(slots_needed >= lo) & (slots_needed < hi)]
+        if ps.size == 0:
+            continue
+        Y[ps] = swiglu_expert(Wg[e], Wu[e], Wd[e], x[gather[ps]])
+    if tokens is None:
+        out = combine(Y, gate, scatter, k)
+    else:
+        sc = scatter.reshape(T, k)[tok]
+        out = np.zeros((tok.size, x.shape[1]))
+        for j in range(k):
+            out += gate[tok, j:j + 1] * Y[sc[:, j]]
+    return {"x": x, "z": z, "s": s, "sel": sel, "sel_oracle": sel_o, "margin": margin,
+            "gate": gate, "counts": counts, "offsets": offsets, "gather": gather,
+            "scatter": scatter, "out": out, "tokens": tok}

@@ -1,0 +1,298 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each check is chosen so that a plausible slip in the oracle (a dropped eps or
+gain, the bias leaking into a gate, a transposed weight, a wrong SiLU, a
+wrong combine index, an unstable permutation) fails at least one of them:
+
+* pure-Python brute force on tiny inputs (every expert for every token,
+  dense one-hot gate matrix, bucket permutation);
+* hand-worked closed-form examples;
+* library routines for the steps that have one (torch rms_norm / silu /
+  linear, scipy softmax / expit);
+* the E=1, k=1 special case, which is a dense SwiGLU FFN;
+* invariants (token permutation, expert relabelling, linearity in W_down,
+  zero input, forced routing by a huge bias, determinism).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from oracle import moe_oracle as O
+from oracle.brute import brute_forward
+
+
+def _rand_layer(rng, T, d, E, F, bias_std=0.3):
+    return {
+        "hidden": rng.standard_normal((T, d)),
+        "gain": 1.0 + 0.3 * rng.standard_normal(d),
+        "w_router": rng.standard_normal((E, d)) / math.sqrt(d),
+        "bias": bias_std * rng.standard_normal(E),
+        "w_gate": rng.standard_normal((E, F, d)) / math.sqrt(d),
+        "w_up": rng.standard_normal((E, F, d)) / math.sqrt(d),
+        "w_down": rng.standard_normal((E, d, F)) / math.sqrt(F),
+    }
+
+
+# ----------------------------------------------------------------- brute force
+@pytest.mark.parametrize("T,d,E,F,k,seed", [
+    (7, 5, 3, 4, 1, 0), (6, 4, 4, 3, 2, 1), (5, 6, 2, 7, 2, 2), (8, 3, 4, 2, 1, 3),
+    (4, 5, 3, 6, 3, 4), (1, 4, 4, 5, 1, 5),
+])
+def test_oracle_matches_brute_force(T, d, E, F, k, seed):
+    rng = np.random.default_rng(seed)
+    L = _rand_layer(rng, T, d, E, F)
+    eps = 1e-6
+    ref = brute_forward(L["hidden"], L["gain"], L["w_router"], L["bias"], L["w_gate"],
+                        L["w_up"], L["w_down"], k, eps)
+    got = O.oracle_forward(L, k=k, eps=eps)
+    np.testing.assert_array_equal(got["sel"], np.array(ref["sel"]))
+    np.testing.assert_allclose(got["gate"], np.array(ref["gate"]), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(got["out"], np.array(ref["out"]), rtol=1e-11, atol=1e-13)
+    np.testing.assert_array_equal(got["counts"], ref["counts"])
+    np.testing.assert_array_equal(got["gather"], ref["gather"])
+    np.testing.assert_array_equal(got["scatter"], ref["scatter"])
+
+
+def test_oracle_matches_brute_force_forced_routing():
+    rng = np.random.default_rng(11)
+    T, d, E, F, k = 6, 4, 4, 3, 2
+    L = _rand_layer(rng, T, d, E, F)
+    forced = np.array([[3, 0], [1, 2], [2, 1], [0, 3], [3, 2], [1, 0]], np.int32)
+    got = O.oracle_forward(L, k=k, eps=1e-6, forced_sel=forced)
+    # no single bias vector reproduces an arbitrary per-token choice, so the
+    # forced routing is evaluated here with scalar loops
+    H, g = L["hidden"], L["gain"]
+    x = np.array([[g[i] * H[t][i] / math.sqrt(sum(v * v for v in H[t]) / d + 1e-6)
+                   for i in range(d)] for t in range(T)])
+    z = np.array([[sum(L["w_router"][e][i] * x[t][i] for i in range(d)) for e in range(E)]
+                  for t in range(T)])
+    for t in range(T):
+        zz = z[t, forced[t]]
+        gt = np.exp(zz - zz.max())
+        gt /= gt.sum()
+        ref = np.zeros(d)
+        for j in range(k):
+            e = forced[t, j]
+            a = [0.0] * F
+            for f in range(F):
+                gg = sum(L["w_gate"][e][f][i] * x[t][i] for i in range(d))
+                uu = sum(L["w_up"][e][f][i] * x[t][i] for i in range(d))
+                a[f] = gg / (1 + math.exp(-gg)) * uu
+            for m in range(d):
+                ref[m] += gt[j] * sum(L["w_down"][e][m][f] * a[f] for f in range(F))
+        np.testing.assert_allclose(got["out"][t], ref, rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------ closed forms
+def test_hand_worked_top1_bias_flips_selection_not_gate():
+    """d=2, E=2, F=1, eps=0, worked by hand.
+
+    h = (1, -1): mean square 1, so x = g*h = (1, -2) for g = (1, 2).
+    W_r = [[1, .5], [0, 1]] gives z = (0, -2)  (the transpose would give (1, -1.5)).
+    b = (0, 3): s = (0, 1), expert 1 wins although z favours expert 0; margin 1.
+    gate = softmax(z)[1] = 1 / (1 + e^2)   (with s it would be e / (1 + e)).
+    Expert 1: G = 0.5*1 + 1*(-2) = -1.5, U = 2*1 + 0.25*(-2) = 1.5,
+    a = SiLU(-1.5)*1.5, y = W_down[1] a = (a, -3a), out = gate*y.
+    """
+    L = {
+        "hidden": np.array([[1.0, -1.0]]),
+        "gain": np.array([1.0, 2.0]),
+        "w_router": np.array([[1.0, 0.5], [0.0, 1.0]]),
+        "bias": np.array([0.0, 3.0]),
+        "w_gate": np.array([[[7.0, 7.0]], [[0.5, 1.0]]]),
+        "w_up": np.array([[[7.0, 7.0]], [[2.0, 0.25]]]),
+        "w_down": np.array([[[7.0], [7.0]], [[1.0], [-3.0]]]),
+    }
+    r = O.oracle_forward(L, k=1, eps=0.0)
+    np.testing.assert_allclose(r["x"], [[1.0, -2.0]], rtol=0, atol=0)
+    np.testing.assert_allclose(r["z"], [[0.0, -2.0]], rtol=0, atol=0)
+    assert r["sel"].tolist() == [[1]]
+    assert r["margin"][0] == pytest.approx(1.0, abs=0)
+    gate = 1.0 / (1.0 + math.exp(2.0))
+    assert r["gate"][0, 0] == pytest.approx(gate, rel=1e-15)
+    a = (-1.5 / (1.0 + math.exp(1.5))) * 1.5
+    np.testing.assert_allclose(r["out"], [[gate * a, gate * -3.0 * a]], rtol=1e-15)
+    assert r["counts"].tolist() == [0, 1]
+    assert r["offsets"].tolist() == [0, 0, 1]
+
+
+def test_hand_worked_top2_pair_softmax():
+    """E=3, k=2 with W_r = I, g = 1, h chosen with mean square 1:
+    h = (sqrt(1.5), -sqrt(1.5), 0) so x = h and z = h.  b = (0, 0, 5) makes
+    s = (1.2247, -1.2247, 5): the pair is (2, 0) in that order, and the gates
+    are softmax over (z_2, z_0) = (0, 1.2247): (1/(1+e^r), e^r/(1+e^r))."""
+    r15 = math.sqrt(1.5)
+    L = {
+        "hidden": np.array([[r15, -r15, 0.0]]),
+        "gain": np.ones(3),
+        "w_router": np.eye(3),
+        "bias": np.array([0.0, 0.0, 5.0]),
+        "w_gate": np.zeros((3, 2, 3)), "w_up": np.zeros((3, 2, 3)),
+        "w_down": np.zeros((3, 3, 2)),
+    }
+    r = O.oracle_forward(L, k=2, eps=0.0)
+    assert r["sel"].tolist() == [[2, 0]]
+    np.testing.assert_allclose(r["gate"][0], [1 / (1 + math.exp(r15)),
+                                              math.exp(r15) / (1 + math.exp(r15))], rtol=1e-14)
+    # margin: min(s_(1)-s_(2), s_(2)-s_(3)) = min(5 - r15, 2 r15)
+    assert r["margin"][0] == pytest.approx(min(5 - r15, 2 * r15), rel=1e-14)
+    assert r["gather"].tolist() == [0, 0]
+    assert r["scatter"].tolist() == [1, 0]      # assignment (t0, j0)=expert 2 -> slot 1
+
+
+def test_exact_ties_go_to_lower_index():
+    s = np.array([[1.0, 1.0, 0.0], [0.0, 2.0, 2.0], [3.0, 3.0, 3.0]])
+    sel1, m1 = O.select_topk(s, 1)
+    assert sel1[:, 0].tolist() == [0, 1, 0]
+    np.testing.assert_array_equal(m1, [0.0, 0.0, 0.0])
+    sel2, _ = O.select_topk(s, 2)
+    assert sel2.tolist() == [[0, 1], [1, 2], [0, 1]]
+
+
+def test_topk_agrees_with_lexsort_and_margin_definition():
+    rng = np.random.default_rng(3)
+    s = rng.standard_normal((200, 6))
+    for k in (1, 2, 3):
+        sel, margin = O.select_topk(s, k)
+        for t in range(s.shape[0]):
+            order = np.lexsort((np.arange(6), -s[t]))
+            assert sel[t].tolist() == order[:k].tolist()
+            srt = np.sort(s[t])[::-1]
+            gaps = [srt[i] - srt[i + 1] for i in range(k)]
+            assert margin[t] == pytest.approx(min(gaps), abs=0)
+
+
+def test_single_expert_margin_is_infinite():
+    _, m = O.select_topk(np.zeros((3, 1)), 1)
+    assert np.all(np.isinf(m))
+
+
+def test_gates_against_scipy_softmax_and_k_equals_E():
+    rng = np.random.default_rng(4)
+    z = 3 * rng.standard_normal((50, 5))
+    sel, _ = O.select_topk(z + rng.standard_normal(5), 1)
+    p = scipy.special.softmax(z, axis=1)
+    np.testing.assert_allclose(O.gates(z, sel)[:, 0], p[np.arange(50), sel[:, 0]], rtol=1e-13)
+    # k = E = 2: the renormalised pair is the full softmax
+    z2 = z[:, :2]
+    sel2, _ = O.select_topk(z2, 2)
+    p2 = scipy.special.softmax(z2, axis=1)
+    np.testing.assert_allclose(O.gates(z2, sel2), np.take_along_axis(p2, sel2, axis=1),
+                               rtol=1e-13)
+    # equal logits: every gate is 1/E for k = 1
+    np.testing.assert_allclose(O.gates(np.zeros((2, 4)), np.array([[1], [3]])), 0.25, rtol=0)
+    # large logits do not overflow
+    g = O.gates(np.array([[1000.0, 999.0, -1000.0]]), np.array([[0, 1]]))
+    np.testing.assert_allclose(g, [[1 / (1 + math.exp(-1)), 1 / (1 + math.exp(1))]], rtol=1e-14)
+
+
+def test_silu_against_scipy_expit():
+    v = np.linspace(-40, 40, 1001)
+    np.testing.assert_allclose(O.silu(v), v * scipy.special.expit(v), rtol=1e-14, atol=1e-300)
+    assert O.silu(np.array([-800.0]))[0] == 0.0
+
+
+def test_rmsnorm_against_torch_and_closed_form():
+    rng = np.random.default_rng(5)
+    H = rng.standard_normal((9, 33)) * 3.0
+    g = 1 + rng.standard_normal(33)
+    for eps in (1e-6, 0.5):
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(H), (33,), torch.from_numpy(g),
+                                           eps=eps).numpy()
+        np.testing.assert_allclose(O.rmsnorm(H, g, eps), ref, rtol=1e-14, atol=1e-15)
+    # constant row c: x = g * c / sqrt(c^2 + eps)
+    c, eps = -2.5, 0.75
+    x = O.rmsnorm(np.full((1, 4), c), np.array([1.0, 2.0, 3.0, 4.0]), eps)
+    np.testing.assert_allclose(x[0], np.array([1, 2, 3, 4]) * c / math.sqrt(c * c + eps),
+                               rtol=1e-15)
+    np.testing.assert_array_equal(O.rmsnorm(np.zeros((2, 3)), np.ones(3), 1e-6), 0.0)
+
+
+# ------------------------------------------------------ dense special case
+def test_single_expert_layer_is_dense_swiglu_ffn():
+    """E=1, k=1: the gate is softmax over one logit = 1 and the layer is the
+    dense SwiGLU FFN W_down(SiLU(W_gate x) * W_up x) on the RMSNorm output
+    (the digest's dense layers 0-2 and 27 are this case)."""
+    rng = np.random.default_rng(6)
+    T, d, F = 12, 16, 24
+    L = _rand_layer(rng, T, d, 1, F)
+    r = O.oracle_forward(L, k=1, eps=1e-6)
+    np.testing.assert_array_equal(r["gate"], 1.0)
+    tt = {k: torch.from_numpy(np.asarray(v, np.float64)) for k, v in L.items()}
+    x = torch.nn.functional.rms_norm(tt["hidden"], (d,), tt["gain"], eps=1e-6)
+    f = torch.nn.functional
+    ref = f.linear(f.silu(f.linear(x, tt["w_gate"][0])) * f.linear(x, tt["w_up"][0]),
+                   tt["w_down"][0]).numpy()
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-12, atol=1e-14)
+    assert r["gather"].tolist() == list(range(T))
+
+
+# ------------------------------------------------------------ permutation
+def test_permutation_against_bucket_sort_and_invariants():
+    rng = np.random.default_rng(7)
+    for T, E, k in [(50, 5, 2), (33, 4, 1), (1, 3, 1), (64, 16, 2)]:
+        sel = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+        counts, offsets = O.histogram(sel, E)
+        gather, scatter = O.permutation(sel)
+        buckets = [[] for _ in range(E)]
+        for t in range(T):
+            for j in range(k):
+                buckets[sel[t, j]].append(t * k + j)
+        assert counts.tolist() == [len(b) for b in buckets]
+        assert int(counts.sum()) == T * k and offsets[-1] == T * k
+        flat = [a for b in buckets for a in b]
+        assert gather.tolist() == [a // k for a in flat]
+        # bijection: scatter inverts the assignment order
+        assert sorted(scatter.tolist()) == list(range(T * k))
+        for p, a in enumerate(flat):
+            assert scatter[a] == p
+        # every token appears exactly k times; stable (increasing) within an expert
+        assert np.bincount(gather, minlength=T).tolist() == [k] * T
+        for e in range(E):
+            seg = gather[offsets[e]:offsets[e + 1]]
+            assert np.all(np.diff(seg) > 0)
+
+
+# ------------------------------------------------------------- invariants
+def test_invariants():
+    rng = np.random.default_rng(8)
+    T, d, E, F = 20, 12, 4, 10
+    L = _rand_layer(rng, T, d, E, F)
+    base = O.oracle_forward(L, k=2, eps=1e-6)
+    # determinism
+    again = O.oracle_forward(L, k=2, eps=1e-6)
+    np.testing.assert_array_equal(base["out"], again["out"])
+    # token permutation
+    p = rng.permutation(T)
+    Lp = dict(L, hidden=L["hidden"][p])
+    rp = O.oracle_forward(Lp, k=2, eps=1e-6)
+    np.testing.assert_array_equal(rp["sel"], base["sel"][p])
+    np.testing.assert_allclose(rp["out"], base["out"][p], rtol=1e-13, atol=1e-15)
+    # expert relabelling: new expert i is old expert q[i]
+    q = rng.permutation(E)
+    Lq = dict(L, w_router=L["w_router"][q], bias=L["bias"][q], w_gate=L["w_gate"][q],
+              w_up=L["w_up"][q], w_down=L["w_down"][q])
+    rq = O.oracle_forward(Lq, k=2, eps=1e-6)
+    np.testing.assert_array_equal(q[rq["sel"]], base["sel"])
+    np.testing.assert_allclose(rq["out"], base["out"], rtol=1e-13, atol=1e-15)
+    # linear in W_down
+    rs = O.oracle_forward(dict(L, w_down=L["w_down"] * -2.5), k=2, eps=1e-6)
+    np.testing.assert_allclose(rs["out"], -2.5 * base["out"], rtol=1e-13, atol=1e-15)
+    # zero input -> zero output, everyone on argmax(b)
+    r0 = O.oracle_forward(dict(L, hidden=np.zeros((T, d))), k=1, eps=1e-6)
+    np.testing.assert_array_equal(r0["out"], 0.0)
+    assert set(r0["sel"][:, 0].tolist()) == {int(np.argmax(L["bias"]))}
+    # a +1e4 bias routes every token to that expert
+    b = np.zeros(E)
+    b[2] = 1e4
+    rb = O.oracle_forward(dict(L, bias=b), k=1, eps=1e-6)
+    assert rb["counts"].tolist() == [0, 0, T, 0]
+    assert rb["gather"].tolist() == list(range(T))
+    # a sampled-token evaluation reproduces the full rows
+    tok = np.array([3, 0, 19, 7])
+    rt = O.oracle_forward(L, k=2, eps=1e-6, tokens=tok)
+    np.testing.assert_allclose(rt["out"], base["out"][tok], rtol=1e-14, atol=1e-16)
