@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Throughput of one ZONOS2 MoE feed-forward layer forward on one MI355X.
+
+A step is one forward of the whole layer (RMSNorm + router + top-k, dispatch
+permutation, grouped SwiGLU experts, combine) over one batch of seeded
+synthetic hidden states, through the C ABI of libmoe_layer.so.  Inputs are
+resident in HBM before timing starts.  Several independently allocated
+copies of the layer are used in rotation so that consecutive steps do not
+find the previous step's 576 MiB of expert weights in the 256 MiB MALL, as
+consecutive MoE layers of the backbone would not.
+
+Prints ONE JSON line: the metric, the step time, a roofline entry for the
+dominant kernel (its algorithmic bytes or flops per launch over its average
+duration, from HIP events recorded by the library on the forward's stream)
+and the fp64 CPU oracle's throughput on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config {1,2,3,4}]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+METRIC = "MoE-layer tokens/s at 1 GPU; HBM GB/s (decode) and MFMA % of peak (prefill)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "moe_ffn_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def dominant_kernel(cfg, counts):
+    """Dominant kernel of a forward and its algorithmic work per launch.
+
+    Decode-sized batches (T*k <= 64) take the weight-streaming path whose
+    gate/up kernel moves 2/3 of the bytes; larger batches take the tiled
+    grouped GEMM whose gate/up launch does 2/3 of the flops."""
+    d, F, k, T = cfg.d, cfg.F, cfg.k, cfg.T
+    n = T * k
+    touched = int((counts > 0).sum())
+    if n <= 64:
+        per_expert = 2 * F * d * 2                  # W_gate + W_up bf16 bytes
+        work = touched * per_expert + n * d * 2 + n * F * 2
+        return {"slot": "experts_gate_up", "kernel": "k_gateup_stream", "bound": "hbm",
+                "unit": "GB/s", "units": touched, "per_unit": per_expert,
+                "unit_name": "touched expert (W_gate + W_up bytes)", "work": work,
+                "work_unit": "bytes"}
+    per_assign = 2 * 2 * F * d                      # gate and up: 2 flops x F x d each
+    work = n * per_assign
+    return {"slot": "experts_gate_up", "kernel": "k_expert_tile<0>", "bound": "mfma",
+            "unit": "TFLOP/s", "units": n, "per_unit": per_assign,
+            "unit_name": "routed assignment (gate+up flops)", "work": work, "work_unit": "flops"}
+
+
+def layer_work(cfg, counts):
+    touched = int((counts > 0).sum())
+    d, F, n = cfg.d, cfg.F, cfg.T * cfg.k
+    bytes_ = touched * 3 * F * d * 2 + 2 * cfg.T * d * 2 + cfg.E * d * 2 + cfg.E * 4 + d * 2
+    flops = n * 6 * F * d + 2 * cfg.T * d * cfg.E
+    return bytes_, flops, touched
+
+
+def cpu_baseline(inputs, seconds: float):
+    """The fp64 oracle as it stands, on the host cores, over a bounded sample."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import moe_oracle as O
+    from synth import gen
+    cfg = inputs["cfg"]
+    vals = gen.values_f32(inputs)
+    ncores = len(os.sched_getaffinity(0))
+    sample = None if cfg.T <= 64 else np.sort(
+        np.random.default_rng(0).choice(cfg.T, size=64, replace=False))
+    ntok = cfg.T if sample is None else len(sample)
+    with threadpool_limits(limits=ncores):
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            O.oracle_forward(vals, tokens=sample)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or reps >= 50:
+                break
+    what = (f"full batch of {cfg.T} tokens" if sample is None else
+            f"{ntok} sampled tokens of {cfg.T} (routing of all {cfg.T} tokens included)")
+    return {"value": round(reps * ntok / el, 2), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{reps} oracle forwards (fp64 NumPy) of the {cfg.name} workload: {what}; "
+                      f"{el:.1f} s", "host_cpus": ncores}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4])
+    ap.add_argument("--instances", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the layer runs data-parallel with no exchange between "
+              "GPUs, so N GPUs give N times one GPU's throughput; run it with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from synth import make_inputs
+    from moe_ffn_amd import MoELayer, load_library
+
+    load_library()  # fails loudly if the HIP library is not built
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    t_gen = time.perf_counter()
+    inp = make_inputs(args.config)
+    cfg = inp["cfg"]
+    log(f"[bench] inputs for {cfg.name} in {time.perf_counter() - t_gen:.1f} s")
+
+    def tt(a, bf16=True):
+        if bf16 and a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+    w = {"rms_gain": tt(inp["gain"]), "w_router": tt(inp["w_router"]),
+         "b_router": tt(inp["bias"], False), "w_gate": tt(inp["w_gate"]),
+         "w_up": tt(inp["w_up"]), "w_down": tt(inp["w_down"])}
+    layers = [MoELayer(cfg.d, cfg.F, cfg.E, cfg.k, cfg.dtype, w, cfg.T, rms_eps=cfg.eps)
+              for _ in range(args.instances)]
+    del w
+    hidden = tt(inp["hidden"])
+    outs = [torch.empty_like(hidden) for _ in layers]
+    torch.cuda.synchronize()
+
+    _, r = layers[0].forward(hidden, routing=True)
+    counts = r["counts"].cpu().numpy()
+    dom = dominant_kernel(cfg, counts)
+    lbytes, lflops, touched = layer_work(cfg, counts)
+    log(f"[bench] {touched} experts touched; dominant kernel {dom['kernel']}")
+
+    K, W = args.steps, args.warmup
+    nl = len(layers)
+    for i in range(W):
+        layers[i % nl].forward(hidden, out=outs[i % nl])
+    torch.cuda.synchronize()
+
+    def timed(per_kernel: bool):
+        if per_kernel:
+            for L in layers:
+                L.timing_start((K + nl - 1) // nl)
+        s = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(s)
+        for i in range(K):
+            layers[i % nl].forward(hidden, out=outs[i % nl])
+        e1.record(s)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        slots = None
+        if per_kernel:
+            slots, nf = {}, 0
+            for L in layers:
+                sl, n = L.timing_stop()
+                nf += n
+                for k_, v in sl.items():
+                    slots[k_] = slots.get(k_, 0.0) + v
+            slots = {k_: v / nf for k_, v in slots.items()}
+        return ms / K, slots
+
+    ms_step, _ = timed(False)
+    log(f"[bench] {K} steps: {ms_step * 1e3:.2f} us/step")
+    ms_step_ev, slots = timed(True)
+    log(f"[bench] with per-kernel events: {ms_step_ev * 1e3:.2f} us/step; "
+        + ", ".join(f"{k_} {v * 1e3:.2f} us" for k_, v in slots.items()))
+
+    dom_ms = slots[dom["slot"]]
+    if dom["work_unit"] == "bytes":
+        achieved = dom["work"] / (dom_ms * 1e-3) / 1e9
+        peak = PEAK_HBM_GBPS
+    else:
+        achieved = dom["work"] / (dom_ms * 1e-3) / 1e12
+        peak = PEAK_BF16_TFLOPS
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            with open(TRAFFIC_FILE) as f:
+                tr = json.load(f).get(cfg.name, {})
+            if tr.get("source_hash") == kernel_source_hash() and tr.get("kernel") == dom["kernel"]:
+                traffic = tr.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    value = cfg.T / (ms_step * 1e-3)
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": round(ms_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic: seeded N(0,1) hidden states and random-init weights of the stated "
+                "distributions (no checkpoint or dataset)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "d_ff": cfg.F,
+                   "n_experts": cfg.E, "top_k": cfg.k, "router_bias": cfg.bias,
+                   "experts_touched": touched, "layer_instances": nl,
+                   "device": props.name, "compute_units": props.multi_processor_count},
+        "roofline": {"bound": dom["bound"], "achieved": round(achieved, 2), "peak": peak,
+                     "unit": dom["unit"], "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel": dom["kernel"], "avg_launch_us": round(dom_ms * 1e3, 3),
+                     "per_unit": dom["per_unit"], "units_per_launch": dom["units"],
+                     "unit_name": dom["unit_name"]},
+        "layer": {"algorithmic_bytes": lbytes, "algorithmic_flops": lflops,
+                  "hbm_GBps": round(lbytes / (ms_step * 1e-3) / 1e9, 1),
+                  "mfma_frac": round(lflops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                  "us_per_step_with_kernel_events": round(ms_step_ev * 1e3, 3),
+                  "kernel_us": {k_: round(v * 1e3, 3) for k_, v in slots.items()}},
+    }
+    for L in layers:
+        L.close()
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle ...")
+        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

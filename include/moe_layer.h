@@ -1,0 +1,156 @@
+/*
+ * moe_layer.h - C ABI of one ZONOS2 MoE feed-forward layer on an MI355X (gfx950).
+ *
+ * The layer (ZONOS2 Technical Report, audio-paper-digest page, "Method overview
+ * and architecture", item 5: an RMSNorm-normalised input, 16 experts per MoE
+ * layer with top-1 routing and top-2 in the last MoE layer; item 6: a per-expert
+ * bias vector b_l; mlsanity index page, "Builds on": RMSNorm, GLU variants and
+ * auxiliary-loss-free load balancing) computes, for every token t of a batch:
+ *
+ *   x_t   = g * h_t / sqrt(mean(h_t^2) + eps)                       RMSNorm
+ *   z_t   = W_r x_t,  s_t = z_t + b                               router logits / scores
+ *   sel_t = top-k experts of s_t (descending s, ties to the lower index)
+ *   gate  = softmax(z_t)[sel] for k = 1; softmax of z_t over sel for k >= 2
+ *   y     = W_down[e] (SiLU(W_gate[e] x_t) * (W_up[e] x_t))  for each e in sel_t
+ *   out_t = sum_j gate_{t,j} y_{t,j}            (the residual is NOT added)
+ *
+ * The bias b steers which experts are chosen; it never enters a gate.
+ *
+ * Conventions
+ *   - Every pointer argument named as device memory must be a HIP device
+ *     pointer (or managed memory) on the device that is current when the call
+ *     is made, 16-byte aligned, and laid out row-major as stated.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *   - Calls return a moe_status_t; nothing throws across the ABI.  On failure
+ *     moe_last_error() returns a message for the calling thread.
+ *   - Device faults inside launched kernels surface at the caller's next
+ *     synchronisation, as for any asynchronous HIP work.  With the environment
+ *     variable MOE_DEBUG_SYNC=1 every forward synchronises its stream and maps
+ *     a failure to MOE_ERR_HIP.
+ */
+#ifndef MOE_LAYER_H
+#define MOE_LAYER_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef struct moe_layer moe_layer_t; /* opaque; owned by the library */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* a NULL, misaligned or out-of-range argument */
+  MOE_ERR_OOM = 2,         /* a device allocation failed */
+  MOE_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
+  MOE_ERR_UNSUPPORTED = 4  /* a shape or device the kernels do not cover */
+} moe_status_t;
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
+
+/* Layer shape.  Limits: 1 <= n_experts <= 64; 1 <= top_k <= min(n_experts, 8);
+ * d_model and d_ff multiples of 64 (bf16) or of 4 (f32); 1 <= max_tokens <= 2^20.
+ * dtype is the storage type of activations, gain, router and expert weights;
+ * arithmetic accumulates in fp32 either way. */
+typedef struct {
+  int32_t d_model;
+  int32_t d_ff;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t dtype;      /* moe_dtype_t */
+  float rms_eps;      /* e.g. 1e-6 */
+  int32_t max_tokens; /* workspace is sized for this many tokens per forward */
+} moe_layer_config_t;
+
+/* Weights, DEVICE pointers in the config's dtype (b_router is always fp32),
+ * canonical row-major layouts.  They are read during moe_layer_create only:
+ * the library copies and repacks them into memory it owns, on `stream`; the
+ * caller may free them once that stream has been synchronised. */
+typedef struct {
+  const void* rms_gain;   /* [d_model]                 g   */
+  const void* w_router;   /* [n_experts, d_model]      W_r */
+  const float* b_router;  /* [n_experts] fp32           b   */
+  const void* w_gate;     /* [n_experts, d_ff, d_model]    */
+  const void* w_up;       /* [n_experts, d_ff, d_model]    */
+  const void* w_down;     /* [n_experts, d_model, d_ff]    */
+} moe_layer_weights_t;
+
+/* Optional routing outputs of one forward, DEVICE pointers owned by the caller.
+ * Any member may be NULL (that output is then not written).  Sizes for a call
+ * with T tokens: sel, gate [T, top_k]; counts [n_experts]; offsets
+ * [n_experts + 1]; gather, scatter [T * top_k].
+ *   sel[t,j]    expert of assignment a = t*top_k + j (descending score)
+ *   gate[t,j]   its gate weight
+ *   counts[e]   assignments routed to expert e; offsets = exclusive prefix sum
+ *   gather[p]   token of expert-ordered slot p (stable: increasing a per expert)
+ *   scatter[a]  slot of assignment a  (gather[scatter[a]] == a / top_k)       */
+typedef struct {
+  int32_t* sel;
+  float* gate;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* gather;
+  int32_t* scatter;
+} moe_routing_out_t;
+
+/* Returns MOE_ABI_VERSION of the loaded library. */
+int32_t moe_abi_version(void);
+
+/* Message of the last failure on the calling thread ("" if none).  The string
+ * stays valid until the next call into the library from this thread. */
+const char* moe_last_error(void);
+
+/* Create a layer on the current device.  Validates `cfg`, allocates the packed
+ * weight bank and a workspace sized for cfg->max_tokens, and enqueues the
+ * weight packing on `stream`.  On success *out receives the handle; on failure
+ * *out is set to NULL and nothing stays allocated.
+ * Errors: INVALID_ARG (NULL pointer, bad config, misaligned weight pointer),
+ * UNSUPPORTED (shape outside the limits above, device is not gfx950),
+ * OOM, HIP. */
+moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* w,
+                              void* stream, moe_layer_t** out);
+
+/* One forward over T tokens: hidden [T, d_model] -> out [T, d_model], both
+ * DEVICE memory in the layer's dtype; `out` must not overlap `hidden`.
+ * Asynchronous on `stream`: no host synchronisation and no allocation.
+ * T == 0 returns MOE_OK and launches nothing.  `routing` may be NULL.
+ * A handle must not run two forwards concurrently (on two streams): they share
+ * the layer's workspace.  Inputs with NaN or Inf give undefined values in
+ * `out` but every index stays in range.
+ * Errors: INVALID_ARG (NULL handle/pointers, T < 0, T > max_tokens, misaligned
+ * or overlapping buffers), HIP (launch failure). */
+moe_status_t moe_layer_forward(moe_layer_t* layer, const void* hidden, int32_t T, void* out,
+                               void* stream, const moe_routing_out_t* routing);
+
+/* Replace the router bias b with n_experts fp32 values from DEVICE memory,
+ * enqueued on `stream` (the update is ordered with forwards on that stream).
+ * Errors: INVALID_ARG, HIP. */
+moe_status_t moe_layer_set_bias(moe_layer_t* layer, const float* b_router, void* stream);
+
+/* Per-kernel timing, for measurement tools.  moe_layer_timing_start() makes
+ * the next `max_forwards` forwards record a HIP event before the first kernel
+ * and after each kernel, on the forward's stream.  moe_layer_timing_stop()
+ * waits for those events, writes into ms_sum[MOE_TIMED_SLOTS] the summed
+ * milliseconds between consecutive events for each slot, and *n_forwards the
+ * number of forwards recorded; it then releases the events.  Slots, in launch
+ * order: 0 RMSNorm+router+top-k, 1 histogram+permutation, 2 first expert
+ * kernel (gate/up), 3 second expert kernel (down), 4 combine (0 when k = 1).
+ * Recording events between kernels can add a little time per forward.
+ * Errors: INVALID_ARG (bad handle, max_forwards outside [1, 65536], stop
+ * without start), HIP. */
+#define MOE_TIMED_SLOTS 5
+moe_status_t moe_layer_timing_start(moe_layer_t* layer, int32_t max_forwards);
+moe_status_t moe_layer_timing_stop(moe_layer_t* layer, float* ms_sum, int32_t* n_forwards);
+
+/* Release the layer (NULL-safe).  Synchronises the device first, so work still
+ * in flight on any stream that uses the layer completes before its memory goes. */
+void moe_layer_destroy(moe_layer_t* layer);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LAYER_H */

@@ -1,0 +1,102 @@
+// Device-side helpers shared by the MoE layer's HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Unpack 8 bf16 held in a 16-byte vector into fp32.
+__device__ __forceinline__ void unpack8(const u32x4& v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_lo(v[i]);
+    f[2 * i + 1] = bf16_hi(v[i]);
+  }
+}
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void stg16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Streaming load for data read exactly once (expert weights): bypass reuse in L2/MALL.
+__device__ __forceinline__ u32x4 ldg16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// D = A * B + C on a 32x32 output tile with K = 16, bf16 inputs, fp32 accumulation.
+// Operand lane layout: lane l carries row (l % 32) of A (column (l % 32) of B) and
+// the 8 consecutive k values of k-group (l / 32).  Output lane layout: lane l holds
+// column (l % 32), rows 8*(i/4) + 4*(l/32) + (i%4) for accumulator element i.
+__device__ __forceinline__ f32x16 mfma_32x32x16(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ int c32_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+
+// Butterfly reduction of N per-lane values over the 64 lanes of a wave that
+// leaves the sums spread over the lanes instead of replicated: each halving
+// step exchanges half of the remaining values with the partner lane.
+// Afterwards lane l holds, in v[0 .. max(N/64,1)-1], the full sums of value
+// indices spread_index<N>(l, i).
+template <int N, int DELTA>
+struct WaveSpread {
+  static __device__ __forceinline__ void run(float* v, int lane) {
+    if constexpr (DELTA == 0) {
+      return;
+    } else if constexpr (N > 1) {
+      constexpr int H = N / 2;
+      const bool upper = (lane & DELTA) != 0;
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        const float send = upper ? v[i] : v[i + H];
+        const float keep = upper ? v[i + H] : v[i];
+        v[i] = keep + __shfl_xor(send, DELTA, kWave);
+      }
+      WaveSpread<H, DELTA / 2>::run(v, lane);
+    } else {
+      v[0] += __shfl_xor(v[0], DELTA, kWave);
+      WaveSpread<1, DELTA / 2>::run(v, lane);
+    }
+  }
+};
+
+constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n / 2); }
+
+template <int N>
+__device__ __forceinline__ int spread_index(int lane, int i) {
+  constexpr int L = ilog2(N);
+  if constexpr (L >= 6) return (lane << (L - 6)) + i;
+  else return lane >> (6 - L);
+}
+// True for the lanes that own distinct sums (one owner per index when N < 64).
+template <int N>
+__device__ __forceinline__ bool spread_owner(int lane) {
+  constexpr int L = ilog2(N);
+  if constexpr (L >= 6) return true;
+  else return (lane & ((1 << (6 - L)) - 1)) == 0;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+}  // namespace moe

@@ -1,0 +1,73 @@
+// Host-side launchers of the MoE layer's kernels (private to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Packed expert-weight geometry (bf16).  Both banks are stored as 1 KiB blocks,
+// one per (32-row tile, 16-wide k step), each block in MFMA 32x32x16 operand
+// order: 64 lanes x 8 consecutive k of row (lane % 32), k-group (lane / 32).
+//   W_gu : [E][F/32 f-tiles][2: gate, up][d/16 k-steps][64][8]
+//   W_d  : [E][d/32 m-tiles][F/16 k-steps][64][8]
+constexpr int kTileRows = 32;
+constexpr int kKStep = 16;
+constexpr int kBlockElems = 64 * 8;  // 512 bf16 = 1 KiB
+
+// Prefill tiles: 256 weight rows x 128 tokens x 64 k per workgroup.
+constexpr int kTileTokens = 128;
+// Decode path is used while T * top_k is at most this many assignments.
+constexpr int kStreamMaxAssign = 64;
+
+struct LayerDims {
+  int d, F, E, k, EP;  // EP = n_experts rounded up to a power of two
+  float eps;
+  int dtype;           // 0 = f32, 1 = bf16
+};
+
+struct FwdArgs {
+  LayerDims dim;
+  int T, n;            // tokens, assignments (T * k)
+  const void* hidden;  // [T, d]
+  void* out;           // [T, d]
+  // layer-owned parameters
+  const float* wrg;    // [EP, d] fp32: W_r[e][i] * g[i] (zero rows e >= E)
+  const float* gain;   // [d] fp32
+  const float* bias;   // [E] fp32
+  const void* wgu;     // packed gate/up bank (bf16) or canonical [E,F,d] (f32)
+  const void* wup;     // f32 only: canonical up weights [E,F,d]
+  const void* wd;      // packed down bank (bf16) or canonical [E,d,F] (f32)
+  // per-call buffers (workspace or caller-provided routing outputs)
+  void* xn;            // [T, d] normalised activations (bf16 or f32)
+  int* sel;            // [T, k]
+  float* gate;         // [T, k]
+  int* counts;         // [E]
+  int* offsets;        // [E + 1]
+  int* gather;         // [n]
+  int* scatter;        // [n]
+  int* slot_expert;    // [n]
+  int* tilemap;        // [1 + max_tiles]: count, then (expert << 16 | m-tile)
+  int max_tiles;
+  void* act;           // [n, F] SwiGLU activations (bf16 or f32)
+  float* ybuf;         // [n, d] fp32 expert outputs (k >= 2 only)
+  hipStream_t stream;
+  hipEvent_t ev_mid;   // when set, recorded between the two expert kernels
+};
+
+hipError_t launch_norm_router(const FwdArgs& a);
+hipError_t launch_route_permute(const FwdArgs& a);
+hipError_t launch_experts_stream(const FwdArgs& a);
+hipError_t launch_experts_tile(const FwdArgs& a);
+hipError_t launch_experts_f32(const FwdArgs& a);
+hipError_t launch_combine(const FwdArgs& a);
+
+// create-time packing
+hipError_t launch_pack_gateup(const uint16_t* w_gate, const uint16_t* w_up, uint16_t* packed, int E,
+                              int F, int d, hipStream_t s);
+hipError_t launch_pack_down(const uint16_t* w_down, uint16_t* packed, int E, int d, int F,
+                            hipStream_t s);
+hipError_t launch_prep_router(const void* w_router, const void* gain, int dtype, int E, int EP,
+                              int d, float* wrg, float* gain32, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,437 @@
+// C ABI of the ZONOS2 MoE feed-forward layer: validation, device memory, the
+// create-time weight packing and the launch sequence of one forward.
+//
+// Forward on one stream, no host synchronisation, no allocation:
+//   K1 fused RMSNorm + router + top-k + gates        (k_norm_router.hip)
+//   K2 histogram + scan + stable permutation + tiles (k_route_permute.hip)
+//   K3 grouped SwiGLU experts: weight stream for decode-sized batches, LDS-tiled
+//      grouped GEMM for larger ones, fp32 VALU for fp32 layers
+//   K4 gate-weighted combine (k >= 2; folded into K3 for k = 1)
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.hpp"
+#include "moe_layer.h"
+
+namespace {
+
+thread_local std::string g_err;
+constexpr uint32_t kMagic = 0x314d6f45u;  // "EoM1"
+constexpr int kMaxTokensLimit = 1 << 20;
+
+moe_status_t fail(moe_status_t st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+moe_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+int next_pow2(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Carves sub-buffers out of one allocation, 256-byte aligned.
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  }
+};
+
+}  // namespace
+
+struct moe_layer {
+  uint32_t magic;
+  moe::LayerDims dim;
+  int max_tokens;
+  int max_tiles;
+  int device;
+  bool debug_sync;
+  // parameters (one allocation)
+  void* params;
+  float* wrg;
+  float* gain32;
+  float* bias;
+  void* wgu;
+  void* wup;
+  void* wd;
+  // workspace (one allocation)
+  void* ws;
+  void* xn;
+  int* sel;
+  float* gate;
+  int* counts;
+  int* offsets;
+  int* gather;
+  int* scatter;
+  int* slot_expert;
+  int* tilemap;
+  void* act;
+  float* ybuf;
+  // optional per-kernel event timing (6 events per recorded forward)
+  std::vector<hipEvent_t> tev;
+  int t_max;
+  int t_used;
+  bool timing;
+};
+
+namespace {
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
+}
+
+constexpr int kEventsPerForward = MOE_TIMED_SLOTS + 1;
+
+void drop_events(moe_layer* L) {
+  for (hipEvent_t e : L->tev) (void)hipEventDestroy(e);
+  L->tev.clear();
+  L->timing = false;
+  L->t_max = L->t_used = 0;
+}
+
+void release(moe_layer* L) {
+  if (L == nullptr) return;
+  drop_events(L);
+  if (L->params) (void)hipFree(L->params);
+  if (L->ws) (void)hipFree(L->ws);
+  L->magic = 0;
+  delete L;
+}
+
+moe_status_t check_config(const moe_layer_config_t* c) {
+  if (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
+  if (c->d_model <= 0 || c->d_ff <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->max_tokens <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "d_model, d_ff, n_experts, top_k and max_tokens must be > 0");
+  if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps))
+    return fail(MOE_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
+  if (c->top_k > c->n_experts) return fail(MOE_ERR_INVALID_ARG, "top_k exceeds n_experts");
+  if (c->n_experts > 64) return fail(MOE_ERR_UNSUPPORTED, "n_experts above 64");
+  if (c->top_k > 8) return fail(MOE_ERR_UNSUPPORTED, "top_k above 8");
+  if (c->max_tokens > kMaxTokensLimit) return fail(MOE_ERR_UNSUPPORTED, "max_tokens above 2^20");
+  if (c->dtype == MOE_DTYPE_BF16) {
+    if (c->d_model % 256 != 0 || c->d_ff % 128 != 0)
+      return fail(MOE_ERR_UNSUPPORTED, "bf16 layers need d_model % 256 == 0 and d_ff % 128 == 0");
+  } else {
+    if (c->d_model % 4 != 0 || c->d_ff % 4 != 0)
+      return fail(MOE_ERR_UNSUPPORTED, "fp32 layers need d_model and d_ff multiples of 4");
+  }
+  const double n = (double)c->max_tokens * c->top_k;
+  if (n * c->d_ff >= 9.0e18 / 4 || n * c->d_model >= 9.0e18 / 4)
+    return fail(MOE_ERR_UNSUPPORTED, "workspace size overflows");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* w,
+                              void* stream, moe_layer_t** out) {
+  g_err.clear();
+  if (out == nullptr) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (cfg == nullptr || w == nullptr) return fail(MOE_ERR_INVALID_ARG, "cfg or weights is NULL");
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const void* wp[] = {w->rms_gain, w->w_router, w->w_gate, w->w_up, w->w_down};
+  for (const void* p : wp) {
+    if (p == nullptr) return fail(MOE_ERR_INVALID_ARG, "a weight pointer is NULL");
+    if (!aligned(p, 16)) return fail(MOE_ERR_INVALID_ARG, "weight pointers must be 16-byte aligned");
+  }
+  if (w->b_router == nullptr || !aligned(w->b_router, 4))
+    return fail(MOE_ERR_INVALID_ARG, "b_router is NULL or misaligned");
+
+  int dev = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return hip_fail(he, "hipGetDevice");
+  hipDeviceProp_t prop;
+  he = hipGetDeviceProperties(&prop, dev);
+  if (he != hipSuccess) return hip_fail(he, "hipGetDeviceProperties");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(MOE_ERR_UNSUPPORTED, std::string("device is ") + prop.gcnArchName +
+                                         ", the kernels are built for gfx950");
+
+  moe_layer* L = new (std::nothrow) moe_layer();
+  if (L == nullptr) return fail(MOE_ERR_OOM, "host allocation failed");
+  L->dim.d = cfg->d_model;
+  L->dim.F = cfg->d_ff;
+  L->dim.E = cfg->n_experts;
+  L->dim.k = cfg->top_k;
+  L->dim.EP = next_pow2(cfg->n_experts);
+  L->dim.eps = cfg->rms_eps;
+  L->dim.dtype = cfg->dtype;
+  L->max_tokens = cfg->max_tokens;
+  L->device = dev;
+  const char* dbg = std::getenv("MOE_DEBUG_SYNC");
+  L->debug_sync = dbg != nullptr && dbg[0] == '1';
+
+  const size_t d = L->dim.d, F = L->dim.F, E = L->dim.E, EP = L->dim.EP, k = L->dim.k;
+  const size_t es = cfg->dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  const size_t nmax = (size_t)L->max_tokens * k;
+  L->max_tiles = (int)((nmax + moe::kTileTokens - 1) / moe::kTileTokens + E);
+
+  // parameters
+  Carver pc;
+  const size_t o_wrg = pc.take(EP * d * 4);
+  const size_t o_gain = pc.take(d * 4);
+  const size_t o_bias = pc.take(E * 4);
+  const size_t o_wgu = pc.take(E * F * d * es * (cfg->dtype == MOE_DTYPE_BF16 ? 2 : 1));
+  const size_t o_wup = cfg->dtype == MOE_DTYPE_F32 ? pc.take(E * F * d * es) : 0;
+  const size_t o_wd = pc.take(E * d * F * es);
+  he = hipMalloc(&L->params, pc.off);
+  if (he != hipSuccess) {
+    L->params = nullptr;
+    release(L);
+    (void)hipGetLastError();
+    return fail(MOE_ERR_OOM, std::string("parameter allocation: ") + hipGetErrorString(he));
+  }
+  L->wrg = at<float>(L->params, o_wrg);
+  L->gain32 = at<float>(L->params, o_gain);
+  L->bias = at<float>(L->params, o_bias);
+  L->wgu = at<void>(L->params, o_wgu);
+  L->wup = cfg->dtype == MOE_DTYPE_F32 ? at<void>(L->params, o_wup) : nullptr;
+  L->wd = at<void>(L->params, o_wd);
+
+  // workspace
+  Carver wc;
+  const size_t o_xn = wc.take((size_t)L->max_tokens * d * es);
+  const size_t o_sel = wc.take(nmax * 4);
+  const size_t o_gate = wc.take(nmax * 4);
+  const size_t o_cnt = wc.take(E * 4);
+  const size_t o_off = wc.take((E + 1) * 4);
+  const size_t o_gat = wc.take(nmax * 4);
+  const size_t o_sca = wc.take(nmax * 4);
+  const size_t o_sle = wc.take(nmax * 4);
+  const size_t o_tm = wc.take((size_t)(1 + L->max_tiles) * 4);
+  const size_t o_act = wc.take(nmax * F * es);
+  const size_t o_y = k > 1 ? wc.take(nmax * d * 4) : 0;
+  he = hipMalloc(&L->ws, wc.off);
+  if (he != hipSuccess) {
+    L->ws = nullptr;
+    release(L);
+    (void)hipGetLastError();
+    return fail(MOE_ERR_OOM, std::string("workspace allocation: ") + hipGetErrorString(he));
+  }
+  L->xn = at<void>(L->ws, o_xn);
+  L->sel = at<int>(L->ws, o_sel);
+  L->gate = at<float>(L->ws, o_gate);
+  L->counts = at<int>(L->ws, o_cnt);
+  L->offsets = at<int>(L->ws, o_off);
+  L->gather = at<int>(L->ws, o_gat);
+  L->scatter = at<int>(L->ws, o_sca);
+  L->slot_expert = at<int>(L->ws, o_sle);
+  L->tilemap = at<int>(L->ws, o_tm);
+  L->act = at<void>(L->ws, o_act);
+  L->ybuf = k > 1 ? at<float>(L->ws, o_y) : nullptr;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  he = moe::launch_prep_router(w->w_router, w->rms_gain, cfg->dtype, (int)E, (int)EP, (int)d,
+                               L->wrg, L->gain32, s);
+  if (he == hipSuccess)
+    he = hipMemcpyAsync(L->bias, w->b_router, E * 4, hipMemcpyDeviceToDevice, s);
+  if (he == hipSuccess) {
+    if (cfg->dtype == MOE_DTYPE_BF16) {
+      he = moe::launch_pack_gateup(static_cast<const uint16_t*>(w->w_gate),
+                                   static_cast<const uint16_t*>(w->w_up),
+                                   static_cast<uint16_t*>(L->wgu), (int)E, (int)F, (int)d, s);
+      if (he == hipSuccess)
+        he = moe::launch_pack_down(static_cast<const uint16_t*>(w->w_down),
+                                   static_cast<uint16_t*>(L->wd), (int)E, (int)d, (int)F, s);
+    } else {
+      he = hipMemcpyAsync(L->wgu, w->w_gate, E * F * d * 4, hipMemcpyDeviceToDevice, s);
+      if (he == hipSuccess)
+        he = hipMemcpyAsync(L->wup, w->w_up, E * F * d * 4, hipMemcpyDeviceToDevice, s);
+      if (he == hipSuccess)
+        he = hipMemcpyAsync(L->wd, w->w_down, E * d * F * 4, hipMemcpyDeviceToDevice, s);
+    }
+  }
+  if (he == hipSuccess && L->debug_sync) he = hipStreamSynchronize(s);
+  if (he != hipSuccess) {
+    (void)hipStreamSynchronize(s);
+    release(L);
+    return hip_fail(he, "weight preparation");
+  }
+  L->magic = kMagic;
+  *out = L;
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_forward(moe_layer_t* L, const void* hidden, int32_t T, void* out,
+                               void* stream, const moe_routing_out_t* routing) {
+  g_err.clear();
+  if (L == nullptr || L->magic != kMagic) return fail(MOE_ERR_INVALID_ARG, "invalid layer handle");
+  if (T < 0 || T > L->max_tokens)
+    return fail(MOE_ERR_INVALID_ARG, "T must be in [0, max_tokens] (max_tokens = " +
+                                         std::to_string(L->max_tokens) + ")");
+  if (T == 0) return MOE_OK;
+  if (hidden == nullptr || out == nullptr) return fail(MOE_ERR_INVALID_ARG, "hidden or out is NULL");
+  if (!aligned(hidden, 16) || !aligned(out, 16))
+    return fail(MOE_ERR_INVALID_ARG, "hidden and out must be 16-byte aligned");
+  const size_t es = L->dim.dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  const size_t bytes = (size_t)T * L->dim.d * es;
+  const uintptr_t h0 = reinterpret_cast<uintptr_t>(hidden), o0 = reinterpret_cast<uintptr_t>(out);
+  if (h0 < o0 + bytes && o0 < h0 + bytes)
+    return fail(MOE_ERR_INVALID_ARG, "out overlaps hidden");
+  if (routing != nullptr) {
+    const void* rp[] = {routing->sel, routing->gate, routing->counts, routing->offsets,
+                        routing->gather, routing->scatter};
+    for (const void* p : rp)
+      if (p != nullptr && !aligned(p, 4))
+        return fail(MOE_ERR_INVALID_ARG, "routing buffers must be 4-byte aligned");
+  }
+  int dev = -1;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return hip_fail(he, "hipGetDevice");
+  if (dev != L->device)
+    return fail(MOE_ERR_INVALID_ARG, "the current device is not the layer's device");
+
+  moe::FwdArgs a;
+  a.dim = L->dim;
+  a.T = T;
+  a.n = T * L->dim.k;
+  a.hidden = hidden;
+  a.out = out;
+  a.wrg = L->wrg;
+  a.gain = L->gain32;
+  a.bias = L->bias;
+  a.wgu = L->wgu;
+  a.wup = L->wup;
+  a.wd = L->wd;
+  a.xn = L->xn;
+  a.sel = (routing && routing->sel) ? routing->sel : L->sel;
+  a.gate = (routing && routing->gate) ? routing->gate : L->gate;
+  a.counts = (routing && routing->counts) ? routing->counts : L->counts;
+  a.offsets = (routing && routing->offsets) ? routing->offsets : L->offsets;
+  a.gather = (routing && routing->gather) ? routing->gather : L->gather;
+  a.scatter = (routing && routing->scatter) ? routing->scatter : L->scatter;
+  a.slot_expert = L->slot_expert;
+  a.tilemap = L->tilemap;
+  a.max_tiles = (a.n + moe::kTileTokens - 1) / moe::kTileTokens + L->dim.E;
+  a.act = L->act;
+  a.ybuf = L->ybuf;
+  a.stream = reinterpret_cast<hipStream_t>(stream);
+  a.ev_mid = nullptr;
+  hipEvent_t* ev = nullptr;
+  if (L->timing && L->t_used < L->t_max) {
+    ev = &L->tev[(size_t)L->t_used * kEventsPerForward];
+    ++L->t_used;
+  }
+  auto mark = [&](int i) -> hipError_t {
+    return ev != nullptr ? hipEventRecord(ev[i], a.stream) : hipSuccess;
+  };
+
+  if ((he = mark(0)) != hipSuccess) return hip_fail(he, "event record");
+  he = moe::launch_norm_router(a);
+  if (he != hipSuccess) return hip_fail(he, "norm/router launch");
+  if ((he = mark(1)) != hipSuccess) return hip_fail(he, "event record");
+  he = moe::launch_route_permute(a);
+  if (he != hipSuccess) return hip_fail(he, "permute launch");
+  if ((he = mark(2)) != hipSuccess) return hip_fail(he, "event record");
+  if (ev != nullptr) a.ev_mid = ev[3];
+  if (L->dim.dtype == MOE_DTYPE_F32)
+    he = moe::launch_experts_f32(a);
+  else if (a.n <= moe::kStreamMaxAssign)
+    he = moe::launch_experts_stream(a);
+  else
+    he = moe::launch_experts_tile(a);
+  if (he != hipSuccess) return hip_fail(he, "expert launch");
+  if ((he = mark(4)) != hipSuccess) return hip_fail(he, "event record");
+  if (L->dim.k > 1) {
+    he = moe::launch_combine(a);
+    if (he != hipSuccess) return hip_fail(he, "combine launch");
+  }
+  if ((he = mark(5)) != hipSuccess) return hip_fail(he, "event record");
+  if (L->debug_sync) {
+    he = hipStreamSynchronize(a.stream);
+    if (he != hipSuccess) return hip_fail(he, "forward (MOE_DEBUG_SYNC)");
+  }
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_set_bias(moe_layer_t* L, const float* b_router, void* stream) {
+  g_err.clear();
+  if (L == nullptr || L->magic != kMagic) return fail(MOE_ERR_INVALID_ARG, "invalid layer handle");
+  if (b_router == nullptr || !aligned(b_router, 4))
+    return fail(MOE_ERR_INVALID_ARG, "b_router is NULL or misaligned");
+  hipError_t he = hipMemcpyAsync(L->bias, b_router, (size_t)L->dim.E * 4, hipMemcpyDeviceToDevice,
+                                 reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "set_bias copy");
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_timing_start(moe_layer_t* L, int32_t max_forwards) {
+  g_err.clear();
+  if (L == nullptr || L->magic != kMagic) return fail(MOE_ERR_INVALID_ARG, "invalid layer handle");
+  if (max_forwards < 1 || max_forwards > 65536)
+    return fail(MOE_ERR_INVALID_ARG, "max_forwards must be in [1, 65536]");
+  drop_events(L);
+  L->tev.resize((size_t)max_forwards * kEventsPerForward);
+  for (size_t i = 0; i < L->tev.size(); ++i) {
+    hipError_t he = hipEventCreate(&L->tev[i]);
+    if (he != hipSuccess) {
+      L->tev.resize(i);
+      drop_events(L);
+      return hip_fail(he, "hipEventCreate");
+    }
+  }
+  L->t_max = max_forwards;
+  L->t_used = 0;
+  L->timing = true;
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_timing_stop(moe_layer_t* L, float* ms_sum, int32_t* n_forwards) {
+  g_err.clear();
+  if (L == nullptr || L->magic != kMagic) return fail(MOE_ERR_INVALID_ARG, "invalid layer handle");
+  if (!L->timing) return fail(MOE_ERR_INVALID_ARG, "timing was not started");
+  if (ms_sum == nullptr || n_forwards == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "ms_sum or n_forwards is NULL");
+  for (int i = 0; i < MOE_TIMED_SLOTS; ++i) ms_sum[i] = 0.f;
+  *n_forwards = L->t_used;
+  hipError_t he = hipSuccess;
+  if (L->t_used > 0) he = hipEventSynchronize(L->tev[(size_t)L->t_used * kEventsPerForward - 1]);
+  for (int f = 0; f < L->t_used && he == hipSuccess; ++f) {
+    const hipEvent_t* ev = &L->tev[(size_t)f * kEventsPerForward];
+    for (int i = 0; i < MOE_TIMED_SLOTS && he == hipSuccess; ++i) {
+      float ms = 0.f;
+      he = hipEventElapsedTime(&ms, ev[i], ev[i + 1]);
+      ms_sum[i] += ms;
+    }
+  }
+  drop_events(L);
+  if (he != hipSuccess) return hip_fail(he, "event timing");
+  return MOE_OK;
+}
+
+void moe_layer_destroy(moe_layer_t* L) {
+  if (L == nullptr || L->magic != kMagic) return;
+  const int dev = L->device;
+  int cur = -1;
+  (void)hipGetDevice(&cur);
+  if (cur != dev) (void)hipSetDevice(dev);
+  (void)hipDeviceSynchronize();
+  release(L);
+  if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
+}
+
+}  // extern "C"

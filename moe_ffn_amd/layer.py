@@ -1,0 +1,197 @@
+"""ctypes binding of libmoe_layer.so (the C ABI in include/moe_layer.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  PyTorch provides device memory and the current HIP stream.  If the
+library has not been built, loading fails loudly; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_layer.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_OOM, MOE_ERR_HIP, MOE_ERR_UNSUPPORTED = range(5)
+STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_OOM", 3: "MOE_ERR_HIP",
+                4: "MOE_ERR_UNSUPPORTED"}
+MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
+
+# Symbols declared in include/moe_layer.h.
+EXPORTS = ("moe_abi_version", "moe_last_error", "moe_layer_create", "moe_layer_forward",
+           "moe_layer_set_bias", "moe_layer_timing_start", "moe_layer_timing_stop",
+           "moe_layer_destroy")
+TIMED_SLOTS = ("norm_router", "route_permute", "experts_gate_up", "experts_down", "combine")
+
+
+class LayerConfig(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("rms_eps", ctypes.c_float),
+                ("max_tokens", ctypes.c_int32)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [("rms_gain", ctypes.c_void_p), ("w_router", ctypes.c_void_p),
+                ("b_router", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
+                ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p)]
+
+
+class RoutingOut(ctypes.Structure):
+    _fields_ = [("sel", ctypes.c_void_p), ("gate", ctypes.c_void_p), ("counts", ctypes.c_void_p),
+                ("offsets", ctypes.c_void_p), ("gather", ctypes.c_void_p),
+                ("scatter", ctypes.c_void_p)]
+
+
+class MoELayerError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load (once) and type the C ABI.  Raises if the library is not built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m moe_ffn_amd.build`")
+    lib = ctypes.CDLL(p)
+    lib.moe_abi_version.restype = ctypes.c_int32
+    lib.moe_abi_version.argtypes = []
+    lib.moe_last_error.restype = ctypes.c_char_p
+    lib.moe_last_error.argtypes = []
+    lib.moe_layer_create.restype = ctypes.c_int
+    lib.moe_layer_create.argtypes = [ctypes.POINTER(LayerConfig), ctypes.POINTER(LayerWeights),
+                                     ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
+    lib.moe_layer_forward.restype = ctypes.c_int
+    lib.moe_layer_forward.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                      ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.POINTER(RoutingOut)]
+    lib.moe_layer_set_bias.restype = ctypes.c_int
+    lib.moe_layer_set_bias.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.moe_layer_timing_start.restype = ctypes.c_int
+    lib.moe_layer_timing_start.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+    lib.moe_layer_timing_stop.restype = ctypes.c_int
+    lib.moe_layer_timing_stop.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float),
+                                          ctypes.POINTER(ctypes.c_int32)]
+    lib.moe_layer_destroy.restype = None
+    lib.moe_layer_destroy.argtypes = [ctypes.c_void_p]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(lib, status: int):
+    if status != MOE_OK:
+        raise MoELayerError(status, lib.moe_last_error().decode(errors="replace"))
+
+
+def _stream_ptr(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+_TORCH_DTYPE = {MOE_DTYPE_F32: torch.float32, MOE_DTYPE_BF16: torch.bfloat16}
+
+
+class MoELayer:
+    """One MoE FFN layer owned by the library (packed weights + workspace).
+
+    weights: dict of CUDA tensors in canonical row-major layout
+      rms_gain [d], w_router [E, d], b_router [E] (fp32), w_gate [E, F, d],
+      w_up [E, F, d], w_down [E, d, F]; all but b_router in the layer dtype.
+    """
+
+    def __init__(self, d_model: int, d_ff: int, n_experts: int, top_k: int, dtype: str,
+                 weights: dict, max_tokens: int, rms_eps: float = 1e-6, stream=None):
+        self._lib = load_library()
+        self.handle = None
+        self.dtype_code = MOE_DTYPE_BF16 if dtype == "bf16" else MOE_DTYPE_F32
+        self.torch_dtype = _TORCH_DTYPE[self.dtype_code]
+        self.d, self.F, self.E, self.k = d_model, d_ff, n_experts, top_k
+        self.max_tokens = max_tokens
+        shapes = {"rms_gain": (d_model,), "w_router": (n_experts, d_model),
+                  "b_router": (n_experts,), "w_gate": (n_experts, d_ff, d_model),
+                  "w_up": (n_experts, d_ff, d_model), "w_down": (n_experts, d_model, d_ff)}
+        ptrs = {}
+        for name, shp in shapes.items():
+            t = weights[name]
+            want = torch.float32 if name == "b_router" else self.torch_dtype
+            if not (t.is_cuda and t.dtype == want and tuple(t.shape) == shp and t.is_contiguous()):
+                raise ValueError(f"{name}: need a contiguous CUDA {want} tensor of shape {shp}")
+            ptrs[name] = t.data_ptr()
+        cfg = LayerConfig(d_model, d_ff, n_experts, top_k, self.dtype_code, rms_eps, max_tokens)
+        w = LayerWeights(**ptrs)
+        h = ctypes.c_void_p()
+        _check(self._lib, self._lib.moe_layer_create(ctypes.byref(cfg), ctypes.byref(w),
+                                                     ctypes.c_void_p(_stream_ptr(stream)),
+                                                     ctypes.byref(h)))
+        self.handle = h
+
+    def forward(self, hidden: torch.Tensor, out: torch.Tensor | None = None,
+                routing: bool = False, stream=None):
+        """hidden [T, d] -> out [T, d]; with routing=True also returns a dict of
+        sel, gate, counts, offsets, gather, scatter (int32 / fp32 CUDA tensors)."""
+        if self.handle is None:
+            raise RuntimeError("layer is closed")
+        if not (hidden.is_cuda and hidden.dtype == self.torch_dtype and hidden.dim() == 2
+                and hidden.shape[1] == self.d and hidden.is_contiguous()):
+            raise ValueError(f"hidden: need a contiguous CUDA {self.torch_dtype} tensor [T, {self.d}]")
+        T = hidden.shape[0]
+        if out is None:
+            out = torch.empty_like(hidden)
+        r = None
+        rp = None
+        if routing:
+            dev = hidden.device
+            n = T * self.k
+            r = {"sel": torch.empty((T, self.k), dtype=torch.int32, device=dev),
+                 "gate": torch.empty((T, self.k), dtype=torch.float32, device=dev),
+                 "counts": torch.empty(self.E, dtype=torch.int32, device=dev),
+                 "offsets": torch.empty(self.E + 1, dtype=torch.int32, device=dev),
+                 "gather": torch.empty(n, dtype=torch.int32, device=dev),
+                 "scatter": torch.empty(n, dtype=torch.int32, device=dev)}
+            rp = RoutingOut(**{k: v.data_ptr() for k, v in r.items()})
+        st = self._lib.moe_layer_forward(self.handle, ctypes.c_void_p(hidden.data_ptr()), T,
+                                         ctypes.c_void_p(out.data_ptr()),
+                                         ctypes.c_void_p(_stream_ptr(stream)),
+                                         ctypes.byref(rp) if rp is not None else None)
+        _check(self._lib, st)
+        return (out, r) if routing else out
+
+    __call__ = forward
+
+    def set_bias(self, b: torch.Tensor, stream=None):
+        if not (b.is_cuda and b.dtype == torch.float32 and b.numel() == self.E and b.is_contiguous()):
+            raise ValueError("bias: need a contiguous CUDA fp32 tensor of n_experts values")
+        _check(self._lib, self._lib.moe_layer_set_bias(self.handle, ctypes.c_void_p(b.data_ptr()),
+                                                       ctypes.c_void_p(_stream_ptr(stream))))
+
+    def timing_start(self, max_forwards: int):
+        """Record per-kernel HIP events in the next `max_forwards` forwards."""
+        _check(self._lib, self._lib.moe_layer_timing_start(self.handle, int(max_forwards)))
+
+    def timing_stop(self) -> tuple[dict, int]:
+        """Wait for the recorded events; return ({slot: summed ms}, forwards recorded)."""
+        ms = (ctypes.c_float * len(TIMED_SLOTS))()
+        n = ctypes.c_int32()
+        _check(self._lib, self._lib.moe_layer_timing_stop(self.handle, ms, ctypes.byref(n)))
+        return {name: float(ms[i]) for i, name in enumerate(TIMED_SLOTS)}, int(n.value)
+
+    def close(self):
+        if self.handle is not None:
+            self._lib.moe_layer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

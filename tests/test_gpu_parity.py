@@ -1,0 +1,201 @@
+"""Parity of the HIP layer (through the C ABI) with the fp64 oracle.
+
+Covers the five workloads at full size (routing and dispatch in full, output
+rows in full or on a sample the oracle computes one by one), reduced sizes that
+span several tiles with ragged tails on both expert paths, and the edge cases:
+T = 0, T = 1, T = max_tokens, every token on one expert, a single-expert
+(dense) layer, NaN rows, bias updates, determinism and bad arguments.
+"""
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from synth import CONFIGS, make_inputs
+from synth.configs import LayerConfig
+from tests._parity import check_parity, make_layer, to_torch, device_weights, out_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from moe_ffn_amd import load_library
+    load_library()  # fails loudly if the library is not built
+
+
+_layers = {}
+
+
+def family_layer(cid: int, k: int | None = None, max_tokens: int | None = None, bias=None):
+    """One library layer per (family, k, max_tokens, bias) reused across tests."""
+    base = CONFIGS[cid]
+    k = k or base.k
+    max_tokens = max_tokens or 16384
+    key = (base.family, k, max_tokens, base.bias if bias is None else bias)
+    if key not in _layers:
+        inp = make_inputs(replace(base, k=k, bias=base.bias if bias is None else bias))
+        _layers[key] = make_layer(inp, max_tokens=max_tokens)
+    return _layers[key]
+
+
+# ----------------------------------------------------------- full workloads
+def test_tiny_fp32_T64_full():
+    inp = make_inputs(0)
+    check_parity(inp, make_layer(inp), label="c0 tiny fp32")
+
+
+def test_decode_bf16_T32_full():
+    inp = make_inputs(1)
+    check_parity(inp, family_layer(1), label="c1 decode T=32")
+
+
+def test_prefill_bf16_T4096_full_routing_sampled_rows():
+    inp = make_inputs(2)
+    check_parity(inp, family_layer(2), sample=512, label="c2 prefill T=4096")
+
+
+def test_top2_bf16_T4096_full_routing_sampled_rows():
+    inp = make_inputs(3)
+    check_parity(inp, family_layer(3), sample=512, label="c3 top-2 T=4096")
+
+
+def test_skewed_bf16_T16384_full_routing_sampled_rows():
+    inp = make_inputs(4)
+    layer = family_layer(4)
+    st = check_parity(inp, layer, sample=512, label="c4 skewed T=16384")
+    assert st["rows_compared"] >= 500
+    _, r = layer.forward(to_torch(inp["hidden"], "bf16"), routing=True)
+    counts = r["counts"].cpu().numpy()
+    assert counts.sum() == 16384 and (counts == 0).sum() >= 1
+    assert 0.36 < counts.max() / 16384 < 0.41
+
+
+# ------------------------------------------------- reduced sizes, ragged tails
+@pytest.mark.parametrize("cid,T,k", [
+    (2, 300, 1),    # tile path: several 128-token tiles per expert, ragged tails
+    (2, 129, 1),
+    (3, 200, 2),    # tile path + combine
+    (3, 33, 2),     # 66 assignments: just above the decode path's limit
+    (3, 32, 2),     # 64 assignments: decode path + combine
+    (1, 45, 1),     # decode path
+    (1, 7, 1),
+    (1, 1, 1),
+    (4, 1000, 1),   # skewed bias at a reduced size
+])
+def test_reduced_sizes_full_rows(cid, T, k):
+    base = CONFIGS[cid]
+    inp = make_inputs(replace(base, k=k), T=T)
+    check_parity(inp, family_layer(cid, k=k), label=f"c{cid} T={T} k={k}")
+
+
+def test_tiny_fp32_ragged_and_top2():
+    for T, k in [(1, 1), (37, 1), (64, 2), (5, 3)]:
+        inp = make_inputs(replace(CONFIGS[0], k=k), T=T)
+        check_parity(inp, make_layer(inp, max_tokens=64), label=f"c0 T={T} k={k}")
+
+
+# ------------------------------------------------------------------ edges
+def test_T0_launches_nothing_and_T_max():
+    layer = family_layer(1, max_tokens=256)
+    h = torch.empty((0, 2048), dtype=torch.bfloat16, device="cuda")
+    out = layer.forward(h)
+    assert out.shape == (0, 2048)
+    inp = make_inputs(CONFIGS[1], T=256)   # same weights and bias as the layer
+    check_parity(inp, layer, label="T = max_tokens = 256")
+
+
+def test_every_token_on_one_expert():
+    for T in (64, 300):   # decode path with two 32-token passes; tile path with 3 tiles
+        cfg = replace(CONFIGS[2], T=T)
+        inp = make_inputs(cfg)
+        b = np.zeros(16, np.float32)
+        b[5] = 1e4
+        inp = dict(inp, bias=b)
+        layer = make_layer(inp, max_tokens=T)
+        st = check_parity(inp, layer, label=f"all on expert 5, T={T}")
+        _, r = layer.forward(to_torch(inp["hidden"], "bf16"), routing=True)
+        c = r["counts"].cpu().numpy()
+        assert c[5] == T and c.sum() == T
+        assert np.array_equal(r["gather"].cpu().numpy(), np.arange(T))
+        assert st["near_ties"] == 0
+
+
+@pytest.mark.parametrize("dtype,d,F", [("bf16", 256, 128), ("f32", 64, 96)])
+def test_single_expert_dense_layer(dtype, d, F):
+    cfg = LayerConfig(90, "dense", T=77, d=d, E=1, F=F, k=1, dtype=dtype, bias="zero",
+                      family="dense_" + dtype)
+    inp = make_inputs(cfg)
+    layer = make_layer(inp)
+    st = check_parity(inp, layer, label=f"E=1 dense {dtype}")
+    assert st["near_ties"] == 0  # a single expert has an infinite margin
+    _, r = layer.forward(to_torch(inp["hidden"], dtype), routing=True)
+    assert torch.all(r["gate"] == 1.0) and torch.all(r["sel"] == 0)
+
+
+def test_deterministic_bytes():
+    inp = make_inputs(3, T=1000)
+    layer = family_layer(3)
+    h = to_torch(inp["hidden"], "bf16")
+    o1, r1 = layer.forward(h, routing=True)
+    o2, r2 = layer.forward(h, routing=True)
+    o3 = layer.forward(h)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+    for key in r1:
+        assert torch.equal(r1[key], r2[key]), key
+
+
+def test_nan_row_stays_in_bounds_and_leaves_other_rows_alone():
+    for cid, T in [(1, 32), (2, 300)]:
+        inp = make_inputs(CONFIGS[cid], T=T)
+        layer = family_layer(cid)
+        h = to_torch(inp["hidden"], "bf16")
+        hn = h.clone()
+        hn[3, 17] = float("nan")
+        o, r = layer.forward(h, routing=True)
+        on, rn = layer.forward(hn, routing=True)
+        torch.cuda.synchronize()
+        sel = rn["sel"]
+        assert int(sel.min()) >= 0 and int(sel.max()) < 16
+        assert int(rn["counts"].sum()) == T
+        g = rn["gather"].cpu().numpy()
+        assert sorted(g.tolist()) == list(range(T))
+        keep = torch.ones(T, dtype=torch.bool, device="cuda")
+        keep[3] = False
+        # rows do not interact: every other row is bit-identical when its route is
+        assert torch.equal(rn["sel"][keep], r["sel"][keep])
+        assert torch.equal(on[keep].view(torch.int16), o[keep].view(torch.int16))
+
+
+def test_set_bias_steers_routing():
+    inp = make_inputs(CONFIGS[1])
+    layer = make_layer(inp, max_tokens=32)
+    b = torch.zeros(16, dtype=torch.float32, device="cuda")
+    b[11] = 1e4
+    layer.set_bias(b)
+    inp2 = dict(inp, bias=b.cpu().numpy())
+    check_parity(inp2, layer, label="after set_bias")
+    _, r = layer.forward(to_torch(inp["hidden"], "bf16"), routing=True)
+    assert int(r["counts"][11]) == 32
+
+
+def test_bad_arguments_raise():
+    from moe_ffn_amd import MoELayerError, MOE_ERR_INVALID_ARG
+    layer = family_layer(1, max_tokens=256)
+    h = torch.zeros((257, 2048), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(MoELayerError) as ei:
+        layer.forward(h)
+    assert ei.value.status == MOE_ERR_INVALID_ARG
+    h = torch.zeros((64, 2048), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(MoELayerError) as ei:
+        layer.forward(h, out=h)
+    assert ei.value.status == MOE_ERR_INVALID_ARG
+    buf = torch.zeros(64 * 2048 + 8, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(MoELayerError):
+        layer.forward(h, out=buf[1:1 + 64 * 2048].view(64, 2048))   # misaligned out
