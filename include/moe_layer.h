@@ -131,14 +131,15 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const void* hidden, int32_t T
 moe_status_t moe_layer_set_bias(moe_layer_t* layer, const float* b_router, void* stream);
 
 /* Per-kernel timing, for measurement tools.  moe_layer_timing_start() makes
- * the next `max_forwards` forwards record a HIP event before the first kernel
- * and after each kernel, on the forward's stream.  moe_layer_timing_stop()
- * waits for those events, writes into ms_sum[MOE_TIMED_SLOTS] the summed
- * milliseconds between consecutive events for each slot, and *n_forwards the
- * number of forwards recorded; it then releases the events.  Slots, in launch
- * order: 0 RMSNorm+router+top-k, 1 histogram+permutation, 2 first expert
- * kernel (gate/up), 3 second expert kernel (down), 4 combine (0 when k = 1).
- * Recording events between kernels can add a little time per forward.
+ * the next `max_forwards` forwards launch every kernel with a start and a stop
+ * HIP event carried by the kernel's own dispatch (no extra packets on the
+ * stream).  moe_layer_timing_stop() waits for those events, writes into
+ * ms_sum[MOE_TIMED_SLOTS] each slot's summed kernel milliseconds and into
+ * *n_forwards the number of forwards recorded, then releases the events.
+ * Slots, in launch order: 0 RMSNorm+router+top-k, 1 histogram+permutation
+ * (0 for bf16 layers with T*top_k <= 64, whose expert kernels dispatch), 2 first
+ * expert kernel (gate/up), 3 second expert kernel (down), 4 combine (0 when
+ * top_k = 1, where the combine is part of slot 3).
  * Errors: INVALID_ARG (bad handle, max_forwards outside [1, 65536], stop
  * without start), HIP. */
 #define MOE_TIMED_SLOTS 5

@@ -40,13 +40,12 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ybuf,
 hipError_t launch_combine(const FwdArgs& a) {
   const size_t total = (size_t)a.T * (a.dim.d / 4);
   const unsigned grid = (unsigned)((total + 255) / 256);
+  const KEv& ev = a.ev[kSlotCombine];
   if (a.dim.dtype == 1)
-    hipLaunchKernelGGL((k_combine<true>), dim3(grid), dim3(256), 0, a.stream, a.ybuf, a.gate,
-                       a.scatter, a.T, a.dim.k, a.dim.d, a.out);
-  else
-    hipLaunchKernelGGL((k_combine<false>), dim3(grid), dim3(256), 0, a.stream, a.ybuf, a.gate,
-                       a.scatter, a.T, a.dim.k, a.dim.d, a.out);
-  return hipGetLastError();
+    return launch(k_combine<true>, dim3(grid), dim3(256), a.stream, ev, (const float*)a.ybuf,
+                  (const float*)a.gate, (const int*)a.scatter, a.T, a.dim.k, a.dim.d, a.out);
+  return launch(k_combine<false>, dim3(grid), dim3(256), a.stream, ev, (const float*)a.ybuf,
+                (const float*)a.gate, (const int*)a.scatter, a.T, a.dim.k, a.dim.d, a.out);
 }
 
 }  // namespace moe

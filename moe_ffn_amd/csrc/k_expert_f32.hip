@@ -13,7 +13,8 @@ __global__ __launch_bounds__(256) void k_gateup_f32(const float* __restrict__ wg
                                                     const float* __restrict__ wu,
                                                     const float* __restrict__ xn,
                                                     const int* __restrict__ gather,
-                                                    const int* __restrict__ slot_expert, int n,
+                                                    const int* __restrict__ slot_expert,
+                                                    const float* __restrict__ inv, int n,
                                                     int d, int F, float* __restrict__ act) {
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (size_t)n * F) return;
@@ -33,6 +34,9 @@ __global__ __launch_bounds__(256) void k_gateup_f32(const float* __restrict__ wg
       su = fmaf(uv[q], xv[q], su);
     }
   }
+  const float s = inv[gather[p]];  // RMSNorm scale of this token
+  sg *= s;
+  su *= s;
   act[(size_t)p * F + f] = sg / (1.0f + expf(-sg)) * su;
 }
 
@@ -67,17 +71,16 @@ __global__ __launch_bounds__(256) void k_down_f32(const float* __restrict__ wd,
 hipError_t launch_experts_f32(const FwdArgs& a) {
   const int d = a.dim.d, F = a.dim.F, n = a.n;
   const size_t g1 = ((size_t)n * F + 255) / 256;
-  hipLaunchKernelGGL(k_gateup_f32, dim3((unsigned)g1), dim3(256), 0, a.stream,
-                     (const float*)a.wgu, (const float*)a.wup, (const float*)a.xn, a.gather,
-                     a.slot_expert, n, d, F, (float*)a.act);
-  hipError_t err = hipGetLastError();
+  hipError_t err = launch(k_gateup_f32, dim3((unsigned)g1), dim3(256), a.stream,
+                          a.ev[kSlotExpertsA], (const float*)a.wgu, (const float*)a.wup,
+                          (const float*)a.xn, (const int*)a.gather, (const int*)a.slot_expert,
+                          (const float*)a.inv, n, d, F, (float*)a.act);
   if (err != hipSuccess) return err;
-  if (a.ev_mid != nullptr && (err = hipEventRecord(a.ev_mid, a.stream)) != hipSuccess) return err;
   const size_t g2 = ((size_t)n * d + 255) / 256;
-  hipLaunchKernelGGL(k_down_f32, dim3((unsigned)g2), dim3(256), 0, a.stream, (const float*)a.wd,
-                     (const float*)a.act, a.gather, a.slot_expert, a.gate, n, d, F, a.dim.k,
-                     (float*)a.out, a.ybuf);
-  return hipGetLastError();
+  return launch(k_down_f32, dim3((unsigned)g2), dim3(256), a.stream, a.ev[kSlotExpertsB],
+                (const float*)a.wd, (const float*)a.act, (const int*)a.gather,
+                (const int*)a.slot_expert, (const float*)a.gate, n, d, F, a.dim.k, (float*)a.out,
+                a.ybuf);
 }
 
 }  // namespace moe

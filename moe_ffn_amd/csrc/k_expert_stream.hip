@@ -12,15 +12,28 @@
 //
 // Each workgroup owns one 32-row weight tile of one expert; its four waves
 // split the reduction axis into quarters and combine partial sums through LDS
-// in a fixed order (deterministic).
+// in a fixed order (deterministic).  Each wave keeps a rolling queue of D
+// k-steps of loads in flight, so the weight stream never drains between
+// multiplies; registers stay low enough for four workgroups per CU, which
+// keeps every tile of a forward resident at once (no tail wave).
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 
 namespace {
-constexpr int kSplit = 4;   // waves per weight tile (split of the reduction axis)
-constexpr int kBatch = 8;   // k-steps whose loads are issued together
+constexpr int kSplit = 4;  // waves per weight tile (split of the reduction axis)
+#ifndef MOE_STREAM_NT
+#define MOE_STREAM_NT 1
+#endif
+
+__device__ __forceinline__ u32x4 ldw(const uint16_t* p) {
+#if MOE_STREAM_NT
+  return ldg16_stream(p);
+#else
+  return ldg16(p);
+#endif
+}
 
 // Partial sums of waves 1..3 -> wave 0, fixed order.
 template <int NACC>
@@ -42,74 +55,135 @@ __device__ __forceinline__ void reduce_split(f32x16 (&acc)[NACC], float* red, in
   }
   __syncthreads();
 }
+
+// Dispatch of a decode-sized batch (n = T*k <= 64 assignments) for expert e,
+// computed by wave 0 from the routing choice itself: the expert's slot count
+// and offset (popcounts of two ballots) and its tokens in slot order (stable:
+// increasing assignment index) in `list`.  With `write`, the workgroup also
+// stores expert e's part of the routing outputs.  Every workgroup of both
+// expert kernels derives the same arrays, so no separate dispatch kernel runs.
+struct Route {
+  int cnt, off;
+};
+__device__ __forceinline__ Route small_dispatch(const int* __restrict__ sel, int n, int k, int E,
+                                                int e, int lane, int wave, int* list, int* sh,
+                                                bool write, int* __restrict__ counts,
+                                                int* __restrict__ offsets,
+                                                int* __restrict__ gather,
+                                                int* __restrict__ scatter) {
+  if (wave == 0) {
+    const int my = lane < n ? sel[lane] : -1;
+    const uint64_t me = __ballot(my == e);
+    const uint64_t lt = __ballot(my >= 0 && my < e);
+    const int cnt = __popcll(me), off = __popcll(lt);
+    if (my == e) {
+      const int r = __popcll(me & ((1ull << lane) - 1ull));
+      list[r] = lane / k;
+      if (write) {
+        gather[off + r] = lane / k;
+        scatter[lane] = off + r;
+      }
+    }
+    if (lane == 0) {
+      sh[0] = cnt;
+      sh[1] = off;
+      if (write) {
+        counts[e] = cnt;
+        offsets[e] = off;
+        if (e == E - 1) offsets[E] = n;
+      }
+    }
+  }
+  __syncthreads();
+  return {sh[0], sh[1]};
+}
+
+// Rolling prefetch over `kper` k-steps (a multiple of D): D k-steps of
+// operands are always in flight while the oldest one is multiplied.
+// NW weight streams share one activation operand per k-step.
+// Lanes without a token read a row of zeros, so every load is unconditional
+// (a branch around a load would make the compiler drain the queue).
+template <int D, int NW>
+__device__ __forceinline__ void stream_mac(const uint16_t* const (&w)[NW], const uint16_t* xb,
+                                           int ks0, int kper, f32x16 (&acc)[NW]) {
+  u32x4 qw[NW][D], qx[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+#pragma unroll
+    for (int j = 0; j < NW; ++j) qw[j][i] = ldw(w[j] + (size_t)(ks0 + i) * kBlockElems);
+    qx[i] = ldg16(xb + (ks0 + i) * kKStep);
+  }
+  const int rounds = kper / D;
+  for (int r = 1; r < rounds; ++r) {
+    const int sn = ks0 + r * D;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+#pragma unroll
+      for (int j = 0; j < NW; ++j) acc[j] = mfma_32x32x16(qw[j][i], qx[i], acc[j]);
+#pragma unroll
+      for (int j = 0; j < NW; ++j) qw[j][i] = ldw(w[j] + (size_t)(sn + i) * kBlockElems);
+      qx[i] = ldg16(xb + (sn + i) * kKStep);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+#pragma unroll
+    for (int j = 0; j < NW; ++j) acc[j] = mfma_32x32x16(qw[j][i], qx[i], acc[j]);
+}
 }  // namespace
 
 // Gate/up projections and the SiLU(gate) * up epilogue for one 32-column F tile.
-__global__ __launch_bounds__(256) void k_gateup_stream(const uint16_t* __restrict__ wgu,
-                                                       const uint16_t* __restrict__ xn,
-                                                       const int* __restrict__ counts,
-                                                       const int* __restrict__ offsets,
-                                                       const int* __restrict__ gather,
-                                                       uint16_t* __restrict__ act, int d, int F) {
+// The workgroups with ft == 0 also write the routing outputs of their expert.
+template <int D>
+__global__ __launch_bounds__(256) void k_gateup_stream(
+    const uint16_t* __restrict__ wgu, const uint16_t* __restrict__ xn,
+    const int* __restrict__ sel, int n, int k, int E, int* __restrict__ counts,
+    int* __restrict__ offsets, int* __restrict__ gather, int* __restrict__ scatter,
+    const float* __restrict__ inv, const uint16_t* __restrict__ zrow,
+    uint16_t* __restrict__ act, int d, int F) {
   __shared__ float red[(kSplit - 1) * 2 * 16 * 64];
+  __shared__ int list[64];
+  __shared__ int sh[2];
   const int e = blockIdx.y;
-  const int cnt = counts[e];
-  if (cnt == 0) return;
-  const int off = offsets[e];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const Route rt = small_dispatch(sel, n, k, E, e, lane, wave, list, sh, blockIdx.x == 0, counts,
+                                  offsets, gather, scatter);
+  const int cnt = rt.cnt, off = rt.off;
+  if (cnt == 0) return;
   const int ft = blockIdx.x;
   const int ksteps = d / kKStep;
   const int kper = ksteps / kSplit;
   const int ks0 = wave * kper;
   const size_t tile_elems = (size_t)ksteps * kBlockElems;
   const uint16_t* wg = wgu + (((size_t)e * (F / kTileRows) + ft) * 2) * tile_elems + lane * 8;
-  const uint16_t* wu = wg + tile_elems;
+  const uint16_t* const wp[2] = {wg, wg + tile_elems};
   const int col = lane & 31;
 
   for (int c0 = 0; c0 < cnt; c0 += 32) {
     const int ntok = min(32, cnt - c0);
     const bool valid = col < ntok;
-    const uint16_t* xrow = xn + (size_t)(valid ? gather[off + c0 + col] : 0) * d + (lane >> 5) * 8;
+    const int tok = valid ? list[c0 + col] : 0;
+    const uint16_t* xrow = (valid ? xn + (size_t)tok * d : zrow) + (lane >> 5) * 8;
     f32x16 acc[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[q][i] = 0.f;
-
-    int s = ks0;
-    for (; s + kBatch <= ks0 + kper; s += kBatch) {
-      u32x4 ag[kBatch], au[kBatch], b[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        ag[u] = ldg16_stream(wg + (size_t)(s + u) * kBlockElems);
-        au[u] = ldg16_stream(wu + (size_t)(s + u) * kBlockElems);
-        b[u] = valid ? ldg16(xrow + (s + u) * kKStep) : u32x4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        acc[0] = mfma_32x32x16(ag[u], b[u], acc[0]);
-        acc[1] = mfma_32x32x16(au[u], b[u], acc[1]);
-      }
-    }
-    for (; s < ks0 + kper; ++s) {
-      const u32x4 ag = ldg16_stream(wg + (size_t)s * kBlockElems);
-      const u32x4 au = ldg16_stream(wu + (size_t)s * kBlockElems);
-      const u32x4 b = valid ? ldg16(xrow + s * kKStep) : u32x4{0, 0, 0, 0};
-      acc[0] = mfma_32x32x16(ag, b, acc[0]);
-      acc[1] = mfma_32x32x16(au, b, acc[1]);
-    }
+    stream_mac<D, 2>(wp, xrow, ks0, kper, acc);
     reduce_split<2>(acc, red, wave, lane);
 
     if (wave == 0 && valid) {
+      const float s = inv[tok];  // RMSNorm scale of this token
       uint16_t* dst = act + (size_t)(off + c0 + col) * F + ft * kTileRows;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int r = c32_row(4 * g, lane);
+        float v4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v4[q] = silu(s * acc[0][4 * g + q]) * (s * acc[1][4 * g + q]);
         u32x2 v;
-        v[0] = pack_bf16x2(silu(acc[0][4 * g]) * acc[1][4 * g],
-                           silu(acc[0][4 * g + 1]) * acc[1][4 * g + 1]);
-        v[1] = pack_bf16x2(silu(acc[0][4 * g + 2]) * acc[1][4 * g + 2],
-                           silu(acc[0][4 * g + 3]) * acc[1][4 * g + 3]);
+        v[0] = pack_bf16x2(v4[0], v4[1]);
+        v[1] = pack_bf16x2(v4[2], v4[3]);
         *reinterpret_cast<u32x2*>(dst + r) = v;
       }
     }
@@ -118,56 +192,44 @@ __global__ __launch_bounds__(256) void k_gateup_stream(const uint16_t* __restric
 
 // Down projection for one 32-row d_model tile; k = 1 writes gate * y into the
 // output row of the token, k > 1 writes y (fp32) for the combine kernel.
+template <int D>
 __global__ __launch_bounds__(256) void k_down_stream(
     const uint16_t* __restrict__ wd, const uint16_t* __restrict__ act,
-    const int* __restrict__ counts, const int* __restrict__ offsets,
-    const int* __restrict__ gather, const float* __restrict__ gate, int k,
-    uint16_t* __restrict__ out, float* __restrict__ ybuf, int d, int F) {
+    const int* __restrict__ sel, int n, int k, int E, const float* __restrict__ gate,
+    const uint16_t* __restrict__ zrow, uint16_t* __restrict__ out, float* __restrict__ ybuf, int d,
+    int F) {
   __shared__ float red[(kSplit - 1) * 16 * 64];
+  __shared__ int list[64];
+  __shared__ int sh[2];
   const int e = blockIdx.y;
-  const int cnt = counts[e];
-  if (cnt == 0) return;
-  const int off = offsets[e];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const Route rt = small_dispatch(sel, n, k, E, e, lane, wave, list, sh, false, nullptr, nullptr,
+                                  nullptr, nullptr);
+  const int cnt = rt.cnt, off = rt.off;
+  if (cnt == 0) return;
   const int mt = blockIdx.x;
   const int ksteps = F / kKStep;
   const int kper = ksteps / kSplit;
   const int ks0 = wave * kper;
-  const uint16_t* wrow =
-      wd + ((size_t)e * (d / kTileRows) + mt) * (size_t)ksteps * kBlockElems + lane * 8;
+  const uint16_t* const wp[1] = {
+      wd + ((size_t)e * (d / kTileRows) + mt) * (size_t)ksteps * kBlockElems + lane * 8};
   const int col = lane & 31;
 
   for (int c0 = 0; c0 < cnt; c0 += 32) {
     const int ntok = min(32, cnt - c0);
     const bool valid = col < ntok;
     const int slot = off + c0 + (valid ? col : 0);
-    const uint16_t* arow = act + (size_t)slot * F + (lane >> 5) * 8;
+    const uint16_t* arow = (valid ? act + (size_t)slot * F : zrow) + (lane >> 5) * 8;
     f32x16 acc[1];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[0][i] = 0.f;
-
-    int s = ks0;
-    for (; s + kBatch <= ks0 + kper; s += kBatch) {
-      u32x4 aw[kBatch], b[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        aw[u] = ldg16_stream(wrow + (size_t)(s + u) * kBlockElems);
-        b[u] = valid ? ldg16(arow + (s + u) * kKStep) : u32x4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) acc[0] = mfma_32x32x16(aw[u], b[u], acc[0]);
-    }
-    for (; s < ks0 + kper; ++s) {
-      const u32x4 aw = ldg16_stream(wrow + (size_t)s * kBlockElems);
-      const u32x4 b = valid ? ldg16(arow + s * kKStep) : u32x4{0, 0, 0, 0};
-      acc[0] = mfma_32x32x16(aw, b, acc[0]);
-    }
+    stream_mac<D, 1>(wp, arow, ks0, kper, acc);
     reduce_split<1>(acc, red, wave, lane);
 
     if (wave == 0 && valid) {
       const int m0 = mt * kTileRows;
       if (k == 1) {
-        const int tok = gather[slot];
+        const int tok = list[c0 + col];
         const float g = gate[tok];
         uint16_t* dst = out + (size_t)tok * d + m0;
 #pragma unroll
@@ -191,18 +253,33 @@ __global__ __launch_bounds__(256) void k_down_stream(
   }
 }
 
+namespace {
+#ifndef MOE_STREAM_DEPTH
+#define MOE_STREAM_DEPTH 4
+#endif
+// Largest prefetch depth (k-steps) up to MOE_STREAM_DEPTH that divides a wave's share.
+int pick_depth(int kper) {
+  for (int D = MOE_STREAM_DEPTH; D > 1; D /= 2)
+    if (kper % D == 0) return D;
+  return 1;
+}
+}  // namespace
+
 hipError_t launch_experts_stream(const FwdArgs& a) {
   const int d = a.dim.d, F = a.dim.F, E = a.dim.E;
-  hipLaunchKernelGGL(k_gateup_stream, dim3(F / kTileRows, E), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.wgu, (const uint16_t*)a.xn, a.counts, a.offsets, a.gather,
-                     (uint16_t*)a.act, d, F);
-  hipError_t err = hipGetLastError();
+  const int Da = pick_depth(d / kKStep / kSplit), Db = pick_depth(F / kKStep / kSplit);
+  auto gu = Da == 8 ? k_gateup_stream<8> : Da == 4 ? k_gateup_stream<4>
+          : Da == 2 ? k_gateup_stream<2> : k_gateup_stream<1>;
+  auto dn = Db == 8 ? k_down_stream<8> : Db == 4 ? k_down_stream<4>
+          : Db == 2 ? k_down_stream<2> : k_down_stream<1>;
+  hipError_t err = launch(gu, dim3(F / kTileRows, E), dim3(256), a.stream, a.ev[kSlotExpertsA],
+                          (const uint16_t*)a.wgu, (const uint16_t*)a.xn, (const int*)a.sel, a.n,
+                          a.dim.k, E, a.counts, a.offsets, a.gather, a.scatter,
+                          (const float*)a.inv, (const uint16_t*)a.zrow, (uint16_t*)a.act, d, F);
   if (err != hipSuccess) return err;
-  if (a.ev_mid != nullptr && (err = hipEventRecord(a.ev_mid, a.stream)) != hipSuccess) return err;
-  hipLaunchKernelGGL(k_down_stream, dim3(d / kTileRows, E), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.wd, (const uint16_t*)a.act, a.counts, a.offsets, a.gather,
-                     a.gate, a.dim.k, (uint16_t*)a.out, a.ybuf, d, F);
-  return hipGetLastError();
+  return launch(dn, dim3(d / kTileRows, E), dim3(256), a.stream, a.ev[kSlotExpertsB],
+                (const uint16_t*)a.wd, (const uint16_t*)a.act, (const int*)a.sel, a.n, a.dim.k, E,
+                (const float*)a.gate, (const uint16_t*)a.zrow, (uint16_t*)a.out, a.ybuf, d, F);
 }
 
 }  // namespace moe

@@ -33,7 +33,8 @@ __global__ __launch_bounds__(256) void k_expert_tile(
     const uint16_t* __restrict__ wpk, const uint16_t* __restrict__ src,
     const int* __restrict__ tilemap, const int* __restrict__ counts,
     const int* __restrict__ offsets, const int* __restrict__ gather,
-    const float* __restrict__ gate, int k, uint16_t* __restrict__ dst16,
+    const float* __restrict__ gate, const float* __restrict__ inv, int k,
+    uint16_t* __restrict__ dst16,
     float* __restrict__ ybuf, int d, int F) {
   __shared__ u32x4 lds_w[2][kWChunks];
   __shared__ u32x4 lds_x[2][kXChunks];
@@ -131,6 +132,7 @@ __global__ __launch_bounds__(256) void k_expert_tile(
     if (r >= nvalid) continue;
     const int slot = off + row0 + r;
     if constexpr (MODE == 0) {
+      const float sc = inv[gather[slot]];  // RMSNorm scale of this token
       uint16_t* dst = dst16 + (size_t)slot * F;
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
@@ -141,9 +143,12 @@ __global__ __launch_bounds__(256) void k_expert_tile(
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int f = ft * kTileRows + c32_row(4 * q, lane);
+          float v4[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v4[c] = silu(sc * g[4 * q + c]) * (sc * u[4 * q + c]);
           u32x2 v;
-          v[0] = pack_bf16x2(silu(g[4 * q]) * u[4 * q], silu(g[4 * q + 1]) * u[4 * q + 1]);
-          v[1] = pack_bf16x2(silu(g[4 * q + 2]) * u[4 * q + 2], silu(g[4 * q + 3]) * u[4 * q + 3]);
+          v[0] = pack_bf16x2(v4[0], v4[1]);
+          v[1] = pack_bf16x2(v4[2], v4[3]);
           *reinterpret_cast<u32x2*>(dst + f) = v;
         }
       }
@@ -174,16 +179,17 @@ __global__ __launch_bounds__(256) void k_expert_tile(
 
 hipError_t launch_experts_tile(const FwdArgs& a) {
   const int d = a.dim.d, F = a.dim.F;
-  hipLaunchKernelGGL((k_expert_tile<0>), dim3(a.max_tiles, F / 128), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.wgu, (const uint16_t*)a.xn, a.tilemap, a.counts,
-                     a.offsets, a.gather, a.gate, a.dim.k, (uint16_t*)a.act, a.ybuf, d, F);
-  hipError_t err = hipGetLastError();
+  hipError_t err = launch(k_expert_tile<0>, dim3(a.max_tiles, F / 128), dim3(256), a.stream,
+                          a.ev[kSlotExpertsA], (const uint16_t*)a.wgu, (const uint16_t*)a.xn,
+                          (const int*)a.tilemap, (const int*)a.counts, (const int*)a.offsets,
+                          (const int*)a.gather, (const float*)a.gate, (const float*)a.inv,
+                          a.dim.k, (uint16_t*)a.act, a.ybuf, d, F);
   if (err != hipSuccess) return err;
-  if (a.ev_mid != nullptr && (err = hipEventRecord(a.ev_mid, a.stream)) != hipSuccess) return err;
-  hipLaunchKernelGGL((k_expert_tile<1>), dim3(a.max_tiles, d / 256), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.wd, (const uint16_t*)a.act, a.tilemap, a.counts,
-                     a.offsets, a.gather, a.gate, a.dim.k, (uint16_t*)a.out, a.ybuf, d, F);
-  return hipGetLastError();
+  return launch(k_expert_tile<1>, dim3(a.max_tiles, d / 256), dim3(256), a.stream,
+                a.ev[kSlotExpertsB], (const uint16_t*)a.wd, (const uint16_t*)a.act,
+                (const int*)a.tilemap, (const int*)a.counts, (const int*)a.offsets,
+                (const int*)a.gather, (const float*)a.gate, (const float*)a.inv, a.dim.k,
+                (uint16_t*)a.out, a.ybuf, d, F);
 }
 
 }  // namespace moe

@@ -1,4 +1,4 @@
-// K1: fused RMSNorm + linear router + bias-steered top-k + gates.
+// K1 (fp32 layers): fused RMSNorm + linear router + bias-steered top-k + gates.
 //
 // ZONOS2 Technical Report (audio-paper-digest page, "Method overview and
 // architecture"): item 5 normalises the backbone input with RMSNorm and routes
@@ -12,7 +12,8 @@
 // (W_r[e][i] * g[i], exact in fp32 for bf16 operands):  z_e = inv_rms * sum_i
 // (W_r g)_{e,i} h_i.  The TOK x E partial sums are reduced by a butterfly that
 // spreads the totals over the lanes, then across the four waves through LDS.
-// A second pass writes x = h * inv_rms * g (bf16 or fp32) for the experts.
+// A second pass writes x' = g * h for the experts and inv_rms per token; the
+// experts apply inv_rms to their fp32 accumulators.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -24,6 +25,7 @@ __global__ __launch_bounds__(256) void k_norm_router(const void* __restrict__ hi
                                                      const float* __restrict__ gain,
                                                      const float* __restrict__ bias, int E, int k,
                                                      float eps, void* __restrict__ xn,
+                                                     float* __restrict__ inv_out,
                                                      int* __restrict__ sel, float* __restrict__ gate) {
   constexpr int VEC = BF16 ? 8 : 4;  // elements per 16-byte chunk
   constexpr int NV = TOK * EP;
@@ -149,9 +151,10 @@ __global__ __launch_bounds__(256) void k_norm_router(const void* __restrict__ hi
       sel[(size_t)t * k + j] = chosen[j];
       gate[(size_t)t * k + j] = expf(zc[j] - zmax) / den;
     }
+    inv_out[t] = inv;
   }
 
-  // second pass: x = h * inv_rms * g for the experts
+  // second pass: x' = g * h for the experts
   for (int c = tid; c < nch; c += 256) {
     float g[VEC];
 #pragma unroll
@@ -163,7 +166,6 @@ __global__ __launch_bounds__(256) void k_norm_router(const void* __restrict__ hi
 #pragma unroll
     for (int t = 0; t < TOK; ++t) {
       if (t0 + t >= T) break;
-      const float inv = inv_s[t];
       const u32x4 v = ldg16(hb + (size_t)(t0 + t) * row_bytes + (size_t)c * 16);
       u32x4 o;
       if constexpr (BF16) {
@@ -171,10 +173,10 @@ __global__ __launch_bounds__(256) void k_norm_router(const void* __restrict__ hi
         unpack8(v, h);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          o[i] = pack_bf16x2(h[2 * i] * inv * g[2 * i], h[2 * i + 1] * inv * g[2 * i + 1]);
+          o[i] = pack_bf16x2(h[2 * i] * g[2 * i], h[2 * i + 1] * g[2 * i + 1]);
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(__uint_as_float(v[i]) * inv * g[i]);
+        for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(__uint_as_float(v[i]) * g[i]);
       }
       stg16(reinterpret_cast<char*>(xn) + (size_t)(t0 + t) * row_bytes + (size_t)c * 16, o);
     }
@@ -190,16 +192,14 @@ hipError_t launch_ep(const FwdArgs& a) {
   constexpr int TS = TB < 2 ? TB : 2;
   const int T = a.T;
   const bool small = (T + TB - 1) / TB < 256;
-  if (small) {
-    hipLaunchKernelGGL((k_norm_router<BF16, EP, TS>), dim3((T + TS - 1) / TS), dim3(256), 0,
-                       a.stream, a.hidden, T, a.dim.d, a.wrg, a.gain, a.bias, a.dim.E, a.dim.k,
-                       a.dim.eps, a.xn, a.sel, a.gate);
-  } else {
-    hipLaunchKernelGGL((k_norm_router<BF16, EP, TB>), dim3((T + TB - 1) / TB), dim3(256), 0,
-                       a.stream, a.hidden, T, a.dim.d, a.wrg, a.gain, a.bias, a.dim.E, a.dim.k,
-                       a.dim.eps, a.xn, a.sel, a.gate);
-  }
-  return hipGetLastError();
+  const KEv& ev = a.ev[kSlotNormRouter];
+  if (small)
+    return launch(k_norm_router<BF16, EP, TS>, dim3((T + TS - 1) / TS), dim3(256), a.stream, ev,
+                  a.hidden, T, a.dim.d, a.wrg, a.gain, a.bias, a.dim.E, a.dim.k, a.dim.eps, a.xn,
+                  a.inv, a.sel, a.gate);
+  return launch(k_norm_router<BF16, EP, TB>, dim3((T + TB - 1) / TB), dim3(256), a.stream, ev,
+                a.hidden, T, a.dim.d, a.wrg, a.gain, a.bias, a.dim.E, a.dim.k, a.dim.eps, a.xn,
+                a.inv, a.sel, a.gate);
 }
 
 template <bool BF16>
@@ -217,8 +217,6 @@ hipError_t launch_dtype(const FwdArgs& a) {
 }
 }  // namespace
 
-hipError_t launch_norm_router(const FwdArgs& a) {
-  return a.dim.dtype == 1 ? launch_dtype<true>(a) : launch_dtype<false>(a);
-}
+hipError_t launch_norm_router(const FwdArgs& a) { return launch_dtype<false>(a); }
 
 }  // namespace moe

@@ -116,10 +116,9 @@ __global__ __launch_bounds__(1024) void k_route_permute(
 namespace {
 template <int EP>
 hipError_t launch_ep(const FwdArgs& a) {
-  hipLaunchKernelGGL((k_route_permute<EP>), dim3(1), dim3(1024), 0, a.stream, a.sel, a.n, a.dim.k,
-                     a.dim.E, a.counts, a.offsets, a.gather, a.scatter, a.slot_expert, a.tilemap,
-                     kTileTokens, a.max_tiles);
-  return hipGetLastError();
+  return launch(k_route_permute<EP>, dim3(1), dim3(1024), a.stream, a.ev[kSlotPermute], a.sel, a.n,
+                a.dim.k, a.dim.E, a.counts, a.offsets, a.gather, a.scatter, a.slot_expert,
+                a.tilemap, kTileTokens, a.max_tiles);
 }
 }  // namespace
 

@@ -1,0 +1,228 @@
+// K1 (bf16 layers, prefill-sized batches): fused RMSNorm statistics + linear
+// router on bf16 MFMA + bias-steered top-k + gates.
+//
+// ZONOS2 Technical Report (audio-paper-digest page, "Method overview and
+// architecture"): item 5 normalises the backbone input with RMSNorm and routes
+// each token to 1 of 16 experts (2 in the last MoE layer); item 6 keeps a
+// per-expert bias b_l for load balancing, which here only moves the choice
+// (s = z + b) while gates come from the unbiased logits z.
+//
+// Exact router on bf16 matrix cores: with x' = g * h (the gain times the bf16
+// input) every product is exact in fp32 because both factors are bf16, and
+// x' carries at most 16 significant bits, so x' = hi + lo with hi = bf16(x')
+// and lo = bf16(x' - hi) both exact.  z_raw = W_r x' = W_r hi + W_r lo is
+// therefore two bf16 MFMAs with fp32 accumulation: fp32-router precision at
+// matrix-core speed.  z = inv_rms * z_raw with inv_rms = 1/sqrt(mean(h^2)+eps).
+//
+// Outputs: xg = bf16(g * h) for the experts (hi itself; inv_rms is applied to
+// the experts' fp32 accumulators instead of to the activations), inv_rms[T],
+// sel[T,k], gate[T,k].
+//
+// Layout: a workgroup of NW waves owns 32*TT tokens; wave w covers the d/NW
+// slice [w*d/NW, (w+1)*d/NW) of the reduction axis, issuing its loads four
+// k-steps at a time.  MFMA 32x32x16: A = router rows (32 experts per tile, NA
+// tiles), B = tokens (32 per tile, TT tiles).  Partial logits of the waves meet
+// in LDS and are summed in a fixed order, one (token, expert) pair per thread.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+constexpr int kRBatch = 4;  // k-steps whose loads are issued together
+}
+
+
+// NW waves; wave w covers k-steps [w*kper, (w+1)*kper) of the d/16 steps.
+template <int NA, int TT, int NW>
+__global__ __launch_bounds__(NW * 64) void k_router_mfma(
+    const uint16_t* __restrict__ hidden, int T, int d, const uint16_t* __restrict__ wr,
+    const uint16_t* __restrict__ gain, const float* __restrict__ bias, int E, int k, float eps,
+    const uint16_t* __restrict__ zrow, uint16_t* __restrict__ sink, uint16_t* __restrict__ xg,
+    float* __restrict__ inv_out, int* __restrict__ sel, float* __restrict__ gate) {
+  constexpr int NTOK = 32 * TT;
+  constexpr int EPAD = 32 * NA;
+  __shared__ float red[NW][TT][NA][16][64];
+  __shared__ float ssr[NW][TT][64];
+  __shared__ float zs[NTOK][EPAD + 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * NTOK;
+  const int kgrp = (lane >> 5) * 8;
+  const int kper = d / (kKStep * NW);  // k-steps per wave
+  const int k0 = wave * kper * kKStep;
+
+  const uint16_t* ap[NA];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    const int e = a * 32 + (lane & 31);
+    ap[a] = (e < E ? wr + (size_t)e * d : zrow) + kgrp + k0;
+  }
+  const uint16_t* hp[TT];
+  uint16_t* xp[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    const int t = t0 + tt * 32 + (lane & 31);
+    const bool valid = t < T;
+    hp[tt] = (valid ? hidden + (size_t)t * d : zrow) + kgrp + k0;
+    xp[tt] = (valid ? xg + (size_t)t * d : sink) + kgrp + k0;
+  }
+  const uint16_t* gp = gain + kgrp + k0;
+
+  f32x16 acc[TT][NA];
+  float ss[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    ss[tt] = 0.f;
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[tt][a][i] = 0.f;
+  }
+
+  // one k-step: x' = g*h split into exact bf16 hi + lo, two MFMAs per tile
+  auto step = [&](const u32x4& gv, const u32x4 (&av)[NA], const u32x4 (&hv)[TT], int ko) {
+    float g[8];
+    unpack8(gv, g);
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      float h[8];
+      unpack8(hv[tt], h);
+      u32x4 bhi, blo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = g[2 * i] * h[2 * i], x1 = g[2 * i + 1] * h[2 * i + 1];
+        ss[tt] = fmaf(h[2 * i], h[2 * i], ss[tt]);
+        ss[tt] = fmaf(h[2 * i + 1], h[2 * i + 1], ss[tt]);
+        const uint32_t hi = pack_bf16x2(x0, x1);
+        bhi[i] = hi;
+        blo[i] = pack_bf16x2(x0 - bf16_lo(hi), x1 - bf16_hi(hi));
+      }
+      stg16(xp[tt] + ko, bhi);
+#pragma unroll
+      for (int a = 0; a < NA; ++a) {
+        acc[tt][a] = mfma_32x32x16(av[a], bhi, acc[tt][a]);
+        acc[tt][a] = mfma_32x32x16(av[a], blo, acc[tt][a]);
+      }
+    }
+  };
+
+  int s = 0;
+  for (; s + kRBatch <= kper; s += kRBatch) {
+    u32x4 gv[kRBatch], av[kRBatch][NA], hv[kRBatch][TT];
+#pragma unroll
+    for (int b = 0; b < kRBatch; ++b) {
+      const int ko = (s + b) * kKStep;
+      gv[b] = ldg16(gp + ko);
+#pragma unroll
+      for (int a = 0; a < NA; ++a) av[b][a] = ldg16(ap[a] + ko);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) hv[b][tt] = ldg16(hp[tt] + ko);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the whole batch of loads in flight together
+#pragma unroll
+    for (int b = 0; b < kRBatch; ++b) step(gv[b], av[b], hv[b], (s + b) * kKStep);
+  }
+  for (; s < kper; ++s) {
+    const int ko = s * kKStep;
+    u32x4 av[NA], hv[TT];
+#pragma unroll
+    for (int a = 0; a < NA; ++a) av[a] = ldg16(ap[a] + ko);
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) hv[tt] = ldg16(hp[tt] + ko);
+    step(ldg16(gp + ko), av, hv, ko);
+  }
+
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    ssr[wave][tt][lane] = ss[tt];
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) red[wave][tt][a][i][lane] = acc[tt][a][i];
+  }
+  __syncthreads();
+
+  // cross-wave sums in a fixed order, one (token, expert) pair per thread:
+  // C[row e][column c] of a 32x32 tile sits in lane c + 32*((e/4)%2),
+  // accumulator element (e/8)*4 + e%4.
+  for (int p = tid; p < NTOK * EPAD; p += NW * 64) {
+    const int t = p % NTOK, e = p / NTOK;
+    const int tt = t >> 5, c = t & 31, a = e >> 5, r = e & 31;
+    const int l = c + 32 * ((r >> 2) & 1), i = (r >> 3) * 4 + (r & 3);
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += red[w][tt][a][i][l];
+    zs[t][e] = v;
+  }
+  __syncthreads();
+
+  if (tid < NTOK) {
+    const int tt = tid >> 5, c = tid & 31;
+    const int t = t0 + tid;
+    float sq = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) sq += ssr[w][tt][c] + ssr[w][tt][c + 32];
+    const float inv = 1.0f / sqrtf(sq / (float)d + eps);
+    float z[EPAD], sc[EPAD];
+#pragma unroll
+    for (int e = 0; e < EPAD; ++e) {
+      z[e] = zs[tid][e] * inv;
+      sc[e] = z[e] + bias[e];  // bias is padded with zeros to a power of two >= EPAD
+    }
+    if (t < T) {
+      // top-k by descending score, exact ties to the lower index; NaN never wins
+      uint64_t taken = 0;
+      int chosen[8];
+      float zc[8];
+      for (int j = 0; j < k; ++j) {
+        int best = -1;
+        float bs = 0.f, bz = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPAD; ++e) {
+          const bool ok = e < E && !((taken >> e) & 1) && (best < 0 || sc[e] > bs);
+          best = ok ? e : best;
+          bs = ok ? sc[e] : bs;
+          bz = ok ? z[e] : bz;
+        }
+        chosen[j] = best;
+        zc[j] = bz;
+        taken |= 1ull << best;
+      }
+      float zmax = -INFINITY, den = 0.f;
+      if (k == 1) {
+#pragma unroll
+        for (int e = 0; e < EPAD; ++e) zmax = e < E ? fmaxf(zmax, z[e]) : zmax;
+#pragma unroll
+        for (int e = 0; e < EPAD; ++e) den += e < E ? expf(z[e] - zmax) : 0.f;
+      } else {
+        for (int j = 0; j < k; ++j) zmax = fmaxf(zmax, zc[j]);
+        for (int j = 0; j < k; ++j) den += expf(zc[j] - zmax);
+      }
+      for (int j = 0; j < k; ++j) {
+        sel[(size_t)t * k + j] = chosen[j];
+        gate[(size_t)t * k + j] = expf(zc[j] - zmax) / den;
+      }
+      inv_out[t] = inv;
+    }
+  }
+
+}
+
+namespace {
+template <int NA, int TT, int NW>
+hipError_t go(const FwdArgs& a) {
+  const int grid = (a.T + 32 * TT - 1) / (32 * TT);
+  return launch(k_router_mfma<NA, TT, NW>, dim3(grid), dim3(NW * 64), a.stream,
+                a.ev[kSlotNormRouter], (const uint16_t*)a.hidden, a.T, a.dim.d,
+                (const uint16_t*)a.wr16, (const uint16_t*)a.gain16, (const float*)a.bias, a.dim.E,
+                a.dim.k, a.dim.eps, (const uint16_t*)a.zrow, (uint16_t*)a.sink,
+                (uint16_t*)a.xn, a.inv, a.sel, a.gate);
+}
+}  // namespace
+
+hipError_t launch_router_mfma(const FwdArgs& a) {
+  return a.dim.E > 32 ? go<2, 1, 8>(a) : go<1, 1, 8>(a);
+}
+
+}  // namespace moe

@@ -1,0 +1,157 @@
+// K1 (bf16 layers, decode-sized batches): RMSNorm statistics + linear router +
+// bias-steered top-k + gates, one workgroup per token.
+//
+// Same computation as the prefill router (ZONOS2 Technical Report,
+// audio-paper-digest page, "Method overview and architecture", items 5 and 6:
+// RMSNorm-normalised input, top-1/top-2 over 16 experts, a per-expert bias that
+// moves the choice but not the gate).  At decode sizes a batch of T <= 64
+// tokens would leave a single workgroup pulling the whole router and every
+// hidden row through one CU, so each token gets its own workgroup: 256 threads
+// own 8-element chunks of the token's row and accumulate, in one pass,
+//   sum h^2,  x' = g * h (stored as bf16 for the experts),
+//   z_raw[e] = sum_i W_r[e][i] * x'_i     (every product exact in fp32).
+// The E partial sums are reduced by a spreading butterfly inside each wave and
+// across the four waves in LDS (fixed order), then one thread applies
+// inv_rms = 1/sqrt(mean(h^2) + eps), adds the bias, picks the top-k and writes
+// the gates.  The dispatch of decode batches happens in the expert kernels.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+template <int EP>
+__global__ __launch_bounds__(256) void k_router_token(
+    const uint16_t* __restrict__ hidden, int d, const uint16_t* __restrict__ wr,
+    const uint16_t* __restrict__ gain, const float* __restrict__ bias, int E, int k, float eps,
+    const uint16_t* __restrict__ zrow, uint16_t* __restrict__ xg, float* __restrict__ inv_out,
+    int* __restrict__ sel, float* __restrict__ gate) {
+  constexpr int NV = EP;
+  constexpr int R = NV >= 64 ? NV / 64 : 1;
+  __shared__ float red[4][NV];
+  __shared__ float ssr[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = blockIdx.x;
+  const uint16_t* hrow = hidden + (size_t)t * d;
+  uint16_t* xrow = xg + (size_t)t * d;
+  const uint16_t* wrow[EP];
+#pragma unroll
+  for (int e = 0; e < EP; ++e) wrow[e] = e < E ? wr + (size_t)e * d : zrow;
+
+  float acc[NV];
+#pragma unroll
+  for (int e = 0; e < NV; ++e) acc[e] = 0.f;
+  float ss = 0.f;
+  constexpr int G = EP < 16 ? EP : 16;  // router rows loaded together
+  for (int c = tid * 8; c < d; c += 256 * 8) {
+    u32x4 wv[G];
+#pragma unroll
+    for (int e = 0; e < G; ++e) wv[e] = ldg16(wrow[e] + c);
+    float h[8], g[8], x[8];
+    unpack8(ldg16(hrow + c), h);
+    unpack8(ldg16(gain + c), g);
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ss = fmaf(h[i], h[i], ss);
+      x[i] = g[i] * h[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    stg16(xrow + c, o);
+#pragma unroll
+    for (int e0 = 0; e0 < EP; e0 += G) {
+      if (e0 > 0) {
+#pragma unroll
+        for (int e = 0; e < G; ++e) wv[e] = ldg16(wrow[e0 + e] + c);
+      }
+#pragma unroll
+      for (int e = 0; e < G; ++e) {
+        float w[8];
+        unpack8(wv[e], w);
+        float s = acc[e0 + e];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = fmaf(w[i], x[i], s);
+        acc[e0 + e] = s;
+      }
+    }
+  }
+  WaveSpread<NV, 32>::run(acc, lane);
+#pragma unroll
+  for (int dlt = 32; dlt >= 1; dlt >>= 1) ss += __shfl_xor(ss, dlt, kWave);
+  if (spread_owner<NV>(lane)) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) red[wave][spread_index<NV>(lane, i)] = acc[i];
+  }
+  if (lane == 0) ssr[wave] = ss;
+  __syncthreads();
+
+  if (tid == 0) {
+    const float sq = ((ssr[0] + ssr[1]) + ssr[2]) + ssr[3];
+    const float inv = 1.0f / sqrtf(sq / (float)d + eps);
+    float z[EP], sc[EP];
+#pragma unroll
+    for (int e = 0; e < EP; ++e) {
+      z[e] = (((red[0][e] + red[1][e]) + red[2][e]) + red[3][e]) * inv;
+      sc[e] = z[e] + bias[e];  // bias is zero-padded to 64 entries
+    }
+    // top-k by descending score, exact ties to the lower index; NaN never wins
+    uint64_t taken = 0;
+    int chosen[8];
+    float zc[8];
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      float bs = 0.f, bz = 0.f;
+#pragma unroll
+      for (int e = 0; e < EP; ++e) {
+        const bool ok = e < E && !((taken >> e) & 1) && (best < 0 || sc[e] > bs);
+        best = ok ? e : best;
+        bs = ok ? sc[e] : bs;
+        bz = ok ? z[e] : bz;
+      }
+      chosen[j] = best;
+      zc[j] = bz;
+      taken |= 1ull << best;
+    }
+    float zmax = -INFINITY, den = 0.f;
+    if (k == 1) {
+#pragma unroll
+      for (int e = 0; e < EP; ++e) zmax = e < E ? fmaxf(zmax, z[e]) : zmax;
+#pragma unroll
+      for (int e = 0; e < EP; ++e) den += e < E ? expf(z[e] - zmax) : 0.f;
+    } else {
+      for (int j = 0; j < k; ++j) zmax = fmaxf(zmax, zc[j]);
+      for (int j = 0; j < k; ++j) den += expf(zc[j] - zmax);
+    }
+    for (int j = 0; j < k; ++j) {
+      sel[(size_t)t * k + j] = chosen[j];
+      gate[(size_t)t * k + j] = expf(zc[j] - zmax) / den;
+    }
+    inv_out[t] = inv;
+  }
+}
+
+namespace {
+template <int EP>
+hipError_t go(const FwdArgs& a) {
+  return launch(k_router_token<EP>, dim3(a.T), dim3(256), a.stream, a.ev[kSlotNormRouter],
+                (const uint16_t*)a.hidden, a.dim.d, (const uint16_t*)a.wr16,
+                (const uint16_t*)a.gain16, (const float*)a.bias, a.dim.E, a.dim.k, a.dim.eps,
+                (const uint16_t*)a.zrow, (uint16_t*)a.xn, a.inv, a.sel, a.gate);
+}
+}  // namespace
+
+hipError_t launch_router_token(const FwdArgs& a) {
+  switch (a.dim.EP) {
+    case 1: return go<1>(a);
+    case 2: return go<2>(a);
+    case 4: return go<4>(a);
+    case 8: return go<8>(a);
+    case 16: return go<16>(a);
+    case 32: return go<32>(a);
+    case 64: return go<64>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace moe

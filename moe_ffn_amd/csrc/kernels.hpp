@@ -1,10 +1,28 @@
 // Host-side launchers of the MoE layer's kernels (private to the library).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace moe {
+
+// Kernel slots of one forward, in launch order (per-kernel timing).
+enum Slot { kSlotNormRouter = 0, kSlotPermute = 1, kSlotExpertsA = 2, kSlotExpertsB = 3,
+            kSlotCombine = 4, kNumSlots = 5 };
+
+// Optional start/stop events carried by a kernel's own dispatch packet.
+struct KEv {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+template <typename F, typename... Args>
+inline hipError_t launch(F kernel, dim3 grid, dim3 block, hipStream_t s, const KEv& ev,
+                         Args... args) {
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+  return hipGetLastError();
+}
 
 // Packed expert-weight geometry (bf16).  Both banks are stored as 1 KiB blocks,
 // one per (32-row tile, 16-wide k step), each block in MFMA 32x32x16 operand
@@ -32,14 +50,17 @@ struct FwdArgs {
   const void* hidden;  // [T, d]
   void* out;           // [T, d]
   // layer-owned parameters
-  const float* wrg;    // [EP, d] fp32: W_r[e][i] * g[i] (zero rows e >= E)
+  const float* wrg;    // [EP, d] fp32: W_r[e][i] * g[i] (zero rows e >= E), fp32 layers
   const float* gain;   // [d] fp32
+  const void* wr16;    // [E, d] bf16 router weights as given (bf16 layers)
+  const void* gain16;  // [d] bf16 gain as given (bf16 layers)
   const float* bias;   // [E] fp32
   const void* wgu;     // packed gate/up bank (bf16) or canonical [E,F,d] (f32)
   const void* wup;     // f32 only: canonical up weights [E,F,d]
   const void* wd;      // packed down bank (bf16) or canonical [E,d,F] (f32)
   // per-call buffers (workspace or caller-provided routing outputs)
-  void* xn;            // [T, d] normalised activations (bf16 or f32)
+  void* xn;            // [T, d] gain-scaled activations g * h (bf16 or f32)
+  float* inv;          // [T] 1 / rms of each token's hidden state
   int* sel;            // [T, k]
   float* gate;         // [T, k]
   int* counts;         // [E]
@@ -51,11 +72,15 @@ struct FwdArgs {
   int max_tiles;
   void* act;           // [n, F] SwiGLU activations (bf16 or f32)
   float* ybuf;         // [n, d] fp32 expert outputs (k >= 2 only)
+  const void* zrow;    // max(d, F) zero elements (16-byte aligned), read-only
+  void* sink;          // max(d, F) elements that absorb stores of lanes without a token
   hipStream_t stream;
-  hipEvent_t ev_mid;   // when set, recorded between the two expert kernels
+  KEv ev[kNumSlots];   // per-kernel timing events (null when not timing)
 };
 
-hipError_t launch_norm_router(const FwdArgs& a);
+hipError_t launch_norm_router(const FwdArgs& a);   // fp32 layers
+hipError_t launch_router_mfma(const FwdArgs& a);   // bf16 layers, T*k > kStreamMaxAssign
+hipError_t launch_router_token(const FwdArgs& a);  // bf16 layers, T*k <= kStreamMaxAssign
 hipError_t launch_route_permute(const FwdArgs& a);
 hipError_t launch_experts_stream(const FwdArgs& a);
 hipError_t launch_experts_tile(const FwdArgs& a);

@@ -2,10 +2,15 @@
 // create-time weight packing and the launch sequence of one forward.
 //
 // Forward on one stream, no host synchronisation, no allocation:
-//   K1 fused RMSNorm + router + top-k + gates        (k_norm_router.hip)
-//   K2 histogram + scan + stable permutation + tiles (k_route_permute.hip)
-//   K3 grouped SwiGLU experts: weight stream for decode-sized batches, LDS-tiled
-//      grouped GEMM for larger ones, fp32 VALU for fp32 layers
+// bf16 layers, decode-sized batches (T * top_k <= 64):
+//   K1 per-token RMSNorm + router + top-k + gates (k_router_token.hip)
+//   K3 weight-streaming gate/up and down kernels, each workgroup deriving its
+//      expert's dispatch from the routing choice (k_expert_stream.hip)
+// bf16 layers, larger batches:
+//   K1 RMSNorm + router on bf16 MFMA + top-k + gates (k_router_mfma.hip)
+//   K2 histogram + scan + stable permutation + GEMM tile map (k_route_permute.hip)
+//   K3 LDS-tiled grouped GEMMs, gate/up with SiLU epilogue then down (k_expert_tile.hip)
+// fp32 layers: VALU router (k_norm_router.hip), K2, VALU experts (k_expert_f32.hip)
 //   K4 gate-weighted combine (k >= 2; folded into K3 for k = 1)
 #include <hip/hip_runtime.h>
 
@@ -65,12 +70,15 @@ struct moe_layer {
   float* wrg;
   float* gain32;
   float* bias;
+  void* wr16;
+  void* gain16;
   void* wgu;
   void* wup;
   void* wd;
   // workspace (one allocation)
   void* ws;
   void* xn;
+  float* inv;
   int* sel;
   float* gate;
   int* counts;
@@ -81,8 +89,11 @@ struct moe_layer {
   int* tilemap;
   void* act;
   float* ybuf;
-  // optional per-kernel event timing (6 events per recorded forward)
+  void* zrow;
+  void* sink;
+  // optional per-kernel event timing (start/stop per kernel of a recorded forward)
   std::vector<hipEvent_t> tev;
+  std::vector<uint8_t> tslots;  // per recorded forward: bit i set if slot i ran
   int t_max;
   int t_used;
   bool timing;
@@ -95,11 +106,13 @@ T* at(void* base, size_t off) {
   return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
 }
 
-constexpr int kEventsPerForward = MOE_TIMED_SLOTS + 1;
+static_assert(moe::kNumSlots == MOE_TIMED_SLOTS, "timing slots");
+constexpr int kEventsPerForward = 2 * MOE_TIMED_SLOTS;  // start and stop per kernel
 
 void drop_events(moe_layer* L) {
   for (hipEvent_t e : L->tev) (void)hipEventDestroy(e);
   L->tev.clear();
+  L->tslots.clear();
   L->timing = false;
   L->t_max = L->t_used = 0;
 }
@@ -194,7 +207,10 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_wei
   Carver pc;
   const size_t o_wrg = pc.take(EP * d * 4);
   const size_t o_gain = pc.take(d * 4);
-  const size_t o_bias = pc.take(E * 4);
+  const size_t o_bias = pc.take(64 * 4);  // zero-padded to 64 experts
+  const bool bf16 = cfg->dtype == MOE_DTYPE_BF16;
+  const size_t o_wr16 = bf16 ? pc.take(E * d * 2) : 0;
+  const size_t o_g16 = bf16 ? pc.take(d * 2) : 0;
   const size_t o_wgu = pc.take(E * F * d * es * (cfg->dtype == MOE_DTYPE_BF16 ? 2 : 1));
   const size_t o_wup = cfg->dtype == MOE_DTYPE_F32 ? pc.take(E * F * d * es) : 0;
   const size_t o_wd = pc.take(E * d * F * es);
@@ -208,6 +224,8 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_wei
   L->wrg = at<float>(L->params, o_wrg);
   L->gain32 = at<float>(L->params, o_gain);
   L->bias = at<float>(L->params, o_bias);
+  L->wr16 = bf16 ? at<void>(L->params, o_wr16) : nullptr;
+  L->gain16 = bf16 ? at<void>(L->params, o_g16) : nullptr;
   L->wgu = at<void>(L->params, o_wgu);
   L->wup = cfg->dtype == MOE_DTYPE_F32 ? at<void>(L->params, o_wup) : nullptr;
   L->wd = at<void>(L->params, o_wd);
@@ -215,6 +233,7 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_wei
   // workspace
   Carver wc;
   const size_t o_xn = wc.take((size_t)L->max_tokens * d * es);
+  const size_t o_inv = wc.take((size_t)L->max_tokens * 4);
   const size_t o_sel = wc.take(nmax * 4);
   const size_t o_gate = wc.take(nmax * 4);
   const size_t o_cnt = wc.take(E * 4);
@@ -225,6 +244,9 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_wei
   const size_t o_tm = wc.take((size_t)(1 + L->max_tiles) * 4);
   const size_t o_act = wc.take(nmax * F * es);
   const size_t o_y = k > 1 ? wc.take(nmax * d * 4) : 0;
+  const size_t zbytes = (d > F ? d : F) * 4;
+  const size_t o_z = wc.take(zbytes);
+  const size_t o_sink = wc.take(zbytes);
   he = hipMalloc(&L->ws, wc.off);
   if (he != hipSuccess) {
     L->ws = nullptr;
@@ -233,6 +255,7 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_wei
     return fail(MOE_ERR_OOM, std::string("workspace allocation: ") + hipGetErrorString(he));
   }
   L->xn = at<void>(L->ws, o_xn);
+  L->inv = at<float>(L->ws, o_inv);
   L->sel = at<int>(L->ws, o_sel);
   L->gate = at<float>(L->ws, o_gate);
   L->counts = at<int>(L->ws, o_cnt);
@@ -243,12 +266,20 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_wei
   L->tilemap = at<int>(L->ws, o_tm);
   L->act = at<void>(L->ws, o_act);
   L->ybuf = k > 1 ? at<float>(L->ws, o_y) : nullptr;
+  L->zrow = at<void>(L->ws, o_z);
+  L->sink = at<void>(L->ws, o_sink);
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   he = moe::launch_prep_router(w->w_router, w->rms_gain, cfg->dtype, (int)E, (int)EP, (int)d,
                                L->wrg, L->gain32, s);
+  if (he == hipSuccess) he = hipMemsetAsync(L->bias, 0, 64 * 4, s);
   if (he == hipSuccess)
     he = hipMemcpyAsync(L->bias, w->b_router, E * 4, hipMemcpyDeviceToDevice, s);
+  if (he == hipSuccess) he = hipMemsetAsync(L->zrow, 0, zbytes, s);
+  if (he == hipSuccess && bf16)
+    he = hipMemcpyAsync(L->wr16, w->w_router, E * d * 2, hipMemcpyDeviceToDevice, s);
+  if (he == hipSuccess && bf16)
+    he = hipMemcpyAsync(L->gain16, w->rms_gain, d * 2, hipMemcpyDeviceToDevice, s);
   if (he == hipSuccess) {
     if (cfg->dtype == MOE_DTYPE_BF16) {
       he = moe::launch_pack_gateup(static_cast<const uint16_t*>(w->w_gate),
@@ -314,10 +345,13 @@ moe_status_t moe_layer_forward(moe_layer_t* L, const void* hidden, int32_t T, vo
   a.wrg = L->wrg;
   a.gain = L->gain32;
   a.bias = L->bias;
+  a.wr16 = L->wr16;
+  a.gain16 = L->gain16;
   a.wgu = L->wgu;
   a.wup = L->wup;
   a.wd = L->wd;
   a.xn = L->xn;
+  a.inv = L->inv;
   a.sel = (routing && routing->sel) ? routing->sel : L->sel;
   a.gate = (routing && routing->gate) ? routing->gate : L->gate;
   a.counts = (routing && routing->counts) ? routing->counts : L->counts;
@@ -329,38 +363,38 @@ moe_status_t moe_layer_forward(moe_layer_t* L, const void* hidden, int32_t T, vo
   a.max_tiles = (a.n + moe::kTileTokens - 1) / moe::kTileTokens + L->dim.E;
   a.act = L->act;
   a.ybuf = L->ybuf;
+  a.zrow = L->zrow;
+  a.sink = L->sink;
   a.stream = reinterpret_cast<hipStream_t>(stream);
-  a.ev_mid = nullptr;
-  hipEvent_t* ev = nullptr;
   if (L->timing && L->t_used < L->t_max) {
-    ev = &L->tev[(size_t)L->t_used * kEventsPerForward];
+    const hipEvent_t* ev = &L->tev[(size_t)L->t_used * kEventsPerForward];
+    for (int i = 0; i < moe::kNumSlots; ++i) {
+      a.ev[i].start = ev[2 * i];
+      a.ev[i].stop = ev[2 * i + 1];
+    }
     ++L->t_used;
   }
-  auto mark = [&](int i) -> hipError_t {
-    return ev != nullptr ? hipEventRecord(ev[i], a.stream) : hipSuccess;
-  };
+  const bool bf16 = L->dim.dtype == MOE_DTYPE_BF16;
+  const bool decode = bf16 && a.n <= moe::kStreamMaxAssign;
+  if (L->timing && L->t_used > 0 && a.ev[0].start != nullptr)
+    L->tslots[L->t_used - 1] = (uint8_t)(0x0d | (decode ? 0 : 0x02) | (L->dim.k > 1 ? 0x10 : 0));
 
-  if ((he = mark(0)) != hipSuccess) return hip_fail(he, "event record");
-  he = moe::launch_norm_router(a);
-  if (he != hipSuccess) return hip_fail(he, "norm/router launch");
-  if ((he = mark(1)) != hipSuccess) return hip_fail(he, "event record");
-  he = moe::launch_route_permute(a);
-  if (he != hipSuccess) return hip_fail(he, "permute launch");
-  if ((he = mark(2)) != hipSuccess) return hip_fail(he, "event record");
-  if (ev != nullptr) a.ev_mid = ev[3];
-  if (L->dim.dtype == MOE_DTYPE_F32)
-    he = moe::launch_experts_f32(a);
-  else if (a.n <= moe::kStreamMaxAssign)
+  if (decode) {
+    he = moe::launch_router_token(a);
+    if (he != hipSuccess) return hip_fail(he, "router launch");
     he = moe::launch_experts_stream(a);
-  else
-    he = moe::launch_experts_tile(a);
+  } else {
+    he = bf16 ? moe::launch_router_mfma(a) : moe::launch_norm_router(a);
+    if (he != hipSuccess) return hip_fail(he, "router launch");
+    he = moe::launch_route_permute(a);
+    if (he != hipSuccess) return hip_fail(he, "permute launch");
+    he = bf16 ? moe::launch_experts_tile(a) : moe::launch_experts_f32(a);
+  }
   if (he != hipSuccess) return hip_fail(he, "expert launch");
-  if ((he = mark(4)) != hipSuccess) return hip_fail(he, "event record");
   if (L->dim.k > 1) {
     he = moe::launch_combine(a);
     if (he != hipSuccess) return hip_fail(he, "combine launch");
   }
-  if ((he = mark(5)) != hipSuccess) return hip_fail(he, "event record");
   if (L->debug_sync) {
     he = hipStreamSynchronize(a.stream);
     if (he != hipSuccess) return hip_fail(he, "forward (MOE_DEBUG_SYNC)");
@@ -386,6 +420,7 @@ moe_status_t moe_layer_timing_start(moe_layer_t* L, int32_t max_forwards) {
     return fail(MOE_ERR_INVALID_ARG, "max_forwards must be in [1, 65536]");
   drop_events(L);
   L->tev.resize((size_t)max_forwards * kEventsPerForward);
+  L->tslots.assign((size_t)max_forwards, 0);
   for (size_t i = 0; i < L->tev.size(); ++i) {
     hipError_t he = hipEventCreate(&L->tev[i]);
     if (he != hipSuccess) {
@@ -409,12 +444,13 @@ moe_status_t moe_layer_timing_stop(moe_layer_t* L, float* ms_sum, int32_t* n_for
   for (int i = 0; i < MOE_TIMED_SLOTS; ++i) ms_sum[i] = 0.f;
   *n_forwards = L->t_used;
   hipError_t he = hipSuccess;
-  if (L->t_used > 0) he = hipEventSynchronize(L->tev[(size_t)L->t_used * kEventsPerForward - 1]);
   for (int f = 0; f < L->t_used && he == hipSuccess; ++f) {
     const hipEvent_t* ev = &L->tev[(size_t)f * kEventsPerForward];
     for (int i = 0; i < MOE_TIMED_SLOTS && he == hipSuccess; ++i) {
+      if (!((L->tslots[f] >> i) & 1)) continue;
       float ms = 0.f;
-      he = hipEventElapsedTime(&ms, ev[i], ev[i + 1]);
+      he = hipEventSynchronize(ev[2 * i + 1]);
+      if (he == hipSuccess) he = hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]);
       ms_sum[i] += ms;
     }
   }

@@ -12,7 +12,9 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_layer.so")
+# The in-tree build; MOE_LAYER_LIB may name another build of the same sources.
+LIB_PATH = os.environ.get("MOE_LAYER_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libmoe_layer.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_OOM, MOE_ERR_HIP, MOE_ERR_UNSUPPORTED = range(5)
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_OOM", 3: "MOE_ERR_HIP",
