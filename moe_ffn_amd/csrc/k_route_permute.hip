@@ -101,10 +101,12 @@ __global__ __launch_bounds__(1024) void k_route_permute(
     base += add;
   }
 
-  // tile map for the grouped GEMM: entry = expert << 16 | m-tile
+  // tile map for the grouped GEMM: count, entries (expert << 16 | m-tile),
+  // then the first tile of each expert (E + 1 values)
   if (tilemap != nullptr) {
     const int total = min(tstart[E], max_tiles);
     if (tid == 0) tilemap[0] = total;
+    if (tid <= E) tilemap[1 + max_tiles + tid] = min(tstart[tid], max_tiles);
     for (int e = 0; e < E; ++e) {
       const int s0 = tstart[e], nt = tstart[e + 1] - tstart[e];
       for (int i = tid; i < nt; i += 1024)

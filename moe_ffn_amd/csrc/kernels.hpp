@@ -33,8 +33,11 @@ constexpr int kTileRows = 32;
 constexpr int kKStep = 16;
 constexpr int kBlockElems = 64 * 8;  // 512 bf16 = 1 KiB
 
-// Prefill tiles: 256 weight rows x 128 tokens x 64 k per workgroup.
-constexpr int kTileTokens = 128;
+// Prefill tiles: 256 weight rows x kTileTokens tokens x 64 k per workgroup.
+#ifndef MOE_TILE_TOK
+#define MOE_TILE_TOK 128
+#endif
+constexpr int kTileTokens = MOE_TILE_TOK;
 // Decode path is used while T * top_k is at most this many assignments.
 constexpr int kStreamMaxAssign = 64;
 
@@ -68,7 +71,7 @@ struct FwdArgs {
   int* gather;         // [n]
   int* scatter;        // [n]
   int* slot_expert;    // [n]
-  int* tilemap;        // [1 + max_tiles]: count, then (expert << 16 | m-tile)
+  int* tilemap;        // [1 + max_tiles + E + 1]: count, (expert << 16 | m-tile), tile starts
   int max_tiles;
   void* act;           // [n, F] SwiGLU activations (bf16 or f32)
   float* ybuf;         // [n, d] fp32 expert outputs (k >= 2 only)

@@ -241,7 +241,7 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_wei
   const size_t o_gat = wc.take(nmax * 4);
   const size_t o_sca = wc.take(nmax * 4);
   const size_t o_sle = wc.take(nmax * 4);
-  const size_t o_tm = wc.take((size_t)(1 + L->max_tiles) * 4);
+  const size_t o_tm = wc.take((size_t)(1 + L->max_tiles + 65) * 4);
   const size_t o_act = wc.take(nmax * F * es);
   const size_t o_y = k > 1 ? wc.take(nmax * d * 4) : 0;
   const size_t zbytes = (d > F ? d : F) * 4;
