@@ -40,13 +40,76 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+# sources that decide the dominant kernel's memory traffic (its counters are
+# void once any of them changes)
+DOMINANT_SOURCES = {"k_gateup_stream": ["k_expert_stream.hip", "common.hpp", "kernels.hpp"],
+                    "k_expert_tile<0>": ["k_expert_tile.hip", "common.hpp", "kernels.hpp"]}
+
+
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "moe_ffn_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in DOMINANT_SOURCES[kernel]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
+
+
+def dominant_kernel_name(cfg) -> str:
+    return "k_gateup_stream" if cfg.T * cfg.k <= 64 else "k_expert_tile<0>"
+
+
+def _counter_means(run_dir: str) -> dict:
+    """Mean counter value (KiB) per dispatch of each kernel in a rocprofv3 --pmc run."""
+    import csv
+    import re
+    sums: dict = {}
+    for r in csv.DictReader(open(os.path.join(run_dir, "run_counter_collection.csv"))):
+        name = r["Kernel_Name"]
+        m = re.match(r"(?:void )?(?:moe::)?([A-Za-z_]\w*(?:<[^>(]*>)?)", name)
+        key = "torch_neg" if "neg_kernel" in name else (m.group(1) if m else name)
+        s = sums.setdefault(key, [0.0, 0])
+        s[0] += float(r["Counter_Value"])
+        s[1] += 1
+    return {k: v[0] / v[1] for k, v in sums.items()}
+
+
+def ingest_counters(pmc_dir: str) -> None:
+    """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs into profiles/traffic.json.
+
+    Expects pmc_dir/copy_fetch and pmc_dir/copy_write (bench.py
+    --copy-calibration 1024 under --pmc FETCH_SIZE, resp. WRITE_SIZE) and
+    pmc_dir/c<N>_fetch, pmc_dir/c<N>_write for each --config N profiled.  Each
+    counter is scaled by the bytes the copy kernel really moves over what the
+    same counter reads for it."""
+    from synth.configs import CONFIGS
+    copy_bytes = 1024 << 20
+    cf = _counter_means(os.path.join(pmc_dir, "copy_fetch"))["torch_neg"] * 1024
+    cw = _counter_means(os.path.join(pmc_dir, "copy_write"))["torch_neg"] * 1024
+    ffac, wfac = copy_bytes / cf, copy_bytes / cw
+    out = {"_calibration": {"copy_bytes_each_way": copy_bytes, "fetch_counter_bytes": cf,
+                            "write_counter_bytes": cw, "fetch_factor": round(ffac, 5),
+                            "write_factor": round(wfac, 5)}}
+    for cid in (1, 2, 3, 4):
+        fd, wd = (os.path.join(pmc_dir, f"c{cid}_{x}") for x in ("fetch", "write"))
+        if not (os.path.isdir(fd) and os.path.isdir(wd)):
+            continue
+        cfg = CONFIGS[cid]
+        fm, wm = _counter_means(fd), _counter_means(wd)
+        kernels = {}
+        for kname in fm:
+            if kname.startswith("k_") and kname in wm and not kname.startswith("k_pack") \
+                    and not kname.startswith("k_prep"):
+                kernels[kname] = {"fetch_bytes": round(fm[kname] * 1024 * ffac),
+                                  "write_bytes": round(wm[kname] * 1024 * wfac)}
+        dom = dominant_kernel_name(cfg)
+        dk = next(k for k in kernels if k == dom or k.startswith(dom + "<"))
+        out[cfg.name] = {"kernel": dom, "source_hash": kernel_source_hash(dom),
+                         "bytes_per_launch": kernels[dk]["fetch_bytes"] + kernels[dk]["write_bytes"],
+                         "kernels": kernels}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def dominant_kernel(cfg, counts):
@@ -118,7 +181,15 @@ def main():
     ap.add_argument("--instances", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run only a plain device copy (dst = -src, MIB MiB read and MIB MiB\n"
+                         "written) five times, to scale the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--ingest-counters", metavar="DIR",
+                    help="no GPU: write profiles/traffic.json from rocprofv3 --pmc runs in DIR")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(args.ingest_counters)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the layer runs data-parallel with no exchange between "
@@ -137,6 +208,18 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
+
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"kernel": "elementwise neg (torch)",
+                                               "bytes_read": nbytes, "bytes_written": nbytes,
+                                               "launches": 5}}), flush=True)
+        return
 
     t_gen = time.perf_counter()
     inp = make_inputs(args.config)
@@ -212,7 +295,8 @@ def main():
         try:
             with open(TRAFFIC_FILE) as f:
                 tr = json.load(f).get(cfg.name, {})
-            if tr.get("source_hash") == kernel_source_hash() and tr.get("kernel") == dom["kernel"]:
+            if tr.get("kernel") == dom["kernel"] and \
+                    tr.get("source_hash") == kernel_source_hash(dom["kernel"]):
                 traffic = tr.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
