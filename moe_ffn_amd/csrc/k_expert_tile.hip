@@ -6,17 +6,18 @@
 //   MODE 0  act[slot, f] = bf16( SiLU(x W_gate^T) * (x W_up^T) )   K = d_model
 //   MODE 1  y[slot, m]   = act[slot] W_down^T                       K = d_ff
 //           k = 1: out[token] = bf16(gate * y); k > 1: y kept in fp32.
-// A workgroup computes a 256-weight-row x 256-token tile: four waves stacked
-// along the weight rows, each owning two 32-row MFMA tiles against all eight
-// 32-token tiles (16 accumulators of 32x32 = 256 registers).  Weights are read
-// straight from the packed bank (MFMA operand order, 1 KiB per wave-wide load)
-// into registers, eight k-steps ahead, so they never pass through LDS.  Only
-// the token tile is shared, staged in LDS in operand order (conflict-free
-// 1 KiB reads) from rows gathered on load through the expert-ordered slot
-// list; it is fetched two k-tiles ahead and double-buffered, one barrier per
-// 64-wide k-tile.  One workgroup per CU (the register file holds the deep
-// queues).  Partial token tiles (the tail of each expert) run a variant that
-// skips the empty 32-token tiles.
+// A workgroup computes a 256-weight-row x 128-token tile: four waves stacked
+// along the weight rows, each owning two 32-row MFMA tiles against all four
+// 32-token tiles (8 accumulators of 32x32).  Weights are read straight from
+// the packed bank (MFMA operand order, 1 KiB per wave-wide load) into
+// registers, four k-steps ahead, so they never pass through LDS.  Only the
+// token tile is shared: rows gathered on load through the expert-ordered slot
+// list (8 rows x 128 contiguous bytes per wave-wide load) are written to LDS in
+// operand order (conflict-free 1 KiB reads), three 64-wide k-tiles in flight
+// (two in registers, one in LDS) and one barrier per k-tile.  Two workgroups
+// per CU, so one's barrier and load waits overlap the other's MFMAs.  Partial
+// token tiles (the tail of each expert) run a variant that skips the empty
+// 32-token tiles.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -24,24 +25,22 @@ namespace moe {
 
 namespace {
 constexpr int kTT = kTileTokens / 32;      // 32-token MFMA tiles per workgroup (4)
-constexpr int kCons = 4;                   // consumer waves (MFMA), stacked along weight rows
-constexpr int kProd = 4;                   // producer waves (token staging)
-constexpr int kThreads = (kCons + kProd) * 64;
-constexpr int kWR = 2;                     // 32-row weight tiles per consumer wave
-constexpr int kRowsWG = kCons * kWR * 32;  // 256 weight rows per workgroup
-constexpr int kPre = 8;                    // k-steps of weight loads in flight per consumer
+constexpr int kWaves = 4;                  // waves per workgroup, stacked along weight rows
+constexpr int kWR = 2;                     // 32-row weight tiles per wave
+constexpr int kRowsWG = kWaves * kWR * 32; // 256 weight rows per workgroup
+constexpr int kPre = 4;                    // k-steps of weight loads in flight per wave
 constexpr int kKT = 64;                    // k per LDS stage of the token tile
 constexpr int kBlk = kTT * (kKT / kKStep); // 1 KiB operand blocks per token stage (16)
-constexpr int kStages = 3;                 // LDS ring of token stages
-constexpr int kPC = kBlk * 64 / (kProd * 64);  // 16-byte chunks per producer thread per stage (4)
+constexpr int kBW = kBlk / kWaves;         // blocks staged by each wave per stage
+constexpr int kTPW = kTT / kWaves;         // token tiles staged by each wave
 
 struct TileCtx {
-  const uint16_t* wa;        // consumer: first weight tile of this wave (lane offset applied)
-  size_t tile_elems;         // elements of one packed 32-row tile
-  int ksteps;                // K / 16
-  const uint16_t* brow[kPC]; // producer: source of each staged chunk (k offset applied)
-  int bdst;                  // producer: LDS index (16-byte units) of chunk 0
-  int lane;
+  const uint16_t* wa;     // this wave's first weight tile (lane offset applied)
+  size_t tile_elems;      // elements of one packed 32-row tile
+  int ksteps;             // K / 16
+  const uint16_t* brow[kBW];  // this thread's source for each staged chunk (k offset applied)
+  int bdst;                   // LDS index (16-byte units) of chunk 0; chunk j adds j * kBlk*64/kBW
+  int wave, lane;
 };
 
 __device__ __forceinline__ void load_a(const TileCtx& c, int s, u32x4 (&q)[kWR]) {
@@ -50,18 +49,19 @@ __device__ __forceinline__ void load_a(const TileCtx& c, int s, u32x4 (&q)[kWR])
   for (int r = 0; r < kWR; ++r) q[r] = ldg16(c.wa + r * c.tile_elems + (size_t)sc * kBlockElems);
 }
 
-// Producer thread pt copies 16-byte chunks j = 0..kPC-1 of the stage: row
-// (j*256 + pt)/8 of the token tile, k-chunk pt%8 -- each wave-wide load reads
-// 8 rows x 128 contiguous bytes.  The LDS write scatters each chunk to its
-// place in MFMA operand order: block (row/32)*4 + kc/2, lane (kc%2)*32 + row%32.
-__device__ __forceinline__ void load_b(const TileCtx& c, int kt, int nkt, u32x4 (&p)[kPC]) {
+// Token staging: the workgroup's 256 threads copy a kTileTokens x 64 slice of
+// gathered rows per k-tile, each wave-wide load reading 8 rows x 128 contiguous
+// bytes (8 full cache lines): thread t, chunk j covers row r = (j*256 + t) / 8
+// and 16-byte k-chunk kc = t % 8.  The LDS write scatters each chunk to its
+// place in MFMA operand order: block (r/32)*4 + kc/2, lane (kc%2)*32 + r%32.
+__device__ __forceinline__ void load_b(const TileCtx& c, int kt, int nkt, u32x4 (&p)[kBW]) {
   const int kc = kt < nkt ? kt : nkt - 1;
 #pragma unroll
-  for (int j = 0; j < kPC; ++j) p[j] = ldg16(c.brow[j] + kc * kKT);
+  for (int j = 0; j < kBW; ++j) p[j] = ldg16(c.brow[j] + kc * kKT);
 }
-__device__ __forceinline__ void store_b(u32x4* buf, const TileCtx& c, const u32x4 (&p)[kPC]) {
+__device__ __forceinline__ void store_b(u32x4* buf, const TileCtx& c, const u32x4 (&p)[kBW]) {
 #pragma unroll
-  for (int j = 0; j < kPC; ++j) buf[c.bdst + j * 256] = p[j];
+  for (int j = 0; j < kBW; ++j) buf[c.bdst + j * (kBlk * 64 / kBW)] = p[j];
 }
 
 template <int NT>
@@ -92,67 +92,59 @@ __device__ __forceinline__ void step_schedule() {
   __builtin_amdgcn_sched_group_barrier(0x020, kWR, 0);
 }
 
-// Consumer waves: multiply k-tile kt from stage kt % 3.  Per k-step the token
-// operands of the next k-step are read into a second register set while this
-// k-step's MFMAs run; at the last k-step of a k-tile the next stage (written
-// two k-tiles ago, published by the previous barrier) is already readable.
-// The weight queue runs kPre k-steps ahead; these waves issue no other global
-// load, so nothing slow can sit ahead of a weight load in the in-order return
-// queue.  Two k-tiles per iteration keep the queue slots static.
+// Main loop over K for a tile whose first NT 32-token tiles hold tokens.
+// Software pipeline, per k-step: the token operands of the next k-step are
+// read from LDS into a second register set while this k-step's 2*NT MFMAs run;
+// the weight queue runs kPre k-steps ahead.  Per 64-wide k-tile the staged
+// token slice of the next k-tile is written to the other LDS buffer and the
+// barrier placed before the last k-step, so even the first operands of a
+// k-tile are read under MFMA work; the token loads of the k-tile after that
+// are already in flight.  Two k-tiles per iteration keep every queue slot and
+// buffer static; loads are unconditional (clamped), so nothing in the loop
+// branches.
 template <int NT>
-__device__ __forceinline__ void consumer_loop(const TileCtx& c, u32x4 (*lds)[kBlk * 64],
+__device__ __forceinline__ void tile_mainloop(const TileCtx& c, u32x4 (*lds)[kBlk * 64],
                                               f32x16 (&acc)[kWR][kTT]) {
   const int nkt = c.ksteps / (kKT / kKStep);
   u32x4 qa[kPre][kWR], bc[NT], bn[NT];
+  // The prologue issues its loads in the loop's own order (stage k+1, stage
+  // k+2, then the weight queue), so the wait counts the compiler derives at the
+  // loop head are the steady-state ones rather than a tighter prologue bound.
+  u32x4 pbs[2][kBW];  // token stages k2+1 and k2+2 in flight
+  load_b(c, 0, nkt, pbs[0]);
+  store_b(lds[0], c, pbs[0]);
+  load_b(c, 1, nkt, pbs[1]);
+  load_b(c, 2, nkt, pbs[0]);
 #pragma unroll
   for (int i = 0; i < kPre; ++i) load_a(c, i, qa[i]);
-  __syncthreads();  // stages 0 and 1 published
+  __syncthreads();
   read_b<NT>(lds[0], 0, c.lane, bc);
-  int st = 0;  // stage of the current k-tile
   for (int kt = 0; kt < nkt; kt += 2) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int k2 = kt + half;
-      const int nst = st == kStages - 1 ? 0 : st + 1;
-      const u32x4* buf = lds[st];
+      const u32x4* buf = lds[half];
+      u32x4* nbuf = lds[half ^ 1];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q = half * 4 + i;
-        read_b<NT>(i < 3 ? buf : lds[nst], i < 3 ? i + 1 : 0, c.lane, bn);
+      for (int i = 0; i < 3; ++i) {
+        const int q = (half * 4 + i) % kPre;
+        read_b<NT>(buf, i + 1, c.lane, bn);
         mac<NT>(qa[q], bc, acc);
         load_a(c, k2 * 4 + i + kPre, qa[q]);
         step_schedule<NT>();
 #pragma unroll
         for (int j = 0; j < NT; ++j) bc[j] = bn[j];
       }
+      store_b(nbuf, c, pbs[half ^ 1]);
       __syncthreads();
-      st = nst;
-    }
-  }
-}
-
-// Producer waves: at k-tile kt write stage (kt+2) % 3 with the token slice of
-// k-tile kt+2 (its loads were issued during k-tile kt-1) and issue the loads of
-// k-tile kt+3; the stage being written was last read before the previous
-// barrier.  Same number of barriers as the consumers.
-__device__ __forceinline__ void producer_loop(const TileCtx& c, u32x4 (*lds)[kBlk * 64]) {
-  const int nkt = c.ksteps / (kKT / kKStep);
-  u32x4 pb[2][kPC];
-  load_b(c, 0, nkt, pb[0]);
-  load_b(c, 1, nkt, pb[1]);
-  store_b(lds[0], c, pb[0]);
-  store_b(lds[1], c, pb[1]);
-  load_b(c, 2, nkt, pb[0]);
-  __syncthreads();  // stages 0 and 1 published
-  int st = 2;       // stage receiving k-tile kt + 2
-  for (int kt = 0; kt < nkt; kt += 2) {
+      load_b(c, k2 + 3, nkt, pbs[half ^ 1]);
+      const int q = (half * 4 + 3) % kPre;
+      read_b<NT>(nbuf, 0, c.lane, bn);
+      mac<NT>(qa[q], bc, acc);
+      load_a(c, k2 * 4 + 3 + kPre, qa[q]);
+      step_schedule<NT>();
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int k2 = kt + half;
-      load_b(c, k2 + 3, nkt, pb[half ^ 1]);
-      store_b(lds[st], c, pb[half]);
-      __syncthreads();
-      st = st == kStages - 1 ? 0 : st + 1;
+      for (int j = 0; j < NT; ++j) bc[j] = bn[j];
     }
   }
 }
@@ -163,14 +155,14 @@ __device__ __forceinline__ void producer_loop(const TileCtx& c, u32x4 (*lds)[kBl
 // contiguous ranges (workgroup b runs on XCD b % 8), so the token tiles that
 // share a weight block run at the same time on one XCD and share its L2.
 template <int MODE>
-__global__ __launch_bounds__(kThreads, 1) void k_expert_tile(
+__global__ __launch_bounds__(256, 2) void k_expert_tile(
     const uint16_t* __restrict__ wpk, const uint16_t* __restrict__ src,
     const int* __restrict__ tilemap, int max_tiles, const int* __restrict__ counts,
     const int* __restrict__ offsets, const int* __restrict__ gather,
     const float* __restrict__ gate, const float* __restrict__ inv, int k, int E,
     const uint16_t* __restrict__ zrow, uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
     int d, int F) {
-  __shared__ u32x4 lds[kStages][kBlk * 64];
+  __shared__ u32x4 lds[2][kBlk * 64];
 
   const int K = MODE == 0 ? d : F;
   const int nwb = MODE == 0 ? 2 * F / kRowsWG : d / kRowsWG;
@@ -182,17 +174,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tile(
   int e = 0;
   while (e + 1 < E && tstart[e + 1] * nwb <= L) ++e;
   const int r = L - tstart[e] * nwb, nt = tstart[e + 1] - tstart[e];
-#if MOE_TILE_ORDER == 1
-  const int mtile = r / nwb, wb = r - mtile * nwb;  // weight blocks of one token tile adjacent
-#elif MOE_TILE_ORDER == 2
-  // groups of up to 8 token tiles: within a group, the token tiles of one
-  // weight block are adjacent, and consecutive weight blocks follow
-  const int gsz = 8 * nwb, g = r / gsz, rem = r - g * gsz;
-  const int gm = min(8, nt - g * 8);
-  const int wb = rem / gm, mtile = g * 8 + (rem - (rem / gm) * gm);
-#else
   const int wb = r / nt, mtile = r - (r / nt) * nt;  // token tiles of one weight block adjacent
-#endif
   const int cnt = counts[e], off = offsets[e];
   const int row0 = mtile * kTileTokens;
   const int nvalid = min(kTileTokens, cnt - row0);
@@ -200,9 +182,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tile(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   TileCtx c;
+  c.wave = wave;
   c.lane = lane;
   c.ksteps = K / kKStep;
   c.tile_elems = (size_t)c.ksteps * kBlockElems;
+  // this wave's weight tiles: gate and up of F tile (4*wb + wave), or
+  // d_model tiles (8*wb + 2*wave, +1)
+  const size_t blk = MODE == 0 ? ((size_t)e * (F / kTileRows) + (size_t)wb * 4 + wave) * 2
+                               : (size_t)e * (d / kTileRows) + (size_t)wb * 8 + wave * 2;
+  c.wa = wpk + blk * c.tile_elems + lane * 8;
+  {
+    const int kc = tid & 7;
+#pragma unroll
+    for (int j = 0; j < kBW; ++j) {
+      const int rr = (j * 256 + tid) >> 3;  // token row of this chunk (tile-local)
+      const bool valid = rr < nvalid;
+      const int slot = off + row0 + rr;
+      const uint16_t* row = valid ? src + (size_t)(MODE == 0 ? gather[slot] : slot) * K : zrow;
+      c.brow[j] = row + kc * 8;
+    }
+    const int r0 = tid >> 3;  // row of chunk 0; chunk j is row r0 + 32 j (same lane, next tile)
+    c.bdst = ((r0 >> 5) * 4 + (kc >> 1)) * 64 + (kc & 1) * 32 + (r0 & 31);
+  }
 
   f32x16 acc[kWR][kTT];
 #pragma unroll
@@ -212,38 +213,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tile(
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  if (wave >= kCons) {
-    // producer: gathered token rows, coalesced 8 rows x 128 B per wave-wide load
-    const int pt = tid - kCons * 64;
-    const int kc = pt & 7;
-#pragma unroll
-    for (int j = 0; j < kPC; ++j) {
-      const int rr = (j * 256 + pt) >> 3;  // token row of this chunk (tile-local)
-      const bool valid = rr < nvalid;
-      const int slot = off + row0 + rr;
-      const uint16_t* row = valid ? src + (size_t)(MODE == 0 ? gather[slot] : slot) * K : zrow;
-      c.brow[j] = row + kc * 8;
-    }
-    const int r0 = pt >> 3;  // chunk j is row r0 + 32 j: next token tile, same lane
-    c.bdst = (kc >> 1) * 64 + (kc & 1) * 32 + r0;
-    producer_loop(c, lds);
-    return;
-  }
-  // consumer: gate and up of F tile (4*wb + wave), or d_model tiles (8*wb + 2*wave, +1)
-  const size_t blk = MODE == 0 ? ((size_t)e * (F / kTileRows) + (size_t)wb * 4 + wave) * 2
-                               : (size_t)e * (d / kTileRows) + (size_t)wb * 8 + wave * 2;
-  c.wa = wpk + blk * c.tile_elems + lane * 8;
   switch (ntt) {
-#if MOE_TILE_TOK > 128
-    case 8: consumer_loop<8>(c, lds, acc); break;
-    case 7: consumer_loop<7>(c, lds, acc); break;
-    case 6: consumer_loop<6>(c, lds, acc); break;
-    case 5: consumer_loop<5>(c, lds, acc); break;
-#endif
-    case 4: consumer_loop<4>(c, lds, acc); break;
-    case 3: consumer_loop<3>(c, lds, acc); break;
-    case 2: consumer_loop<2>(c, lds, acc); break;
-    default: consumer_loop<1>(c, lds, acc); break;
+    case 4: tile_mainloop<4>(c, lds, acc); break;
+    case 3: tile_mainloop<3>(c, lds, acc); break;
+    case 2: tile_mainloop<2>(c, lds, acc); break;
+    default: tile_mainloop<1>(c, lds, acc); break;
   }
 
   // epilogue
@@ -297,14 +271,14 @@ hipError_t launch_experts_tile(const FwdArgs& a) {
   const int d = a.dim.d, F = a.dim.F;
   const int g0 = ((2 * F / kRowsWG) * a.max_tiles + 7) / 8 * 8;
   const int g1 = ((d / kRowsWG) * a.max_tiles + 7) / 8 * 8;
-  hipError_t err = launch(k_expert_tile<0>, dim3(g0), dim3(kThreads), a.stream, a.ev[kSlotExpertsA],
+  hipError_t err = launch(k_expert_tile<0>, dim3(g0), dim3(256), a.stream, a.ev[kSlotExpertsA],
                           (const uint16_t*)a.wgu, (const uint16_t*)a.xn, (const int*)a.tilemap,
                           a.max_tiles, (const int*)a.counts, (const int*)a.offsets,
                           (const int*)a.gather, (const float*)a.gate, (const float*)a.inv,
                           a.dim.k, a.dim.E, (const uint16_t*)a.zrow, (uint16_t*)a.act, a.ybuf, d,
                           F);
   if (err != hipSuccess) return err;
-  return launch(k_expert_tile<1>, dim3(g1), dim3(kThreads), a.stream, a.ev[kSlotExpertsB],
+  return launch(k_expert_tile<1>, dim3(g1), dim3(256), a.stream, a.ev[kSlotExpertsB],
                 (const uint16_t*)a.wd, (const uint16_t*)a.act, (const int*)a.tilemap, a.max_tiles,
                 (const int*)a.counts, (const int*)a.offsets, (const int*)a.gather,
                 (const float*)a.gate, (const float*)a.inv, a.dim.k, a.dim.E,

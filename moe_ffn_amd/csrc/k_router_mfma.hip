@@ -18,10 +18,12 @@
 // the experts' fp32 accumulators instead of to the activations), inv_rms[T],
 // sel[T,k], gate[T,k].
 //
-// Layout: a workgroup of NW waves owns 32*TT tokens; wave w covers the d/NW
-// slice [w*d/NW, (w+1)*d/NW) of the reduction axis, issuing its loads four
-// k-steps at a time.  MFMA 32x32x16: A = router rows (32 experts per tile, NA
-// tiles), B = tokens (32 per tile, TT tiles).  Partial logits of the waves meet
+// The kernel moves T*d*2 bytes in and the same out, so it is sized for
+// memory-level parallelism: a workgroup owns 16*TT tokens (MFMA 16x16x32:
+// A = 16 router rows per tile, NA tiles; B = 16 tokens per tile, TT tiles),
+// its NW waves split the reduction axis into NW slices, and each wave issues
+// the loads of up to kRBatch k-steps at once.  One wave-wide token load reads
+// 64 contiguous bytes from each of 16 rows.  Partial logits of the waves meet
 // in LDS and are summed in a fixed order, one (token, expert) pair per thread.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -29,58 +31,64 @@
 namespace moe {
 
 namespace {
-constexpr int kRBatch = 4;  // k-steps whose loads are issued together
+constexpr int kRK = 32;     // k per MFMA 16x16x32 step
+constexpr int kRBatch = 8;  // k-steps whose loads are issued together
+
+// D = A * B + C on a 16x16 tile with K = 32, bf16 inputs, fp32 accumulation.
+// Operands: lane l carries row (l % 16) of A (column (l % 16) of B) and 8
+// consecutive k of k-group (l / 16).  Output: lane l holds column (l % 16),
+// rows 4*(l/16) + i for accumulator element i.
+__device__ __forceinline__ f32x4 mfma_16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+}  // namespace
 
-
-// NW waves; wave w covers k-steps [w*kper, (w+1)*kper) of the d/16 steps.
 template <int NA, int TT, int NW>
 __global__ __launch_bounds__(NW * 64) void k_router_mfma(
     const uint16_t* __restrict__ hidden, int T, int d, const uint16_t* __restrict__ wr,
     const uint16_t* __restrict__ gain, const float* __restrict__ bias, int E, int k, float eps,
     const uint16_t* __restrict__ zrow, uint16_t* __restrict__ sink, uint16_t* __restrict__ xg,
     float* __restrict__ inv_out, int* __restrict__ sel, float* __restrict__ gate) {
-  constexpr int NTOK = 32 * TT;
-  constexpr int EPAD = 32 * NA;
-  __shared__ float red[NW][TT][NA][16][64];
+  constexpr int NTOK = 16 * TT;
+  constexpr int EPAD = 16 * NA;
+  __shared__ float red[NW][TT][NA][4][64];
   __shared__ float ssr[NW][TT][64];
   __shared__ float zs[NTOK][EPAD + 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * NTOK;
-  const int kgrp = (lane >> 5) * 8;
-  const int kper = d / (kKStep * NW);  // k-steps per wave
-  const int k0 = wave * kper * kKStep;
+  const int kgrp = (lane >> 4) * 8;
+  const int kper = d / (kRK * NW);  // k-steps per wave
+  const int k0 = wave * kper * kRK;
 
   const uint16_t* ap[NA];
 #pragma unroll
   for (int a = 0; a < NA; ++a) {
-    const int e = a * 32 + (lane & 31);
+    const int e = a * 16 + (lane & 15);
     ap[a] = (e < E ? wr + (size_t)e * d : zrow) + kgrp + k0;
   }
   const uint16_t* hp[TT];
   uint16_t* xp[TT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) {
-    const int t = t0 + tt * 32 + (lane & 31);
+    const int t = t0 + tt * 16 + (lane & 15);
     const bool valid = t < T;
     hp[tt] = (valid ? hidden + (size_t)t * d : zrow) + kgrp + k0;
     xp[tt] = (valid ? xg + (size_t)t * d : sink) + kgrp + k0;
   }
   const uint16_t* gp = gain + kgrp + k0;
 
-  f32x16 acc[TT][NA];
+  f32x4 acc[TT][NA];
   float ss[TT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) {
     ss[tt] = 0.f;
 #pragma unroll
-    for (int a = 0; a < NA; ++a)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[tt][a][i] = 0.f;
+    for (int a = 0; a < NA; ++a) acc[tt][a] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // one k-step: x' = g*h split into exact bf16 hi + lo, two MFMAs per tile
+  // one k-step: x' = g*h split into exact bf16 hi + lo, two MFMAs per tile pair
   auto step = [&](const u32x4& gv, const u32x4 (&av)[NA], const u32x4 (&hv)[TT], int ko) {
     float g[8];
     unpack8(gv, g);
@@ -101,8 +109,8 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
       stg16(xp[tt] + ko, bhi);
 #pragma unroll
       for (int a = 0; a < NA; ++a) {
-        acc[tt][a] = mfma_32x32x16(av[a], bhi, acc[tt][a]);
-        acc[tt][a] = mfma_32x32x16(av[a], blo, acc[tt][a]);
+        acc[tt][a] = mfma_16x16x32(av[a], bhi, acc[tt][a]);
+        acc[tt][a] = mfma_16x16x32(av[a], blo, acc[tt][a]);
       }
     }
   };
@@ -112,24 +120,24 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
     u32x4 gv[kRBatch], av[kRBatch][NA], hv[kRBatch][TT];
 #pragma unroll
     for (int b = 0; b < kRBatch; ++b) {
-      const int ko = (s + b) * kKStep;
+      const int ko = (s + b) * kRK;
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) hv[b][tt] = ldg16(hp[tt] + ko);
       gv[b] = ldg16(gp + ko);
 #pragma unroll
       for (int a = 0; a < NA; ++a) av[b][a] = ldg16(ap[a] + ko);
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) hv[b][tt] = ldg16(hp[tt] + ko);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the whole batch of loads in flight together
 #pragma unroll
-    for (int b = 0; b < kRBatch; ++b) step(gv[b], av[b], hv[b], (s + b) * kKStep);
+    for (int b = 0; b < kRBatch; ++b) step(gv[b], av[b], hv[b], (s + b) * kRK);
   }
   for (; s < kper; ++s) {
-    const int ko = s * kKStep;
+    const int ko = s * kRK;
     u32x4 av[NA], hv[TT];
 #pragma unroll
-    for (int a = 0; a < NA; ++a) av[a] = ldg16(ap[a] + ko);
-#pragma unroll
     for (int tt = 0; tt < TT; ++tt) hv[tt] = ldg16(hp[tt] + ko);
+#pragma unroll
+    for (int a = 0; a < NA; ++a) av[a] = ldg16(ap[a] + ko);
     step(ldg16(gp + ko), av, hv, ko);
   }
 
@@ -139,17 +147,16 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
 #pragma unroll
     for (int a = 0; a < NA; ++a)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) red[wave][tt][a][i][lane] = acc[tt][a][i];
+      for (int i = 0; i < 4; ++i) red[wave][tt][a][i][lane] = acc[tt][a][i];
   }
   __syncthreads();
 
   // cross-wave sums in a fixed order, one (token, expert) pair per thread:
-  // C[row e][column c] of a 32x32 tile sits in lane c + 32*((e/4)%2),
-  // accumulator element (e/8)*4 + e%4.
+  // C[row r][column c] of a 16x16 tile sits in lane c + 16*(r/4), element r%4.
   for (int p = tid; p < NTOK * EPAD; p += NW * 64) {
     const int t = p % NTOK, e = p / NTOK;
-    const int tt = t >> 5, c = t & 31, a = e >> 5, r = e & 31;
-    const int l = c + 32 * ((r >> 2) & 1), i = (r >> 3) * 4 + (r & 3);
+    const int tt = t >> 4, c = t & 15, a = e >> 4, r = e & 15;
+    const int l = c + 16 * (r >> 2), i = r & 3;
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) v += red[w][tt][a][i][l];
@@ -158,17 +165,18 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
   __syncthreads();
 
   if (tid < NTOK) {
-    const int tt = tid >> 5, c = tid & 31;
+    const int tt = tid >> 4, c = tid & 15;
     const int t = t0 + tid;
     float sq = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) sq += ssr[w][tt][c] + ssr[w][tt][c + 32];
+    for (int w = 0; w < NW; ++w)
+      sq += (ssr[w][tt][c] + ssr[w][tt][c + 16]) + (ssr[w][tt][c + 32] + ssr[w][tt][c + 48]);
     const float inv = 1.0f / sqrtf(sq / (float)d + eps);
     float z[EPAD], sc[EPAD];
 #pragma unroll
     for (int e = 0; e < EPAD; ++e) {
       z[e] = zs[tid][e] * inv;
-      sc[e] = z[e] + bias[e];  // bias is padded with zeros to a power of two >= EPAD
+      sc[e] = z[e] + bias[e];  // bias is padded with zeros to 64 entries
     }
     if (t < T) {
       // top-k by descending score, exact ties to the lower index; NaN never wins
@@ -206,23 +214,30 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
       inv_out[t] = inv;
     }
   }
-
 }
 
 namespace {
-template <int NA, int TT, int NW>
+template <int NA, int TT>
 hipError_t go(const FwdArgs& a) {
-  const int grid = (a.T + 32 * TT - 1) / (32 * TT);
+  constexpr int NW = 8;
+  if (a.dim.d % (kRK * NW) != 0) return hipErrorInvalidValue;
+  const int grid = (a.T + 16 * TT - 1) / (16 * TT);
   return launch(k_router_mfma<NA, TT, NW>, dim3(grid), dim3(NW * 64), a.stream,
                 a.ev[kSlotNormRouter], (const uint16_t*)a.hidden, a.T, a.dim.d,
                 (const uint16_t*)a.wr16, (const uint16_t*)a.gain16, (const float*)a.bias, a.dim.E,
                 a.dim.k, a.dim.eps, (const uint16_t*)a.zrow, (uint16_t*)a.sink,
                 (uint16_t*)a.xn, a.inv, a.sel, a.gate);
 }
+template <int TT>
+hipError_t go_tt(const FwdArgs& a) {
+  const int E = a.dim.E;
+  return E > 32 ? go<4, TT>(a) : E > 16 ? go<2, TT>(a) : go<1, TT>(a);
+}
 }  // namespace
 
+// Two token tiles per workgroup once that still leaves two workgroups per CU.
 hipError_t launch_router_mfma(const FwdArgs& a) {
-  return a.dim.E > 32 ? go<2, 1, 8>(a) : go<1, 1, 8>(a);
+  return a.T >= 32 * 512 ? go_tt<2>(a) : go_tt<1>(a);
 }
 
 }  // namespace moe

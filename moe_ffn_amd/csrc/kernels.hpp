@@ -34,10 +34,7 @@ constexpr int kKStep = 16;
 constexpr int kBlockElems = 64 * 8;  // 512 bf16 = 1 KiB
 
 // Prefill tiles: 256 weight rows x kTileTokens tokens x 64 k per workgroup.
-#ifndef MOE_TILE_TOK
-#define MOE_TILE_TOK 128
-#endif
-constexpr int kTileTokens = MOE_TILE_TOK;
+constexpr int kTileTokens = 128;
 // Decode path is used while T * top_k is at most this many assignments.
 constexpr int kStreamMaxAssign = 64;
 
