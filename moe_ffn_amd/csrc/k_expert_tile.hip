@@ -6,18 +6,21 @@
 //   MODE 0  act[slot, f] = bf16( SiLU(x W_gate^T) * (x W_up^T) )   K = d_model
 //   MODE 1  y[slot, m]   = act[slot] W_down^T                       K = d_ff
 //           k = 1: out[token] = bf16(gate * y); k > 1: y kept in fp32.
-// A workgroup computes a 256-weight-row x 128-token tile: four waves stacked
-// along the weight rows, each owning two 32-row MFMA tiles against all four
-// 32-token tiles (8 accumulators of 32x32).  Weights are read straight from
-// the packed bank (MFMA operand order, 1 KiB per wave-wide load) into
-// registers, four k-steps ahead, so they never pass through LDS.  Only the
-// token tile is shared: rows gathered on load through the expert-ordered slot
-// list (8 rows x 128 contiguous bytes per wave-wide load) are written to LDS in
-// operand order (conflict-free 1 KiB reads), three 64-wide k-tiles in flight
-// (two in registers, one in LDS) and one barrier per k-tile.  Two workgroups
-// per CU, so one's barrier and load waits overlap the other's MFMAs.  Partial
-// token tiles (the tail of each expert) run a variant that skips the empty
-// 32-token tiles.
+// A workgroup computes a (NWV*64)-weight-row x 128-token tile: NWV waves (8,
+// or 4 where the rows do not divide by 512) stacked along the weight rows,
+// each owning two 32-row MFMA tiles against all four 32-token tiles (8
+// accumulators of 32x32).  Weights are read straight from the packed bank
+// (MFMA operand order, 1 KiB per wave-wide load) into registers, four k-steps
+// ahead, so they never pass through LDS.  Only the token tile is shared: rows
+// gathered on load through the expert-ordered slot list (8 rows x 128
+// contiguous bytes per wave-wide load) are written to LDS in operand order
+// (swizzled, conflict-free both ways), three 64-wide k-tiles in flight (two
+// in registers, one in LDS) and one barrier per k-tile.  The operand bytes a
+// CU pulls from L2 per flop fall as its resident tile grows (per 16-wide
+// k-step: 16 KiB of weights + 4 KiB of tokens for 2 MFLOP with eight waves,
+// against 24 KiB for two four-wave workgroups), and that L2-to-CU stream is
+// what bounds this kernel.  Partial token tiles (the tail of each expert) run
+// a variant that skips the empty 32-token tiles.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -25,49 +28,70 @@ namespace moe {
 
 namespace {
 constexpr int kTT = kTileTokens / 32;      // 32-token MFMA tiles per workgroup (4)
-constexpr int kWaves = 4;                  // waves per workgroup, stacked along weight rows
 constexpr int kWR = 2;                     // 32-row weight tiles per wave
-constexpr int kRowsWG = kWaves * kWR * 32; // 256 weight rows per workgroup
 constexpr int kPre = 4;                    // k-steps of weight loads in flight per wave
 constexpr int kKT = 64;                    // k per LDS stage of the token tile
 constexpr int kBlk = kTT * (kKT / kKStep); // 1 KiB operand blocks per token stage (16)
-constexpr int kBW = kBlk / kWaves;         // blocks staged by each wave per stage
-constexpr int kTPW = kTT / kWaves;         // token tiles staged by each wave
 
+// NWV waves per workgroup, stacked along the weight rows (NWV*64 weight rows).
+template <int NWV>
+struct Geo {
+  static constexpr int kThreads = NWV * 64;
+  static constexpr int kRowsWG = NWV * kWR * 32;
+  static constexpr int kBW = kBlk * 64 / kThreads;  // 16-byte chunks staged per thread per stage
+};
+
+template <int NWV>
 struct TileCtx {
   const uint16_t* wa;     // this wave's first weight tile (lane offset applied)
   size_t tile_elems;      // elements of one packed 32-row tile
   int ksteps;             // K / 16
-  const uint16_t* brow[kBW];  // this thread's source for each staged chunk (k offset applied)
-  int bdst;                   // LDS index (16-byte units) of chunk 0; chunk j adds j * kBlk*64/kBW
+  const uint16_t* brow[Geo<NWV>::kBW];  // source of each staged chunk (k offset applied)
+  int bdst;  // LDS index (16-byte units) of chunk 0; chunk j is NWV*8 rows = NWV blocks further
   int wave, lane;
 };
 
-__device__ __forceinline__ void load_a(const TileCtx& c, int s, u32x4 (&q)[kWR]) {
+template <int NWV>
+__device__ __forceinline__ void load_a(const TileCtx<NWV>& c, int s, u32x4 (&q)[kWR]) {
   const int sc = s < c.ksteps ? s : c.ksteps - 1;  // clamp: surplus loads stay in bounds
 #pragma unroll
   for (int r = 0; r < kWR; ++r) q[r] = ldg16(c.wa + r * c.tile_elems + (size_t)sc * kBlockElems);
 }
 
-// Token staging: the workgroup's 256 threads copy a kTileTokens x 64 slice of
-// gathered rows per k-tile, each wave-wide load reading 8 rows x 128 contiguous
-// bytes (8 full cache lines): thread t, chunk j covers row r = (j*256 + t) / 8
-// and 16-byte k-chunk kc = t % 8.  The LDS write scatters each chunk to its
-// place in MFMA operand order: block (r/32)*4 + kc/2, lane (kc%2)*32 + r%32.
-__device__ __forceinline__ void load_b(const TileCtx& c, int kt, int nkt, u32x4 (&p)[kBW]) {
+// Token staging: the workgroup's NWV*64 threads copy a kTileTokens x 64 slice
+// of gathered rows per k-tile, each wave-wide load reading 8 rows x 128
+// contiguous bytes (8 full cache lines): thread t, chunk j covers row
+// r = (j*NWV*64 + t) / 8 and 16-byte k-chunk kc = t % 8.  The LDS write scatters each chunk to its
+// place in MFMA operand order: block (r/32)*4 + kc/2, operand lane
+// li = (kc%2)*32 + r%32, stored at 16-byte slot swz(block, li) of the block.
+//
+// swz(block, li) = li ^ ((4*(block%4) + 2*(li/32)) & 15) permutes the slots
+// inside each group of 16: the 16 lanes an MFMA operand read serves together
+// still cover 16 consecutive slots (all 64 banks), while the 8 k-chunks of one
+// token row, which the staging write issues together, now land in 8
+// different bank groups instead of the same one (block stride 1 KiB and
+// k-group stride 512 B are multiples of the 256-byte bank cycle).
+__device__ __forceinline__ int swz(int block, int li) {
+  return li ^ ((4 * (block & 3) + 2 * (li >> 5)) & 15);
+}
+template <int NWV>
+__device__ __forceinline__ void load_b(const TileCtx<NWV>& c, int kt, int nkt,
+                                       u32x4 (&p)[Geo<NWV>::kBW]) {
   const int kc = kt < nkt ? kt : nkt - 1;
 #pragma unroll
-  for (int j = 0; j < kBW; ++j) p[j] = ldg16(c.brow[j] + kc * kKT);
+  for (int j = 0; j < Geo<NWV>::kBW; ++j) p[j] = ldg16(c.brow[j] + kc * kKT);
 }
-__device__ __forceinline__ void store_b(u32x4* buf, const TileCtx& c, const u32x4 (&p)[kBW]) {
+template <int NWV>
+__device__ __forceinline__ void store_b(u32x4* buf, const TileCtx<NWV>& c,
+                                        const u32x4 (&p)[Geo<NWV>::kBW]) {
 #pragma unroll
-  for (int j = 0; j < kBW; ++j) buf[c.bdst + j * (kBlk * 64 / kBW)] = p[j];
+  for (int j = 0; j < Geo<NWV>::kBW; ++j) buf[c.bdst + j * (NWV * 64)] = p[j];
 }
 
 template <int NT>
 __device__ __forceinline__ void read_b(const u32x4* buf, int s16, int lane, u32x4 (&bv)[NT]) {
 #pragma unroll
-  for (int j = 0; j < NT; ++j) bv[j] = buf[(j * 4 + s16) * 64 + lane];
+  for (int j = 0; j < NT; ++j) bv[j] = buf[(j * 4 + s16) * 64 + swz(s16, lane)];
 }
 
 template <int NT>
@@ -102,15 +126,15 @@ __device__ __forceinline__ void step_schedule() {
 // are already in flight.  Two k-tiles per iteration keep every queue slot and
 // buffer static; loads are unconditional (clamped), so nothing in the loop
 // branches.
-template <int NT>
-__device__ __forceinline__ void tile_mainloop(const TileCtx& c, u32x4 (*lds)[kBlk * 64],
+template <int NT, int NWV>
+__device__ __forceinline__ void tile_mainloop(const TileCtx<NWV>& c, u32x4 (*lds)[kBlk * 64],
                                               f32x16 (&acc)[kWR][kTT]) {
   const int nkt = c.ksteps / (kKT / kKStep);
   u32x4 qa[kPre][kWR], bc[NT], bn[NT];
   // The prologue issues its loads in the loop's own order (stage k+1, stage
   // k+2, then the weight queue), so the wait counts the compiler derives at the
   // loop head are the steady-state ones rather than a tighter prologue bound.
-  u32x4 pbs[2][kBW];  // token stages k2+1 and k2+2 in flight
+  u32x4 pbs[2][Geo<NWV>::kBW];  // token stages k2+1 and k2+2 in flight
   load_b(c, 0, nkt, pbs[0]);
   store_b(lds[0], c, pbs[0]);
   load_b(c, 1, nkt, pbs[1]);
@@ -154,8 +178,8 @@ __device__ __forceinline__ void tile_mainloop(const TileCtx& c, u32x4 (*lds)[kBl
 // expert-major, then weight block, then token tile, and dealt to the 8 XCDs in
 // contiguous ranges (workgroup b runs on XCD b % 8), so the token tiles that
 // share a weight block run at the same time on one XCD and share its L2.
-template <int MODE>
-__global__ __launch_bounds__(256, 2) void k_expert_tile(
+template <int MODE, int NWV>
+__global__ __launch_bounds__(NWV * 64, 8 / NWV) void k_expert_tile(
     const uint16_t* __restrict__ wpk, const uint16_t* __restrict__ src,
     const int* __restrict__ tilemap, int max_tiles, const int* __restrict__ counts,
     const int* __restrict__ offsets, const int* __restrict__ gather,
@@ -165,6 +189,7 @@ __global__ __launch_bounds__(256, 2) void k_expert_tile(
   __shared__ u32x4 lds[2][kBlk * 64];
 
   const int K = MODE == 0 ? d : F;
+  constexpr int kRowsWG = Geo<NWV>::kRowsWG;
   const int nwb = MODE == 0 ? 2 * F / kRowsWG : d / kRowsWG;
   const int G = gridDim.x, b = blockIdx.x;
   const int L = (b & 7) * (G >> 3) + (b >> 3);
@@ -181,28 +206,29 @@ __global__ __launch_bounds__(256, 2) void k_expert_tile(
   const int ntt = (nvalid + 31) >> 5;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  TileCtx c;
+  TileCtx<NWV> c;
   c.wave = wave;
   c.lane = lane;
   c.ksteps = K / kKStep;
   c.tile_elems = (size_t)c.ksteps * kBlockElems;
-  // this wave's weight tiles: gate and up of F tile (4*wb + wave), or
-  // d_model tiles (8*wb + 2*wave, +1)
-  const size_t blk = MODE == 0 ? ((size_t)e * (F / kTileRows) + (size_t)wb * 4 + wave) * 2
-                               : (size_t)e * (d / kTileRows) + (size_t)wb * 8 + wave * 2;
+  // this wave's weight tiles: gate and up of F tile (NWV*wb + wave), or
+  // d_model tiles (2*NWV*wb + 2*wave, +1)
+  const size_t blk = MODE == 0
+      ? ((size_t)e * (F / kTileRows) + (size_t)wb * NWV + wave) * 2
+      : (size_t)e * (d / kTileRows) + (size_t)wb * 2 * NWV + wave * 2;
   c.wa = wpk + blk * c.tile_elems + lane * 8;
   {
     const int kc = tid & 7;
 #pragma unroll
-    for (int j = 0; j < kBW; ++j) {
-      const int rr = (j * 256 + tid) >> 3;  // token row of this chunk (tile-local)
+    for (int j = 0; j < Geo<NWV>::kBW; ++j) {
+      const int rr = (j * NWV * 64 + tid) >> 3;  // token row of this chunk (tile-local)
       const bool valid = rr < nvalid;
       const int slot = off + row0 + rr;
       const uint16_t* row = valid ? src + (size_t)(MODE == 0 ? gather[slot] : slot) * K : zrow;
       c.brow[j] = row + kc * 8;
     }
-    const int r0 = tid >> 3;  // row of chunk 0; chunk j is row r0 + 32 j (same lane, next tile)
-    c.bdst = ((r0 >> 5) * 4 + (kc >> 1)) * 64 + (kc & 1) * 32 + (r0 & 31);
+    const int r0 = tid >> 3;  // row of chunk 0; chunk j is row r0 + j*NWV*8
+    c.bdst = ((r0 >> 5) * 4 + (kc >> 1)) * 64 + swz(kc >> 1, (kc & 1) * 32 + (r0 & 31));
   }
 
   f32x16 acc[kWR][kTT];
@@ -229,7 +255,7 @@ __global__ __launch_bounds__(256, 2) void k_expert_tile(
     const int slot = off + row0 + rr;
     if constexpr (MODE == 0) {
       const float sc = inv[gather[slot]];  // RMSNorm scale of this token
-      const int ft = wb * 4 + wave;
+      const int ft = wb * NWV + wave;
       uint16_t* dst = dst16 + (size_t)slot * F + ft * kTileRows;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -247,7 +273,7 @@ __global__ __launch_bounds__(256, 2) void k_expert_tile(
       const float gw = k == 1 ? gate[tok] : 0.f;
 #pragma unroll
       for (int i = 0; i < kWR; ++i) {
-        const int mbase = (wb * 8 + wave * 2 + i) * kTileRows;
+        const int mbase = (wb * 2 * NWV + wave * 2 + i) * kTileRows;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int m = mbase + c32_row(4 * q, lane);
@@ -267,22 +293,33 @@ __global__ __launch_bounds__(256, 2) void k_expert_tile(
   }
 }
 
-hipError_t launch_experts_tile(const FwdArgs& a) {
+namespace {
+template <int MODE, int NWV>
+hipError_t launch_mode(const FwdArgs& a) {
+  constexpr int kRowsWG = Geo<NWV>::kRowsWG;
   const int d = a.dim.d, F = a.dim.F;
-  const int g0 = ((2 * F / kRowsWG) * a.max_tiles + 7) / 8 * 8;
-  const int g1 = ((d / kRowsWG) * a.max_tiles + 7) / 8 * 8;
-  hipError_t err = launch(k_expert_tile<0>, dim3(g0), dim3(256), a.stream, a.ev[kSlotExpertsA],
-                          (const uint16_t*)a.wgu, (const uint16_t*)a.xn, (const int*)a.tilemap,
-                          a.max_tiles, (const int*)a.counts, (const int*)a.offsets,
-                          (const int*)a.gather, (const float*)a.gate, (const float*)a.inv,
-                          a.dim.k, a.dim.E, (const uint16_t*)a.zrow, (uint16_t*)a.act, a.ybuf, d,
-                          F);
-  if (err != hipSuccess) return err;
-  return launch(k_expert_tile<1>, dim3(g1), dim3(256), a.stream, a.ev[kSlotExpertsB],
-                (const uint16_t*)a.wd, (const uint16_t*)a.act, (const int*)a.tilemap, a.max_tiles,
+  const int rows = MODE == 0 ? 2 * F : d;
+  const int grid = ((rows / kRowsWG) * a.max_tiles + 7) / 8 * 8;
+  return launch(k_expert_tile<MODE, NWV>, dim3(grid), dim3(NWV * 64), a.stream,
+                a.ev[MODE == 0 ? kSlotExpertsA : kSlotExpertsB],
+                (const uint16_t*)(MODE == 0 ? a.wgu : a.wd),
+                (const uint16_t*)(MODE == 0 ? a.xn : a.act), (const int*)a.tilemap, a.max_tiles,
                 (const int*)a.counts, (const int*)a.offsets, (const int*)a.gather,
                 (const float*)a.gate, (const float*)a.inv, a.dim.k, a.dim.E,
-                (const uint16_t*)a.zrow, (uint16_t*)a.out, a.ybuf, d, F);
+                (const uint16_t*)a.zrow, (uint16_t*)(MODE == 0 ? a.act : a.out), a.ybuf, d, F);
+}
+}  // namespace
+
+// Eight waves (512 weight rows, one workgroup per CU) where the rows divide
+// into them, else four (256 rows, two workgroups per CU).  The down
+// projection of top-k > 1 layers keeps four waves: its fp32 epilogue is
+// twice as large and is hidden only behind a second resident workgroup.
+hipError_t launch_experts_tile(const FwdArgs& a) {
+  const bool w8_gu = (2 * a.dim.F) % 512 == 0;
+  const bool w8_d = a.dim.d % 512 == 0 && a.dim.k == 1;
+  hipError_t err = w8_gu ? launch_mode<0, 8>(a) : launch_mode<0, 4>(a);
+  if (err != hipSuccess) return err;
+  return w8_d ? launch_mode<1, 8>(a) : launch_mode<1, 4>(a);
 }
 
 }  // namespace moe
