@@ -6,9 +6,9 @@
 //   MODE 0  act[slot, f] = bf16( SiLU(x W_gate^T) * (x W_up^T) )   K = d_model
 //   MODE 1  y[slot, m]   = act[slot] W_down^T                       K = d_ff
 //           k = 1: out[token] = bf16(gate * y); k > 1: y kept in fp32.
-// A workgroup computes a (NWV*64)-weight-row x 128-token tile: NWV waves (8,
-// or 4 where the rows do not divide by 512) stacked along the weight rows,
-// each owning two 32-row MFMA tiles against all four 32-token tiles (8
+// A workgroup computes a (NR*64)-weight-row x 128-token tile: NR waves (8, or
+// 4 where the rows do not divide by 512) stacked along the weight rows, each
+// owning two 32-row MFMA tiles against all four 32-token tiles (8
 // accumulators of 32x32).  Weights are read straight from the packed bank
 // (MFMA operand order, 1 KiB per wave-wide load) into registers, four k-steps
 // ahead, so they never pass through LDS.  Only the token tile is shared: rows
@@ -33,35 +33,42 @@ constexpr int kPre = 4;                    // k-steps of weight loads in flight 
 constexpr int kKT = 64;                    // k per LDS stage of the token tile
 constexpr int kBlk = kTT * (kKT / kKStep); // 1 KiB operand blocks per token stage (16)
 
-// NWV waves per workgroup, stacked along the weight rows (NWV*64 weight rows).
-template <int NWV>
+// Workgroup shape: NR x NTG waves, NR stacked along the weight rows (NR*64
+// rows), NTG along the tokens (NTG*128 tokens).  Waves of one row group load
+// the same weight tiles (the second load hits the CU's L1).
+template <int NR_, int NTG_>
 struct Geo {
-  static constexpr int kThreads = NWV * 64;
-  static constexpr int kRowsWG = NWV * kWR * 32;
-  static constexpr int kBW = kBlk * 64 / kThreads;  // 16-byte chunks staged per thread per stage
+  static constexpr int NR = NR_, NTG = NTG_;
+  static constexpr int kWaves = NR * NTG;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kRowsWG = NR * kWR * 32;
+  static constexpr int kTokWG = NTG * kTileTokens;
+  static constexpr int kStage = NTG * kBlk;                // operand blocks per token stage
+  static constexpr int kBW = kStage * 64 / kThreads;       // chunks staged per thread per stage
 };
 
-template <int NWV>
+template <class GEO>
 struct TileCtx {
   const uint16_t* wa;     // this wave's first weight tile (lane offset applied)
   size_t tile_elems;      // elements of one packed 32-row tile
   int ksteps;             // K / 16
-  const uint16_t* brow[Geo<NWV>::kBW];  // source of each staged chunk (k offset applied)
-  int bdst;  // LDS index (16-byte units) of chunk 0; chunk j is NWV*8 rows = NWV blocks further
+  const uint16_t* brow[GEO::kBW];  // source of each staged chunk (k offset applied)
+  int bdst;  // LDS slot (16-byte units) of chunk 0; chunk j is kThreads/8 rows = kThreads slots on
+  int bofs;  // LDS slot of this wave's token group (kBlk blocks per group)
   int wave, lane;
 };
 
-template <int NWV>
-__device__ __forceinline__ void load_a(const TileCtx<NWV>& c, int s, u32x4 (&q)[kWR]) {
+template <class GEO>
+__device__ __forceinline__ void load_a(const TileCtx<GEO>& c, int s, u32x4 (&q)[kWR]) {
   const int sc = s < c.ksteps ? s : c.ksteps - 1;  // clamp: surplus loads stay in bounds
 #pragma unroll
   for (int r = 0; r < kWR; ++r) q[r] = ldg16(c.wa + r * c.tile_elems + (size_t)sc * kBlockElems);
 }
 
-// Token staging: the workgroup's NWV*64 threads copy a kTileTokens x 64 slice
-// of gathered rows per k-tile, each wave-wide load reading 8 rows x 128
-// contiguous bytes (8 full cache lines): thread t, chunk j covers row
-// r = (j*NWV*64 + t) / 8 and 16-byte k-chunk kc = t % 8.  The LDS write scatters each chunk to its
+// Token staging: the workgroup's threads copy a kTokWG x 64 slice of gathered
+// rows per k-tile, each wave-wide load reading 8 rows x 128 contiguous bytes
+// (8 full cache lines): thread t, chunk j covers row r = (j*kThreads + t) / 8
+// and 16-byte k-chunk kc = t % 8.  The LDS write scatters each chunk to its
 // place in MFMA operand order: block (r/32)*4 + kc/2, operand lane
 // li = (kc%2)*32 + r%32, stored at 16-byte slot swz(block, li) of the block.
 //
@@ -74,18 +81,18 @@ __device__ __forceinline__ void load_a(const TileCtx<NWV>& c, int s, u32x4 (&q)[
 __device__ __forceinline__ int swz(int block, int li) {
   return li ^ ((4 * (block & 3) + 2 * (li >> 5)) & 15);
 }
-template <int NWV>
-__device__ __forceinline__ void load_b(const TileCtx<NWV>& c, int kt, int nkt,
-                                       u32x4 (&p)[Geo<NWV>::kBW]) {
+template <class GEO>
+__device__ __forceinline__ void load_b(const TileCtx<GEO>& c, int kt, int nkt,
+                                       u32x4 (&p)[GEO::kBW]) {
   const int kc = kt < nkt ? kt : nkt - 1;
 #pragma unroll
-  for (int j = 0; j < Geo<NWV>::kBW; ++j) p[j] = ldg16(c.brow[j] + kc * kKT);
+  for (int j = 0; j < GEO::kBW; ++j) p[j] = ldg16(c.brow[j] + kc * kKT);
 }
-template <int NWV>
-__device__ __forceinline__ void store_b(u32x4* buf, const TileCtx<NWV>& c,
-                                        const u32x4 (&p)[Geo<NWV>::kBW]) {
+template <class GEO>
+__device__ __forceinline__ void store_b(u32x4* buf, const TileCtx<GEO>& c,
+                                        const u32x4 (&p)[GEO::kBW]) {
 #pragma unroll
-  for (int j = 0; j < Geo<NWV>::kBW; ++j) buf[c.bdst + j * (NWV * 64)] = p[j];
+  for (int j = 0; j < GEO::kBW; ++j) buf[c.bdst + j * GEO::kThreads] = p[j];
 }
 
 template <int NT>
@@ -126,15 +133,16 @@ __device__ __forceinline__ void step_schedule() {
 // are already in flight.  Two k-tiles per iteration keep every queue slot and
 // buffer static; loads are unconditional (clamped), so nothing in the loop
 // branches.
-template <int NT, int NWV>
-__device__ __forceinline__ void tile_mainloop(const TileCtx<NWV>& c, u32x4 (*lds)[kBlk * 64],
+template <int NT, class GEO>
+__device__ __forceinline__ void tile_mainloop(const TileCtx<GEO>& c,
+                                              u32x4 (*lds)[GEO::kStage * 64],
                                               f32x16 (&acc)[kWR][kTT]) {
   const int nkt = c.ksteps / (kKT / kKStep);
   u32x4 qa[kPre][kWR], bc[NT], bn[NT];
   // The prologue issues its loads in the loop's own order (stage k+1, stage
   // k+2, then the weight queue), so the wait counts the compiler derives at the
   // loop head are the steady-state ones rather than a tighter prologue bound.
-  u32x4 pbs[2][Geo<NWV>::kBW];  // token stages k2+1 and k2+2 in flight
+  u32x4 pbs[2][GEO::kBW];  // token stages k2+1 and k2+2 in flight
   load_b(c, 0, nkt, pbs[0]);
   store_b(lds[0], c, pbs[0]);
   load_b(c, 1, nkt, pbs[1]);
@@ -142,12 +150,12 @@ __device__ __forceinline__ void tile_mainloop(const TileCtx<NWV>& c, u32x4 (*lds
 #pragma unroll
   for (int i = 0; i < kPre; ++i) load_a(c, i, qa[i]);
   __syncthreads();
-  read_b<NT>(lds[0], 0, c.lane, bc);
+  read_b<NT>(lds[0] + c.bofs, 0, c.lane, bc);
   for (int kt = 0; kt < nkt; kt += 2) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int k2 = kt + half;
-      const u32x4* buf = lds[half];
+      const u32x4* buf = lds[half] + c.bofs;
       u32x4* nbuf = lds[half ^ 1];
 #pragma unroll
       for (int i = 0; i < 3; ++i) {
@@ -163,7 +171,7 @@ __device__ __forceinline__ void tile_mainloop(const TileCtx<NWV>& c, u32x4 (*lds
       __syncthreads();
       load_b(c, k2 + 3, nkt, pbs[half ^ 1]);
       const int q = (half * 4 + 3) % kPre;
-      read_b<NT>(nbuf, 0, c.lane, bn);
+      read_b<NT>(nbuf + c.bofs, 0, c.lane, bn);
       mac<NT>(qa[q], bc, acc);
       load_a(c, k2 * 4 + 3 + kPre, qa[q]);
       step_schedule<NT>();
@@ -178,56 +186,63 @@ __device__ __forceinline__ void tile_mainloop(const TileCtx<NWV>& c, u32x4 (*lds
 // expert-major, then weight block, then token tile, and dealt to the 8 XCDs in
 // contiguous ranges (workgroup b runs on XCD b % 8), so the token tiles that
 // share a weight block run at the same time on one XCD and share its L2.
-template <int MODE, int NWV>
-__global__ __launch_bounds__(NWV * 64, 8 / NWV) void k_expert_tile(
+template <int MODE, class GEO>
+__global__ __launch_bounds__(GEO::kThreads, 8 / GEO::kWaves) void k_expert_tile(
     const uint16_t* __restrict__ wpk, const uint16_t* __restrict__ src,
     const int* __restrict__ tilemap, int max_tiles, const int* __restrict__ counts,
     const int* __restrict__ offsets, const int* __restrict__ gather,
     const float* __restrict__ gate, const float* __restrict__ inv, int k, int E,
     const uint16_t* __restrict__ zrow, uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
     int d, int F) {
-  __shared__ u32x4 lds[2][kBlk * 64];
+  constexpr int NR = GEO::NR, NTG = GEO::NTG;
+  __shared__ u32x4 lds[2][GEO::kStage * 64];
 
   const int K = MODE == 0 ? d : F;
-  constexpr int kRowsWG = Geo<NWV>::kRowsWG;
-  const int nwb = MODE == 0 ? 2 * F / kRowsWG : d / kRowsWG;
+  const int nwb = MODE == 0 ? 2 * F / GEO::kRowsWG : d / GEO::kRowsWG;
   const int G = gridDim.x, b = blockIdx.x;
   const int L = (b & 7) * (G >> 3) + (b >> 3);
-  const int ntiles = tilemap[0];
-  if (L >= ntiles * nwb) return;
+  // work units: per expert, nwb weight blocks x ceil(tiles / NTG) token spans
   const int* tstart = tilemap + 1 + max_tiles;
-  int e = 0;
-  while (e + 1 < E && tstart[e + 1] * nwb <= L) ++e;
-  const int r = L - tstart[e] * nwb, nt = tstart[e + 1] - tstart[e];
-  const int wb = r / nt, mtile = r - (r / nt) * nt;  // token tiles of one weight block adjacent
+  int e = 0, base = 0, nsp = 0;
+  for (; e < E; ++e) {
+    nsp = (tstart[e + 1] - tstart[e] + NTG - 1) / NTG;
+    if (L < base + nsp * nwb) break;
+    base += nsp * nwb;
+  }
+  if (e >= E) return;
+  const int r = L - base;
+  const int wb = r / nsp, span = r - (r / nsp) * nsp;  // token spans of one weight block adjacent
   const int cnt = counts[e], off = offsets[e];
-  const int row0 = mtile * kTileTokens;
-  const int nvalid = min(kTileTokens, cnt - row0);
-  const int ntt = (nvalid + 31) >> 5;
+  const int row0 = span * GEO::kTokWG;
+  const int nvalid = min(GEO::kTokWG, cnt - row0);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  TileCtx<NWV> c;
+  const int rg = wave % NR, tg = wave / NR;  // row group, token group of this wave
+  const int nvw = nvalid - tg * kTileTokens;  // tokens of this wave's group (may be <= 0)
+  const int ntt = nvw <= 0 ? 1 : (nvw + 31) >> 5;
+  TileCtx<GEO> c;
   c.wave = wave;
   c.lane = lane;
   c.ksteps = K / kKStep;
   c.tile_elems = (size_t)c.ksteps * kBlockElems;
-  // this wave's weight tiles: gate and up of F tile (NWV*wb + wave), or
-  // d_model tiles (2*NWV*wb + 2*wave, +1)
+  c.bofs = tg * kBlk * 64;
+  // this wave's weight tiles: gate and up of F tile (NR*wb + rg), or
+  // d_model tiles (2*NR*wb + 2*rg, +1)
   const size_t blk = MODE == 0
-      ? ((size_t)e * (F / kTileRows) + (size_t)wb * NWV + wave) * 2
-      : (size_t)e * (d / kTileRows) + (size_t)wb * 2 * NWV + wave * 2;
+      ? ((size_t)e * (F / kTileRows) + (size_t)wb * NR + rg) * 2
+      : (size_t)e * (d / kTileRows) + (size_t)wb * 2 * NR + rg * 2;
   c.wa = wpk + blk * c.tile_elems + lane * 8;
   {
     const int kc = tid & 7;
 #pragma unroll
-    for (int j = 0; j < Geo<NWV>::kBW; ++j) {
-      const int rr = (j * NWV * 64 + tid) >> 3;  // token row of this chunk (tile-local)
+    for (int j = 0; j < GEO::kBW; ++j) {
+      const int rr = (j * GEO::kThreads + tid) >> 3;  // token row of this chunk (tile-local)
       const bool valid = rr < nvalid;
       const int slot = off + row0 + rr;
       const uint16_t* row = valid ? src + (size_t)(MODE == 0 ? gather[slot] : slot) * K : zrow;
       c.brow[j] = row + kc * 8;
     }
-    const int r0 = tid >> 3;  // row of chunk 0; chunk j is row r0 + j*NWV*8
+    const int r0 = tid >> 3;  // row of chunk 0; chunk j is row r0 + j*kThreads/8
     c.bdst = ((r0 >> 5) * 4 + (kc >> 1)) * 64 + swz(kc >> 1, (kc & 1) * 32 + (r0 & 31));
   }
 
@@ -250,12 +265,12 @@ __global__ __launch_bounds__(NWV * 64, 8 / NWV) void k_expert_tile(
   const int col = lane & 31;
 #pragma unroll
   for (int j = 0; j < kTT; ++j) {
-    const int rr = j * 32 + col;  // tile-local token row
+    const int rr = tg * kTileTokens + j * 32 + col;  // tile-local token row
     if (rr >= nvalid) continue;
     const int slot = off + row0 + rr;
     if constexpr (MODE == 0) {
       const float sc = inv[gather[slot]];  // RMSNorm scale of this token
-      const int ft = wb * NWV + wave;
+      const int ft = wb * NR + rg;
       uint16_t* dst = dst16 + (size_t)slot * F + ft * kTileRows;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -273,7 +288,7 @@ __global__ __launch_bounds__(NWV * 64, 8 / NWV) void k_expert_tile(
       const float gw = k == 1 ? gate[tok] : 0.f;
 #pragma unroll
       for (int i = 0; i < kWR; ++i) {
-        const int mbase = (wb * 2 * NWV + wave * 2 + i) * kTileRows;
+        const int mbase = (wb * 2 * NR + rg * 2 + i) * kTileRows;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int m = mbase + c32_row(4 * q, lane);
@@ -294,13 +309,12 @@ __global__ __launch_bounds__(NWV * 64, 8 / NWV) void k_expert_tile(
 }
 
 namespace {
-template <int MODE, int NWV>
+template <int MODE, class GEO>
 hipError_t launch_mode(const FwdArgs& a) {
-  constexpr int kRowsWG = Geo<NWV>::kRowsWG;
   const int d = a.dim.d, F = a.dim.F;
   const int rows = MODE == 0 ? 2 * F : d;
-  const int grid = ((rows / kRowsWG) * a.max_tiles + 7) / 8 * 8;
-  return launch(k_expert_tile<MODE, NWV>, dim3(grid), dim3(NWV * 64), a.stream,
+  const int grid = ((rows / GEO::kRowsWG) * a.max_tiles + 7) / 8 * 8;
+  return launch(k_expert_tile<MODE, GEO>, dim3(grid), dim3(GEO::kThreads), a.stream,
                 a.ev[MODE == 0 ? kSlotExpertsA : kSlotExpertsB],
                 (const uint16_t*)(MODE == 0 ? a.wgu : a.wd),
                 (const uint16_t*)(MODE == 0 ? a.xn : a.act), (const int*)a.tilemap, a.max_tiles,
@@ -308,18 +322,25 @@ hipError_t launch_mode(const FwdArgs& a) {
                 (const float*)a.gate, (const float*)a.inv, a.dim.k, a.dim.E,
                 (const uint16_t*)a.zrow, (uint16_t*)(MODE == 0 ? a.act : a.out), a.ybuf, d, F);
 }
+// 512 weight rows x 128 tokens, one workgroup per CU.  (A 256 x 256 shape,
+// Geo<4, 2>, pulls fewer bytes per flop but its two row groups fetch the same
+// weight lines back to back, and the second fetch stalls the CU's L1 on the
+// pending line instead of sharing it: measured 1.5-1.9x slower.)
+using GBig = Geo<8, 1>;
+constexpr int kBigRows = GBig::kRowsWG;
+using G4x1 = Geo<4, 1>;  // 256 weight rows x 128 tokens, two workgroups per CU
 }  // namespace
 
-// Eight waves (512 weight rows, one workgroup per CU) where the rows divide
-// into them, else four (256 rows, two workgroups per CU).  The down
-// projection of top-k > 1 layers keeps four waves: its fp32 epilogue is
-// twice as large and is hidden only behind a second resident workgroup.
+// Eight waves (one workgroup per CU) where the rows divide into them, else
+// four (two workgroups per CU).  The down projection of top-k > 1 layers
+// keeps four waves: its fp32 epilogue is twice as large and is hidden only
+// behind a second resident workgroup.
 hipError_t launch_experts_tile(const FwdArgs& a) {
-  const bool w8_gu = (2 * a.dim.F) % 512 == 0;
-  const bool w8_d = a.dim.d % 512 == 0 && a.dim.k == 1;
-  hipError_t err = w8_gu ? launch_mode<0, 8>(a) : launch_mode<0, 4>(a);
+  const bool big_gu = (2 * a.dim.F) % kBigRows == 0;
+  const bool big_d = a.dim.d % kBigRows == 0 && a.dim.k == 1;
+  hipError_t err = big_gu ? launch_mode<0, GBig>(a) : launch_mode<0, G4x1>(a);
   if (err != hipSuccess) return err;
-  return w8_d ? launch_mode<1, 8>(a) : launch_mode<1, 4>(a);
+  return big_d ? launch_mode<1, GBig>(a) : launch_mode<1, G4x1>(a);
 }
 
 }  // namespace moe
