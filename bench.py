@@ -59,6 +59,29 @@ def dominant_kernel_name(cfg) -> str:
     return "k_gateup_stream" if cfg.T * cfg.k <= 64 else "k_expert_tile<0>"
 
 
+def kernel_short_name(name: str) -> str:
+    """'void moe::k_x<0, moe::(anonymous namespace)::Geo<8, 1> >(args)' -> 'k_x<0, Geo<8, 1> >'."""
+    import re
+    name = re.sub(r"^void ", "", name).replace("(anonymous namespace)::", "")
+    depth, end = 0, len(name)
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            end = i
+            break
+    return name[:end].replace("moe::", "").strip()
+
+
+def _matches(short: str, kernel: str) -> bool:
+    """Does a profiled kernel name belong to the kernel named `kernel` ('k_x' or 'k_x<0>')?"""
+    if short == kernel or short.startswith(kernel + "<"):
+        return True
+    return kernel.endswith(">") and short.startswith(kernel[:-1] + ",")
+
+
 def _counter_means(run_dir: str) -> dict:
     """Mean counter value (KiB) per dispatch of each kernel in a rocprofv3 --pmc run."""
     import csv
@@ -66,8 +89,7 @@ def _counter_means(run_dir: str) -> dict:
     sums: dict = {}
     for r in csv.DictReader(open(os.path.join(run_dir, "run_counter_collection.csv"))):
         name = r["Kernel_Name"]
-        m = re.match(r"(?:void )?(?:moe::)?([A-Za-z_]\w*(?:<[^>(]*>)?)", name)
-        key = "torch_neg" if "neg_kernel" in name else (m.group(1) if m else name)
+        key = "torch_neg" if "neg_kernel" in name else kernel_short_name(name)
         s = sums.setdefault(key, [0.0, 0])
         s[0] += float(r["Counter_Value"])
         s[1] += 1
@@ -103,7 +125,7 @@ def ingest_counters(pmc_dir: str) -> None:
                 kernels[kname] = {"fetch_bytes": round(fm[kname] * 1024 * ffac),
                                   "write_bytes": round(wm[kname] * 1024 * wfac)}
         dom = dominant_kernel_name(cfg)
-        dk = next(k for k in kernels if k == dom or k.startswith(dom + "<"))
+        dk = next(k for k in kernels if _matches(k, dom))
         out[cfg.name] = {"kernel": dom, "source_hash": kernel_source_hash(dom),
                          "bytes_per_launch": kernels[dk]["fetch_bytes"] + kernels[dk]["write_bytes"],
                          "kernels": kernels}
@@ -162,7 +184,7 @@ def cpu_baseline(inputs, seconds: float):
             O.oracle_forward(vals, tokens=sample)
             reps += 1
             el = time.perf_counter() - t0
-            if el >= seconds or reps >= 50:
+            if el >= seconds or reps >= 10000:
                 break
     what = (f"full batch of {cfg.T} tokens" if sample is None else
             f"{ntok} sampled tokens of {cfg.T} (routing of all {cfg.T} tokens included)")

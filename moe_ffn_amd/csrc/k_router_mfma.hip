@@ -19,7 +19,7 @@
 // sel[T,k], gate[T,k].
 //
 // The kernel moves T*d*2 bytes in and the same out, so it is sized for
-// memory-level parallelism: a workgroup owns 16*TT tokens (MFMA 16x16x32:
+// memory-level parallelism: a workgroup owns 16*TT tokens (TT = 1; MFMA 16x16x32:
 // A = 16 router rows per tile, NA tiles; B = 16 tokens per tile, TT tiles),
 // its NW waves split the reduction axis into NW slices, and each wave issues
 // the loads of up to kRBatch k-steps at once.  One wave-wide token load reads
@@ -228,16 +228,13 @@ hipError_t go(const FwdArgs& a) {
                 a.dim.k, a.dim.eps, (const uint16_t*)a.zrow, (uint16_t*)a.sink,
                 (uint16_t*)a.xn, a.inv, a.sel, a.gate);
 }
-template <int TT>
-hipError_t go_tt(const FwdArgs& a) {
-  const int E = a.dim.E;
-  return E > 32 ? go<4, TT>(a) : E > 16 ? go<2, TT>(a) : go<1, TT>(a);
-}
 }  // namespace
 
-// Two token tiles per workgroup once that still leaves two workgroups per CU.
+// One 16-token tile per workgroup: at 16384 tokens two tiles per workgroup
+// (half the workgroups) measured 6% slower.
 hipError_t launch_router_mfma(const FwdArgs& a) {
-  return a.T >= 32 * 512 ? go_tt<2>(a) : go_tt<1>(a);
+  const int E = a.dim.E;
+  return E > 32 ? go<4, 1>(a) : E > 16 ? go<2, 1>(a) : go<1, 1>(a);
 }
 
 }  // namespace moe
