@@ -194,6 +194,60 @@ def cpu_baseline(inputs, seconds: float):
                       f"{el:.1f} s", "host_cpus": ncores}
 
 
+def per_forward(layers, hidden, outs, n: int) -> dict:
+    """Distribution of single-forward times (an event pair around each forward)."""
+    import torch
+    nl = len(layers)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        layers[i % nl].forward(hidden, out=outs[i % nl])
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    q = lambda f: round(t[min(len(t) - 1, int(f * len(t)))], 3)  # noqa: E731
+    return {"p10": q(0.1), "median": q(0.5), "p90": q(0.9), "n": n}
+
+
+def graph_timing(layers, hidden, outs, K: int) -> dict:
+    """One forward per layer copy captured into a HIP graph, replayed ~K/nl times."""
+    import torch
+    nl = len(layers)
+    torch.cuda.synchronize()
+    for L, o in zip(layers, outs):
+        L.forward(hidden, out=o)
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for L, o in zip(layers, outs):
+            L.forward(hidden, out=o)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for L, o in zip(layers, outs):
+            L.forward(hidden, out=o)
+    for o in outs:
+        o.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    same = all(torch.equal(o, r) for o, r in zip(outs, ref))
+    reps = max(1, K // nl)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * nl)
+    del g
+    return {"ms_per_step": ms, "matches_eager": bool(same)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -301,6 +355,11 @@ def main():
 
     ms_step, _ = timed(False)
     log(f"[bench] {K} steps: {ms_step * 1e3:.2f} us/step")
+    pf = per_forward(layers, hidden, outs, min(K, 1000))
+    log(f"[bench] per forward: p10 {pf['p10']} median {pf['median']} p90 {pf['p90']} us")
+    gr = graph_timing(layers, hidden, outs, K)
+    log(f"[bench] HIP graph of {nl} forwards: {gr['ms_per_step'] * 1e3:.2f} us/step, "
+        f"replay equals eager: {gr['matches_eager']}")
     ms_step_ev, slots = timed(True)
     log(f"[bench] with per-kernel events: {ms_step_ev * 1e3:.2f} us/step; "
         + ", ".join(f"{k_} {v * 1e3:.2f} us" for k_, v in slots.items()))
@@ -343,6 +402,9 @@ def main():
                   "hbm_GBps": round(lbytes / (ms_step * 1e-3) / 1e9, 1),
                   "mfma_frac": round(lflops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                   "us_per_step_with_kernel_events": round(ms_step_ev * 1e3, 3),
+                  "per_forward_us": pf,
+                  "graph": {"us_per_step": round(gr["ms_per_step"] * 1e3, 3),
+                            "forwards_per_graph": nl, "replay_equals_eager": gr["matches_eager"]},
                   "kernel_us": {k_: round(v * 1e3, 3) for k_, v in slots.items()}},
     }
     for L in layers:

@@ -17,10 +17,15 @@ struct KEv {
   hipEvent_t stop = nullptr;
 };
 
+// Plain launch unless per-kernel timing events are attached, so that a
+// forward can be captured into a HIP graph.
 template <typename F, typename... Args>
 inline hipError_t launch(F kernel, dim3 grid, dim3 block, hipStream_t s, const KEv& ev,
                          Args... args) {
-  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+  if (ev.start == nullptr && ev.stop == nullptr)
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  else
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
   return hipGetLastError();
 }
 
