@@ -43,7 +43,7 @@ def log(*a):
 # sources that decide the dominant kernel's memory traffic (its counters are
 # void once any of them changes)
 DOMINANT_SOURCES = {"k_gateup_stream": ["k_expert_stream.hip", "common.hpp", "kernels.hpp"],
-                    "k_expert_tile<0>": ["k_expert_tile.hip", "common.hpp", "kernels.hpp"]}
+                    "k_expert_gemm<0>": ["k_expert_gemm.hip", "common.hpp", "kernels.hpp"]}
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -56,7 +56,7 @@ def kernel_source_hash(kernel: str) -> str:
 
 
 def dominant_kernel_name(cfg) -> str:
-    return "k_gateup_stream" if cfg.T * cfg.k <= 64 else "k_expert_tile<0>"
+    return "k_gateup_stream" if cfg.T * cfg.k <= 64 else "k_expert_gemm<0>"
 
 
 def kernel_short_name(name: str) -> str:
@@ -152,7 +152,7 @@ def dominant_kernel(cfg, counts):
                 "work_unit": "bytes"}
     per_assign = 2 * 2 * F * d                      # gate and up: 2 flops x F x d each
     work = n * per_assign
-    return {"slot": "experts_gate_up", "kernel": "k_expert_tile<0>", "bound": "mfma",
+    return {"slot": "experts_gate_up", "kernel": "k_expert_gemm<0>", "bound": "mfma",
             "unit": "TFLOP/s", "units": n, "per_unit": per_assign,
             "unit_name": "routed assignment (gate+up flops)", "work": work, "work_unit": "flops"}
 

@@ -136,13 +136,14 @@ moe_status_t moe_layer_set_bias(moe_layer_t* layer, const float* b_router, void*
  * stream).  moe_layer_timing_stop() waits for those events, writes into
  * ms_sum[MOE_TIMED_SLOTS] each slot's summed kernel milliseconds and into
  * *n_forwards the number of forwards recorded, then releases the events.
- * Slots, in launch order: 0 RMSNorm+router+top-k, 1 histogram+permutation
- * (0 for bf16 layers with T*top_k <= 64, whose expert kernels dispatch), 2 first
- * expert kernel (gate/up), 3 second expert kernel (down), 4 combine (0 when
- * top_k = 1, where the combine is part of slot 3).
+ * Slots: 0 RMSNorm+router+top-k, 1 histogram+permutation (0 for bf16 layers
+ * with T*top_k <= 64, whose expert kernels dispatch), 2 first expert kernel
+ * (gate/up), 3 second expert kernel (down), 4 combine (0 when top_k = 1, where
+ * the combine is part of slot 3), 5 gather of the routed rows into expert
+ * order (bf16 layers with T*top_k > 64 only; it runs between slots 1 and 2).
  * Errors: INVALID_ARG (bad handle, max_forwards outside [1, 65536], stop
  * without start), HIP. */
-#define MOE_TIMED_SLOTS 5
+#define MOE_TIMED_SLOTS 6
 moe_status_t moe_layer_timing_start(moe_layer_t* layer, int32_t max_forwards);
 moe_status_t moe_layer_timing_stop(moe_layer_t* layer, float* ms_sum, int32_t* n_forwards);
 

@@ -132,7 +132,7 @@ __device__ __forceinline__ void stream_mac(const uint16_t* const (&w)[NW], const
 }
 }  // namespace
 
-// Gate/up projections and the SiLU(gate) * up epilogue for one 32-column F tile.
+// Gate/up projections and the SiLU(gate) * up epilogue for 32 columns of d_ff.
 // The workgroups with ft == 0 also write the routing outputs of their expert.
 template <int D>
 __global__ __launch_bounds__(256) void k_gateup_stream(
@@ -155,7 +155,8 @@ __global__ __launch_bounds__(256) void k_gateup_stream(
   const int kper = ksteps / kSplit;
   const int ks0 = wave * kper;
   const size_t tile_elems = (size_t)ksteps * kBlockElems;
-  const uint16_t* wg = wgu + (((size_t)e * (F / kTileRows) + ft) * 2) * tile_elems + lane * 8;
+  // the two interleaved gate/up tiles of columns 32*ft .. 32*ft+31
+  const uint16_t* wg = wgu + ((size_t)e * (2 * F / kTileRows) + 2 * ft) * tile_elems + lane * 8;
   const uint16_t* const wp[2] = {wg, wg + tile_elems};
   const int col = lane & 31;
 
@@ -173,19 +174,22 @@ __global__ __launch_bounds__(256) void k_gateup_stream(
     reduce_split<2>(acc, red, wave, lane);
 
     if (wave == 0 && valid) {
+      // stream q covers columns 32*ft + 16*q ..: gate(f) in element i, up(f) in i + 8
       const float s = inv[tok];  // RMSNorm scale of this token
-      uint16_t* dst = act + (size_t)(off + c0 + col) * F + ft * kTileRows;
+      uint16_t* dst = act + (size_t)(off + c0 + col) * F + ft * kTileRows + 4 * (lane >> 5);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r = c32_row(4 * g, lane);
-        float v4[4];
+      for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v4[q] = silu(s * acc[0][4 * g + q]) * (s * acc[1][4 * g + q]);
-        u32x2 v;
-        v[0] = pack_bf16x2(v4[0], v4[1]);
-        v[1] = pack_bf16x2(v4[2], v4[3]);
-        *reinterpret_cast<u32x2*>(dst + r) = v;
-      }
+        for (int g = 0; g < 2; ++g) {
+          float v4[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            v4[t] = silu(s * acc[q][4 * g + t]) * (s * acc[q][4 * g + 8 + t]);
+          u32x2 v;
+          v[0] = pack_bf16x2(v4[0], v4[1]);
+          v[1] = pack_bf16x2(v4[2], v4[3]);
+          *reinterpret_cast<u32x2*>(dst + 16 * q + 8 * g) = v;
+        }
     }
   }
 }

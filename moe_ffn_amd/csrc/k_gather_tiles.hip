@@ -1,0 +1,68 @@
+// K2b (prefill shapes): gather of the routed token rows into expert-ordered
+// MFMA operand tiles.
+//
+// The dispatch step (telknet.cc article, section 2.1: each token's row goes to
+// the experts TopK chose for it) made explicit as a copy: slot p of expert e
+// holds the normalised row x' = g * h of token gather[p].  Rows are stored in
+// 32-slot subtiles, each expert's slots padded to a whole number of subtiles
+// (the expert owning ceil(count / 32) subtiles from psub[e], the running sum
+// of those numbers), and every subtile in the B-operand order of
+// v_mfma_f32_32x32x16_bf16:
+//   xt[P][s][lane][8],  lane = row + 32 * (k-group),  k = 16 s + 8 * (k-group) + 0..7
+// so that the grouped GEMM reads its token operands as contiguous 1 KiB
+// blocks, like its weights.  Padding rows are zero.
+//
+// One wave per (subtile, 64-wide k group): four wave-wide loads, each reading
+// 8 rows x 128 contiguous bytes, and four stores, each writing 8 runs of 128
+// contiguous bytes.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void k_gather_tiles(const uint16_t* __restrict__ xn,
+                                                      const int* __restrict__ counts,
+                                                      const int* __restrict__ offsets,
+                                                      const int* __restrict__ gather, int E, int d,
+                                                      uint16_t* __restrict__ xt) {
+  const int groups = d / 64;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);  // wave of the grid
+  const int P = gw / groups, g = gw - (gw / groups) * groups;
+  int e = 0, base = 0;
+  for (; e < E; ++e) {
+    const int ns = (counts[e] + 31) >> 5;
+    if (P < base + ns) break;
+    base += ns;
+  }
+  if (e >= E) return;  // past the last subtile (no barrier in this kernel)
+  const int r0 = (P - base) * 32, cnt = counts[e], off = offsets[e];
+  const int lane = threadIdx.x & 63;
+  uint16_t* dst = xt + (size_t)P * (d / kKStep) * kBlockElems;
+  u32x4 v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int idx = q * 64 + lane;
+    const int rr = idx >> 3, c = idx & 7;  // row of the subtile, 16-byte chunk of the 128 bytes
+    v[q] = u32x4{0u, 0u, 0u, 0u};
+    if (r0 + rr < cnt) v[q] = ldg16(xn + (size_t)gather[off + r0 + rr] * d + g * 64 + c * 8);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int idx = q * 64 + lane;
+    const int rr = idx >> 3, c = idx & 7;
+    const int s = g * 4 + (c >> 1), li = (c & 1) * 32 + rr;
+    stg16(dst + ((size_t)s * 64 + li) * 8, v[q]);
+  }
+}
+
+// Subtiles of all experts for n assignments: at most floor((n + 31 E) / 32).
+int max_subtiles(int n, int E) { return (n + 31 * E) / 32; }
+
+hipError_t launch_gather_tiles(const FwdArgs& a) {
+  const int waves = max_subtiles(a.n, a.dim.E) * (a.dim.d / 64);
+  return launch(k_gather_tiles, dim3((waves + 3) / 4), dim3(256), a.stream, a.ev[kSlotGather],
+                (const uint16_t*)a.xn, (const int*)a.counts, (const int*)a.offsets,
+                (const int*)a.gather, a.dim.E, a.dim.d, (uint16_t*)a.xt);
+}
+
+}  // namespace moe

@@ -4,7 +4,8 @@
 // into 1 KiB blocks in MFMA 32x32x16 operand order, so that at run time each
 // wave-wide load is one contiguous KiB of HBM and lands in the operand
 // registers (or an LDS stage) without any shuffle:
-//   W_gu : [E][F/32][gate|up][d/16][64 lanes][8]   lane = row % 32 + 32 * (k-group)
+//   W_gu : [E][2F/32][d/16][64 lanes][8]   lane = row % 32 + 32 * (k-group); tile t
+//          holds the gate rows of columns 16t .. 16t+15, then their up rows
 //   W_d  : [E][d/32][F/16][64 lanes][8]
 // The router rows are stored in fp32 with the RMSNorm gain folded in,
 // wrg[e][i] = W_r[e][i] * g[i] (exact for bf16 operands), padded with zero rows
@@ -18,19 +19,19 @@ __global__ void k_pack_gateup(const uint16_t* __restrict__ wg, const uint16_t* _
                               uint16_t* __restrict__ packed, int E, int F, int d) {
   const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;  // 16-byte chunk index
   const int ks = d / kKStep;
-  const size_t total = (size_t)E * (F / kTileRows) * 2 * ks * 64;
+  const int nt = 2 * F / kTileRows;  // interleaved 32-row tiles per expert
+  const size_t total = (size_t)E * nt * ks * 64;
   if (q >= total) return;
   const int lane = (int)(q % 64);
   size_t r = q / 64;
   const int s = (int)(r % ks);
   r /= ks;
-  const int gu = (int)(r % 2);
-  r /= 2;
-  const int ft = (int)(r % (F / kTileRows));
-  const int e = (int)(r / (F / kTileRows));
-  const int row = ft * kTileRows + (lane & 31);
+  const int gt = (int)(r % nt);
+  const int e = (int)(r / nt);
+  const int rr = lane & 31;  // rows 0-15: gate, rows 16-31: up, of columns 16*gt ..
+  const int f = gt * 16 + (rr & 15);
   const int kk = s * kKStep + (lane >> 5) * 8;
-  const uint16_t* src = (gu ? wu : wg) + ((size_t)e * F + row) * d + kk;
+  const uint16_t* src = (rr < 16 ? wg : wu) + ((size_t)e * F + f) * d + kk;
   stg16(packed + q * 8, ldg16(src));
 }
 
@@ -74,7 +75,7 @@ __global__ void k_prep_router(const void* __restrict__ w_router, const void* __r
 
 hipError_t launch_pack_gateup(const uint16_t* w_gate, const uint16_t* w_up, uint16_t* packed,
                               int E, int F, int d, hipStream_t s) {
-  const size_t total = (size_t)E * (F / kTileRows) * 2 * (d / kKStep) * 64;
+  const size_t total = (size_t)E * (2 * F / kTileRows) * (d / kKStep) * 64;
   hipLaunchKernelGGL(k_pack_gateup, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, w_gate,
                      w_up, packed, E, F, d);
   return hipGetLastError();

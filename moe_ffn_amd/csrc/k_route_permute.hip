@@ -12,8 +12,7 @@
 // number of such peers below it; across chunks a per-wave, per-expert running
 // base in LDS advances by the peer count; across waves the bases start from an
 // exclusive scan of the per-wave counts of a first pass.  The result is
-// deterministic and identical to a stable sort by expert.  The same workgroup
-// then writes the tile map of the grouped GEMM.
+// deterministic and identical to a stable sort by expert.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -56,12 +55,11 @@ template <int EP>
 __global__ __launch_bounds__(1024) void k_route_permute(
     const int* __restrict__ sel, int n, int k, int E, int* __restrict__ counts,
     int* __restrict__ offsets, int* __restrict__ gather, int* __restrict__ scatter,
-    int* __restrict__ slot_expert, int* __restrict__ tilemap, int tile_rows, int max_tiles) {
+    int* __restrict__ slot_expert) {
   constexpr int NB = ilog2(EP);
   __shared__ int wc[16][EP];  // per-wave counts, then per-wave running bases
   __shared__ int cnt_s[EP];
   __shared__ int off_s[EP + 1];
-  __shared__ int tstart[EP + 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nchunks = (n + 63) / 64;
@@ -100,15 +98,12 @@ __global__ __launch_bounds__(1024) void k_route_permute(
   }
   __syncthreads();
   if (tid == 0) {
-    int o = 0, ts = 0;
+    int o = 0;
     for (int e = 0; e < E; ++e) {
       off_s[e] = o;
-      tstart[e] = ts;
       o += cnt_s[e];
-      ts += (cnt_s[e] + tile_rows - 1) / tile_rows;
     }
     off_s[E] = o;
-    tstart[E] = ts;
   }
   __syncthreads();
   if (tid < E) {
@@ -140,27 +135,13 @@ __global__ __launch_bounds__(1024) void k_route_permute(
       }
     }
   }
-
-  // tile map for the grouped GEMM: count, entries (expert << 16 | m-tile),
-  // then the first tile of each expert (E + 1 values)
-  if (tilemap != nullptr) {
-    const int total = min(tstart[E], max_tiles);
-    if (tid == 0) tilemap[0] = total;
-    if (tid <= E) tilemap[1 + max_tiles + tid] = min(tstart[tid], max_tiles);
-    for (int e = 0; e < E; ++e) {
-      const int s0 = tstart[e], nt = tstart[e + 1] - tstart[e];
-      for (int i = tid; i < nt; i += 1024)
-        if (s0 + i < max_tiles) tilemap[1 + s0 + i] = (e << 16) | i;
-    }
-  }
 }
 
 namespace {
 template <int EP>
 hipError_t launch_ep(const FwdArgs& a) {
   return launch(k_route_permute<EP>, dim3(1), dim3(1024), a.stream, a.ev[kSlotPermute], a.sel, a.n,
-                a.dim.k, a.dim.E, a.counts, a.offsets, a.gather, a.scatter, a.slot_expert,
-                a.tilemap, kTileTokens, a.max_tiles);
+                a.dim.k, a.dim.E, a.counts, a.offsets, a.gather, a.scatter, a.slot_expert);
 }
 }  // namespace
 

@@ -7,9 +7,10 @@
 
 namespace moe {
 
-// Kernel slots of one forward, in launch order (per-kernel timing).
+// Kernel slots of one forward (per-kernel timing).  Launch order: router,
+// permutation, gather (bf16 prefill only), gate/up, down, combine.
 enum Slot { kSlotNormRouter = 0, kSlotPermute = 1, kSlotExpertsA = 2, kSlotExpertsB = 3,
-            kSlotCombine = 4, kNumSlots = 5 };
+            kSlotCombine = 4, kSlotGather = 5, kNumSlots = 6 };
 
 // Optional start/stop events carried by a kernel's own dispatch packet.
 struct KEv {
@@ -32,14 +33,14 @@ inline hipError_t launch(F kernel, dim3 grid, dim3 block, hipStream_t s, const K
 // Packed expert-weight geometry (bf16).  Both banks are stored as 1 KiB blocks,
 // one per (32-row tile, 16-wide k step), each block in MFMA 32x32x16 operand
 // order: 64 lanes x 8 consecutive k of row (lane % 32), k-group (lane / 32).
-//   W_gu : [E][F/32 f-tiles][2: gate, up][d/16 k-steps][64][8]
+//   W_gu : [E][2F/32 tiles][d/16 k-steps][64][8], tile t = gate rows of columns
+//          16t .. 16t+15 then the up rows of the same columns (an MFMA output
+//          lane holds gate(f) in element i and up(f) in element i + 8, i < 8)
 //   W_d  : [E][d/32 m-tiles][F/16 k-steps][64][8]
 constexpr int kTileRows = 32;
 constexpr int kKStep = 16;
 constexpr int kBlockElems = 64 * 8;  // 512 bf16 = 1 KiB
 
-// Prefill tiles: 256 weight rows x kTileTokens tokens x 64 k per workgroup.
-constexpr int kTileTokens = 128;
 // Decode path is used while T * top_k is at most this many assignments.
 constexpr int kStreamMaxAssign = 64;
 
@@ -73,9 +74,8 @@ struct FwdArgs {
   int* gather;         // [n]
   int* scatter;        // [n]
   int* slot_expert;    // [n]
-  int* tilemap;        // [1 + max_tiles + E + 1]: count, (expert << 16 | m-tile), tile starts
-  int max_tiles;
-  void* act;           // [n, F] SwiGLU activations (bf16 or f32)
+  void* xt;            // bf16 prefill: gathered token rows in operand tiles (k_gather_tiles.hip)
+  void* act;           // [n, F] SwiGLU activations (decode, f32); operand tiles (bf16 prefill)
   float* ybuf;         // [n, d] fp32 expert outputs (k >= 2 only)
   const void* zrow;    // max(d, F) zero elements (16-byte aligned), read-only
   void* sink;          // max(d, F) elements that absorb stores of lanes without a token
@@ -87,6 +87,9 @@ hipError_t launch_norm_router(const FwdArgs& a);   // fp32 layers
 hipError_t launch_router_mfma(const FwdArgs& a);   // bf16 layers, T*k > kStreamMaxAssign
 hipError_t launch_router_token(const FwdArgs& a);  // bf16 layers, T*k <= kStreamMaxAssign
 hipError_t launch_route_permute(const FwdArgs& a);
+hipError_t launch_gather_tiles(const FwdArgs& a);
+// 32-slot subtiles of all experts for n assignments, each expert padded to whole subtiles
+int max_subtiles(int n, int E);
 hipError_t launch_experts_stream(const FwdArgs& a);
 hipError_t launch_experts_tile(const FwdArgs& a);
 hipError_t launch_experts_f32(const FwdArgs& a);

@@ -8,8 +8,9 @@
 //      expert's dispatch from the routing choice (k_expert_stream.hip)
 // bf16 layers, larger batches:
 //   K1 RMSNorm + router on bf16 MFMA + top-k + gates (k_router_mfma.hip)
-//   K2 histogram + scan + stable permutation + GEMM tile map (k_route_permute.hip)
-//   K3 LDS-tiled grouped GEMMs, gate/up with SiLU epilogue then down (k_expert_tile.hip)
+//   K2 histogram + scan + stable permutation (k_route_permute.hip), then the
+//      routed rows gathered into expert-ordered operand tiles (k_gather_tiles.hip)
+//   K3 LDS-staged grouped GEMMs, gate/up with SiLU epilogue then down (k_expert_gemm.hip)
 // fp32 layers: VALU router (k_norm_router.hip), K2, VALU experts (k_expert_f32.hip)
 //   K4 gate-weighted combine (k >= 2; folded into K3 for k = 1)
 #include <hip/hip_runtime.h>
@@ -62,7 +63,6 @@ struct moe_layer {
   uint32_t magic;
   moe::LayerDims dim;
   int max_tokens;
-  int max_tiles;
   int device;
   bool debug_sync;
   // parameters (one allocation)
@@ -86,7 +86,7 @@ struct moe_layer {
   int* gather;
   int* scatter;
   int* slot_expert;
-  int* tilemap;
+  void* xt;
   void* act;
   float* ybuf;
   void* zrow;
@@ -201,7 +201,6 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_wei
   const size_t d = L->dim.d, F = L->dim.F, E = L->dim.E, EP = L->dim.EP, k = L->dim.k;
   const size_t es = cfg->dtype == MOE_DTYPE_BF16 ? 2 : 4;
   const size_t nmax = (size_t)L->max_tokens * k;
-  L->max_tiles = (int)((nmax + moe::kTileTokens - 1) / moe::kTileTokens + E);
 
   // parameters
   Carver pc;
@@ -241,8 +240,10 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_wei
   const size_t o_gat = wc.take(nmax * 4);
   const size_t o_sca = wc.take(nmax * 4);
   const size_t o_sle = wc.take(nmax * 4);
-  const size_t o_tm = wc.take((size_t)(1 + L->max_tiles + 65) * 4);
-  const size_t o_act = wc.take(nmax * F * es);
+  // bf16: slot-ordered activations (decode) or padded operand tiles (prefill)
+  const size_t npad = bf16 ? (size_t)moe::max_subtiles((int)nmax, (int)E) * 32 : 0;
+  const size_t o_xt = bf16 ? wc.take(npad * d * 2) : 0;
+  const size_t o_act = wc.take((nmax > npad ? nmax : npad) * F * es);
   const size_t o_y = k > 1 ? wc.take(nmax * d * 4) : 0;
   const size_t zbytes = (d > F ? d : F) * 4;
   const size_t o_z = wc.take(zbytes);
@@ -263,7 +264,7 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_wei
   L->gather = at<int>(L->ws, o_gat);
   L->scatter = at<int>(L->ws, o_sca);
   L->slot_expert = at<int>(L->ws, o_sle);
-  L->tilemap = at<int>(L->ws, o_tm);
+  L->xt = bf16 ? at<void>(L->ws, o_xt) : nullptr;
   L->act = at<void>(L->ws, o_act);
   L->ybuf = k > 1 ? at<float>(L->ws, o_y) : nullptr;
   L->zrow = at<void>(L->ws, o_z);
@@ -359,8 +360,7 @@ moe_status_t moe_layer_forward(moe_layer_t* L, const void* hidden, int32_t T, vo
   a.gather = (routing && routing->gather) ? routing->gather : L->gather;
   a.scatter = (routing && routing->scatter) ? routing->scatter : L->scatter;
   a.slot_expert = L->slot_expert;
-  a.tilemap = L->tilemap;
-  a.max_tiles = (a.n + moe::kTileTokens - 1) / moe::kTileTokens + L->dim.E;
+  a.xt = L->xt;
   a.act = L->act;
   a.ybuf = L->ybuf;
   a.zrow = L->zrow;
@@ -377,7 +377,8 @@ moe_status_t moe_layer_forward(moe_layer_t* L, const void* hidden, int32_t T, vo
   const bool bf16 = L->dim.dtype == MOE_DTYPE_BF16;
   const bool decode = bf16 && a.n <= moe::kStreamMaxAssign;
   if (L->timing && L->t_used > 0 && a.ev[0].start != nullptr)
-    L->tslots[L->t_used - 1] = (uint8_t)(0x0d | (decode ? 0 : 0x02) | (L->dim.k > 1 ? 0x10 : 0));
+    L->tslots[L->t_used - 1] = (uint8_t)(0x0d | (decode ? 0 : 0x02) | (L->dim.k > 1 ? 0x10 : 0) |
+                                         (bf16 && !decode ? 0x20 : 0));
 
   if (decode) {
     he = moe::launch_router_token(a);
@@ -388,6 +389,10 @@ moe_status_t moe_layer_forward(moe_layer_t* L, const void* hidden, int32_t T, vo
     if (he != hipSuccess) return hip_fail(he, "router launch");
     he = moe::launch_route_permute(a);
     if (he != hipSuccess) return hip_fail(he, "permute launch");
+    if (bf16) {
+      he = moe::launch_gather_tiles(a);
+      if (he != hipSuccess) return hip_fail(he, "gather launch");
+    }
     he = bf16 ? moe::launch_experts_tile(a) : moe::launch_experts_f32(a);
   }
   if (he != hipSuccess) return hip_fail(he, "expert launch");

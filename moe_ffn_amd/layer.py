@@ -25,7 +25,8 @@ MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 EXPORTS = ("moe_abi_version", "moe_last_error", "moe_layer_create", "moe_layer_forward",
            "moe_layer_set_bias", "moe_layer_timing_start", "moe_layer_timing_stop",
            "moe_layer_destroy")
-TIMED_SLOTS = ("norm_router", "route_permute", "experts_gate_up", "experts_down", "combine")
+TIMED_SLOTS = ("norm_router", "route_permute", "experts_gate_up", "experts_down", "combine",
+               "gather")
 
 
 class LayerConfig(ctypes.Structure):
