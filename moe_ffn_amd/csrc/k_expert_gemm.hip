@@ -1,5 +1,4 @@
-// K3 (prefill shapes): grouped SwiGLU GEMMs over the experts, both operands
-// staged through LDS.
+// K3 (prefill shapes): grouped SwiGLU GEMMs over the experts.
 //
 // Expert FFN y = W_down (SiLU(W_gate x) * (W_up x)) per routed assignment
 // (SwiGLU: GLU variants paper on the ZONOS2 report's "Builds on" list; 16
@@ -8,24 +7,26 @@
 //   MODE 1  y[slot, m]   = act[slot] W_down^T                                    K = d_ff
 //           k = 1: out[token] = bf16(gate * y); k > 1: y kept in fp32.
 //
-// Work unit: (expert, block of 64*RT weight rows, span of at most 320 of the
+// Work unit: (expert, block of 128*RT weight rows, span of at most 160 of the
 // expert's slots).  An expert's slots are cut into the fewest spans of at most
-// ten 32-token subtiles, split evenly, so a unit usually holds all of an
-// expert's tokens at prefill sizes and every weight byte is read once.
+// five 32-token subtiles, split evenly; the spans of one weight block are
+// adjacent in the unit order, so they run together under one L2 and the block
+// comes from HBM once.
 //
-// Workgroup: four waves, one per SIMD, as 2 row groups x 2 token groups; a
-// wave owns RT 32-row tiles against TT 32-token subtiles (RT*TT accumulators
-// of 32x32 fp32).  Both operands are stored as 1 KiB MFMA operand blocks: the
-// weights in the packed bank, the tokens in expert-ordered subtiles (gate/up:
-// the gathered rows of k_gather_tiles.hip; down: the activations, which the
-// gate/up epilogue writes in that layout).  Every wave-wide load therefore
-// reads one contiguous KiB (8 full cache lines), which is what keeps the
-// L2-to-CU stream fast (16-row gathers of 64 bytes each ran at well under half
-// its rate).  Per 32-wide k stage the workgroup copies the blocks into one of
-// three LDS stages (slot = lane, conflict-free both ways); two stages of
-// global loads are in flight in registers.  The barrier of a stage is passed
-// with the next stage's first operands already in registers, so the MFMA pipe
-// does not wait on it.
+// Workgroup: four waves, one per SIMD, stacked along the weight rows; a wave
+// owns RT 32-row tiles against the unit's TT token subtiles (RT*TT
+// accumulators of 32x32 fp32).  Both operands are stored as 1 KiB MFMA operand
+// blocks: the weights in the packed bank, the tokens in expert-ordered
+// subtiles (gate/up: the gathered rows of k_gather_tiles.hip; down: the
+// activations, which the gate/up epilogue writes in that layout), so every
+// wave-wide load reads one contiguous KiB.
+//  * Weights go straight from HBM into each wave's operand registers through a
+//    queue Q k-steps deep (8 at RT = 3: 96 KiB in flight per CU; 16 at
+//    RT = 2: 128 KiB): the weight stream is what needs latency cover, and a
+//    register queue costs no LDS.
+//  * Tokens, shared by the four waves, go through three LDS stages of 64 k
+//    (two staged in registers in flight); one barrier per stage, passed with
+//    the next stage's first operands already read.
 //
 // Gate/up rows are packed as 32-row tiles of 16 gate rows followed by the 16
 // up rows of the same columns, so the lane that holds gate(f) in accumulator
@@ -37,150 +38,164 @@
 namespace moe {
 
 namespace {
-constexpr int kSub = 32;             // tokens per MFMA subtile
-constexpr int kTTMax = 5;            // token subtiles per wave, at most
-constexpr int kSubCap = 2 * kTTMax;  // token subtiles per work unit
-constexpr int kStages = 3;           // LDS stages
-constexpr int kStageK = 32;          // k per stage (two MFMA k-steps)
+constexpr int kSub = 32;      // tokens per MFMA subtile
+constexpr int kTTMax = 5;     // token subtiles per work unit, at most
+constexpr int kBK = 4;        // k-steps (of 16) per token stage
+constexpr int kBStages = 3;   // LDS token stages
+constexpr int kBStageEnt = kTTMax * kBK * 64;  // 16-byte LDS entries per token stage
 
 template <int RT>
 struct Geo {
-  static constexpr int kRowTiles = 2 * RT;         // 32-row weight tiles per unit
-  static constexpr int kRows = kRowTiles * 32;
-  static constexpr int kABlk = kRowTiles * 2;      // weight blocks (1 KiB) per stage
-  static constexpr int kBBlk = kSubCap * 2;        // token blocks per stage, at most
-  static constexpr int kStageEnt = (kABlk + kBBlk) * 64;  // 16-byte LDS entries per stage
+  static constexpr int kTiles = 4 * RT;  // 32-row weight tiles per unit
+  static constexpr int kRows = kTiles * 32;
 };
 
 template <int RT, int TT>
 struct Ctx {
-  static constexpr int NL = RT + TT;  // wave-wide block loads per wave and stage
-  const uint16_t* src[NL];            // block of stage 0 (lane offset applied)
-  size_t step[NL];                    // elements from one stage to the next (0: zero block)
-  int a_rd;                           // LDS entry of this wave's first weight operand
-  int b_rd;                           // LDS entry of its first token operand
-  int wave;
+  const uint16_t* wa;     // this wave's first weight tile (lane offset applied)
+  size_t tile_elems;      // elements of one packed 32-row tile
+  int ksteps;             // K / 16
+  const uint16_t* bsrc[TT];  // token blocks copied by this wave (stage 0, lane offset applied)
+  int bstep[TT];          // elements from one token stage to the next (0: zero block)
+  int wave, lane;
 };
 
-// Blocks of a stage: j < 4 RT are weight blocks (tile j / 2, k-step j % 2),
-// the rest token blocks (subtile (j - 4 RT) / 2, k-step j % 2).  Wave w copies
-// blocks w, w + 4, ...; block j sits at LDS entries j * 64 .. j * 64 + 63.
 template <int RT, int TT>
-__device__ __forceinline__ void gload(const Ctx<RT, TT>& c, int st, int nst,
-                                      u32x4 (&r)[RT + TT]) {
-  const int s = st < nst ? st : nst - 1;  // clamp: surplus loads stay in bounds
+__device__ __forceinline__ void load_a(const Ctx<RT, TT>& c, int ks, u32x4 (&q)[RT]) {
+  const int s = ks < c.ksteps ? ks : c.ksteps - 1;  // clamp: surplus loads stay in bounds
 #pragma unroll
-  for (int q = 0; q < RT + TT; ++q) r[q] = ldg16(c.src[q] + (size_t)s * c.step[q]);
+  for (int r = 0; r < RT; ++r) q[r] = ldg16(c.wa + r * c.tile_elems + (size_t)s * kBlockElems);
+}
+
+// Token stage st: blocks j = wave + 4q (subtile j / 4, k-step j % 4) of the
+// stage, at LDS entries j * 64 .. j * 64 + 63 of the stage buffer.
+template <int RT, int TT>
+__device__ __forceinline__ void load_b(const Ctx<RT, TT>& c, int st, int nst, u32x4 (&p)[TT]) {
+  const int s = st < nst ? st : nst - 1;
+#pragma unroll
+  for (int q = 0; q < TT; ++q) p[q] = ldg16(c.bsrc[q] + s * c.bstep[q]);
+}
+template <int RT, int TT>
+__device__ __forceinline__ void store_b(const Ctx<RT, TT>& c, u32x4* buf, const u32x4 (&p)[TT]) {
+#pragma unroll
+  for (int q = 0; q < TT; ++q) buf[(c.wave + 4 * q) * 64 + c.lane] = p[q];
+}
+template <int TT>
+__device__ __forceinline__ void read_b(const u32x4* buf, int s, int lane, u32x4 (&bv)[TT]) {
+#pragma unroll
+  for (int j = 0; j < TT; ++j) bv[j] = buf[(j * kBK + s) * 64 + lane];
 }
 
 template <int RT, int TT>
-__device__ __forceinline__ void swrite(const Ctx<RT, TT>& c, u32x4* buf, const u32x4 (&r)[RT + TT]) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int q = 0; q < RT + TT; ++q) buf[(c.wave + 4 * q) * 64 + lane] = r[q];
-}
-
-template <int RT, int TT>
-__device__ __forceinline__ void sread(const Ctx<RT, TT>& c, const u32x4* buf, int ss,
-                                      u32x4 (&xa)[RT], u32x4 (&xb)[TT]) {
-#pragma unroll
-  for (int r = 0; r < RT; ++r) xa[r] = buf[c.a_rd + (2 * r + ss) * 64];
-#pragma unroll
-  for (int j = 0; j < TT; ++j) xb[j] = buf[c.b_rd + (2 * j + ss) * 64];
-}
-
-template <int RT, int TT>
-__device__ __forceinline__ void mac(const u32x4 (&xa)[RT], const u32x4 (&xb)[TT],
+__device__ __forceinline__ void mac(const u32x4 (&a)[RT], const u32x4 (&bv)[TT],
                                     f32x16 (&acc)[RT][TT]) {
 #pragma unroll
   for (int j = 0; j < TT; ++j)
 #pragma unroll
-    for (int r = 0; r < RT; ++r) acc[r][j] = mfma_32x32x16(xa[r], xb[j], acc[r][j]);
+    for (int r = 0; r < RT; ++r) acc[r][j] = mfma_32x32x16(a[r], bv[j], acc[r][j]);
 }
 
-// One stage kt: MFMAs of its two k-steps; meanwhile the registers holding stage
-// kt+2 go to LDS buffer (kt+2)%3 (last read in stage kt-1, released by that
-// stage's barrier), the loads of stage kt+4 are issued into them, and the first
-// operands of stage kt+1 (written one stage earlier) are read.  Scheduling
-// barriers keep this order: the operands of a k-step are always read a whole
-// k-step of MFMAs ahead of their use (masks: 0x008 MFMA, 0x100 DS read,
-// 0x200 DS write, 0x020 VMEM read).
-template <int RT, int TT>
-__device__ __forceinline__ void stage(const Ctx<RT, TT>& c, u32x4* lds, int& buf, int kt, int nst,
-                                      u32x4 (&rg)[RT + TT], u32x4 (&oa)[RT], u32x4 (&ob)[TT],
-                                      f32x16 (&acc)[RT][TT]) {
-  constexpr int SE = Geo<RT>::kStageEnt;
-  constexpr int NL = RT + TT;             // staged 16-byte pieces per thread
-  constexpr int NM = RT * TT;             // MFMAs per k-step
-  const int b1 = buf == kStages - 1 ? 0 : buf + 1;
-  const int b2 = b1 == kStages - 1 ? 0 : b1 + 1;
-  u32x4 na[RT], nb[TT];
-  sread(c, lds + buf * SE, 1, na, nb);
-  __builtin_amdgcn_sched_barrier(0);
-  mac(oa, ob, acc);
-  swrite(c, lds + b2 * SE, rg);
-  gload(c, kt + 4, nst, rg);
+// One token stage kb (k-steps 4kb .. 4kb+3).  Per k-step: the token operands
+// of the next k-step are read from LDS while this k-step's MFMAs run, and the
+// weight queue slot just consumed is refilled eight k-steps ahead.  In the
+// second k-step the staged registers holding token stage kb+2 go to LDS buffer
+// (kb+2)%3 (last read in stage kb-1, released by its barrier) and the loads of
+// stage kb+4 are issued into them.  The last k-step reads the first operands
+// of stage kb+1 (written one stage earlier).  Scheduling barriers keep this
+// order (masks: 0x008 MFMA, 0x100 DS read, 0x200 DS write, 0x020 VMEM read).
+template <int RT, int TT, int Q, int P>
+__device__ __forceinline__ void bstage(const Ctx<RT, TT>& c, u32x4* lds, int& buf, int kb,
+                                       int nsb, u32x4 (&qa)[Q][RT], u32x4 (&rb)[TT],
+                                       u32x4 (&bc)[TT], f32x16 (&acc)[RT][TT]) {
+  constexpr int NM = RT * TT;
+  const int b1 = buf == kBStages - 1 ? 0 : buf + 1;
+  const int b2 = b1 == kBStages - 1 ? 0 : b1 + 1;
+  const u32x4* cur = lds + buf * kBStageEnt;
 #pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i < NL) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-    else if (i < 2 * NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  sread(c, lds + b1 * SE, 0, oa, ob);
-  mac(na, nb, acc);
+  for (int i = 0; i < kBK; ++i) {
+    const int slot = P * kBK + i;  // weight queue slot of this k-step
+    u32x4 bn[TT];
+    if (i < kBK - 1) read_b<TT>(cur, i + 1, c.lane, bn);
+    else read_b<TT>(lds + b1 * kBStageEnt, 0, c.lane, bn);
+    mac(qa[slot], bc, acc);
+    load_a(c, (kb * kBK + i) + Q, qa[slot]);
+    if (i == 1) {
+      store_b(c, lds + b2 * kBStageEnt, rb);
+      load_b(c, kb + 4, nsb, rb);
 #pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    if (i < RT + TT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      for (int m = 0; m < NM; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (m < TT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        else if (m < 2 * TT) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        else if (m < 3 * TT + RT) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (m < TT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        else if (m < TT + RT) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < TT; ++j) bc[j] = bn[j];
   }
-  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
   buf = b1;
 }
 
-template <int RT, int TT>
-__device__ __forceinline__ void mainloop(const Ctx<RT, TT>& c, u32x4* lds, int nst,
-                                         f32x16 (&acc)[RT][TT]) {
-  constexpr int SE = Geo<RT>::kStageEnt;
-  u32x4 r0[RT + TT], r1[RT + TT];
-  u32x4 oa[RT], ob[TT];
-  gload(c, 0, nst, r0);
-  gload(c, 1, nst, r1);
-  swrite(c, lds, r0);
-  gload(c, 2, nst, r0);
-  swrite(c, lds + SE, r1);
-  gload(c, 3, nst, r1);
+// Q: depth of the weight queue in k-steps (a multiple of 2 * kBK that divides
+// the k-steps of the reduction).
+template <int RT, int TT, int Q>
+__device__ __forceinline__ void mainloop(const Ctx<RT, TT>& c, u32x4* lds, f32x16 (&acc)[RT][TT]) {
+  constexpr int NP = Q / kBK;      // token stages per loop iteration
+  const int nsb = c.ksteps / kBK;  // token stages (a multiple of NP)
+  u32x4 qa[Q][RT], rb0[TT], rb1[TT], bc[TT];
+  load_b(c, 0, nsb, rb0);
+  load_b(c, 1, nsb, rb1);
+  store_b(c, lds, rb0);
+  load_b(c, 2, nsb, rb0);
+  store_b(c, lds + kBStageEnt, rb1);
+  load_b(c, 3, nsb, rb1);
+#pragma unroll
+  for (int i = 0; i < Q; ++i) load_a(c, i, qa[i]);
   __syncthreads();
-  sread(c, lds, 0, oa, ob);
+  read_b<TT>(lds, 0, c.lane, bc);
   int buf = 0;
-  for (int kt = 0; kt < nst; kt += 2) {
-    stage(c, lds, buf, kt, nst, r0, oa, ob, acc);
-    stage(c, lds, buf, kt + 1, nst, r1, oa, ob, acc);
+  for (int kb = 0; kb < nsb; kb += NP) {
+    bstage<RT, TT, Q, 0>(c, lds, buf, kb, nsb, qa, rb0, bc, acc);
+    bstage<RT, TT, Q, 1>(c, lds, buf, kb + 1, nsb, qa, rb1, bc, acc);
+    if constexpr (NP == 4) {
+      bstage<RT, TT, Q, 2>(c, lds, buf, kb + 2, nsb, qa, rb0, bc, acc);
+      bstage<RT, TT, Q, 3>(c, lds, buf, kb + 3, nsb, qa, rb1, bc, acc);
+    }
   }
 }
 
-// Work unit of a workgroup, or false for a surplus workgroup.  Units are
-// numbered expert-major, then weight block, then span (the spans sharing a
-// weight block are adjacent), and dealt to the 8 XCDs in contiguous ranges
-// (workgroup b runs on XCD b % 8) so that units sharing weights or token rows
-// run at the same time under one L2.
+// Work units.  Units are numbered expert-major, then weight block, then span
+// (the spans sharing a weight block are adjacent).  The grid is persistent,
+// one workgroup per CU: the unit list is cut into 8 contiguous ranges, one per
+// XCD (workgroup b runs on XCD b % 8), so that units sharing weights or token
+// rows run at the same time under one L2; inside a range the XCD's workgroups
+// take units in snake order (round r deals left to right for even r, right to
+// left for odd r), which pairs large and small units of neighbouring spans.
 struct Unit {
   int e, rb, slot0, nrows, nsub;
   int sub0;  // first subtile of the unit in the padded, expert-ordered subtile list
 };
 __device__ __forceinline__ int span_count(int cnt) {
   const int nsub = (cnt + kSub - 1) / kSub;
-  return (nsub + kSubCap - 1) / kSubCap;
+  return (nsub + kTTMax - 1) / kTTMax;
 }
-__device__ __forceinline__ bool find_unit(const int* __restrict__ counts,
-                                          const int* __restrict__ offsets, int E, int nrb, Unit& u) {
+__device__ __forceinline__ int unit_total(const int* __restrict__ counts, int E, int nrb) {
   int U = 0;
   for (int e = 0; e < E; ++e) U += nrb * span_count(counts[e]);
-  const int per = (U + 7) >> 3;
-  const int b = blockIdx.x, i = b >> 3;
-  const int L = (b & 7) * per + i;
-  if (i >= per || L >= U) return false;
+  return U;
+}
+__device__ __forceinline__ void decode_unit(const int* __restrict__ counts,
+                                            const int* __restrict__ offsets, int E, int nrb, int L,
+                                            Unit& u) {
   int base = 0, psub = 0;
   for (int e = 0; e < E; ++e) {
     const int cnt = counts[e];
@@ -196,15 +211,14 @@ __device__ __forceinline__ bool find_unit(const int* __restrict__ counts,
       u.nrows = min(cnt, s1 * kSub) - s0 * kSub;
       u.nsub = s1 - s0;
       u.sub0 = psub + s0;
-      return true;
+      return;
     }
     base += nrb * ns;
     psub += (cnt + kSub - 1) / kSub;
   }
-  return false;
 }
 
-template <int MODE, int RT, int TT>
+template <int MODE, int RT, int Q, int TT>
 __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16_t* __restrict__ wpk,
                                          const uint16_t* __restrict__ src,
                                          const int* __restrict__ gather,
@@ -215,33 +229,25 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
                                          int d, int F) {
   using G = Geo<RT>;
   const int K = MODE == 0 ? d : F;
-  const int nst = K / kStageK;
   const int rows_e = MODE == 0 ? 2 * F : d;  // weight rows of one expert
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rg = wave & 1, tg = wave >> 1;  // row group, token group
-  const size_t tile_elems = (size_t)(K / kKStep) * kBlockElems;
-  const int tile0 = u.rb * G::kRowTiles;  // first 32-row tile of the unit within the expert
+  const int tile0 = u.rb * G::kTiles + wave * RT;  // this wave's first tile within the expert
 
   Ctx<RT, TT> c;
   c.wave = wave;
+  c.lane = lane;
+  c.ksteps = K / kKStep;
+  c.tile_elems = (size_t)c.ksteps * kBlockElems;
+  c.wa = wpk + ((size_t)u.e * (rows_e / kTileRows) + tile0) * c.tile_elems + lane * 8;
 #pragma unroll
-  for (int q = 0; q < RT + TT; ++q) {
-    const int j = wave + 4 * q;  // block of the stage copied by this wave
-    if (q < RT) {                // weight tile j / 2, k-step j % 2
-      c.src[q] = wpk + ((size_t)u.e * (rows_e / kTileRows) + tile0 + (j >> 1)) * tile_elems +
-                 (j & 1) * kBlockElems + lane * 8;
-      c.step[q] = 2 * kBlockElems;
-    } else {                     // token subtile jb / 2, k-step jb % 2
-      const int jb = j - 4 * RT;
-      const bool valid = (jb >> 1) < u.nsub;
-      c.src[q] = valid ? src + ((size_t)(u.sub0 + (jb >> 1)) * (K / kKStep) + (jb & 1)) * kBlockElems +
-                             lane * 8
-                       : zrow + lane * 8;
-      c.step[q] = valid ? 2 * kBlockElems : 0;
-    }
+  for (int q = 0; q < TT; ++q) {
+    const int j = wave + 4 * q;  // token block of the stage: subtile j / 4, k-step j % 4
+    const bool valid = (j >> 2) < u.nsub;
+    c.bsrc[q] = valid ? src + ((size_t)(u.sub0 + (j >> 2)) * c.ksteps + (j & 3)) * kBlockElems +
+                            lane * 8
+                      : zrow + lane * 8;
+    c.bstep[q] = valid ? kBK * kBlockElems : 0;
   }
-  c.a_rd = (2 * rg * RT) * 64 + lane;
-  c.b_rd = (G::kABlk + 2 * tg * TT) * 64 + lane;
 
   f32x16 acc[RT][TT];
 #pragma unroll
@@ -251,24 +257,22 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[r][j][q] = 0.f;
 
-  mainloop(c, lds, nst, acc);
+  mainloop<RT, TT, Q>(c, lds, acc);
 
   // epilogue
   const int col = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int j = 0; j < TT; ++j) {
-    const int us = tg * TT + j;   // subtile of the unit
-    const int r = us * kSub + col;  // unit row
+    const int r = j * kSub + col;  // unit row
     if constexpr (MODE == 0) {
-      // activations in the down projection's operand tiles: subtile sub0 + us,
+      // activations in the down projection's operand tiles: subtile sub0 + j,
       // k-step gt (16 columns of d_ff per gate/up tile); each wave store of a
       // (tile, subtile) pair fills one whole 1 KiB block
-      if (us >= u.nsub) continue;
       const float sc = r < u.nrows ? inv[gather[u.slot0 + r]] : 0.f;  // RMSNorm scale
-      uint16_t* blk = dst16 + (size_t)(u.sub0 + us) * (F / kKStep) * kBlockElems;
+      uint16_t* blk = dst16 + (size_t)(u.sub0 + j) * (F / kKStep) * kBlockElems;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const int gt = tile0 + rg * RT + rt;  // 16 gate rows + 16 up rows: columns 16*gt ..
+        const int gt = tile0 + rt;  // 16 gate rows + 16 up rows: columns 16*gt ..
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
           float v4[4];
@@ -289,7 +293,7 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
       const float gw = k == 1 ? gate[tok] : 0.f;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const int m0 = (tile0 + rg * RT + rt) * kTileRows + 4 * hi;
+        const int m0 = (tile0 + rt) * kTileRows + 4 * hi;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int m = m0 + 8 * q;
@@ -310,57 +314,63 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
 }
 }  // namespace
 
-template <int MODE, int RT>
+template <int MODE, int RT, int Q>
 __global__ __launch_bounds__(256, 1) void k_expert_gemm(
     const uint16_t* __restrict__ wpk, const uint16_t* __restrict__ src,
     const int* __restrict__ counts, const int* __restrict__ offsets,
     const int* __restrict__ gather, const float* __restrict__ gate,
     const float* __restrict__ inv, int k, int E, const uint16_t* __restrict__ zrow,
     uint16_t* __restrict__ dst16, float* __restrict__ ybuf, int d, int F) {
-  __shared__ u32x4 lds[kStages * Geo<RT>::kStageEnt];
+  __shared__ u32x4 lds[kBStages * kBStageEnt];
   const int nrb = (MODE == 0 ? 2 * F : d) / Geo<RT>::kRows;
-  Unit u;
-  if (!find_unit(counts, offsets, E, nrb, u)) return;
-  // token subtiles per wave: the first group takes the larger half
-  switch ((u.nsub + 1) >> 1) {
-    case 5: run_unit<MODE, RT, 5>(u, lds, wpk, src, gather, gate, inv, k, zrow, dst16, ybuf, d, F); break;
-    case 4: run_unit<MODE, RT, 4>(u, lds, wpk, src, gather, gate, inv, k, zrow, dst16, ybuf, d, F); break;
-    case 3: run_unit<MODE, RT, 3>(u, lds, wpk, src, gather, gate, inv, k, zrow, dst16, ybuf, d, F); break;
-    case 2: run_unit<MODE, RT, 2>(u, lds, wpk, src, gather, gate, inv, k, zrow, dst16, ybuf, d, F); break;
-    default: run_unit<MODE, RT, 1>(u, lds, wpk, src, gather, gate, inv, k, zrow, dst16, ybuf, d, F); break;
+  const int U = unit_total(counts, E, nrb);
+  const int per = (U + 7) >> 3;          // units per XCD range
+  const int nw = gridDim.x >> 3;         // workgroups per XCD (the grid is a multiple of 8)
+  const int x = blockIdx.x & 7, w = blockIdx.x >> 3;
+  const int lo = x * per, hi = min(U, lo + per);
+  for (int r = 0; r * nw < per; ++r) {
+    const int L = lo + ((r & 1) ? (r + 1) * nw - 1 - w : r * nw + w);
+    if (L >= hi) continue;
+    Unit u;
+    decode_unit(counts, offsets, E, nrb, L, u);
+    __syncthreads();  // the previous unit's last LDS reads are done everywhere
+    switch (u.nsub) {
+      case 5: run_unit<MODE, RT, Q, 5>(u, lds, wpk, src, gather, gate, inv, k, zrow, dst16, ybuf, d, F); break;
+      case 4: run_unit<MODE, RT, Q, 4>(u, lds, wpk, src, gather, gate, inv, k, zrow, dst16, ybuf, d, F); break;
+      case 3: run_unit<MODE, RT, Q, 3>(u, lds, wpk, src, gather, gate, inv, k, zrow, dst16, ybuf, d, F); break;
+      case 2: run_unit<MODE, RT, Q, 2>(u, lds, wpk, src, gather, gate, inv, k, zrow, dst16, ybuf, d, F); break;
+      default: run_unit<MODE, RT, Q, 1>(u, lds, wpk, src, gather, gate, inv, k, zrow, dst16, ybuf, d, F); break;
+    }
   }
 }
 
 namespace {
-// Upper bound on the spans of all experts for n assignments: the subtiles
-// number at most floor((n + 31 E) / 32), and each expert adds at most
-// kSubCap - 1 to the rounding-up of its span count.
-int max_spans(int n, int E) { return ((n + 31 * E) / kSub + E * (kSubCap - 1)) / kSubCap; }
-
-template <int MODE, int RT>
+template <int MODE, int RT, int Q>
 hipError_t launch_gemm(const FwdArgs& a) {
-  const int d = a.dim.d, F = a.dim.F;
-  const int nrb = (MODE == 0 ? 2 * F : d) / Geo<RT>::kRows;
-  const int units = nrb * max_spans(a.n, a.dim.E);
-  const int grid = (units + 7) / 8 * 8;
-  return launch(k_expert_gemm<MODE, RT>, dim3(grid), dim3(256), a.stream,
+  const int grid = (a.num_cu + 7) / 8 * 8;  // persistent: one workgroup per CU
+  return launch(k_expert_gemm<MODE, RT, Q>, dim3(grid), dim3(256), a.stream,
                 a.ev[MODE == 0 ? kSlotExpertsA : kSlotExpertsB],
                 (const uint16_t*)(MODE == 0 ? a.wgu : a.wd),
                 (const uint16_t*)(MODE == 0 ? a.xt : a.act), (const int*)a.counts,
                 (const int*)a.offsets, (const int*)a.gather, (const float*)a.gate,
                 (const float*)a.inv, a.dim.k, a.dim.E, (const uint16_t*)a.zrow,
-                (uint16_t*)(MODE == 0 ? a.act : a.out), a.ybuf, d, F);
+                (uint16_t*)(MODE == 0 ? a.act : a.out), a.ybuf, a.dim.d, a.dim.F);
 }
 }  // namespace
 
-// Gate/up on 192-row blocks where 2 * d_ff divides into them, else 128-row
-// blocks; the down projection on 128-row blocks (d_model / 128 blocks per
-// expert, one unit per CU for 16 experts of ~256 tokens at d_model = 2048).
+// Gate/up on 384-row blocks (192 columns of d_ff) with an 8-k-step weight
+// queue where 2 * d_ff divides into them; the down projection, and gate/up
+// otherwise, on 256-row blocks with a 16-k-step queue where the reduction
+// divides into it (else 8).  On the prefill workloads the 384-row gate/up
+// units are faster (fewer re-reads of the token tiles per weight byte); the
+// deeper queue that fits the 256-row units' registers did not make up for it.
 hipError_t launch_experts_tile(const FwdArgs& a) {
-  hipError_t err = (2 * a.dim.F) % Geo<3>::kRows == 0 ? launch_gemm<0, 3>(a)
-                                                      : launch_gemm<0, 2>(a);
+  const int ksd = a.dim.d / kKStep, ksf = a.dim.F / kKStep;
+  hipError_t err;
+  if ((2 * a.dim.F) % Geo<3>::kRows == 0) err = launch_gemm<0, 3, 8>(a);
+  else err = ksd % 16 == 0 ? launch_gemm<0, 2, 16>(a) : launch_gemm<0, 2, 8>(a);
   if (err != hipSuccess) return err;
-  return launch_gemm<1, 2>(a);
+  return ksf % 16 == 0 ? launch_gemm<1, 2, 16>(a) : launch_gemm<1, 2, 8>(a);
 }
 
 }  // namespace moe

@@ -79,6 +79,7 @@ struct FwdArgs {
   float* ybuf;         // [n, d] fp32 expert outputs (k >= 2 only)
   const void* zrow;    // max(d, F) zero elements (16-byte aligned), read-only
   void* sink;          // max(d, F) elements that absorb stores of lanes without a token
+  int num_cu;          // compute units of the device (persistent grids)
   hipStream_t stream;
   KEv ev[kNumSlots];   // per-kernel timing events (null when not timing)
 };

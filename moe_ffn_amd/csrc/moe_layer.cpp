@@ -64,6 +64,7 @@ struct moe_layer {
   moe::LayerDims dim;
   int max_tokens;
   int device;
+  int num_cu;
   bool debug_sync;
   // parameters (one allocation)
   void* params;
@@ -195,6 +196,7 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_wei
   L->dim.dtype = cfg->dtype;
   L->max_tokens = cfg->max_tokens;
   L->device = dev;
+  L->num_cu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
   const char* dbg = std::getenv("MOE_DEBUG_SYNC");
   L->debug_sync = dbg != nullptr && dbg[0] == '1';
 
@@ -365,6 +367,7 @@ moe_status_t moe_layer_forward(moe_layer_t* L, const void* hidden, int32_t T, vo
   a.ybuf = L->ybuf;
   a.zrow = L->zrow;
   a.sink = L->sink;
+  a.num_cu = L->num_cu;
   a.stream = reinterpret_cast<hipStream_t>(stream);
   if (L->timing && L->t_used < L->t_max) {
     const hipEvent_t* ev = &L->tev[(size_t)L->t_used * kEventsPerForward];
