@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef struct moe_layer moe_layer_t; /* opaque; owned by the library */
 
@@ -129,6 +129,28 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const void* hidden, int32_t T
  * enqueued on `stream` (the update is ordered with forwards on that stream).
  * Errors: INVALID_ARG, HIP. */
 moe_status_t moe_layer_set_bias(moe_layer_t* layer, const float* b_router, void* stream);
+
+/* Copy the layer's current router bias (n_experts fp32) into DEVICE memory
+ * b_out (4-byte aligned), enqueued on `stream`.  Errors: INVALID_ARG, HIP. */
+moe_status_t moe_layer_get_bias(moe_layer_t* layer, float* b_out, void* stream);
+
+/* One step of auxiliary-loss-free load balancing on the router bias (the
+ * ZONOS2 report keeps b_l to push expert usage toward uniform, digest item 6;
+ * the step is that of the auxiliary-loss-free load-balancing paper listed on
+ * the index page's "Builds on" list):
+ *   b_e <- b_e + rate * sign(mean(c) - c_e),  e = 0 .. n_experts-1,
+ * the sign taken exactly as the sign of the integer sum(c) - n_experts * c_e
+ * (0 leaves b_e unchanged), the float32 sum b_e + rate * sign rounded once.
+ *   counts  DEVICE int32[n_experts], 4-byte aligned: assignment counts of a
+ *           batch (e.g. moe_routing_out_t.counts of a forward).  NULL means the
+ *           layer's own counts buffer, which holds the counts of the latest
+ *           forward whose routing argument was NULL or had a NULL counts.
+ *   rate    the step size (finite; negative values push away from balance).
+ * Enqueued on `stream` after the forward that produced the counts; the next
+ * forward on that stream routes with the updated bias.  Nothing is
+ * allocated; the host is not synchronised.  Errors: INVALID_ARG, HIP. */
+moe_status_t moe_layer_update_bias(moe_layer_t* layer, const int32_t* counts, float rate,
+                                   void* stream);
 
 /* Per-kernel timing, for measurement tools.  moe_layer_timing_start() makes
  * the next `max_forwards` forwards launch every kernel with a start and a stop

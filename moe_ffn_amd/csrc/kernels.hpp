@@ -96,6 +96,9 @@ hipError_t launch_experts_tile(const FwdArgs& a);
 hipError_t launch_experts_f32(const FwdArgs& a);
 hipError_t launch_combine(const FwdArgs& a);
 
+// balancing step on the router bias (between forwards)
+hipError_t launch_bias_update(const int* counts, int E, float rate, float* bias, hipStream_t s);
+
 // create-time packing
 hipError_t launch_pack_gateup(const uint16_t* w_gate, const uint16_t* w_up, uint16_t* packed, int E,
                               int F, int d, hipStream_t s);

@@ -421,6 +421,35 @@ moe_status_t moe_layer_set_bias(moe_layer_t* L, const float* b_router, void* str
   return MOE_OK;
 }
 
+moe_status_t moe_layer_get_bias(moe_layer_t* L, float* b_out, void* stream) {
+  g_err.clear();
+  if (L == nullptr || L->magic != kMagic) return fail(MOE_ERR_INVALID_ARG, "invalid layer handle");
+  if (b_out == nullptr || !aligned(b_out, 4))
+    return fail(MOE_ERR_INVALID_ARG, "b_out is NULL or misaligned");
+  hipError_t he = hipMemcpyAsync(b_out, L->bias, (size_t)L->dim.E * 4, hipMemcpyDeviceToDevice,
+                                 reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "get_bias copy");
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_update_bias(moe_layer_t* L, const int32_t* counts, float rate,
+                                   void* stream) {
+  g_err.clear();
+  if (L == nullptr || L->magic != kMagic) return fail(MOE_ERR_INVALID_ARG, "invalid layer handle");
+  if (!std::isfinite(rate)) return fail(MOE_ERR_INVALID_ARG, "rate must be finite");
+  if (counts != nullptr && !aligned(counts, 4))
+    return fail(MOE_ERR_INVALID_ARG, "counts must be 4-byte aligned");
+  const int* c = counts != nullptr ? counts : L->counts;
+  hipError_t he = moe::launch_bias_update(c, L->dim.E, rate, L->bias,
+                                          reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "bias update launch");
+  if (L->debug_sync) {
+    he = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+    if (he != hipSuccess) return hip_fail(he, "bias update (MOE_DEBUG_SYNC)");
+  }
+  return MOE_OK;
+}
+
 moe_status_t moe_layer_timing_start(moe_layer_t* L, int32_t max_forwards) {
   g_err.clear();
   if (L == nullptr || L->magic != kMagic) return fail(MOE_ERR_INVALID_ARG, "invalid layer handle");

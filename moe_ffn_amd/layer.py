@@ -23,8 +23,9 @@ MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 
 # Symbols declared in include/moe_layer.h.
 EXPORTS = ("moe_abi_version", "moe_last_error", "moe_layer_create", "moe_layer_forward",
-           "moe_layer_set_bias", "moe_layer_timing_start", "moe_layer_timing_stop",
-           "moe_layer_destroy")
+           "moe_layer_set_bias", "moe_layer_get_bias", "moe_layer_update_bias",
+           "moe_layer_timing_start",
+           "moe_layer_timing_stop", "moe_layer_destroy")
 TIMED_SLOTS = ("norm_router", "route_permute", "experts_gate_up", "experts_down", "combine",
                "gather")
 
@@ -79,6 +80,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                       ctypes.POINTER(RoutingOut)]
     lib.moe_layer_set_bias.restype = ctypes.c_int
     lib.moe_layer_set_bias.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.moe_layer_get_bias.restype = ctypes.c_int
+    lib.moe_layer_get_bias.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.moe_layer_update_bias.restype = ctypes.c_int
+    lib.moe_layer_update_bias.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+                                          ctypes.c_void_p]
     lib.moe_layer_timing_start.restype = ctypes.c_int
     lib.moe_layer_timing_start.argtypes = [ctypes.c_void_p, ctypes.c_int32]
     lib.moe_layer_timing_stop.restype = ctypes.c_int
@@ -176,6 +182,28 @@ class MoELayer:
             raise ValueError("bias: need a contiguous CUDA fp32 tensor of n_experts values")
         _check(self._lib, self._lib.moe_layer_set_bias(self.handle, ctypes.c_void_p(b.data_ptr()),
                                                        ctypes.c_void_p(_stream_ptr(stream))))
+
+    def get_bias(self, stream=None) -> torch.Tensor:
+        """The layer's current router bias (fp32 CUDA tensor of n_experts values)."""
+        b = torch.empty(self.E, dtype=torch.float32, device="cuda")
+        _check(self._lib, self._lib.moe_layer_get_bias(self.handle, ctypes.c_void_p(b.data_ptr()),
+                                                       ctypes.c_void_p(_stream_ptr(stream))))
+        return b
+
+    def update_bias(self, rate: float, counts: torch.Tensor | None = None, stream=None):
+        """One balancing step b_e += rate * sign(mean(c) - c_e) on the layer's bias.
+
+        counts: int32 CUDA tensor of n_experts counts (e.g. routing["counts"] of
+        a forward), or None for the counts of the latest forward that did not
+        return its routing counts."""
+        ptr = None
+        if counts is not None:
+            if not (counts.is_cuda and counts.dtype == torch.int32 and counts.numel() == self.E
+                    and counts.is_contiguous()):
+                raise ValueError("counts: need a contiguous CUDA int32 tensor of n_experts values")
+            ptr = ctypes.c_void_p(counts.data_ptr())
+        _check(self._lib, self._lib.moe_layer_update_bias(self.handle, ptr, ctypes.c_float(rate),
+                                                          ctypes.c_void_p(_stream_ptr(stream))))
 
     def timing_start(self, max_forwards: int):
         """Record per-kernel HIP events in the next `max_forwards` forwards."""

@@ -23,6 +23,7 @@ state and TopK keeps a few of them)):
               gather[p] = token of slot p, scatter[a] = slot of assignment a
   O7  y_p   = W_down[e] (SiLU(W_gate[e] u) * (W_up[e] u)),  u = x_{gather[p]}
   O8  out_t = sum_{j<k} gate_{t,j} * y_{scatter[t*k+j]}       (no residual)
+  O9  balancing step: b_e <- b_e + rate * sign(mean_load - c_e)  (between forwards)
 
 Readings where the pages are silent (each is listed in the design doc):
 the bias only steers selection and never enters a gate; the layer returns
@@ -169,6 +170,30 @@ def combine(Y, gate, scatter, k: int) -> np.ndarray:
     for j in range(k):
         out += gate[:, j:j + 1] * Y[sc[:, j]]
     return out
+
+
+# O9 -------------------------------------------------------------------------
+def bias_update(b, counts, rate: float) -> np.ndarray:
+    """One step of auxiliary-loss-free load balancing on the router bias.
+
+    The ZONOS2 report keeps a per-expert bias b_l that pushes expert usage
+    toward uniform (digest item 6) and builds on the auxiliary-loss-free
+    load-balancing paper (title on the index page's "Builds on" list), whose
+    step moves each bias by a fixed rate toward balance:
+
+        b_e <- b_e + rate * sign(mean_load - c_e),   mean_load = sum(c) / E
+
+    The sign is the sign of the integer sum(c) - E * c_e (exact, no division);
+    sign(0) = 0 leaves a perfectly loaded expert alone.  The bias is stored
+    in float32 (the layer's bias type): the exact sum b_e + rate * s_e is
+    rounded once to float32.
+    """
+    c = np.asarray(counts, np.int64)
+    E = c.size
+    s = np.sign(c.sum() - E * c)
+    b32 = np.asarray(b, np.float32)
+    r32 = np.float32(rate)
+    return (b32.astype(np.float64) + np.float64(r32) * s).astype(np.float32)
 
 
 # whole layer ----------------------------------------------------------------

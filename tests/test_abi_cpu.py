@@ -28,8 +28,10 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["moe_abi_version", "moe_last_error", "moe_layer_create",
-                            "moe_layer_forward", "moe_layer_set_bias", "moe_layer_timing_start",
-                            "moe_layer_timing_stop", "moe_layer_destroy"])
+                            "moe_layer_forward", "moe_layer_set_bias", "moe_layer_get_bias",
+                            "moe_layer_update_bias",
+                            "moe_layer_timing_start", "moe_layer_timing_stop",
+                            "moe_layer_destroy"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -37,7 +39,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), f"missing export {name}"
     assert set(layer.EXPORTS) == set(declared_functions())
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def test_abi_structs_match_header_sizes():
@@ -87,13 +89,17 @@ def test_create_rejects_null_and_misaligned_weights_on_host():
     assert b"aligned" in lib.moe_last_error()
 
 
-def test_forward_and_set_bias_reject_bad_handles_and_destroy_is_null_safe():
+def test_entry_points_reject_bad_handles_and_destroy_is_null_safe():
     lib, layer = _lib()
     assert lib.moe_layer_forward(None, None, 1, None, None, None) == layer.MOE_ERR_INVALID_ARG
     bogus = (ctypes.c_uint32 * 64)()
     assert lib.moe_layer_forward(ctypes.addressof(bogus), None, 1, None, None,
                                  None) == layer.MOE_ERR_INVALID_ARG
     assert lib.moe_layer_set_bias(None, None, None) == layer.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_update_bias(None, None, 0.01, None) == layer.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_get_bias(None, None, None) == layer.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_update_bias(ctypes.addressof(bogus), None, 0.01,
+                                     None) == layer.MOE_ERR_INVALID_ARG
     assert lib.moe_layer_timing_start(None, 4) == layer.MOE_ERR_INVALID_ARG
     assert lib.moe_layer_timing_stop(None, None, None) == layer.MOE_ERR_INVALID_ARG
     lib.moe_layer_destroy(None)

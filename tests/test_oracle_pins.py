@@ -296,3 +296,44 @@ def test_invariants():
     tok = np.array([3, 0, 19, 7])
     rt = O.oracle_forward(L, k=2, eps=1e-6, tokens=tok)
     np.testing.assert_allclose(rt["out"], base["out"][tok], rtol=1e-14, atol=1e-16)
+
+
+# ------------------------------------------------------- O9 balancing step
+def test_bias_update_hand_example():
+    # E = 3, counts (5, 1, 2): mean 8/3, so expert 0 is over-loaded (bias
+    # down) and experts 1, 2 under-loaded (bias up); worked by hand.
+    b = np.array([0.25, -0.5, 1.0], np.float32)
+    got = O.bias_update(b, [5, 1, 2], 0.125)
+    np.testing.assert_array_equal(got, np.array([0.125, -0.375, 1.125], np.float32))
+    assert got.dtype == np.float32
+
+
+def test_bias_update_balanced_and_exact_mean():
+    b = np.array([0.1, 0.2, 0.3, 0.4], np.float32)
+    # perfectly uniform load: nothing moves
+    np.testing.assert_array_equal(O.bias_update(b, [7, 7, 7, 7], 1e-3), b)
+    # an expert exactly at the mean load (sum 12, E 4, mean 3) stays put
+    got = O.bias_update(b, [3, 5, 1, 3], 1e-3)
+    assert got[0] == b[0] and got[3] == b[3]
+    assert got[1] < b[1] and got[2] > b[2]
+
+
+def test_bias_update_single_float32_rounding():
+    # the exact sum b + rate is rounded once to float32 (not rate rounded
+    # then added in float64 and kept): 1 + 2**-30 rounds back to 1
+    b = np.array([1.0, 1.0], np.float32)
+    got = O.bias_update(b, [0, 2], 2.0 ** -30)
+    np.testing.assert_array_equal(got, np.array([1.0, 1.0], np.float32))
+    got = O.bias_update(b, [0, 2], 2.0 ** -20)
+    np.testing.assert_array_equal(got, np.array([1.0 + 2.0 ** -20, 1.0 - 2.0 ** -20], np.float32))
+
+
+def test_bias_update_relabelling_and_balance_direction():
+    rng = np.random.default_rng(3)
+    b = rng.standard_normal(16).astype(np.float32)
+    c = rng.integers(0, 50, 16)
+    perm = rng.permutation(16)
+    np.testing.assert_array_equal(O.bias_update(b[perm], c[perm], 0.01), O.bias_update(b, c, 0.01)[perm])
+    d = O.bias_update(b, c, 0.01).astype(np.float64) - b
+    mean = c.mean()
+    assert np.all(d[c > mean] < 0) and np.all(d[c < mean] > 0) and np.all(d[c == mean] == 0)
