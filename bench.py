@@ -248,6 +248,99 @@ def graph_timing(layers, hidden, outs, K: int) -> dict:
     return {"ms_per_step": ms, "matches_eager": bool(same)}
 
 
+def run_stack(args):
+    """Per-frame latency of the FFN half of the full 28-layer backbone at decode.
+
+    Layers (digest item 5): 3 dense, 24 MoE (16 experts; top-1, the last one
+    top-2), 1 dense; a dense layer is the one-expert case.  d_model=2048,
+    d_ff=3072, T=32 (32 streams x one frame).  Weights are drawn on the GPU
+    (seeded torch generator, the layer distributions of the workloads); no
+    oracle runs here (the stack's parity is in tests/test_gpu_stack.py).
+    """
+    import torch
+    from moe_ffn_amd import MoELayer, MoEStack, load_library
+    load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d, F, E, T = 2048, 3072, 16, 32
+    plan = [(1, 1)] * 3 + [(E, 1)] * 23 + [(E, 2)] + [(1, 1)]
+    g = torch.Generator(device=dev)
+    layers = []
+    t0 = time.perf_counter()
+    for l, (ne, k) in enumerate(plan):
+        g.manual_seed(1000 + l)
+        def rnd(*shape, std=1.0):
+            return (torch.randn(*shape, generator=g, device=dev) * std).to(torch.bfloat16)
+        w = {"rms_gain": (1.0 + torch.randn(d, generator=g, device=dev) * 0.1 ** 0.5).to(torch.bfloat16),
+             "w_router": rnd(ne, d, std=d ** -0.5),
+             "b_router": (torch.randn(ne, generator=g, device=dev) * 0.1 ** 0.5) if ne > 1
+             else torch.zeros(1, device=dev),
+             "w_gate": rnd(ne, F, d, std=d ** -0.5), "w_up": rnd(ne, F, d, std=d ** -0.5),
+             "w_down": rnd(ne, d, F, std=F ** -0.5)}
+        layers.append(MoELayer(d, F, ne, k, "bf16", w, T))
+        del w
+    torch.cuda.synchronize()
+    log(f"[bench] {len(layers)} layers created in {time.perf_counter() - t0:.1f} s")
+    g.manual_seed(7)
+    h0 = torch.randn(T, d, generator=g, device=dev).to(torch.bfloat16)
+    # routing of every layer on this frame (eager loop), for the bytes touched
+    touched, h = [], h0
+    for L in layers:
+        y, r = L.forward(h, routing=True)
+        touched.append(int((r["counts"] > 0).sum()))
+        h = (h.float() + y.float()).to(torch.bfloat16)
+    stack = MoEStack(layers, max_tokens=T)
+    out = stack.forward(h0)
+    torch.cuda.synchronize()
+    same_as_loop = bool(torch.equal(out.view(torch.int16), h.view(torch.int16)))
+    per_expert = 3 * F * d * 2
+    wbytes = sum(t * per_expert for t in touched)
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        stack.forward(h0, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        stack.forward(h0, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_eager = e0.elapsed_time(e1) / K
+    side = torch.cuda.Stream()
+    gout = torch.empty_like(h0)
+    stack.capture(h0, gout, side)
+    stack.replay(side)
+    side.synchronize()
+    graph_same = bool(torch.equal(gout.view(torch.int16), out.view(torch.int16)))
+    e0.record(side)
+    for _ in range(K):
+        stack.replay(side)
+    e1.record(side)
+    side.synchronize()
+    ms_graph = e0.elapsed_time(e1) / K
+    log(f"[bench] stack of {len(layers)} FFN layers: eager {ms_eager * 1e3:.1f} us, "
+        f"graph {ms_graph * 1e3:.1f} us per frame of {T} tokens; experts touched per layer "
+        f"{touched}; stack equals layer loop: {same_as_loop}, graph equals eager: {graph_same}")
+    line = {"metric": "FFN-stack frames of 32 tokens per second (28 layers, decode)",
+            "value": round(1e3 / ms_graph, 2), "unit": "frames/s", "n_gpus": 1, "steps": K,
+            "warmup": W, "ms_per_step": round(ms_graph, 6), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic: random-init weights drawn on the GPU (seeded), N(0,1) hidden states",
+            "config": {"workload": "ffn_stack_28_layers_decode_T32_d2048_E16_F3072",
+                       "layers": "3 dense, 23 MoE top-1, 1 MoE top-2, 1 dense", "T": T},
+            "stack": {"us_per_frame_graph": round(ms_graph * 1e3, 2),
+                      "us_per_frame_eager": round(ms_eager * 1e3, 2),
+                      "tokens_per_s": round(T / (ms_graph * 1e-3), 1),
+                      "weight_bytes_per_frame": wbytes,
+                      "weight_GBps": round(wbytes / (ms_graph * 1e-3) / 1e9, 1),
+                      "experts_touched": touched, "stack_equals_layer_loop": same_as_loop,
+                      "graph_equals_eager": graph_same}}
+    stack.close()
+    for L in layers:
+        L.close()
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,6 +353,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy (dst = -src, MIB MiB read and MIB MiB\n"
                          "written) five times, to scale the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--stack", action="store_true",
+                    help="time the FFN half of the full 28-layer backbone at decode instead")
     ap.add_argument("--ingest-counters", metavar="DIR",
                     help="no GPU: write profiles/traffic.json from rocprofv3 --pmc runs in DIR")
     args = ap.parse_args()
@@ -272,6 +367,12 @@ def main():
               "GPUs, so N GPUs give N times one GPU's throughput; run it with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.stack:
+        if args.steps == 2000:
+            args.steps = 100
+        run_stack(args)
+        return
 
     import numpy as np
     import torch

@@ -169,6 +169,47 @@ moe_status_t moe_layer_update_bias(moe_layer_t* layer, const int32_t* counts, fl
 moe_status_t moe_layer_timing_start(moe_layer_t* layer, int32_t max_forwards);
 moe_status_t moe_layer_timing_stop(moe_layer_t* layer, float* ms_sum, int32_t* n_forwards);
 
+/* ---- FFN stack ------------------------------------------------------------
+ * The feed-forward half of the backbone's layers in order (digest item 5: a
+ * 28-layer stack, the first three and the last one dense, the middle ones MoE,
+ * top-1 except the last MoE layer, top-2), each followed by its residual add:
+ *   h_0 = hidden_in;  h_{l+1} = h_l + FFN_l(h_l);  hidden_out = h_L,
+ * the sum rounded once to the activations' type (bf16: round to nearest even
+ * of the fp32 sum of the two bf16 values).  A dense layer is a layer created
+ * with n_experts = top_k = 1.  Attention and the rest of each layer are not
+ * part of the stack. */
+typedef struct moe_stack moe_stack_t;
+
+/* layers: n_layers handles (1..4096) created by moe_layer_create on the
+ * current device, all with the same d_model and dtype and max_tokens >=
+ * max_tokens; BORROWED: they must outlive the stack, which never destroys
+ * them.  The stack allocates two residual buffers and one FFN output buffer of
+ * [max_tokens, d_model].  Errors: INVALID_ARG, OOM, HIP. */
+moe_status_t moe_stack_create(int32_t n_layers, moe_layer_t* const* layers, int32_t max_tokens,
+                              moe_stack_t** out);
+
+/* One pass through the stack, enqueued on `stream` (no host synchronisation,
+ * no allocation).  hidden_in / hidden_out: DEVICE [T, d_model] of the layers'
+ * dtype, 16-byte aligned; hidden_out may equal hidden_in.  T in [0, max_tokens].
+ * The layers' workspaces and the stack's buffers are shared by every call:
+ * calls that overlap (on two streams) race.  Errors: INVALID_ARG, HIP. */
+moe_status_t moe_stack_forward(moe_stack_t* stack, const void* hidden_in, int32_t T,
+                               void* hidden_out, void* stream);
+
+/* Record the launch sequence of moe_stack_forward(stack, hidden_in, T,
+ * hidden_out) on `stream` (a created stream, not NULL) into a HIP graph owned
+ * by the stack, replacing any earlier one; nothing runs.  moe_stack_replay()
+ * launches the recorded graph on a stream: the same pointers, T and layer
+ * parameters at replay time (a bias changed in between is used).  Layers with
+ * per-kernel timing on cannot be recorded.  Errors: INVALID_ARG, HIP. */
+moe_status_t moe_stack_capture(moe_stack_t* stack, const void* hidden_in, int32_t T,
+                               void* hidden_out, void* stream);
+moe_status_t moe_stack_replay(moe_stack_t* stack, void* stream);
+
+/* Release the stack (NULL-safe) after synchronising the device; the layers
+ * stay valid. */
+void moe_stack_destroy(moe_stack_t* stack);
+
 /* Release the layer (NULL-safe).  Synchronises the device first, so work still
  * in flight on any stream that uses the layer completes before its memory goes. */
 void moe_layer_destroy(moe_layer_t* layer);

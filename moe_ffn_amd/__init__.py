@@ -7,7 +7,7 @@ step and a ctypes binding; PyTorch is used only for device memory and streams.
 """
 
 from .layer import (  # noqa: F401
-    MoELayer, MoELayerError, load_library, LIB_PATH, EXPORTS,
+    MoELayer, MoEStack, MoELayerError, load_library, LIB_PATH, EXPORTS,
     MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_OOM, MOE_ERR_HIP, MOE_ERR_UNSUPPORTED,
     LayerConfig, LayerWeights, RoutingOut, TIMED_SLOTS,
 )

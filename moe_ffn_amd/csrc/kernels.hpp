@@ -99,6 +99,10 @@ hipError_t launch_combine(const FwdArgs& a);
 // balancing step on the router bias (between forwards)
 hipError_t launch_bias_update(const int* counts, int E, float rate, float* bias, hipStream_t s);
 
+// residual add of an FFN stack: out = h + y (n elements, dtype 1 = bf16, 0 = fp32)
+hipError_t launch_residual(const void* h, const void* y, void* out, size_t n, int dtype,
+                           hipStream_t s);
+
 // create-time packing
 hipError_t launch_pack_gateup(const uint16_t* w_gate, const uint16_t* w_up, uint16_t* packed, int E,
                               int F, int d, hipStream_t s);

@@ -310,9 +310,13 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_wei
   return MOE_OK;
 }
 
-moe_status_t moe_layer_forward(moe_layer_t* L, const void* hidden, int32_t T, void* out,
-                               void* stream, const moe_routing_out_t* routing) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+// One forward; `allow_sync` is false inside a HIP graph capture, where the
+// MOE_DEBUG_SYNC synchronisation must not run.
+moe_status_t forward_impl(moe_layer_t* L, const void* hidden, int32_t T, void* out, void* stream,
+                          const moe_routing_out_t* routing, bool allow_sync) {
   if (L == nullptr || L->magic != kMagic) return fail(MOE_ERR_INVALID_ARG, "invalid layer handle");
   if (T < 0 || T > L->max_tokens)
     return fail(MOE_ERR_INVALID_ARG, "T must be in [0, max_tokens] (max_tokens = " +
@@ -403,11 +407,20 @@ moe_status_t moe_layer_forward(moe_layer_t* L, const void* hidden, int32_t T, vo
     he = moe::launch_combine(a);
     if (he != hipSuccess) return hip_fail(he, "combine launch");
   }
-  if (L->debug_sync) {
+  if (L->debug_sync && allow_sync) {
     he = hipStreamSynchronize(a.stream);
     if (he != hipSuccess) return hip_fail(he, "forward (MOE_DEBUG_SYNC)");
   }
   return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_layer_forward(moe_layer_t* L, const void* hidden, int32_t T, void* out,
+                               void* stream, const moe_routing_out_t* routing) {
+  g_err.clear();
+  return forward_impl(L, hidden, T, out, stream, routing, true);
 }
 
 moe_status_t moe_layer_set_bias(moe_layer_t* L, const float* b_router, void* stream) {
@@ -504,6 +517,193 @@ void moe_layer_destroy(moe_layer_t* L) {
   if (cur != dev) (void)hipSetDevice(dev);
   (void)hipDeviceSynchronize();
   release(L);
+  if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// FFN stack: the feed-forward half of the ZONOS2 backbone's layers in order
+// (digest item 5: 28 layers, the first three and the last one dense, the
+// MoE layers top-1 except the last one, top-2), each followed by the residual
+// add, h_{l+1} = h_l + FFN_l(h_l).  The stack borrows layer handles created by
+// the caller (a dense layer is a one-expert layer) and owns two residual
+// buffers, one FFN output buffer and, once captured, a HIP graph of the
+// whole sequence.
+
+struct moe_stack {
+  uint32_t magic;
+  std::vector<moe_layer_t*> layers;
+  int d, dtype, max_tokens, device;
+  void* buf;   // one allocation: residual A, residual B, FFN output, each [max_tokens, d]
+  void* hA;
+  void* hB;
+  void* y;
+  hipGraphExec_t exec;
+  hipStream_t exec_stream;
+};
+
+namespace {
+constexpr uint32_t kStackMagic = 0x4b745345u;  // "EStK"
+
+void stack_release(moe_stack* S) {
+  if (S == nullptr) return;
+  if (S->exec) (void)hipGraphExecDestroy(S->exec);
+  if (S->buf) (void)hipFree(S->buf);
+  S->magic = 0;
+  delete S;
+}
+
+moe_status_t stack_check(moe_stack* S, const void* hin, int32_t T, void* hout) {
+  if (S == nullptr || S->magic != kStackMagic) return fail(MOE_ERR_INVALID_ARG, "invalid stack handle");
+  if (T < 0 || T > S->max_tokens)
+    return fail(MOE_ERR_INVALID_ARG, "T must be in [0, max_tokens] (max_tokens = " +
+                                         std::to_string(S->max_tokens) + ")");
+  if (T > 0 && (hin == nullptr || hout == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "hidden_in or hidden_out is NULL");
+  if (!aligned(hin, 16) || !aligned(hout, 16))
+    return fail(MOE_ERR_INVALID_ARG, "hidden_in and hidden_out must be 16-byte aligned");
+  int dev = -1;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return hip_fail(he, "hipGetDevice");
+  if (dev != S->device) return fail(MOE_ERR_INVALID_ARG, "the current device is not the stack's device");
+  for (moe_layer_t* L : S->layers)
+    if (L == nullptr || L->magic != kMagic) return fail(MOE_ERR_INVALID_ARG, "a layer of the stack was destroyed");
+  return MOE_OK;
+}
+
+// The launch sequence of one stack forward (no validation, no synchronisation).
+moe_status_t stack_enqueue(moe_stack* S, const void* hin, int32_t T, void* hout, hipStream_t s,
+                           bool allow_sync) {
+  if (T == 0) return MOE_OK;
+  const size_t n = (size_t)T * S->d;
+  const void* cur = hin;
+  const int nl = (int)S->layers.size();
+  for (int l = 0; l < nl; ++l) {
+    moe_status_t st = forward_impl(S->layers[l], cur, T, S->y, s, nullptr, allow_sync);
+    if (st != MOE_OK) return st;
+    void* nxt = l == nl - 1 ? hout : ((l & 1) ? S->hB : S->hA);
+    hipError_t he = moe::launch_residual(cur, S->y, nxt, n, S->dtype, s);
+    if (he != hipSuccess) return hip_fail(he, "residual launch");
+    cur = nxt;
+  }
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_stack_create(int32_t n_layers, moe_layer_t* const* layers, int32_t max_tokens,
+                              moe_stack_t** out) {
+  g_err.clear();
+  if (out == nullptr) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (n_layers < 1 || n_layers > 4096 || layers == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "need 1 to 4096 layers");
+  if (max_tokens < 1) return fail(MOE_ERR_INVALID_ARG, "max_tokens must be > 0");
+  int d = 0, dtype = 0, dev = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    moe_layer_t* L = layers[l];
+    if (L == nullptr || L->magic != kMagic) return fail(MOE_ERR_INVALID_ARG, "invalid layer handle");
+    if (l == 0) {
+      d = L->dim.d;
+      dtype = L->dim.dtype;
+      dev = L->device;
+    } else if (L->dim.d != d || L->dim.dtype != dtype || L->device != dev) {
+      return fail(MOE_ERR_INVALID_ARG, "stack layers must share d_model, dtype and device");
+    }
+    if (L->max_tokens < max_tokens)
+      return fail(MOE_ERR_INVALID_ARG, "a layer's max_tokens is below the stack's");
+  }
+  int cur = -1;
+  hipError_t he = hipGetDevice(&cur);
+  if (he != hipSuccess) return hip_fail(he, "hipGetDevice");
+  if (cur != dev) return fail(MOE_ERR_INVALID_ARG, "the current device is not the layers' device");
+  moe_stack* S = new (std::nothrow) moe_stack();
+  if (S == nullptr) return fail(MOE_ERR_OOM, "host allocation failed");
+  S->layers.assign(layers, layers + n_layers);
+  S->d = d;
+  S->dtype = dtype;
+  S->max_tokens = max_tokens;
+  S->device = dev;
+  const size_t es = dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  const size_t one = align_up((size_t)max_tokens * d * es, 256);
+  he = hipMalloc(&S->buf, 3 * one);
+  if (he != hipSuccess) {
+    S->buf = nullptr;
+    stack_release(S);
+    (void)hipGetLastError();
+    return fail(MOE_ERR_OOM, std::string("stack buffers: ") + hipGetErrorString(he));
+  }
+  S->hA = S->buf;
+  S->hB = at<void>(S->buf, one);
+  S->y = at<void>(S->buf, 2 * one);
+  S->magic = kStackMagic;
+  *out = S;
+  return MOE_OK;
+}
+
+moe_status_t moe_stack_forward(moe_stack_t* S, const void* hidden_in, int32_t T, void* hidden_out,
+                               void* stream) {
+  g_err.clear();
+  moe_status_t st = stack_check(S, hidden_in, T, hidden_out);
+  if (st != MOE_OK) return st;
+  return stack_enqueue(S, hidden_in, T, hidden_out, reinterpret_cast<hipStream_t>(stream), true);
+}
+
+moe_status_t moe_stack_capture(moe_stack_t* S, const void* hidden_in, int32_t T, void* hidden_out,
+                               void* stream) {
+  g_err.clear();
+  moe_status_t st = stack_check(S, hidden_in, T, hidden_out);
+  if (st != MOE_OK) return st;
+  if (stream == nullptr) return fail(MOE_ERR_INVALID_ARG, "capture needs a created (non-null) stream");
+  for (moe_layer_t* L : S->layers)
+    if (L->timing) return fail(MOE_ERR_INVALID_ARG, "a layer of the stack has per-kernel timing on");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (S->exec) {
+    (void)hipGraphExecDestroy(S->exec);
+    S->exec = nullptr;
+  }
+  hipError_t he = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+  if (he != hipSuccess) return hip_fail(he, "hipStreamBeginCapture");
+  st = stack_enqueue(S, hidden_in, T, hidden_out, s, false);
+  const std::string enqueue_err = st != MOE_OK ? g_err : std::string();
+  hipGraph_t graph = nullptr;
+  he = hipStreamEndCapture(s, &graph);
+  if (st != MOE_OK) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return fail(st, enqueue_err);
+  }
+  if (he != hipSuccess) return hip_fail(he, "hipStreamEndCapture");
+  he = hipGraphInstantiate(&S->exec, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (he != hipSuccess) {
+    S->exec = nullptr;
+    return hip_fail(he, "hipGraphInstantiate");
+  }
+  S->exec_stream = s;
+  return MOE_OK;
+}
+
+moe_status_t moe_stack_replay(moe_stack_t* S, void* stream) {
+  g_err.clear();
+  if (S == nullptr || S->magic != kStackMagic) return fail(MOE_ERR_INVALID_ARG, "invalid stack handle");
+  if (S->exec == nullptr) return fail(MOE_ERR_INVALID_ARG, "nothing captured");
+  for (moe_layer_t* L : S->layers)
+    if (L == nullptr || L->magic != kMagic) return fail(MOE_ERR_INVALID_ARG, "a layer of the stack was destroyed");
+  hipError_t he = hipGraphLaunch(S->exec, reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "hipGraphLaunch");
+  return MOE_OK;
+}
+
+void moe_stack_destroy(moe_stack_t* S) {
+  if (S == nullptr || S->magic != kStackMagic) return;
+  const int dev = S->device;
+  int cur = -1;
+  (void)hipGetDevice(&cur);
+  if (cur != dev) (void)hipSetDevice(dev);
+  (void)hipDeviceSynchronize();
+  stack_release(S);
   if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
 }
 

@@ -25,7 +25,8 @@ MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 EXPORTS = ("moe_abi_version", "moe_last_error", "moe_layer_create", "moe_layer_forward",
            "moe_layer_set_bias", "moe_layer_get_bias", "moe_layer_update_bias",
            "moe_layer_timing_start",
-           "moe_layer_timing_stop", "moe_layer_destroy")
+           "moe_layer_timing_stop", "moe_layer_destroy", "moe_stack_create", "moe_stack_forward",
+           "moe_stack_capture", "moe_stack_replay", "moe_stack_destroy")
 TIMED_SLOTS = ("norm_router", "route_permute", "experts_gate_up", "experts_down", "combine",
                "gather")
 
@@ -92,6 +93,18 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                           ctypes.POINTER(ctypes.c_int32)]
     lib.moe_layer_destroy.restype = None
     lib.moe_layer_destroy.argtypes = [ctypes.c_void_p]
+    lib.moe_stack_create.restype = ctypes.c_int
+    lib.moe_stack_create.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
+                                     ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
+    for name in ("moe_stack_forward", "moe_stack_capture"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                      ctypes.c_void_p]
+    lib.moe_stack_replay.restype = ctypes.c_int
+    lib.moe_stack_replay.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.moe_stack_destroy.restype = None
+    lib.moe_stack_destroy.argtypes = [ctypes.c_void_p]
     if path is None:
         _lib = lib
     return lib
@@ -219,6 +232,63 @@ class MoELayer:
     def close(self):
         if self.handle is not None:
             self._lib.moe_layer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class MoEStack:
+    """The FFN half of a stack of layers with residual adds, run by the library:
+    h_{l+1} = h_l + layer_l(h_l).  The MoELayer objects are borrowed and must
+    stay alive (and open) while the stack is used."""
+
+    def __init__(self, layers: list, max_tokens: int):
+        self._lib = load_library()
+        self.handle = None
+        if not layers:
+            raise ValueError("a stack needs at least one layer")
+        self.layers = list(layers)
+        self.d, self.torch_dtype, self.max_tokens = layers[0].d, layers[0].torch_dtype, max_tokens
+        arr = (ctypes.c_void_p * len(layers))(*[L.handle.value for L in layers])
+        h = ctypes.c_void_p()
+        _check(self._lib, self._lib.moe_stack_create(len(layers), arr, int(max_tokens),
+                                                     ctypes.byref(h)))
+        self.handle = h
+
+    def _io(self, hidden: torch.Tensor, out):
+        if not (hidden.is_cuda and hidden.dtype == self.torch_dtype and hidden.dim() == 2
+                and hidden.shape[1] == self.d and hidden.is_contiguous()):
+            raise ValueError(f"hidden: need a contiguous CUDA {self.torch_dtype} tensor [T, {self.d}]")
+        if out is None:
+            out = torch.empty_like(hidden)
+        return out
+
+    def forward(self, hidden: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+        out = self._io(hidden, out)
+        _check(self._lib, self._lib.moe_stack_forward(self.handle, ctypes.c_void_p(hidden.data_ptr()),
+                                                      hidden.shape[0], ctypes.c_void_p(out.data_ptr()),
+                                                      ctypes.c_void_p(_stream_ptr(stream))))
+        return out
+
+    __call__ = forward
+
+    def capture(self, hidden: torch.Tensor, out: torch.Tensor, stream):
+        """Record one pass (these pointers, this T) into the stack's HIP graph."""
+        out = self._io(hidden, out)
+        _check(self._lib, self._lib.moe_stack_capture(self.handle, ctypes.c_void_p(hidden.data_ptr()),
+                                                      hidden.shape[0], ctypes.c_void_p(out.data_ptr()),
+                                                      ctypes.c_void_p(_stream_ptr(stream))))
+
+    def replay(self, stream=None):
+        _check(self._lib, self._lib.moe_stack_replay(self.handle, ctypes.c_void_p(_stream_ptr(stream))))
+
+    def close(self):
+        if self.handle is not None:
+            self._lib.moe_stack_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

@@ -24,6 +24,7 @@ state and TopK keeps a few of them)):
   O7  y_p   = W_down[e] (SiLU(W_gate[e] u) * (W_up[e] u)),  u = x_{gather[p]}
   O8  out_t = sum_{j<k} gate_{t,j} * y_{scatter[t*k+j]}       (no residual)
   O9  balancing step: b_e <- b_e + rate * sign(mean_load - c_e)  (between forwards)
+  O10 FFN stack: h_{l+1} = h_l + FFN_l(h_l) over the backbone's layers
 
 Readings where the pages are silent (each is listed in the design doc):
 the bias only steers selection and never enters a gate; the layer returns
@@ -247,3 +248,26 @@ def oracle_forward(vals: dict, k: int | None = None, forced_sel=None, tokens=Non
     return {"x": x, "z": z, "s": s, "sel": sel, "sel_oracle": sel_o, "margin": margin,
             "gate": gate, "counts": counts, "offsets": offsets, "gather": gather,
             "scatter": scatter, "out": out, "tokens": tok}
+
+
+# O10 ------------------------------------------------------------------------
+def stack_forward(layer_vals: list, H, ks: list, eps: float, forced_sels=None) -> dict:
+    """The FFN half of a stack of backbone layers with residual adds (digest
+    item 5: a 28-layer stack whose first three and last layers are dense and
+    whose middle layers are MoE, the last MoE layer top-2):
+
+        h_0 = H;   h_{l+1} = h_l + FFN_l(h_l)
+
+    FFN_l is the layer of O1-O8 (a dense layer is its one-expert case).
+    Everything stays in float64; forced_sels[l] optionally replaces layer l's
+    routing choice.  Returns the final h and every layer's routing.
+    """
+    h = _f64(H)
+    sels = []
+    for l, vals in enumerate(layer_vals):
+        v = dict(vals, hidden=h)
+        fs = None if forced_sels is None else forced_sels[l]
+        r = oracle_forward(v, k=ks[l], forced_sel=fs, eps=eps)
+        h = h + r["out"]
+        sels.append(r["sel"])
+    return {"out": h, "sel": sels}

@@ -67,14 +67,18 @@ def _store(x32: np.ndarray, dtype: str) -> np.ndarray:
     return round_to_bf16_bits(x32) if dtype == "bf16" else np.ascontiguousarray(x32, np.float32)
 
 
-def family_weights(cfg: LayerConfig) -> dict:
-    """Gain, router and expert weights; shared by every config of one family."""
-    ck = (cfg.family, cfg.d, cfg.E, cfg.F, cfg.dtype)
+def family_weights(cfg: LayerConfig, layer: int | None = None) -> dict:
+    """Gain, router and expert weights; shared by every config of one family.
+
+    ``layer`` selects the weights of one layer of a stack (an independent
+    stream per layer index); None is the single-layer family."""
+    ck = (cfg.family, cfg.d, cfg.E, cfg.F, cfg.dtype, layer)
     if ck in _weight_cache:
         return _weight_cache[ck]
     fam = _FAMILY_KEY.get(cfg.family, 99)
     d, E, F = cfg.d, cfg.E, cfg.F
-    key = lambda name: (fam, _TENSOR_KEY[name], d, E, F)  # noqa: E731
+    extra = () if layer is None else (1000 + int(layer),)
+    key = lambda name: (fam, _TENSOR_KEY[name], d, E, F) + extra  # noqa: E731
     gain = _normal(key("gain"), (d,), float(np.sqrt(0.1)))
     gain += np.float32(1.0)
     w = {
@@ -107,17 +111,19 @@ def load_zipf_bias(E: int) -> np.ndarray:
     return b
 
 
-def make_inputs(cid_or_cfg, T: int | None = None, hidden_seed: int = 0) -> dict:
+def make_inputs(cid_or_cfg, T: int | None = None, hidden_seed: int = 0,
+                layer: int | None = None) -> dict:
     """Inputs of one layer workload in storage form.
 
     ``T`` overrides the token count (hidden states then come from a stream keyed
-    by T as well); ``hidden_seed`` selects another hidden-state stream.
+    by T as well); ``hidden_seed`` selects another hidden-state stream;
+    ``layer`` selects one layer's weights (and bias) of a stack.
     Returned keys: cfg, hidden, gain, w_router, bias, w_gate, w_up, w_down.
     """
     cfg = CONFIGS[int(cid_or_cfg)] if not isinstance(cid_or_cfg, LayerConfig) else cid_or_cfg
     if T is not None and T != cfg.T:
         cfg = replace(cfg, T=int(T))
-    w = family_weights(cfg)
+    w = family_weights(cfg, layer)
     fam = _FAMILY_KEY.get(cfg.family, 99)
     hidden = _store(_normal((fam, _TENSOR_KEY["hidden"], cfg.cid, cfg.T, hidden_seed),
                             (cfg.T, cfg.d), 1.0), cfg.dtype)

@@ -31,7 +31,8 @@ def test_header_declares_the_abi():
                             "moe_layer_forward", "moe_layer_set_bias", "moe_layer_get_bias",
                             "moe_layer_update_bias",
                             "moe_layer_timing_start", "moe_layer_timing_stop",
-                            "moe_layer_destroy"])
+                            "moe_layer_destroy", "moe_stack_create", "moe_stack_forward",
+                            "moe_stack_capture", "moe_stack_replay", "moe_stack_destroy"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -98,6 +99,11 @@ def test_entry_points_reject_bad_handles_and_destroy_is_null_safe():
     assert lib.moe_layer_set_bias(None, None, None) == layer.MOE_ERR_INVALID_ARG
     assert lib.moe_layer_update_bias(None, None, 0.01, None) == layer.MOE_ERR_INVALID_ARG
     assert lib.moe_layer_get_bias(None, None, None) == layer.MOE_ERR_INVALID_ARG
+    assert lib.moe_stack_forward(None, None, 1, None, None) == layer.MOE_ERR_INVALID_ARG
+    assert lib.moe_stack_replay(None, None) == layer.MOE_ERR_INVALID_ARG
+    h = ctypes.c_void_p()
+    assert lib.moe_stack_create(0, None, 1, ctypes.byref(h)) == layer.MOE_ERR_INVALID_ARG
+    lib.moe_stack_destroy(None)
     assert lib.moe_layer_update_bias(ctypes.addressof(bogus), None, 0.01,
                                      None) == layer.MOE_ERR_INVALID_ARG
     assert lib.moe_layer_timing_start(None, 4) == layer.MOE_ERR_INVALID_ARG

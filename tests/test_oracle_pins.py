@@ -337,3 +337,37 @@ def test_bias_update_relabelling_and_balance_direction():
     d = O.bias_update(b, c, 0.01).astype(np.float64) - b
     mean = c.mean()
     assert np.all(d[c > mean] < 0) and np.all(d[c < mean] > 0) and np.all(d[c == mean] == 0)
+
+
+# ------------------------------------------------------------ O10 FFN stack
+def test_stack_matches_brute_force_composition():
+    # a 3-layer stack (dense, top-1 MoE, top-2 MoE) against the pure-Python
+    # brute force applied layer by layer with the residual added by hand
+    rng = np.random.default_rng(11)
+    d, F, T = 4, 5, 6
+    shapes = [(1, 1), (3, 1), (3, 2)]
+    layers = []
+    for E, k in shapes:
+        L = _rand_layer(rng, T, d, E, F)
+        L.pop("hidden")
+        layers.append(L)
+    H = rng.standard_normal((T, d))
+    got = O.stack_forward(layers, H, [k for _, k in shapes], 1e-6)
+    h = [list(map(float, r)) for r in H]
+    for L, (E, k) in zip(layers, shapes):
+        r = brute_forward(h, L["gain"], L["w_router"], L["bias"], L["w_gate"], L["w_up"],
+                          L["w_down"], k, 1e-6)
+        h = [[a + b for a, b in zip(hr, orow)] for hr, orow in zip(h, r["out"])]
+    np.testing.assert_allclose(got["out"], np.array(h), rtol=1e-11, atol=1e-12)
+
+
+def test_stack_of_zero_output_layers_is_identity():
+    rng = np.random.default_rng(12)
+    layers = []
+    for E in (1, 4):
+        L = _rand_layer(rng, 5, 6, E, 3)
+        L.pop("hidden")
+        L["w_down"] = np.zeros_like(L["w_down"])
+        layers.append(L)
+    H = rng.standard_normal((5, 6))
+    np.testing.assert_array_equal(O.stack_forward(layers, H, [1, 1], 1e-6)["out"], H)
