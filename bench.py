@@ -14,7 +14,10 @@ dominant kernel (its algorithmic bytes or flops per launch over its average
 duration, from HIP events recorded by the library on the forward's stream)
 and the fp64 CPU oracle's throughput on a bounded sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config {1,2,3,4}]
+With --fp8 the expert weights are E4M3 codes with per-row fp32 scales
+(moe_layer_create_fp8): decode streams half the weight bytes.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config {1,2,3,4}] [--fp8]
 """
 
 from __future__ import annotations
@@ -101,7 +104,8 @@ def ingest_counters(pmc_dir: str) -> None:
 
     Expects pmc_dir/copy_fetch and pmc_dir/copy_write (bench.py
     --copy-calibration 1024 under --pmc FETCH_SIZE, resp. WRITE_SIZE) and
-    pmc_dir/c<N>_fetch, pmc_dir/c<N>_write for each --config N profiled.  Each
+    pmc_dir/c<N>_fetch, pmc_dir/c<N>_write for each --config N profiled
+    (c<N>fp8_fetch, c<N>fp8_write for --config N --fp8).  Each
     counter is scaled by the bytes the copy kernel really moves over what the
     same counter reads for it."""
     from synth.configs import CONFIGS
@@ -112,11 +116,12 @@ def ingest_counters(pmc_dir: str) -> None:
     out = {"_calibration": {"copy_bytes_each_way": copy_bytes, "fetch_counter_bytes": cf,
                             "write_counter_bytes": cw, "fetch_factor": round(ffac, 5),
                             "write_factor": round(wfac, 5)}}
-    for cid in (1, 2, 3, 4):
-        fd, wd = (os.path.join(pmc_dir, f"c{cid}_{x}") for x in ("fetch", "write"))
+    for cid, tag in [(c, t) for c in (1, 2, 3, 4) for t in ("", "fp8")]:
+        fd, wd = (os.path.join(pmc_dir, f"c{cid}{tag}_{x}") for x in ("fetch", "write"))
         if not (os.path.isdir(fd) and os.path.isdir(wd)):
             continue
         cfg = CONFIGS[cid]
+        wname = cfg.name + ("_fp8w" if tag else "")
         fm, wm = _counter_means(fd), _counter_means(wd)
         kernels = {}
         for kname in fm:
@@ -126,29 +131,32 @@ def ingest_counters(pmc_dir: str) -> None:
                                   "write_bytes": round(wm[kname] * 1024 * wfac)}
         dom = dominant_kernel_name(cfg)
         dk = next(k for k in kernels if _matches(k, dom))
-        out[cfg.name] = {"kernel": dom, "source_hash": kernel_source_hash(dom),
-                         "bytes_per_launch": kernels[dk]["fetch_bytes"] + kernels[dk]["write_bytes"],
-                         "kernels": kernels}
+        out[wname] = {"kernel": dom, "source_hash": kernel_source_hash(dom),
+                      "bytes_per_launch": kernels[dk]["fetch_bytes"] + kernels[dk]["write_bytes"],
+                      "kernels": kernels}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
 
 
-def dominant_kernel(cfg, counts):
+def dominant_kernel(cfg, counts, fp8: bool = False):
     """Dominant kernel of a forward and its algorithmic work per launch.
 
     Decode-sized batches (T*k <= 64) take the weight-streaming path whose
     gate/up kernel moves 2/3 of the bytes; larger batches take the tiled
-    grouped GEMM whose gate/up launch does 2/3 of the flops."""
+    grouped GEMM whose gate/up launch does 2/3 of the flops.  fp8 weights:
+    one byte per weight plus one fp32 scale per row."""
     d, F, k, T = cfg.d, cfg.F, cfg.k, cfg.T
     n = T * k
     touched = int((counts > 0).sum())
     if n <= 64:
-        per_expert = 2 * F * d * 2                  # W_gate + W_up bf16 bytes
+        # W_gate + W_up bytes of one expert
+        per_expert = 2 * F * d + 2 * F * 4 if fp8 else 2 * F * d * 2
         work = touched * per_expert + n * d * 2 + n * F * 2
         return {"slot": "experts_gate_up", "kernel": "k_gateup_stream", "bound": "hbm",
                 "unit": "GB/s", "units": touched, "per_unit": per_expert,
-                "unit_name": "touched expert (W_gate + W_up bytes)", "work": work,
+                "unit_name": "touched expert (W_gate + W_up bytes%s)" % (
+                    ": E4M3 codes + row scales" if fp8 else ""), "work": work,
                 "work_unit": "bytes"}
     per_assign = 2 * 2 * F * d                      # gate and up: 2 flops x F x d each
     work = n * per_assign
@@ -157,15 +165,16 @@ def dominant_kernel(cfg, counts):
             "unit_name": "routed assignment (gate+up flops)", "work": work, "work_unit": "flops"}
 
 
-def layer_work(cfg, counts):
+def layer_work(cfg, counts, fp8: bool = False):
     touched = int((counts > 0).sum())
     d, F, n = cfg.d, cfg.F, cfg.T * cfg.k
-    bytes_ = touched * 3 * F * d * 2 + 2 * cfg.T * d * 2 + cfg.E * d * 2 + cfg.E * 4 + d * 2
+    wexp = 3 * F * d + (2 * F + d) * 4 if fp8 else 3 * F * d * 2  # expert weight bytes
+    bytes_ = touched * wexp + 2 * cfg.T * d * 2 + cfg.E * d * 2 + cfg.E * 4 + d * 2
     flops = n * 6 * F * d + 2 * cfg.T * d * cfg.E
     return bytes_, flops, touched
 
 
-def cpu_baseline(inputs, seconds: float):
+def cpu_baseline(inputs, seconds: float, fp8: dict | None = None):
     """The fp64 oracle as it stands, on the host cores, over a bounded sample."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
@@ -173,6 +182,9 @@ def cpu_baseline(inputs, seconds: float):
     from synth import gen
     cfg = inputs["cfg"]
     vals = gen.values_f32(inputs)
+    if fp8 is not None:  # the oracle on the dequantised fp8 expert weights
+        for name in ("w_gate", "w_up", "w_down"):
+            vals[name] = O.fp8_weights(fp8[name], fp8["s" + name[1:]])
     ncores = len(os.sched_getaffinity(0))
     sample = None if cfg.T <= 64 else np.sort(
         np.random.default_rng(0).choice(cfg.T, size=64, replace=False))
@@ -353,6 +365,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy (dst = -src, MIB MiB read and MIB MiB\n"
                          "written) five times, to scale the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--fp8", action="store_true",
+                    help="expert weights as E4M3 codes with per-row scales")
     ap.add_argument("--stack", action="store_true",
                     help="time the FFN half of the full 28-layer backbone at decode instead")
     ap.add_argument("--ingest-counters", metavar="DIR",
@@ -401,7 +415,12 @@ def main():
     t_gen = time.perf_counter()
     inp = make_inputs(args.config)
     cfg = inp["cfg"]
-    log(f"[bench] inputs for {cfg.name} in {time.perf_counter() - t_gen:.1f} s")
+    q8 = None
+    if args.fp8:
+        from synth.gen import fp8_expert_weights
+        q8 = fp8_expert_weights(inp)
+    wname = cfg.name + ("_fp8w" if args.fp8 else "")
+    log(f"[bench] inputs for {wname} in {time.perf_counter() - t_gen:.1f} s")
 
     def tt(a, bf16=True):
         if bf16 and a.dtype == np.uint16:
@@ -409,19 +428,25 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
 
     w = {"rms_gain": tt(inp["gain"]), "w_router": tt(inp["w_router"]),
-         "b_router": tt(inp["bias"], False), "w_gate": tt(inp["w_gate"]),
-         "w_up": tt(inp["w_up"]), "w_down": tt(inp["w_down"])}
-    layers = [MoELayer(cfg.d, cfg.F, cfg.E, cfg.k, cfg.dtype, w, cfg.T, rms_eps=cfg.eps)
+         "b_router": tt(inp["bias"], False)}
+    scales = None
+    if q8 is None:
+        w.update({n_: tt(inp[n_]) for n_ in ("w_gate", "w_up", "w_down")})
+    else:
+        w.update({n_: torch.from_numpy(q8[n_]).to(dev) for n_ in ("w_gate", "w_up", "w_down")})
+        scales = {n_: tt(q8["s_" + n_], False) for n_ in ("gate", "up", "down")}
+    layers = [MoELayer(cfg.d, cfg.F, cfg.E, cfg.k, cfg.dtype, w, cfg.T, rms_eps=cfg.eps,
+                       fp8_scales=scales)
               for _ in range(args.instances)]
-    del w
+    del w, scales
     hidden = tt(inp["hidden"])
     outs = [torch.empty_like(hidden) for _ in layers]
     torch.cuda.synchronize()
 
     _, r = layers[0].forward(hidden, routing=True)
     counts = r["counts"].cpu().numpy()
-    dom = dominant_kernel(cfg, counts)
-    lbytes, lflops, touched = layer_work(cfg, counts)
+    dom = dominant_kernel(cfg, counts, args.fp8)
+    lbytes, lflops, touched = layer_work(cfg, counts, args.fp8)
     log(f"[bench] {touched} experts touched; dominant kernel {dom['kernel']}")
 
     K, W = args.steps, args.warmup
@@ -476,7 +501,7 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         try:
             with open(TRAFFIC_FILE) as f:
-                tr = json.load(f).get(cfg.name, {})
+                tr = json.load(f).get(wname, {})
             if tr.get("kernel") == dom["kernel"] and \
                     tr.get("source_hash") == kernel_source_hash(dom["kernel"]):
                 traffic = tr.get("bytes_per_launch")
@@ -490,8 +515,9 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
         "data": "synthetic: seeded N(0,1) hidden states and random-init weights of the stated "
                 "distributions (no checkpoint or dataset)",
-        "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "d_ff": cfg.F,
+        "config": {"workload": wname, "T": cfg.T, "d_model": cfg.d, "d_ff": cfg.F,
                    "n_experts": cfg.E, "top_k": cfg.k, "router_bias": cfg.bias,
+                   "expert_weights": "fp8_e4m3_row_scaled" if args.fp8 else cfg.dtype,
                    "experts_touched": touched, "layer_instances": nl,
                    "device": props.name, "compute_units": props.multi_processor_count},
         "roofline": {"bound": dom["bound"], "achieved": round(achieved, 2), "peak": peak,
@@ -512,7 +538,7 @@ def main():
         L.close()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
-        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, q8)
     print(json.dumps(line), flush=True)
 
 

@@ -113,6 +113,33 @@ const char* moe_last_error(void);
 moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* w,
                               void* stream, moe_layer_t** out);
 
+/* Expert weights as OCP FP8 E4M3 codes (the SGLang-Omni ZONOS2 cookbook page,
+ * "Benchmark Results", serves the model with "fp8" and names nothing more; this
+ * ABI reads it as weight-only fp8 with bf16 activations.  E4M3: sign, 4
+ * exponent bits with bias 7, 3 mantissa bits, no infinities) with one fp32
+ * scale per output row: W_gate[e][f][:] = value(code) * gate[e*F + f], W_up
+ * likewise with up, W_down[e][m][:] = value(code) * down[e*d + m].
+ * All DEVICE pointers, 4-byte aligned, borrowed for the duration of create. */
+typedef struct {
+  const float* gate;  /* [E, F] */
+  const float* up;    /* [E, F] */
+  const float* down;  /* [E, d] */
+} moe_fp8_scales_t;
+
+/* As moe_layer_create, with w->w_gate, w_up, w_down pointing to uint8 E4M3
+ * codes ([E,F,d], [E,F,d], [E,d,F], 16-byte aligned) and `scales` giving their
+ * per-row scales; cfg->dtype must be MOE_DTYPE_BF16 (bf16 activations, gain
+ * and router) and d_ff a multiple of 256.  Decode-sized batches
+ * (T * top_k <= 64) stream the codes (half the bytes of bf16); larger batches
+ * run the bf16 MFMA GEMMs on the codes' values (every E4M3 value is a bf16
+ * value).  In both the scales multiply the fp32 accumulators, so no weight
+ * value is rounded.  The layer keeps both banks: 3 bytes per expert weight.
+ * Errors: as moe_layer_create; INVALID_ARG also for NULL `scales`, a NULL or
+ * misaligned scale pointer or an F32 dtype; UNSUPPORTED for d_ff % 256 != 0. */
+moe_status_t moe_layer_create_fp8(const moe_layer_config_t* cfg, const moe_layer_weights_t* w,
+                                  const moe_fp8_scales_t* scales, void* stream,
+                                  moe_layer_t** out);
+
 /* One forward over T tokens: hidden [T, d_model] -> out [T, d_model], both
  * DEVICE memory in the layer's dtype; `out` must not overlap `hidden`.
  * Asynchronous on `stream`: no host synchronisation and no allocation.

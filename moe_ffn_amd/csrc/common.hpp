@@ -99,4 +99,23 @@ __device__ __forceinline__ bool spread_owner(int lane) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Four OCP E4M3 codes (bytes of `four`) -> two of them as bf16x2 bits: the
+// low two bytes (HI = false) or the high two (HI = true).  The hardware
+// conversion to fp32 is exact and every E4M3 value fits bf16, so the high
+// halves of the fp32 results are the exact bf16 values.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pair_to_bf16x2(uint32_t four) {
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)four, HI);
+  return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
+}
+// 8 codes (u32x2) -> 8 bf16 operand values (u32x4)
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  u32x4 o;
+  o[0] = e4m3_pair_to_bf16x2<false>(lo);
+  o[1] = e4m3_pair_to_bf16x2<true>(lo);
+  o[2] = e4m3_pair_to_bf16x2<false>(hi);
+  o[3] = e4m3_pair_to_bf16x2<true>(hi);
+  return o;
+}
+
 }  // namespace moe

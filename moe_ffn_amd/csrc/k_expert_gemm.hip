@@ -32,6 +32,12 @@
 // up rows of the same columns, so the lane that holds gate(f) in accumulator
 // element i holds up(f) in element i + 8 and the SiLU * up epilogue needs no
 // exchange between lanes.
+//
+// fp8 (e4m3) expert weights: the GEMMs read a bank of the codes' exact bf16
+// values (every e4m3 value is a bf16 value), so the MFMA products are the
+// codes' own; the per-row dequantisation scales multiply the fp32
+// accumulators in the epilogue (rsc: per gate/up row, or per output row of
+// the down projection; null for bf16 weights).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -223,7 +229,8 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
                                          const uint16_t* __restrict__ src,
                                          const int* __restrict__ gather,
                                          const float* __restrict__ gate,
-                                         const float* __restrict__ inv, int k,
+                                         const float* __restrict__ inv,
+                                         const float* __restrict__ rsc, int k,
                                          const uint16_t* __restrict__ zrow,
                                          uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
                                          int d, int F) {
@@ -275,10 +282,18 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
         const int gt = tile0 + rt;  // 16 gate rows + 16 up rows: columns 16*gt ..
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
+          // fp8 weights: per-row dequantisation scales of the gate rows
+          // 16*gt + 8g + 4hi .. +3 and of the matching up rows
+          f32x4 sg = {1.f, 1.f, 1.f, 1.f}, su = sg;
+          if (rsc != nullptr) {
+            const float* rs = rsc + (size_t)u.e * 2 * F + 32 * gt + 8 * g + 4 * hi;
+            sg = *reinterpret_cast<const f32x4*>(rs);
+            su = *reinterpret_cast<const f32x4*>(rs + 16);
+          }
           float v4[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t)
-            v4[t] = silu(sc * acc[rt][j][4 * g + t]) * (sc * acc[rt][j][4 * g + 8 + t]);
+            v4[t] = silu(sc * sg[t] * acc[rt][j][4 * g + t]) * (sc * su[t] * acc[rt][j][4 * g + 8 + t]);
           u32x2 v;
           v[0] = pack_bf16x2(v4[0], v4[1]);
           v[1] = pack_bf16x2(v4[2], v4[3]);
@@ -297,6 +312,11 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int m = m0 + 8 * q;
+          if (rsc != nullptr) {  // fp8 weights: per-row scales of output rows m .. m+3
+            const f32x4 s4 = *reinterpret_cast<const f32x4*>(rsc + (size_t)u.e * d + m);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[rt][j][4 * q + t] *= s4[t];
+          }
           if (k == 1) {
             u32x2 v;
             v[0] = pack_bf16x2(gw * acc[rt][j][4 * q], gw * acc[rt][j][4 * q + 1]);
@@ -319,8 +339,9 @@ __global__ __launch_bounds__(256, 1) void k_expert_gemm(
     const uint16_t* __restrict__ wpk, const uint16_t* __restrict__ src,
     const int* __restrict__ counts, const int* __restrict__ offsets,
     const int* __restrict__ gather, const float* __restrict__ gate,
-    const float* __restrict__ inv, int k, int E, const uint16_t* __restrict__ zrow,
-    uint16_t* __restrict__ dst16, float* __restrict__ ybuf, int d, int F) {
+    const float* __restrict__ inv, const float* __restrict__ rsc, int k, int E,
+    const uint16_t* __restrict__ zrow, uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
+    int d, int F) {
   __shared__ u32x4 lds[kBStages * kBStageEnt];
   const int nrb = (MODE == 0 ? 2 * F : d) / Geo<RT>::kRows;
   const int U = unit_total(counts, E, nrb);
@@ -335,11 +356,11 @@ __global__ __launch_bounds__(256, 1) void k_expert_gemm(
     decode_unit(counts, offsets, E, nrb, L, u);
     __syncthreads();  // the previous unit's last LDS reads are done everywhere
     switch (u.nsub) {
-      case 5: run_unit<MODE, RT, Q, 5>(u, lds, wpk, src, gather, gate, inv, k, zrow, dst16, ybuf, d, F); break;
-      case 4: run_unit<MODE, RT, Q, 4>(u, lds, wpk, src, gather, gate, inv, k, zrow, dst16, ybuf, d, F); break;
-      case 3: run_unit<MODE, RT, Q, 3>(u, lds, wpk, src, gather, gate, inv, k, zrow, dst16, ybuf, d, F); break;
-      case 2: run_unit<MODE, RT, Q, 2>(u, lds, wpk, src, gather, gate, inv, k, zrow, dst16, ybuf, d, F); break;
-      default: run_unit<MODE, RT, Q, 1>(u, lds, wpk, src, gather, gate, inv, k, zrow, dst16, ybuf, d, F); break;
+      case 5: run_unit<MODE, RT, Q, 5>(u, lds, wpk, src, gather, gate, inv, rsc, k, zrow, dst16, ybuf, d, F); break;
+      case 4: run_unit<MODE, RT, Q, 4>(u, lds, wpk, src, gather, gate, inv, rsc, k, zrow, dst16, ybuf, d, F); break;
+      case 3: run_unit<MODE, RT, Q, 3>(u, lds, wpk, src, gather, gate, inv, rsc, k, zrow, dst16, ybuf, d, F); break;
+      case 2: run_unit<MODE, RT, Q, 2>(u, lds, wpk, src, gather, gate, inv, rsc, k, zrow, dst16, ybuf, d, F); break;
+      default: run_unit<MODE, RT, Q, 1>(u, lds, wpk, src, gather, gate, inv, rsc, k, zrow, dst16, ybuf, d, F); break;
     }
   }
 }
@@ -353,7 +374,8 @@ hipError_t launch_gemm(const FwdArgs& a) {
                 (const uint16_t*)(MODE == 0 ? a.wgu : a.wd),
                 (const uint16_t*)(MODE == 0 ? a.xt : a.act), (const int*)a.counts,
                 (const int*)a.offsets, (const int*)a.gather, (const float*)a.gate,
-                (const float*)a.inv, a.dim.k, a.dim.E, (const uint16_t*)a.zrow,
+                (const float*)a.inv, MODE == 0 ? a.sgu : a.sd, a.dim.k, a.dim.E,
+                (const uint16_t*)a.zrow,
                 (uint16_t*)(MODE == 0 ? a.act : a.out), a.ybuf, a.dim.d, a.dim.F);
 }
 }  // namespace

@@ -102,4 +102,127 @@ hipError_t launch_prep_router(const void* w_router, const void* gain, int dtype,
   return hipGetLastError();
 }
 
+
+// ---- fp8 (OCP E4M3) expert weights ------------------------------------------
+// The caller gives byte codes and one fp32 scale per output row.  Two copies are
+// packed: an fp8 bank for the weight-streaming decode kernels, in which lane l
+// of a 16-byte piece holds the codes of row l % 32 for two consecutive k-steps,
+//   W_gu8 : [E][2F/32][d/32][64 lanes][16]   bytes 0-7: k-step 2p, 8-15: 2p+1
+//   W_d8  : [E][d/32][F/32][64 lanes][16]
+// (k-group l / 32 of each k-step), and the bf16 banks above holding the code
+// values themselves (every E4M3 value is exact in bf16) for the prefill GEMM.
+// The scales are applied to the fp32 accumulators, so no weight is rounded.
+// gate/up or down codes -> bf16 bank in the layout of k_pack_gateup / k_pack_down
+__global__ void k_pack_gateup_fp8_bf16(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
+                                       uint16_t* __restrict__ packed, int E, int F, int d) {
+  const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const int ks = d / kKStep;
+  const int nt = 2 * F / kTileRows;
+  const size_t total = (size_t)E * nt * ks * 64;
+  if (q >= total) return;
+  const int lane = (int)(q % 64);
+  size_t r = q / 64;
+  const int s = (int)(r % ks);
+  r /= ks;
+  const int gt = (int)(r % nt);
+  const int e = (int)(r / nt);
+  const int rr = lane & 31;
+  const int f = gt * 16 + (rr & 15);
+  const int kk = s * kKStep + (lane >> 5) * 8;
+  const uint8_t* src = (rr < 16 ? wg : wu) + ((size_t)e * F + f) * d + kk;
+  const u32x2 c = *reinterpret_cast<const u32x2*>(src);
+  stg16(packed + q * 8, e4m3x8_to_bf16x8(c[0], c[1]));
+}
+
+__global__ void k_pack_down_fp8_bf16(const uint8_t* __restrict__ wd, uint16_t* __restrict__ packed,
+                                     int E, int d, int F) {
+  const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const int ks = F / kKStep;
+  const size_t total = (size_t)E * (d / kTileRows) * ks * 64;
+  if (q >= total) return;
+  const int lane = (int)(q % 64);
+  size_t r = q / 64;
+  const int s = (int)(r % ks);
+  r /= ks;
+  const int mt = (int)(r % (d / kTileRows));
+  const int e = (int)(r / (d / kTileRows));
+  const int row = mt * kTileRows + (lane & 31);
+  const int kk = s * kKStep + (lane >> 5) * 8;
+  const u32x2 c = *reinterpret_cast<const u32x2*>(wd + ((size_t)e * d + row) * F + kk);
+  stg16(packed + q * 8, e4m3x8_to_bf16x8(c[0], c[1]));
+}
+
+// codes -> fp8 decode banks (16 bytes per lane: k-steps 2p and 2p+1)
+__global__ void k_pack_gateup_fp8(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
+                                  uint8_t* __restrict__ packed, int E, int F, int d) {
+  const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const int kp = d / (2 * kKStep);
+  const int nt = 2 * F / kTileRows;
+  const size_t total = (size_t)E * nt * kp * 64;
+  if (q >= total) return;
+  const int lane = (int)(q % 64);
+  size_t r = q / 64;
+  const int p = (int)(r % kp);
+  r /= kp;
+  const int gt = (int)(r % nt);
+  const int e = (int)(r / nt);
+  const int rr = lane & 31;
+  const int f = gt * 16 + (rr & 15);
+  const uint8_t* row = (rr < 16 ? wg : wu) + ((size_t)e * F + f) * d;
+  const int k0 = 2 * p * kKStep + (lane >> 5) * 8;
+  u32x4 o;
+  const u32x2 a = *reinterpret_cast<const u32x2*>(row + k0);
+  const u32x2 b = *reinterpret_cast<const u32x2*>(row + k0 + kKStep);
+  o[0] = a[0]; o[1] = a[1]; o[2] = b[0]; o[3] = b[1];
+  stg16(packed + q * 16, o);
+}
+
+__global__ void k_pack_down_fp8(const uint8_t* __restrict__ wd, uint8_t* __restrict__ packed,
+                                int E, int d, int F) {
+  const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const int kp = F / (2 * kKStep);
+  const size_t total = (size_t)E * (d / kTileRows) * kp * 64;
+  if (q >= total) return;
+  const int lane = (int)(q % 64);
+  size_t r = q / 64;
+  const int p = (int)(r % kp);
+  r /= kp;
+  const int mt = (int)(r % (d / kTileRows));
+  const int e = (int)(r / (d / kTileRows));
+  const uint8_t* row = wd + ((size_t)e * d + mt * kTileRows + (lane & 31)) * F;
+  const int k0 = 2 * p * kKStep + (lane >> 5) * 8;
+  u32x4 o;
+  const u32x2 a = *reinterpret_cast<const u32x2*>(row + k0);
+  const u32x2 b = *reinterpret_cast<const u32x2*>(row + k0 + kKStep);
+  o[0] = a[0]; o[1] = a[1]; o[2] = b[0]; o[3] = b[1];
+  stg16(packed + q * 16, o);
+}
+
+// gate/up scales in the interleaved tile-row order: sgu[e][32 t + r] is the
+// scale of row r of tile t (r < 16: gate column 16t + r; else up column 16t + r - 16)
+__global__ void k_pack_gateup_scales(const float* __restrict__ sg, const float* __restrict__ su,
+                                     float* __restrict__ sgu, int E, int F) {
+  const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= (size_t)E * 2 * F) return;
+  const int e = (int)(q / (2 * F)), i = (int)(q % (2 * F));
+  const int t = i / 32, r = i % 32;
+  const int f = t * 16 + (r & 15);
+  sgu[q] = (r < 16 ? sg : su)[(size_t)e * F + f];
+}
+
+hipError_t launch_pack_fp8(const uint8_t* w_gate, const uint8_t* w_up, const uint8_t* w_down,
+                           const float* s_gate, const float* s_up, int E, int F, int d,
+                           uint16_t* wgu16, uint16_t* wd16, uint8_t* wgu8, uint8_t* wd8,
+                           float* sgu, hipStream_t s) {
+  auto grid = [](size_t n) { return dim3((unsigned)((n + 255) / 256)); };
+  const size_t n_gu16 = (size_t)E * (2 * F / kTileRows) * (d / kKStep) * 64;
+  const size_t n_d16 = (size_t)E * (d / kTileRows) * (F / kKStep) * 64;
+  hipLaunchKernelGGL(k_pack_gateup_fp8_bf16, grid(n_gu16), dim3(256), 0, s, w_gate, w_up, wgu16, E, F, d);
+  hipLaunchKernelGGL(k_pack_down_fp8_bf16, grid(n_d16), dim3(256), 0, s, w_down, wd16, E, d, F);
+  hipLaunchKernelGGL(k_pack_gateup_fp8, grid(n_gu16 / 2), dim3(256), 0, s, w_gate, w_up, wgu8, E, F, d);
+  hipLaunchKernelGGL(k_pack_down_fp8, grid(n_d16 / 2), dim3(256), 0, s, w_down, wd8, E, d, F);
+  hipLaunchKernelGGL(k_pack_gateup_scales, grid((size_t)E * 2 * F), dim3(256), 0, s, s_gate, s_up, sgu, E, F);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -64,6 +64,13 @@ struct FwdArgs {
   const void* wgu;     // packed gate/up bank (bf16) or canonical [E,F,d] (f32)
   const void* wup;     // f32 only: canonical up weights [E,F,d]
   const void* wd;      // packed down bank (bf16) or canonical [E,d,F] (f32)
+  // fp8 layers (else null): E4M3 decode banks, per-row scales of gate/up (in
+  // interleaved tile-row order, [E][2F]) and of down ([E][d]); the bf16 banks
+  // then hold the code values and the scales multiply the accumulators
+  const void* wgu8;
+  const void* wd8;
+  const float* sgu;
+  const float* sd;
   // per-call buffers (workspace or caller-provided routing outputs)
   void* xn;            // [T, d] gain-scaled activations g * h (bf16 or f32)
   float* inv;          // [T] 1 / rms of each token's hidden state
@@ -108,6 +115,10 @@ hipError_t launch_pack_gateup(const uint16_t* w_gate, const uint16_t* w_up, uint
                               int F, int d, hipStream_t s);
 hipError_t launch_pack_down(const uint16_t* w_down, uint16_t* packed, int E, int d, int F,
                             hipStream_t s);
+hipError_t launch_pack_fp8(const uint8_t* w_gate, const uint8_t* w_up, const uint8_t* w_down,
+                           const float* s_gate, const float* s_up, int E, int F, int d,
+                           uint16_t* wgu16, uint16_t* wd16, uint8_t* wgu8, uint8_t* wd8,
+                           float* sgu, hipStream_t s);
 hipError_t launch_prep_router(const void* w_router, const void* gain, int dtype, int E, int EP,
                               int d, float* wrg, float* gain32, hipStream_t s);
 

@@ -76,6 +76,11 @@ struct moe_layer {
   void* wgu;
   void* wup;
   void* wd;
+  // fp8 layers: decode banks and per-row scales (null otherwise)
+  void* wgu8;
+  void* wd8;
+  float* sgu;
+  float* sd;
   // workspace (one allocation)
   void* ws;
   void* xn;
@@ -159,14 +164,29 @@ int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
 
 const char* moe_last_error(void) { return g_err.c_str(); }
 
-moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* w,
-                              void* stream, moe_layer_t** out) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+// sc != nullptr: expert weights are E4M3 codes with per-row scales.
+moe_status_t create_impl(const moe_layer_config_t* cfg, const moe_layer_weights_t* w,
+                         const moe_fp8_scales_t* sc, void* stream, moe_layer_t** out) {
   if (out == nullptr) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   if (cfg == nullptr || w == nullptr) return fail(MOE_ERR_INVALID_ARG, "cfg or weights is NULL");
   moe_status_t st = check_config(cfg);
   if (st != MOE_OK) return st;
+  const bool fp8 = sc != nullptr;
+  if (fp8) {
+    if (cfg->dtype != MOE_DTYPE_BF16)
+      return fail(MOE_ERR_INVALID_ARG, "fp8 expert weights need dtype MOE_DTYPE_BF16 activations");
+    // the decode streams read k-step pairs: an even count per wave of each split
+    if (cfg->d_ff % 256 != 0)
+      return fail(MOE_ERR_UNSUPPORTED, "fp8 expert weights need d_ff % 256 == 0");
+    const void* sp[] = {sc->gate, sc->up, sc->down};
+    for (const void* p : sp)
+      if (p == nullptr || !aligned(p, 4))
+        return fail(MOE_ERR_INVALID_ARG, "an fp8 scale pointer is NULL or misaligned");
+  }
   const void* wp[] = {w->rms_gain, w->w_router, w->w_gate, w->w_up, w->w_down};
   for (const void* p : wp) {
     if (p == nullptr) return fail(MOE_ERR_INVALID_ARG, "a weight pointer is NULL");
@@ -215,6 +235,10 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_wei
   const size_t o_wgu = pc.take(E * F * d * es * (cfg->dtype == MOE_DTYPE_BF16 ? 2 : 1));
   const size_t o_wup = cfg->dtype == MOE_DTYPE_F32 ? pc.take(E * F * d * es) : 0;
   const size_t o_wd = pc.take(E * d * F * es);
+  const size_t o_wgu8 = fp8 ? pc.take(E * 2 * F * d) : 0;
+  const size_t o_wd8 = fp8 ? pc.take(E * d * F) : 0;
+  const size_t o_sgu = fp8 ? pc.take(E * 2 * F * 4) : 0;
+  const size_t o_sd = fp8 ? pc.take(E * d * 4) : 0;
   he = hipMalloc(&L->params, pc.off);
   if (he != hipSuccess) {
     L->params = nullptr;
@@ -230,6 +254,10 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_wei
   L->wgu = at<void>(L->params, o_wgu);
   L->wup = cfg->dtype == MOE_DTYPE_F32 ? at<void>(L->params, o_wup) : nullptr;
   L->wd = at<void>(L->params, o_wd);
+  L->wgu8 = fp8 ? at<void>(L->params, o_wgu8) : nullptr;
+  L->wd8 = fp8 ? at<void>(L->params, o_wd8) : nullptr;
+  L->sgu = fp8 ? at<float>(L->params, o_sgu) : nullptr;
+  L->sd = fp8 ? at<float>(L->params, o_sd) : nullptr;
 
   // workspace
   Carver wc;
@@ -284,7 +312,16 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_wei
   if (he == hipSuccess && bf16)
     he = hipMemcpyAsync(L->gain16, w->rms_gain, d * 2, hipMemcpyDeviceToDevice, s);
   if (he == hipSuccess) {
-    if (cfg->dtype == MOE_DTYPE_BF16) {
+    if (fp8) {
+      he = moe::launch_pack_fp8(static_cast<const uint8_t*>(w->w_gate),
+                                static_cast<const uint8_t*>(w->w_up),
+                                static_cast<const uint8_t*>(w->w_down), sc->gate, sc->up, (int)E,
+                                (int)F, (int)d, static_cast<uint16_t*>(L->wgu),
+                                static_cast<uint16_t*>(L->wd), static_cast<uint8_t*>(L->wgu8),
+                                static_cast<uint8_t*>(L->wd8), L->sgu, s);
+      if (he == hipSuccess)
+        he = hipMemcpyAsync(L->sd, sc->down, E * d * 4, hipMemcpyDeviceToDevice, s);
+    } else if (cfg->dtype == MOE_DTYPE_BF16) {
       he = moe::launch_pack_gateup(static_cast<const uint16_t*>(w->w_gate),
                                    static_cast<const uint16_t*>(w->w_up),
                                    static_cast<uint16_t*>(L->wgu), (int)E, (int)F, (int)d, s);
@@ -308,6 +345,26 @@ moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_wei
   L->magic = kMagic;
   *out = L;
   return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* w,
+                              void* stream, moe_layer_t** out) {
+  g_err.clear();
+  return create_impl(cfg, w, nullptr, stream, out);
+}
+
+moe_status_t moe_layer_create_fp8(const moe_layer_config_t* cfg, const moe_layer_weights_t* w,
+                                  const moe_fp8_scales_t* scales, void* stream,
+                                  moe_layer_t** out) {
+  g_err.clear();
+  if (scales == nullptr) {
+    if (out != nullptr) *out = nullptr;
+    return fail(MOE_ERR_INVALID_ARG, "scales is NULL");
+  }
+  return create_impl(cfg, w, scales, stream, out);
 }
 
 }  // extern "C"
@@ -357,6 +414,10 @@ moe_status_t forward_impl(moe_layer_t* L, const void* hidden, int32_t T, void* o
   a.wgu = L->wgu;
   a.wup = L->wup;
   a.wd = L->wd;
+  a.wgu8 = L->wgu8;
+  a.wd8 = L->wd8;
+  a.sgu = L->sgu;
+  a.sd = L->sd;
   a.xn = L->xn;
   a.inv = L->inv;
   a.sel = (routing && routing->sel) ? routing->sel : L->sel;

@@ -22,7 +22,8 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_OOM", 3: "MOE
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 
 # Symbols declared in include/moe_layer.h.
-EXPORTS = ("moe_abi_version", "moe_last_error", "moe_layer_create", "moe_layer_forward",
+EXPORTS = ("moe_abi_version", "moe_last_error", "moe_layer_create", "moe_layer_create_fp8",
+           "moe_layer_forward",
            "moe_layer_set_bias", "moe_layer_get_bias", "moe_layer_update_bias",
            "moe_layer_timing_start",
            "moe_layer_timing_stop", "moe_layer_destroy", "moe_stack_create", "moe_stack_forward",
@@ -42,6 +43,10 @@ class LayerWeights(ctypes.Structure):
     _fields_ = [("rms_gain", ctypes.c_void_p), ("w_router", ctypes.c_void_p),
                 ("b_router", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
                 ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p)]
+
+
+class Fp8Scales(ctypes.Structure):
+    _fields_ = [("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p)]
 
 
 class RoutingOut(ctypes.Structure):
@@ -75,6 +80,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.moe_layer_create.restype = ctypes.c_int
     lib.moe_layer_create.argtypes = [ctypes.POINTER(LayerConfig), ctypes.POINTER(LayerWeights),
                                      ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
+    lib.moe_layer_create_fp8.restype = ctypes.c_int
+    lib.moe_layer_create_fp8.argtypes = [ctypes.POINTER(LayerConfig), ctypes.POINTER(LayerWeights),
+                                         ctypes.POINTER(Fp8Scales), ctypes.c_void_p,
+                                         ctypes.POINTER(ctypes.c_void_p)]
     lib.moe_layer_forward.restype = ctypes.c_int
     lib.moe_layer_forward.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                       ctypes.c_void_p, ctypes.c_void_p,
@@ -129,10 +138,15 @@ class MoELayer:
     weights: dict of CUDA tensors in canonical row-major layout
       rms_gain [d], w_router [E, d], b_router [E] (fp32), w_gate [E, F, d],
       w_up [E, F, d], w_down [E, d, F]; all but b_router in the layer dtype.
+    fp8_scales: None, or a dict of contiguous CUDA float32 per-row scales
+      gate [E, F], up [E, F], down [E, d]; then w_gate, w_up and w_down hold
+      E4M3 codes (torch.uint8 or torch.float8_e4m3fn) and dtype must be "bf16"
+      (moe_layer_create_fp8).
     """
 
     def __init__(self, d_model: int, d_ff: int, n_experts: int, top_k: int, dtype: str,
-                 weights: dict, max_tokens: int, rms_eps: float = 1e-6, stream=None):
+                 weights: dict, max_tokens: int, rms_eps: float = 1e-6, stream=None,
+                 fp8_scales: dict | None = None):
         self._lib = load_library()
         self.handle = None
         self.dtype_code = MOE_DTYPE_BF16 if dtype == "bf16" else MOE_DTYPE_F32
@@ -142,19 +156,40 @@ class MoELayer:
         shapes = {"rms_gain": (d_model,), "w_router": (n_experts, d_model),
                   "b_router": (n_experts,), "w_gate": (n_experts, d_ff, d_model),
                   "w_up": (n_experts, d_ff, d_model), "w_down": (n_experts, d_model, d_ff)}
+        self.fp8 = fp8_scales is not None
         ptrs = {}
         for name, shp in shapes.items():
             t = weights[name]
             want = torch.float32 if name == "b_router" else self.torch_dtype
+            if self.fp8 and name in ("w_gate", "w_up", "w_down"):
+                if t.dtype == torch.float8_e4m3fn:
+                    t = t.view(torch.uint8)
+                want = torch.uint8
             if not (t.is_cuda and t.dtype == want and tuple(t.shape) == shp and t.is_contiguous()):
                 raise ValueError(f"{name}: need a contiguous CUDA {want} tensor of shape {shp}")
             ptrs[name] = t.data_ptr()
         cfg = LayerConfig(d_model, d_ff, n_experts, top_k, self.dtype_code, rms_eps, max_tokens)
         w = LayerWeights(**ptrs)
         h = ctypes.c_void_p()
-        _check(self._lib, self._lib.moe_layer_create(ctypes.byref(cfg), ctypes.byref(w),
-                                                     ctypes.c_void_p(_stream_ptr(stream)),
-                                                     ctypes.byref(h)))
+        stream_p = ctypes.c_void_p(_stream_ptr(stream))
+        if self.fp8:
+            sshapes = {"gate": (n_experts, d_ff), "up": (n_experts, d_ff),
+                       "down": (n_experts, d_model)}
+            sptrs = {}
+            for name, shp in sshapes.items():
+                t = fp8_scales[name]
+                if not (t.is_cuda and t.dtype == torch.float32 and tuple(t.shape) == shp
+                        and t.is_contiguous()):
+                    raise ValueError(f"fp8 scale {name}: need a contiguous CUDA float32 tensor "
+                                     f"of shape {shp}")
+                sptrs[name] = t.data_ptr()
+            sc = Fp8Scales(**sptrs)
+            _check(self._lib, self._lib.moe_layer_create_fp8(ctypes.byref(cfg), ctypes.byref(w),
+                                                             ctypes.byref(sc), stream_p,
+                                                             ctypes.byref(h)))
+        else:
+            _check(self._lib, self._lib.moe_layer_create(ctypes.byref(cfg), ctypes.byref(w),
+                                                         stream_p, ctypes.byref(h)))
         self.handle = h
 
     def forward(self, hidden: torch.Tensor, out: torch.Tensor | None = None,

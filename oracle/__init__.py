@@ -9,5 +9,6 @@ constant or table with it; the two meet only through the seeded inputs of the
 
 from .moe_oracle import (  # noqa: F401
     rmsnorm, router_scores, select_topk, gates, histogram, permutation,
-    silu, swiglu_expert, combine, oracle_forward, bias_update, stack_forward, MARGIN_TOL,
+    silu, swiglu_expert, combine, oracle_forward, bias_update, stack_forward, e4m3_value, fp8_weights,
+    MARGIN_TOL,
 )

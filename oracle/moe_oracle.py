@@ -271,3 +271,23 @@ def stack_forward(layer_vals: list, H, ks: list, eps: float, forced_sels=None) -
         h = h + r["out"]
         sels.append(r["sel"])
     return {"out": h, "sel": sels}
+
+
+# fp8 expert weights ------------------------------------------------------------
+def e4m3_value(codes) -> np.ndarray:
+    """Values of OCP FP8 E4M3 byte codes (sign, 4 exponent bits with bias 7,
+    3 mantissa bits; exponent 0 is subnormal, m * 2^-9; S.1111.111 is NaN; no
+    infinities), as float64."""
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    s = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return s * mag
+
+
+def fp8_weights(codes, scale) -> np.ndarray:
+    """Expert weights stored as E4M3 codes with one float32 scale per output
+    row: W[e, r, :] = value(codes[e, r, :]) * scale[e, r] (exact in float64)."""
+    return e4m3_value(codes) * np.asarray(scale, np.float64)[..., None]

@@ -156,3 +156,28 @@ def values_f32(inputs: dict) -> dict:
         else:
             out[name] = np.asarray(v, np.float32)
     return out
+
+
+def fp8_expert_weights(inputs: dict) -> dict:
+    """E4M3 (OCP) codes and per-output-row float32 scales for the expert
+    weights of a bf16 layer's inputs: scale = max|w_row| / 448 (448 being the
+    largest E4M3 value), code = the E4M3 nearest to w / scale (torch's
+    float8_e4m3fn cast, round to nearest even).  This prepares inputs only:
+    the layer consumes the codes and scales as given.
+    Returns w_gate, w_up, w_down (uint8) and s_gate [E,F], s_up [E,F],
+    s_down [E,d] (float32)."""
+    import torch
+    cfg = inputs["cfg"]
+    ck = ("fp8", cfg.family, cfg.d, cfg.E, cfg.F, id(inputs["w_gate"]))
+    if ck in _weight_cache:
+        return _weight_cache[ck]
+    out = {}
+    for name, sname in (("w_gate", "s_gate"), ("w_up", "s_up"), ("w_down", "s_down")):
+        w = torch.from_numpy(bf16_bits_to_f32(inputs[name]))
+        amax = w.abs().amax(dim=-1)
+        scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).to(torch.float32)
+        q = (w / scale[..., None]).to(torch.float8_e4m3fn)
+        out[name] = q.view(torch.uint8).numpy().copy()
+        out[sname] = scale.numpy().copy()
+    _weight_cache[ck] = out
+    return out

@@ -56,13 +56,16 @@ def out_to_f64(t: torch.Tensor) -> np.ndarray:
 
 
 def check_parity(inputs: dict, layer, sample: int | None = None, seed: int = 0,
-                 label: str = "") -> dict:
+                 label: str = "", vals: dict | None = None) -> dict:
     """Run the layer on ``inputs`` and assert the parity protocol.
 
     sample: number of tokens whose output rows are compared (all when None);
-    routing and dispatch are always compared in full."""
+    routing and dispatch are always compared in full.
+    vals: the exact values the oracle runs on (default: those of ``inputs``;
+    fp8 layers pass their dequantised expert weights)."""
     cfg = inputs["cfg"]
-    vals = gen.values_f32(inputs)
+    if vals is None:
+        vals = gen.values_f32(inputs)
     hidden = to_torch(inputs["hidden"], cfg.dtype)
     out, r = layer.forward(hidden, routing=True)
     torch.cuda.synchronize()

@@ -22,12 +22,13 @@ def _lib():
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["moe_abi_version", "moe_last_error", "moe_layer_create",
+                            "moe_layer_create_fp8",
                             "moe_layer_forward", "moe_layer_set_bias", "moe_layer_get_bias",
                             "moe_layer_update_bias",
                             "moe_layer_timing_start", "moe_layer_timing_stop",
@@ -48,6 +49,7 @@ def test_abi_structs_match_header_sizes():
     assert ctypes.sizeof(layer.LayerConfig) == 7 * 4
     assert ctypes.sizeof(layer.LayerWeights) == 6 * 8
     assert ctypes.sizeof(layer.RoutingOut) == 6 * 8
+    assert ctypes.sizeof(layer.Fp8Scales) == 3 * 8
 
 
 def _cfg(layer, **kw):
@@ -88,6 +90,27 @@ def test_create_rejects_null_and_misaligned_weights_on_host():
     assert lib.moe_layer_create(ctypes.byref(cfg), ctypes.byref(w), None,
                                 ctypes.byref(h)) == layer.MOE_ERR_INVALID_ARG
     assert b"aligned" in lib.moe_last_error()
+
+
+def test_create_fp8_rejects_bad_scales_and_dtype_on_host():
+    lib, layer = _lib()
+    cfg = _cfg(layer)
+    w = layer.LayerWeights(16, 16, 16, 16, 16, 16)
+    h = ctypes.c_void_p(123)
+    assert lib.moe_layer_create_fp8(ctypes.byref(cfg), ctypes.byref(w), None, None,
+                                    ctypes.byref(h)) == layer.MOE_ERR_INVALID_ARG
+    assert h.value is None and b"scales" in lib.moe_last_error()
+    sc = layer.Fp8Scales(16, 0, 16)
+    assert lib.moe_layer_create_fp8(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(sc), None,
+                                    ctypes.byref(h)) == layer.MOE_ERR_INVALID_ARG
+    sc = layer.Fp8Scales(16, 18, 16)
+    assert lib.moe_layer_create_fp8(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(sc), None,
+                                    ctypes.byref(h)) == layer.MOE_ERR_INVALID_ARG
+    sc = layer.Fp8Scales(16, 16, 16)
+    cfg32 = _cfg(layer, dtype=0)
+    assert lib.moe_layer_create_fp8(ctypes.byref(cfg32), ctypes.byref(w), ctypes.byref(sc), None,
+                                    ctypes.byref(h)) == layer.MOE_ERR_INVALID_ARG
+    assert b"BF16" in lib.moe_last_error()
 
 
 def test_entry_points_reject_bad_handles_and_destroy_is_null_safe():

@@ -371,3 +371,22 @@ def test_stack_of_zero_output_layers_is_identity():
         layers.append(L)
     H = rng.standard_normal((5, 6))
     np.testing.assert_array_equal(O.stack_forward(layers, H, [1, 1], 1e-6)["out"], H)
+
+
+# ------------------------------------------------------------- fp8 weights
+def test_e4m3_decoder_matches_torch_on_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_value(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2   # 0x7f and 0xff
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    # a few by hand: max normal, min normal, min subnormal, -1.5
+    assert O.e4m3_value([0x7e])[0] == 448.0 and O.e4m3_value([0x08])[0] == 2.0 ** -6
+    assert O.e4m3_value([0x01])[0] == 2.0 ** -9 and O.e4m3_value([0xbc])[0] == -1.5
+
+
+def test_fp8_weights_scale_rows_exactly():
+    codes = np.array([[[0x38, 0x40], [0xb8, 0x00]]], np.uint8)   # 1, 2 / -1, 0
+    scale = np.array([[0.5, 3.0]], np.float32)
+    np.testing.assert_array_equal(O.fp8_weights(codes, scale), [[[0.5, 1.0], [-3.0, 0.0]]])
