@@ -52,7 +52,11 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(const u32x4& a, const u32x4& b, 
 }
 __device__ __forceinline__ int c32_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
-__device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+// SiLU(v) = v * sigmoid(v), the reciprocal from v_rcp_f32 (1 ulp) instead of an
+// IEEE division (a ten-instruction sequence); the result is rounded to bf16.
+__device__ __forceinline__ float silu(float v) {
+  return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
+}
 
 // Butterfly reduction of N per-lane values over the 64 lanes of a wave that
 // leaves the sums spread over the lanes instead of replicated: each halving

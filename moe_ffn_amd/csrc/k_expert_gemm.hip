@@ -119,7 +119,7 @@ __device__ __forceinline__ void bstage(const Ctx<RT, TT>& c, u32x4* lds, int& bu
   const u32x4* cur = lds + buf * kBStageEnt;
 #pragma unroll
   for (int i = 0; i < kBK; ++i) {
-    const int slot = P * kBK + i;  // weight queue slot of this k-step
+    const int slot = (P * kBK + i) % Q;  // weight queue slot of this k-step
     u32x4 bn[TT];
     if (i < kBK - 1) read_b<TT>(cur, i + 1, c.lane, bn);
     else read_b<TT>(lds + b1 * kBStageEnt, 0, c.lane, bn);
@@ -151,12 +151,12 @@ __device__ __forceinline__ void bstage(const Ctx<RT, TT>& c, u32x4* lds, int& bu
   buf = b1;
 }
 
-// Q: depth of the weight queue in k-steps (a multiple of 2 * kBK that divides
-// the k-steps of the reduction).
+// Q: depth of the weight queue in k-steps (kBK, or a multiple of 2 * kBK that
+// divides the k-steps of the reduction).
 template <int RT, int TT, int Q>
 __device__ __forceinline__ void mainloop(const Ctx<RT, TT>& c, u32x4* lds, f32x16 (&acc)[RT][TT]) {
-  constexpr int NP = Q / kBK;      // token stages per loop iteration
-  const int nsb = c.ksteps / kBK;  // token stages (a multiple of NP)
+  constexpr int NP = Q / kBK < 2 ? 2 : Q / kBK;  // token stages per loop iteration
+  const int nsb = c.ksteps / kBK;                // token stages (a multiple of NP)
   u32x4 qa[Q][RT], rb0[TT], rb1[TT], bc[TT];
   load_b(c, 0, nsb, rb0);
   load_b(c, 1, nsb, rb1);
@@ -190,22 +190,25 @@ struct Unit {
   int e, rb, slot0, nrows, nsub;
   int sub0;  // first subtile of the unit in the padded, expert-ordered subtile list
 };
+template <int TTM>
 __device__ __forceinline__ int span_count(int cnt) {
   const int nsub = (cnt + kSub - 1) / kSub;
-  return (nsub + kTTMax - 1) / kTTMax;
+  return (nsub + TTM - 1) / TTM;
 }
+template <int TTM>
 __device__ __forceinline__ int unit_total(const int* __restrict__ counts, int E, int nrb) {
   int U = 0;
-  for (int e = 0; e < E; ++e) U += nrb * span_count(counts[e]);
+  for (int e = 0; e < E; ++e) U += nrb * span_count<TTM>(counts[e]);
   return U;
 }
+template <int TTM>
 __device__ __forceinline__ void decode_unit(const int* __restrict__ counts,
                                             const int* __restrict__ offsets, int E, int nrb, int L,
                                             Unit& u) {
   int base = 0, psub = 0;
   for (int e = 0; e < E; ++e) {
     const int cnt = counts[e];
-    const int ns = span_count(cnt);
+    const int ns = span_count<TTM>(cnt);
     if (L < base + nrb * ns) {
       const int r = L - base;
       const int sp = r % ns;
@@ -334,8 +337,37 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
 }
 }  // namespace
 
-template <int MODE, int RT, int Q>
-__global__ __launch_bounds__(256, 1) void k_expert_gemm(
+namespace {
+// run_unit for the unit's subtile count (at most TTM)
+template <int MODE, int RT, int Q, int TTM>
+__device__ __forceinline__ void run_any(const Unit& u, u32x4* lds, const uint16_t* __restrict__ wpk,
+                                        const uint16_t* __restrict__ src,
+                                        const int* __restrict__ gather,
+                                        const float* __restrict__ gate,
+                                        const float* __restrict__ inv,
+                                        const float* __restrict__ rsc, int k,
+                                        const uint16_t* __restrict__ zrow,
+                                        uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
+                                        int d, int F) {
+#define MOE_RUN(TT) run_unit<MODE, RT, Q, TT>(u, lds, wpk, src, gather, gate, inv, rsc, k, zrow, dst16, ybuf, d, F)
+  if constexpr (TTM >= 5) {
+    if (u.nsub == 5) { MOE_RUN(5); return; }
+  }
+  if constexpr (TTM >= 4) {
+    if (u.nsub == 4) { MOE_RUN(4); return; }
+  }
+  if constexpr (TTM >= 3) {
+    if (u.nsub == 3) { MOE_RUN(3); return; }
+  }
+  if (u.nsub == 2) MOE_RUN(2);
+  else MOE_RUN(1);
+#undef MOE_RUN
+}
+}  // namespace
+
+// OCC workgroups per CU; spans of at most TTM subtiles.
+template <int MODE, int RT, int Q, int OCC, int TTM>
+__global__ __launch_bounds__(256, OCC) void k_expert_gemm(
     const uint16_t* __restrict__ wpk, const uint16_t* __restrict__ src,
     const int* __restrict__ counts, const int* __restrict__ offsets,
     const int* __restrict__ gather, const float* __restrict__ gate,
@@ -344,7 +376,7 @@ __global__ __launch_bounds__(256, 1) void k_expert_gemm(
     int d, int F) {
   __shared__ u32x4 lds[kBStages * kBStageEnt];
   const int nrb = (MODE == 0 ? 2 * F : d) / Geo<RT>::kRows;
-  const int U = unit_total(counts, E, nrb);
+  const int U = unit_total<TTM>(counts, E, nrb);
   const int per = (U + 7) >> 3;          // units per XCD range
   const int nw = gridDim.x >> 3;         // workgroups per XCD (the grid is a multiple of 8)
   const int x = blockIdx.x & 7, w = blockIdx.x >> 3;
@@ -353,23 +385,17 @@ __global__ __launch_bounds__(256, 1) void k_expert_gemm(
     const int L = lo + ((r & 1) ? (r + 1) * nw - 1 - w : r * nw + w);
     if (L >= hi) continue;
     Unit u;
-    decode_unit(counts, offsets, E, nrb, L, u);
+    decode_unit<TTM>(counts, offsets, E, nrb, L, u);
     __syncthreads();  // the previous unit's last LDS reads are done everywhere
-    switch (u.nsub) {
-      case 5: run_unit<MODE, RT, Q, 5>(u, lds, wpk, src, gather, gate, inv, rsc, k, zrow, dst16, ybuf, d, F); break;
-      case 4: run_unit<MODE, RT, Q, 4>(u, lds, wpk, src, gather, gate, inv, rsc, k, zrow, dst16, ybuf, d, F); break;
-      case 3: run_unit<MODE, RT, Q, 3>(u, lds, wpk, src, gather, gate, inv, rsc, k, zrow, dst16, ybuf, d, F); break;
-      case 2: run_unit<MODE, RT, Q, 2>(u, lds, wpk, src, gather, gate, inv, rsc, k, zrow, dst16, ybuf, d, F); break;
-      default: run_unit<MODE, RT, Q, 1>(u, lds, wpk, src, gather, gate, inv, rsc, k, zrow, dst16, ybuf, d, F); break;
-    }
+    run_any<MODE, RT, Q, TTM>(u, lds, wpk, src, gather, gate, inv, rsc, k, zrow, dst16, ybuf, d, F);
   }
 }
 
 namespace {
-template <int MODE, int RT, int Q>
+template <int MODE, int RT, int Q, int OCC, int TTM>
 hipError_t launch_gemm(const FwdArgs& a) {
-  const int grid = (a.num_cu + 7) / 8 * 8;  // persistent: one workgroup per CU
-  return launch(k_expert_gemm<MODE, RT, Q>, dim3(grid), dim3(256), a.stream,
+  const int grid = (a.num_cu * OCC + 7) / 8 * 8;  // persistent: OCC workgroups per CU
+  return launch(k_expert_gemm<MODE, RT, Q, OCC, TTM>, dim3(grid), dim3(256), a.stream,
                 a.ev[MODE == 0 ? kSlotExpertsA : kSlotExpertsB],
                 (const uint16_t*)(MODE == 0 ? a.wgu : a.wd),
                 (const uint16_t*)(MODE == 0 ? a.xt : a.act), (const int*)a.counts,
@@ -386,13 +412,26 @@ hipError_t launch_gemm(const FwdArgs& a) {
 // divides into it (else 8).  On the prefill workloads the 384-row gate/up
 // units are faster (fewer re-reads of the token tiles per weight byte); the
 // deeper queue that fits the 256-row units' registers did not make up for it.
+#ifndef MOE_GU_CFG
+#define MOE_GU_CFG 3, 8, 1, 5   // RT, Q, OCC, TTM of the gate/up GEMM (2 * d_ff % 384 == 0)
+#endif
+#ifndef MOE_DN_CFG
+#define MOE_DN_CFG 2, 16, 1, 5  // of the down GEMM (d_ff / 16 % 16 == 0)
+#endif
+namespace {
+template <int RT, int Q, int OCC, int TTM>
+struct Cfg {
+  static constexpr int kRT = RT;
+};
+}  // namespace
+
 hipError_t launch_experts_tile(const FwdArgs& a) {
   const int ksd = a.dim.d / kKStep, ksf = a.dim.F / kKStep;
   hipError_t err;
-  if ((2 * a.dim.F) % Geo<3>::kRows == 0) err = launch_gemm<0, 3, 8>(a);
-  else err = ksd % 16 == 0 ? launch_gemm<0, 2, 16>(a) : launch_gemm<0, 2, 8>(a);
+  if ((2 * a.dim.F) % Geo<Cfg<MOE_GU_CFG>::kRT>::kRows == 0) err = launch_gemm<0, MOE_GU_CFG>(a);
+  else err = ksd % 16 == 0 ? launch_gemm<0, 2, 16, 1, 5>(a) : launch_gemm<0, 2, 8, 1, 5>(a);
   if (err != hipSuccess) return err;
-  return ksf % 16 == 0 ? launch_gemm<1, 2, 16>(a) : launch_gemm<1, 2, 8>(a);
+  return ksf % 16 == 0 ? launch_gemm<1, MOE_DN_CFG>(a) : launch_gemm<1, 2, 8, 1, 5>(a);
 }
 
 }  // namespace moe
