@@ -125,8 +125,8 @@ def ingest_counters(pmc_dir: str) -> None:
         fm, wm = _counter_means(fd), _counter_means(wd)
         kernels = {}
         for kname in fm:
-            if kname.startswith("k_") and kname in wm and not kname.startswith("k_pack") \
-                    and not kname.startswith("k_prep"):
+            if kname.startswith("k_") and kname in wm and \
+                    not kname.startswith(("k_pack", "k_prep", "k_mfma_rate")):
                 kernels[kname] = {"fetch_bytes": round(fm[kname] * 1024 * ffac),
                                   "write_bytes": round(wm[kname] * 1024 * wfac)}
         dom = dominant_kernel_name(cfg)
@@ -198,12 +198,82 @@ def cpu_baseline(inputs, seconds: float, fp8: dict | None = None):
             el = time.perf_counter() - t0
             if el >= seconds or reps >= 10000:
                 break
+    with threadpool_limits(limits=1):
+        reps1, t1 = 0, time.perf_counter()
+        while True:
+            O.oracle_forward(vals, tokens=sample)
+            reps1 += 1
+            el1 = time.perf_counter() - t1
+            if el1 >= seconds / 3 or reps1 >= 10000:
+                break
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         model)
+    except OSError:
+        pass
     what = (f"full batch of {cfg.T} tokens" if sample is None else
             f"{ntok} sampled tokens of {cfg.T} (routing of all {cfg.T} tokens included)")
     return {"value": round(reps * ntok / el, 2), "unit": "tokens/s", "cores": int(threads),
+            "cpu_model": model, "single_thread_value": round(reps1 * ntok / el1, 2),
             "kind": "oracle",
             "sample": f"{reps} oracle forwards (fp64 NumPy) of the {cfg.name} workload: {what}; "
-                      f"{el:.1f} s", "host_cpus": ncores}
+                      f"{el:.1f} s; single-thread: {reps1} forwards in {el1:.1f} s",
+            "host_cpus": ncores}
+
+
+def hw_context(dev, cus: int) -> dict:
+    """Measured ceilings of this part, as context for the roofline fractions:
+    a 1 GiB device copy (HBM read + write), the MFMA rate probe of
+    libmoe_probe.so (register operands only) and a vendor bf16 GEMM
+    (torch.matmul) of the prefill gate/up shape."""
+    import ctypes
+    import torch
+    from moe_ffn_amd.build import PROBE_LIB
+
+    def best_ms(fn, reps=5):
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return min(ts)
+
+    out = {}
+    n = 1 << 30
+    src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ms = best_ms(lambda: dst.copy_(src))
+    out["hbm_copy_GBps"] = round(2 * n / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+    if os.path.exists(PROBE_LIB):
+        lib = ctypes.CDLL(PROBE_LIB)
+        lib.moe_probe_mfma.restype = ctypes.c_int32
+        lib.moe_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+        lib.moe_probe_mfma_flops.restype = ctypes.c_double
+        lib.moe_probe_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+        blocks, iters = 2 * cus, 20000
+        sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+        def probe():
+            if lib.moe_probe_mfma(blocks, iters, ctypes.c_void_p(sink.data_ptr()), stream) != 0:
+                raise RuntimeError("MFMA probe launch failed")
+        probe()
+        ms = best_ms(probe, 3)
+        out["mfma_probe_TFLOPs"] = round(lib.moe_probe_mfma_flops(blocks, iters) / (ms * 1e-3) / 1e12, 1)
+    a = torch.randn(4096, 2048, device=dev).to(torch.bfloat16)
+    b = torch.randn(2048, 6144, device=dev).to(torch.bfloat16)
+    c = torch.matmul(a, b)
+    ms = best_ms(lambda: torch.matmul(a, b, out=c))
+    out["vendor_gemm_bf16_4096x6144x2048_TFLOPs"] = round(2 * 4096 * 6144 * 2048 / (ms * 1e-3) / 1e12, 1)
+    return out
 
 
 def per_forward(layers, hidden, outs, n: int) -> dict:
@@ -362,6 +432,8 @@ def main():
     ap.add_argument("--instances", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the copy / MFMA-probe / vendor-GEMM context measurements")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy (dst = -src, MIB MiB read and MIB MiB\n"
                          "written) five times, to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -536,6 +608,10 @@ def main():
     }
     for L in layers:
         L.close()
+    if not args.no_context:
+        torch.cuda.synchronize()
+        line["context"] = hw_context(dev, props.multi_processor_count)
+        log(f"[bench] context: {line['context']}")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, q8)
