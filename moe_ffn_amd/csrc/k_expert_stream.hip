@@ -13,7 +13,10 @@
 // Each workgroup owns one 32-row weight tile of one expert (gate/up: one
 // interleaved tile, i.e. 16 columns of d_ff; down: 32 rows of d_model); its
 // eight waves split the reduction axis into eighths and combine partial sums
-// through LDS in a fixed order (deterministic).  Each wave keeps a rolling
+// through LDS in a fixed order (deterministic); the reduction and the
+// epilogue are spread over the eight waves (each sums and stores its own
+// share of the tile's elements), which took the decode gate/up launch from
+// 43.8 to 42.4 us.  Each wave keeps a rolling
 // queue of D k-steps of loads in flight, so the weight stream never drains
 // between multiplies.  One tile and eight waves per workgroup put the most
 // independent 1 KiB streams in flight at once: measured on the decode
@@ -60,6 +63,9 @@ constexpr int kSplitD8 = MOE_DOWN_SPLIT_FP8;
 #ifndef MOE_STREAM_NT
 #define MOE_STREAM_NT 1
 #endif
+#ifndef MOE_STREAM_WAVES_EU
+#define MOE_STREAM_WAVES_EU 1  // waves per SIMD the register budget must allow
+#endif
 
 __device__ __forceinline__ u32x4 ldw8(const uint8_t* p) {
 #if MOE_STREAM_NT
@@ -76,25 +82,23 @@ __device__ __forceinline__ u32x4 ldw(const uint16_t* p) {
 #endif
 }
 
-// Partial sums of waves 1..S-1 -> wave 0, fixed order.
+// Split-K reduction spread over the waves: every wave parks its NACC
+// accumulator tiles in LDS; after a barrier, element i of tile q summed over
+// the S waves in wave order (so the sum does not depend on which wave reads it)
+// is read back by the wave that owns that element's epilogue.
+template <int NACC>
+__device__ __forceinline__ void stash(const f32x16 (&acc)[NACC], float* red, int wave, int lane) {
+#pragma unroll
+  for (int q = 0; q < NACC; ++q)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[((wave * NACC + q) * 16 + i) * 64 + lane] = acc[q][i];
+}
 template <int NACC, int S>
-__device__ __forceinline__ void reduce_split(f32x16 (&acc)[NACC], float* red, int wave, int lane) {
-  if (wave > 0) {
+__device__ __forceinline__ float split_sum(const float* red, int q, int i, int lane) {
+  float v = red[(q * 16 + i) * 64 + lane];
 #pragma unroll
-    for (int q = 0; q < NACC; ++q)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) red[(((wave - 1) * NACC + q) * 16 + i) * 64 + lane] = acc[q][i];
-  }
-  __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int w = 1; w < S; ++w)
-#pragma unroll
-      for (int q = 0; q < NACC; ++q)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[q][i] += red[(((w - 1) * NACC + q) * 16 + i) * 64 + lane];
-  }
-  __syncthreads();
+  for (int w = 1; w < S; ++w) v += red[((w * NACC + q) * 16 + i) * 64 + lane];
+  return v;
 }
 
 // Dispatch of a decode-sized batch (n = T*k <= 64 assignments) for expert e,
@@ -211,30 +215,20 @@ __device__ __forceinline__ void stream_mac_fp8(const uint8_t* const (&w)[NW], co
     }
 }
 
-// acc element i of a 32-row tile holds row c32_row(i, lane): multiply each by
-// its row's scale (rows 8g + 4*(lane/32) + 0..3 are contiguous, g = 0..3).
-__device__ __forceinline__ void scale_rows(f32x16& acc, const float* __restrict__ rs, int lane) {
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(rs + 8 * g + 4 * (lane >> 5));
-#pragma unroll
-    for (int t = 0; t < 4; ++t) acc[4 * g + t] *= v[t];
-  }
-}
 }  // namespace
 
 // Gate/up projections and the SiLU(gate) * up epilogue for 16*NT columns of d_ff
 // (NT interleaved tiles, S waves splitting the reduction axis).
 // The workgroups with ft == 0 also write the routing outputs of their expert.
 template <int D, bool FP8, int NT, int S>
-__global__ __launch_bounds__(64 * S) void k_gateup_stream(
+__global__ __launch_bounds__(64 * S, MOE_STREAM_WAVES_EU) void k_gateup_stream(
     const uint16_t* __restrict__ wgu, const uint8_t* __restrict__ wgu8,
     const float* __restrict__ sgu, const uint16_t* __restrict__ xn,
     const int* __restrict__ sel, int n, int k, int E, int* __restrict__ counts,
     int* __restrict__ offsets, int* __restrict__ gather, int* __restrict__ scatter,
     const float* __restrict__ inv, const uint16_t* __restrict__ zrow,
     uint16_t* __restrict__ act, int d, int F) {
-  __shared__ float red[(S - 1) * NT * 16 * 64];
+  __shared__ float red[S * NT * 16 * 64];
   __shared__ int list[64];
   __shared__ int sh[2];
   const int e = blockIdx.y;
@@ -267,6 +261,7 @@ __global__ __launch_bounds__(64 * S) void k_gateup_stream(
     const bool valid = col < ntok;
     const int tok = valid ? list[c0 + col] : 0;
     const uint16_t* xrow = (valid ? xn + (size_t)tok * d : zrow) + (lane >> 5) * 8;
+    const float rs = valid ? inv[tok] : 0.f;  // RMSNorm scale of this token
     f32x16 acc[NT];
 #pragma unroll
     for (int q = 0; q < NT; ++q)
@@ -274,33 +269,24 @@ __global__ __launch_bounds__(64 * S) void k_gateup_stream(
       for (int i = 0; i < 16; ++i) acc[q][i] = 0.f;
     if constexpr (FP8) stream_mac_fp8<D, NT>(wp8, xrow, ks0, kper, acc);
     else stream_mac<D, NT>(wp, xrow, ks0, kper, acc);
-    reduce_split<NT, S>(acc, red, wave, lane);
-    if constexpr (FP8) {
-      if (wave == 0) {
+    stash<NT>(acc, red, wave, lane);
+    __syncthreads();
+    // gate(f) is element i of tile q, up(f) element i + 8, f = 16 (NT ft + q) +
+    // c32_row(i, lane); the S waves take the NT * 8 (gate, up) pairs in turn
+    uint16_t* dst = act + (size_t)(off + c0 + col) * F + ft * 16 * NT;
 #pragma unroll
-        for (int q = 0; q < NT; ++q)
-          scale_rows(acc[q], sgu + (size_t)e * 2 * F + 32 * (NT * ft + q), lane);
+    for (int p = wave; p < NT * 8; p += S) {
+      const int q = p >> 3, i = p & 7, f = c32_row(i, lane);
+      float g = split_sum<NT, S>(red, q, i, lane);
+      float u = split_sum<NT, S>(red, q, i + 8, lane);
+      if constexpr (FP8) {  // row scales: gate rows 0..15, up rows 16..31 of the tile
+        const float* sc = sgu + (size_t)e * 2 * F + 32 * (NT * ft + q);
+        g *= sc[f];
+        u *= sc[16 + f];
       }
+      if (valid) dst[16 * q + f] = (uint16_t)f32_to_bf16(silu(rs * g) * (rs * u));
     }
-
-    if (wave == 0 && valid) {
-      // tile q covers columns 16*(NT*ft + q) ..: gate(f) in element i, up(f) in i + 8
-      const float s = inv[tok];  // RMSNorm scale of this token
-      uint16_t* dst = act + (size_t)(off + c0 + col) * F + ft * 16 * NT + 4 * (lane >> 5);
-#pragma unroll
-      for (int q = 0; q < NT; ++q)
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          float v4[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            v4[t] = silu(s * acc[q][4 * g + t]) * (s * acc[q][4 * g + 8 + t]);
-          u32x2 v;
-          v[0] = pack_bf16x2(v4[0], v4[1]);
-          v[1] = pack_bf16x2(v4[2], v4[3]);
-          *reinterpret_cast<u32x2*>(dst + 16 * q + 8 * g) = v;
-        }
-    }
+    __syncthreads();  // red is reused by the next pass over the tokens
   }
 }
 
@@ -308,13 +294,13 @@ __global__ __launch_bounds__(64 * S) void k_gateup_stream(
 // output row of the token, k > 1 writes y (fp32) for the combine kernel.
 // SD waves split the reduction axis.
 template <int D, bool FP8, int SD>
-__global__ __launch_bounds__(64 * SD) void k_down_stream(
+__global__ __launch_bounds__(64 * SD, MOE_STREAM_WAVES_EU) void k_down_stream(
     const uint16_t* __restrict__ wd, const uint8_t* __restrict__ wd8,
     const float* __restrict__ sd, const uint16_t* __restrict__ act,
     const int* __restrict__ sel, int n, int k, int E, const float* __restrict__ gate,
     const uint16_t* __restrict__ zrow, uint16_t* __restrict__ out, float* __restrict__ ybuf, int d,
     int F) {
-  __shared__ float red[(SD - 1) * 16 * 64];
+  __shared__ float red[SD * 16 * 64];
   __shared__ int list[64];
   __shared__ int sh[2];
   const int e = blockIdx.y;
@@ -339,40 +325,28 @@ __global__ __launch_bounds__(64 * SD) void k_down_stream(
     const bool valid = col < ntok;
     const int slot = off + c0 + (valid ? col : 0);
     const uint16_t* arow = (valid ? act + (size_t)slot * F : zrow) + (lane >> 5) * 8;
+    const int tok = (k == 1 && valid) ? list[c0 + col] : 0;
+    const float gw = (k == 1 && valid) ? gate[tok] : 0.f;
     f32x16 acc[1];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[0][i] = 0.f;
     if constexpr (FP8) stream_mac_fp8<D, 1>(wp8, arow, ks0, kper, acc);
     else stream_mac<D, 1>(wp, arow, ks0, kper, acc);
-    reduce_split<1, SD>(acc, red, wave, lane);
-    if constexpr (FP8) {
-      if (wave == 0) scale_rows(acc[0], sd + (size_t)e * d + mt * kTileRows, lane);
-    }
-
-    if (wave == 0 && valid) {
-      const int m0 = mt * kTileRows;
-      if (k == 1) {
-        const int tok = list[c0 + col];
-        const float g = gate[tok];
-        uint16_t* dst = out + (size_t)tok * d + m0;
+    stash<1>(acc, red, wave, lane);
+    __syncthreads();
+    // the SD waves take the 16 accumulator elements (rows m0 + c32_row(i, lane)) in turn
+    const int m0 = mt * kTileRows;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = c32_row(4 * q, lane);
-          u32x2 v;
-          v[0] = pack_bf16x2(g * acc[0][4 * q], g * acc[0][4 * q + 1]);
-          v[1] = pack_bf16x2(g * acc[0][4 * q + 2], g * acc[0][4 * q + 3]);
-          *reinterpret_cast<u32x2*>(dst + r) = v;
-        }
-      } else {
-        float* dst = ybuf + (size_t)slot * d + m0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = c32_row(4 * q, lane);
-          f32x4 v = {acc[0][4 * q], acc[0][4 * q + 1], acc[0][4 * q + 2], acc[0][4 * q + 3]};
-          *reinterpret_cast<f32x4*>(dst + r) = v;
-        }
+    for (int i = wave; i < 16; i += SD) {
+      const int r = c32_row(i, lane);
+      float y = split_sum<1, SD>(red, 0, i, lane);
+      if constexpr (FP8) y *= sd[(size_t)e * d + m0 + r];
+      if (valid) {
+        if (k == 1) out[(size_t)tok * d + m0 + r] = (uint16_t)f32_to_bf16(gw * y);
+        else ybuf[(size_t)slot * d + m0 + r] = y;
       }
     }
+    __syncthreads();  // red is reused by the next pass over the tokens
   }
 }
 
