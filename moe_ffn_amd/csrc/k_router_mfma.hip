@@ -14,9 +14,11 @@
 // therefore two bf16 MFMAs with fp32 accumulation: fp32-router precision at
 // matrix-core speed.  z = inv_rms * z_raw with inv_rms = 1/sqrt(mean(h^2)+eps).
 //
-// Outputs: xg = bf16(g * h) for the experts (hi itself; inv_rms is applied to
-// the experts' fp32 accumulators instead of to the activations), inv_rms[T],
-// sel[T,k], gate[T,k].
+// Outputs: inv_rms[T], sel[T,k], gate[T,k] and, with WX, xg = bf16(g * h)
+// for the experts (hi itself; inv_rms is applied to the experts' fp32
+// accumulators instead of to the activations).  The prefill path leaves xg
+// out: its gather kernel forms the same bf16(g * h) from the hidden rows it
+// copies, which saves the T*d*2-byte write and read of xg.
 //
 // The kernel moves T*d*2 bytes in and the same out, so it is sized for
 // memory-level parallelism: a workgroup owns 16*TT tokens (TT = 1; MFMA 16x16x32:
@@ -44,7 +46,7 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(const u32x4& a, const u32x4& b, c
 }
 }  // namespace
 
-template <int NA, int TT, int NW>
+template <int NA, int TT, int NW, bool WX>
 __global__ __launch_bounds__(NW * 64) void k_router_mfma(
     const uint16_t* __restrict__ hidden, int T, int d, const uint16_t* __restrict__ wr,
     const uint16_t* __restrict__ gain, const float* __restrict__ bias, int E, int k, float eps,
@@ -106,7 +108,7 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
         bhi[i] = hi;
         blo[i] = pack_bf16x2(x0 - bf16_lo(hi), x1 - bf16_hi(hi));
       }
-      stg16(xp[tt] + ko, bhi);
+      if constexpr (WX) stg16(xp[tt] + ko, bhi);
 #pragma unroll
       for (int a = 0; a < NA; ++a) {
         acc[tt][a] = mfma_16x16x32(av[a], bhi, acc[tt][a]);
@@ -222,7 +224,7 @@ hipError_t go(const FwdArgs& a) {
   constexpr int NW = 8;
   if (a.dim.d % (kRK * NW) != 0) return hipErrorInvalidValue;
   const int grid = (a.T + 16 * TT - 1) / (16 * TT);
-  return launch(k_router_mfma<NA, TT, NW>, dim3(grid), dim3(NW * 64), a.stream,
+  return launch(k_router_mfma<NA, TT, NW, false>, dim3(grid), dim3(NW * 64), a.stream,
                 a.ev[kSlotNormRouter], (const uint16_t*)a.hidden, a.T, a.dim.d,
                 (const uint16_t*)a.wr16, (const uint16_t*)a.gain16, (const float*)a.bias, a.dim.E,
                 a.dim.k, a.dim.eps, (const uint16_t*)a.zrow, (uint16_t*)a.sink,
