@@ -108,7 +108,7 @@ def ingest_counters(pmc_dir: str) -> None:
     (c<N>fp8_fetch, c<N>fp8_write for --config N --fp8).  Each
     counter is scaled by the bytes the copy kernel really moves over what the
     same counter reads for it."""
-    from synth.configs import CONFIGS
+    from synth.configs import WORKLOADS
     copy_bytes = 1024 << 20
     cf = _counter_means(os.path.join(pmc_dir, "copy_fetch"))["torch_neg"] * 1024
     cw = _counter_means(os.path.join(pmc_dir, "copy_write"))["torch_neg"] * 1024
@@ -120,7 +120,7 @@ def ingest_counters(pmc_dir: str) -> None:
         fd, wd = (os.path.join(pmc_dir, f"c{cid}{tag}_{x}") for x in ("fetch", "write"))
         if not (os.path.isdir(fd) and os.path.isdir(wd)):
             continue
-        cfg = CONFIGS[cid]
+        cfg = WORKLOADS[cid]
         wname = cfg.name + ("_fp8w" if tag else "")
         fm, wm = _counter_means(fd), _counter_means(wd)
         kernels = {}

@@ -1,8 +1,8 @@
 """fp64 CPU oracle of the ZONOS2 MoE feed-forward layer.
 
-TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check of the graft
-entry module and the CPU-baseline leg of the bench may import, call or run
-anything in this package.  The HIP library never uses it and shares no code,
+TEST INFRASTRUCTURE ONLY.  Only the tests, smoke() in __graft_entry__.py
+and the CPU-baseline leg of bench.py may import, call or run anything in
+this package.  The HIP library never uses it and shares no code,
 constant or table with it; the two meet only through the seeded inputs of the
 ``synth`` package.
 """

@@ -31,7 +31,7 @@ if _ROOT not in sys.path:
     sys.path.insert(0, _ROOT)
 
 from oracle.moe_oracle import rmsnorm, router_scores  # noqa: E402
-from synth.configs import CONFIGS, ZIPF_S, ZIPF_RANKS, ZIPF_EMPTY_BIAS  # noqa: E402
+from synth.configs import WORKLOADS, ZIPF_S, ZIPF_RANKS, ZIPF_EMPTY_BIAS  # noqa: E402
 from synth import gen  # noqa: E402
 
 
@@ -74,7 +74,7 @@ def calibrate(z: np.ndarray, tgt: np.ndarray, tol: float = 0.005, iters: int = 5
 
 
 def main():
-    cfg = CONFIGS[4]
+    cfg = WORKLOADS[4]
     E = cfg.E
     inp = gen.make_inputs(cfg.cid) if os.path.exists(gen.ZIPF_BIAS_FILE) else None
     # The bias file may not exist yet: build the other inputs directly.

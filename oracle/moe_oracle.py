@@ -26,7 +26,7 @@ state and TopK keeps a few of them)):
   O9  balancing step: b_e <- b_e + rate * sign(mean_load - c_e)  (between forwards)
   O10 FFN stack: h_{l+1} = h_l + FFN_l(h_l) over the backbone's layers
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 the bias only steers selection and never enters a gate; the layer returns
 the FFN output without the residual; no capacity limit and no dropped
 tokens; no shared expert; a linear router (no EDA smoothing).

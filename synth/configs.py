@@ -32,7 +32,7 @@ class LayerConfig:
         return self.T * self.k
 
 
-CONFIGS = {
+WORKLOADS = {
     0: LayerConfig(0, "tiny_fp32_T64_d256_E4_F512_top1", T=64, d=256, E=4, F=512, k=1,
                    dtype="f32", bias="normal", family="d256_E4_F512"),
     1: LayerConfig(1, "decode_bf16_T32_d2048_E16_F3072_top1", T=32, d=2048, E=16, F=3072,
@@ -54,4 +54,4 @@ ZIPF_EMPTY_BIAS = -1.0e4
 
 
 def get_config(cid: int) -> LayerConfig:
-    return CONFIGS[int(cid)]
+    return WORKLOADS[int(cid)]

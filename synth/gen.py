@@ -20,7 +20,7 @@ from dataclasses import replace
 
 import numpy as np
 
-from .configs import CONFIGS, LayerConfig, ZIPF_EMPTY_BIAS  # noqa: F401
+from .configs import WORKLOADS, LayerConfig, ZIPF_EMPTY_BIAS  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 ZIPF_BIAS_FILE = os.path.join(_HERE, "zipf_bias_T16384_d2048_E16.txt")
@@ -120,7 +120,7 @@ def make_inputs(cid_or_cfg, T: int | None = None, hidden_seed: int = 0,
     ``layer`` selects one layer's weights (and bias) of a stack.
     Returned keys: cfg, hidden, gain, w_router, bias, w_gate, w_up, w_down.
     """
-    cfg = CONFIGS[int(cid_or_cfg)] if not isinstance(cid_or_cfg, LayerConfig) else cid_or_cfg
+    cfg = WORKLOADS[int(cid_or_cfg)] if not isinstance(cid_or_cfg, LayerConfig) else cid_or_cfg
     if T is not None and T != cfg.T:
         cfg = replace(cfg, T=int(T))
     w = family_weights(cfg, layer)

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from oracle import moe_oracle as O
-from synth import CONFIGS, make_inputs
+from synth import WORKLOADS, make_inputs
 from tests._parity import check_parity, make_layer, to_torch
 
 pytestmark = pytest.mark.gpu
@@ -29,7 +29,7 @@ def _need_gpu():
 
 @pytest.mark.parametrize("cid,T", [(1, 32), (2, 2000), (3, 700)])
 def test_update_matches_oracle_bit_for_bit(cid, T):
-    inp = make_inputs(replace(CONFIGS[cid], bias="normal"), T=T)
+    inp = make_inputs(replace(WORKLOADS[cid], bias="normal"), T=T)
     layer = make_layer(inp, max_tokens=T)
     h = to_torch(inp["hidden"], "bf16")
     b = np.asarray(inp["bias"], np.float32)
@@ -57,7 +57,7 @@ def test_update_matches_oracle_bit_for_bit(cid, T):
 
 def test_repeated_steps_flatten_the_load():
     T = 4096
-    inp = make_inputs(replace(CONFIGS[2], bias="normal"), T=T)
+    inp = make_inputs(replace(WORKLOADS[2], bias="normal"), T=T)
     layer = make_layer(inp, max_tokens=T)
     h = to_torch(inp["hidden"], "bf16")
     _, r = layer.forward(h, routing=True)

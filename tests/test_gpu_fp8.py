@@ -15,7 +15,7 @@ import pytest
 import torch
 
 from oracle import moe_oracle as O
-from synth import CONFIGS, make_inputs
+from synth import WORKLOADS, make_inputs
 from synth.gen import fp8_expert_weights, values_f32
 from tests._parity import check_parity, device_weights, to_torch
 
@@ -64,9 +64,9 @@ _layers = {}
 
 
 def family_fp8_layer(cid: int, k: int):
-    key = (CONFIGS[cid].family, k, CONFIGS[cid].bias)
+    key = (WORKLOADS[cid].family, k, WORKLOADS[cid].bias)
     if key not in _layers:
-        _layers[key] = fp8_layer(make_inputs(replace(CONFIGS[cid], k=k)), max_tokens=16384)
+        _layers[key] = fp8_layer(make_inputs(replace(WORKLOADS[cid], k=k)), max_tokens=16384)
     return _layers[key]
 
 
@@ -80,7 +80,7 @@ def family_fp8_layer(cid: int, k: int):
     (3, None, 2, 512),    # top-2 T = 4096
 ])
 def test_fp8_parity(cid, T, k, sample):
-    base = replace(CONFIGS[cid], k=k)
+    base = replace(WORKLOADS[cid], k=k)
     inp = make_inputs(base, T=T) if T is not None else make_inputs(base)
     st = check_parity(inp, family_fp8_layer(cid, k), sample=sample, vals=fp8_vals(inp),
                       label=f"fp8 c{cid} T={inp['cfg'].T} k={k}")
@@ -95,7 +95,7 @@ def test_fp8_matches_bf16_layer_on_code_values():
     waves for fp8 and eight for bf16, so only the fp32 summation order differs
     there."""
     from moe_ffn_amd import MoELayer
-    inp = make_inputs(CONFIGS[1])
+    inp = make_inputs(WORKLOADS[1])
     cfg = inp["cfg"]
     q = fp8_expert_weights(inp)
     w8 = device_weights(inp)
@@ -110,7 +110,7 @@ def test_fp8_matches_bf16_layer_on_code_values():
     l8 = MoELayer(cfg.d, cfg.F, cfg.E, cfg.k, "bf16", w8, 512, rms_eps=cfg.eps, fp8_scales=ones)
     l16 = MoELayer(cfg.d, cfg.F, cfg.E, cfg.k, "bf16", w16, 512, rms_eps=cfg.eps)
     for T in (32, 300):
-        h = to_torch(make_inputs(CONFIGS[1], T=T)["hidden"], "bf16")
+        h = to_torch(make_inputs(WORKLOADS[1], T=T)["hidden"], "bf16")
         o8, r8 = l8.forward(h, routing=True)
         o16, r16 = l16.forward(h, routing=True)
         torch.cuda.synchronize()
@@ -127,7 +127,7 @@ def test_fp8_matches_bf16_layer_on_code_values():
 
 def test_fp8_create_rejects_f32_and_small_dff():
     from moe_ffn_amd import MoELayer, MoELayerError
-    inp = make_inputs(CONFIGS[1])
+    inp = make_inputs(WORKLOADS[1])
     cfg = inp["cfg"]
     q = fp8_expert_weights(inp)
     w = device_weights(inp)

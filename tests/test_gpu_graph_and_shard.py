@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 import torch
 
-from synth import CONFIGS, make_inputs
+from synth import WORKLOADS, make_inputs
 from synth.configs import LayerConfig
 from tests._parity import check_parity, make_layer, to_torch
 
@@ -39,8 +39,8 @@ def _need_gpu():
     (3, 200, 2),    # tile path + combine
 ])
 def test_graph_replay_matches_eager(cid, T, k):
-    inp = make_inputs(replace(CONFIGS[cid], k=k), T=T)
-    other = make_inputs(replace(CONFIGS[cid], k=k), T=T, hidden_seed=7)
+    inp = make_inputs(replace(WORKLOADS[cid], k=k), T=T)
+    other = make_inputs(replace(WORKLOADS[cid], k=k), T=T, hidden_seed=7)
     layer = make_layer(inp, max_tokens=T)
     h = to_torch(inp["hidden"], "bf16")
     h_other = to_torch(other["hidden"], "bf16")

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from synth import CONFIGS, make_inputs
+from synth import WORKLOADS, make_inputs
 from synth.configs import LayerConfig
 from tests._parity import check_parity, make_layer, to_torch, device_weights, out_to_f64
 
@@ -33,7 +33,7 @@ _layers = {}
 
 def family_layer(cid: int, k: int | None = None, max_tokens: int | None = None, bias=None):
     """One library layer per (family, k, max_tokens, bias) reused across tests."""
-    base = CONFIGS[cid]
+    base = WORKLOADS[cid]
     k = k or base.k
     max_tokens = max_tokens or 16384
     key = (base.family, k, max_tokens, base.bias if bias is None else bias)
@@ -88,14 +88,14 @@ def test_skewed_bf16_T16384_full_routing_sampled_rows():
     (4, 1000, 1),   # skewed bias at a reduced size
 ])
 def test_reduced_sizes_full_rows(cid, T, k):
-    base = CONFIGS[cid]
+    base = WORKLOADS[cid]
     inp = make_inputs(replace(base, k=k), T=T)
     check_parity(inp, family_layer(cid, k=k), label=f"c{cid} T={T} k={k}")
 
 
 def test_tiny_fp32_ragged_and_top2():
     for T, k in [(1, 1), (37, 1), (64, 2), (5, 3)]:
-        inp = make_inputs(replace(CONFIGS[0], k=k), T=T)
+        inp = make_inputs(replace(WORKLOADS[0], k=k), T=T)
         check_parity(inp, make_layer(inp, max_tokens=64), label=f"c0 T={T} k={k}")
 
 
@@ -105,13 +105,13 @@ def test_T0_launches_nothing_and_T_max():
     h = torch.empty((0, 2048), dtype=torch.bfloat16, device="cuda")
     out = layer.forward(h)
     assert out.shape == (0, 2048)
-    inp = make_inputs(CONFIGS[1], T=256)   # same weights and bias as the layer
+    inp = make_inputs(WORKLOADS[1], T=256)   # same weights and bias as the layer
     check_parity(inp, layer, label="T = max_tokens = 256")
 
 
 def test_every_token_on_one_expert():
     for T in (64, 300):   # decode path with two 32-token passes; tile path with 3 tiles
-        cfg = replace(CONFIGS[2], T=T)
+        cfg = replace(WORKLOADS[2], T=T)
         inp = make_inputs(cfg)
         b = np.zeros(16, np.float32)
         b[5] = 1e4
@@ -153,7 +153,7 @@ def test_deterministic_bytes():
 
 def test_nan_row_stays_in_bounds_and_leaves_other_rows_alone():
     for cid, T in [(1, 32), (2, 300)]:
-        inp = make_inputs(CONFIGS[cid], T=T)
+        inp = make_inputs(WORKLOADS[cid], T=T)
         layer = family_layer(cid)
         h = to_torch(inp["hidden"], "bf16")
         hn = h.clone()
@@ -174,7 +174,7 @@ def test_nan_row_stays_in_bounds_and_leaves_other_rows_alone():
 
 
 def test_set_bias_steers_routing():
-    inp = make_inputs(CONFIGS[1])
+    inp = make_inputs(WORKLOADS[1])
     layer = make_layer(inp, max_tokens=32)
     b = torch.zeros(16, dtype=torch.float32, device="cuda")
     b[11] = 1e4

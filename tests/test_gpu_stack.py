@@ -15,7 +15,7 @@ import pytest
 import torch
 
 from oracle import moe_oracle as O
-from synth import CONFIGS, make_inputs
+from synth import WORKLOADS, make_inputs
 from synth.gen import values_f32
 from synth.configs import LayerConfig
 from tests._parity import TOL, make_layer, to_torch, out_to_f64
@@ -103,8 +103,8 @@ def test_full_width_stack_matches_layer_loop():
     T = 32
     dense = LayerConfig(82, "stack_dense_bf16_d2048_F3072", T=T, d=2048, E=1, F=3072, k=1,
                         dtype="bf16", bias="zero", family="stack_dense_d2048")
-    inps = [make_inputs(dense, T=T, layer=0), make_inputs(CONFIGS[1], T=T),
-            make_inputs(replace(CONFIGS[1], k=2), T=T), make_inputs(dense, T=T, layer=1)]
+    inps = [make_inputs(dense, T=T, layer=0), make_inputs(WORKLOADS[1], T=T),
+            make_inputs(replace(WORKLOADS[1], k=2), T=T), make_inputs(dense, T=T, layer=1)]
     layers = [make_layer(inp, max_tokens=T) for inp in inps]
     stack = MoEStack(layers, max_tokens=T)
     h0 = to_torch(inps[1]["hidden"], "bf16")

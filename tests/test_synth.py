@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 import torch
 
-from synth import CONFIGS, make_inputs, round_to_bf16_bits, bf16_bits_to_f32
+from synth import WORKLOADS, make_inputs, round_to_bf16_bits, bf16_bits_to_f32
 from synth import gen
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -50,11 +50,11 @@ def test_pages_structure_matches_workloads():
     with open(os.path.join(GOLDEN, "zonos2_structure.json")) as f:
         s = json.load(f)
     for cid in (1, 2, 3, 4):
-        assert CONFIGS[cid].E == s["experts_per_moe_layer"]
-    assert {CONFIGS[c].k for c in (1, 2, 4)} == {s["top_k_moe_layers"]}
-    assert CONFIGS[3].k == s["top_k_last_moe_layer"]
+        assert WORKLOADS[cid].E == s["experts_per_moe_layer"]
+    assert {WORKLOADS[c].k for c in (1, 2, 4)} == {s["top_k_moe_layers"]}
+    assert WORKLOADS[3].k == s["top_k_last_moe_layer"]
     # assumed widths are consistent with 8B total / 900M active parameters
-    cfg = CONFIGS[1]
+    cfg = WORKLOADS[1]
     moe_layers = s["layers"] - len(s["dense_layers"])
     per_expert = 3 * cfg.d * cfg.F
     assert moe_layers * cfg.E * per_expert < s["total_params"]
@@ -64,7 +64,7 @@ def test_pages_structure_matches_workloads():
 
 @pytest.mark.parametrize("cid", [1, 2, 3, 4])
 def test_large_workloads_bf16_storage(cid):
-    cfg = CONFIGS[cid]
+    cfg = WORKLOADS[cid]
     w = gen.family_weights(cfg)
     assert w["w_gate"].dtype == np.uint16 and w["w_gate"].shape == (16, 3072, 2048)
     assert w["w_down"].shape == (16, 2048, 3072)
