@@ -141,3 +141,35 @@ def test_fp8_create_rejects_f32_and_small_dff():
         sm = {"gate": scales["gate"][:, :128].contiguous(),
               "up": scales["up"][:, :128].contiguous(), "down": scales["down"]}
         MoELayer(cfg.d, 128, cfg.E, cfg.k, "bf16", small, 64, fp8_scales=sm)
+
+
+@pytest.mark.parametrize("T", [32, 96])
+def test_fp8_moe_layers_in_a_stack(T):
+    """A stack of bf16 dense layers and fp8 MoE layers (decode streams at T=32,
+    tile GEMMs at T=96) equals the layer-by-layer loop bit for bit and the
+    oracle's stack on the dequantised weights to the layer tolerance."""
+    from moe_ffn_amd import MoEStack
+    from tests._parity import TOL, make_layer, out_to_f64
+    from tests.test_gpu_stack import _loop, _small_stack_inputs
+    inps = _small_stack_inputs(T)
+    layers, vals = [], []
+    for inp in inps:
+        if inp["cfg"].E > 1:
+            layers.append(fp8_layer(inp, max_tokens=T))
+            vals.append(fp8_vals(inp))
+        else:
+            layers.append(make_layer(inp, max_tokens=T))
+            vals.append(values_f32(inp))
+    stack = MoEStack(layers, max_tokens=T)
+    h0 = to_torch(inps[0]["hidden"], "bf16")
+    out = stack.forward(h0)
+    ref_loop, sels = _loop(layers, h0)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref_loop.view(torch.int16))
+    ref = O.stack_forward(vals, vals[0]["hidden"], [inp["cfg"].k for inp in inps],
+                          inps[0]["cfg"].eps, forced_sels=sels)["out"]
+    err = np.abs(out_to_f64(out) - ref).max()
+    assert err <= TOL["bf16"] * np.abs(ref).max(), (err, np.abs(ref).max())
+    stack.close()
+    for L in layers:
+        L.close()
