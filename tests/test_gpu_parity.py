@@ -4,7 +4,8 @@ Covers the five workloads at full size (routing and dispatch in full, output
 rows in full or on a sample the oracle computes one by one), reduced sizes that
 span several tiles with ragged tails on both expert paths, and the edge cases:
 T = 0, T = 1, T = max_tokens, every token on one expert, a single-expert
-(dense) layer, NaN rows, bias updates, determinism and bad arguments.
+(dense) layer, expert counts from 5 to 64 and top-k up to 8 on both paths and
+both dtypes, NaN rows, bias updates, determinism and bad arguments.
 """
 
 from dataclasses import replace
@@ -135,6 +136,27 @@ def test_single_expert_dense_layer(dtype, d, F):
     assert st["near_ties"] == 0  # a single expert has an infinite margin
     _, r = layer.forward(to_torch(inp["hidden"], dtype), routing=True)
     assert torch.all(r["gate"] == 1.0) and torch.all(r["sel"] == 0)
+
+
+@pytest.mark.parametrize("dtype,E,k,T", [
+    ("bf16", 5, 3, 20),     # 60 assignments: decode path, odd expert count
+    ("bf16", 5, 3, 100),    # tile path
+    ("bf16", 24, 2, 32),    # 64 assignments: decode path at its limit
+    ("bf16", 24, 2, 200),
+    ("bf16", 33, 4, 50),    # 33..64 experts: the widest router tiles
+    ("bf16", 64, 8, 8),     # the limits: 64 experts, top-8 (64 assignments)
+    ("bf16", 64, 8, 150),
+    ("bf16", 64, 1, 64),
+    ("f32", 64, 8, 40),
+    ("f32", 7, 2, 33),
+])
+def test_expert_counts_and_top_k_up_to_the_limits(dtype, E, k, T):
+    d, F = (256, 256) if dtype == "bf16" else (64, 96)
+    cfg = LayerConfig(92, f"limits_{dtype}_E{E}_k{k}_T{T}", T=T, d=d, E=E, F=F, k=k,
+                      dtype=dtype, bias="normal", family=f"limits_{dtype}_d{d}_E{E}_F{F}")
+    inp = make_inputs(cfg)
+    st = check_parity(inp, make_layer(inp, max_tokens=T), label=cfg.name)
+    assert st["rows_compared"] == T
 
 
 def test_deterministic_bytes():
