@@ -301,7 +301,7 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
           v[0] = pack_bf16x2(v4[0], v4[1]);
           v[1] = pack_bf16x2(v4[2], v4[3]);
           // operand lane g*32 + col holds columns 8g .. 8g+7 of the k-step
-          *reinterpret_cast<u32x2*>(blk + ((size_t)gt * 64 + g * 32 + col) * 8 + 4 * hi) = v;
+          stg8_stream(blk + ((size_t)gt * 64 + g * 32 + col) * 8 + 4 * hi, v);
         }
       }
     } else {

@@ -15,8 +15,8 @@
 // blocks, like its weights.  Padding rows are zero.
 //
 // One wave per (subtile, 64-wide k group): four wave-wide loads, each reading
-// 8 rows x 128 contiguous bytes, and four stores, each writing 8 runs of 128
-// contiguous bytes.
+// 8 rows x 128 contiguous bytes, and four non-temporal stores, each writing 8
+// runs of 128 contiguous bytes.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void k_gather_tiles(const uint16_t* __restrict
     const int idx = q * 64 + lane;
     const int rr = idx >> 3, c = idx & 7;
     const int s = g * 4 + (c >> 1), li = (c & 1) * 32 + rr;
-    stg16(dst + ((size_t)s * 64 + li) * 8, v[q]);
+    stg16_stream(dst + ((size_t)s * 64 + li) * 8, v[q]);
   }
 }
 
