@@ -52,7 +52,8 @@ typedef enum {
 typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
 
 /* Layer shape.  Limits: 1 <= n_experts <= 64; 1 <= top_k <= min(n_experts, 8);
- * d_model and d_ff multiples of 64 (bf16) or of 4 (f32); 1 <= max_tokens <= 2^20.
+ * bf16: d_model a multiple of 256 and d_ff of 128 (of 256 with fp8 expert
+ * weights); f32: both multiples of 4; 1 <= max_tokens <= 2^20.
  * dtype is the storage type of activations, gain, router and expert weights;
  * arithmetic accumulates in fp32 either way. */
 typedef struct {
