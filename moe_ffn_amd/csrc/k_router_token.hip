@@ -11,9 +11,10 @@
 //   sum h^2,  x' = g * h (stored as bf16 for the experts),
 //   z_raw[e] = sum_i W_r[e][i] * x'_i     (every product exact in fp32).
 // The E partial sums are reduced by a spreading butterfly inside each wave and
-// across the four waves in LDS (fixed order), then one thread applies
-// inv_rms = 1/sqrt(mean(h^2) + eps), adds the bias, picks the top-k and writes
-// the gates.  The dispatch of decode batches happens in the expert kernels.
+// across the four waves in LDS (fixed order); then the lanes of wave 0, one per
+// expert, apply inv_rms = 1/sqrt(mean(h^2) + eps), add the bias, pick the
+// top-k by wave-wide maximum reductions and write the gates.  The dispatch of
+// decode batches happens in the expert kernels.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -86,48 +87,50 @@ __global__ __launch_bounds__(256) void k_router_token(
   if (lane == 0) ssr[wave] = ss;
   __syncthreads();
 
-  if (tid == 0) {
+  if (wave == 0) {
+    // lane e < E owns expert e: logit, score, then the top-k and the gates by
+    // wave-wide reductions (EP <= 64 experts, one per lane)
     const float sq = ((ssr[0] + ssr[1]) + ssr[2]) + ssr[3];
     const float inv = 1.0f / sqrtf(sq / (float)d + eps);
-    float z[EP], sc[EP];
-#pragma unroll
-    for (int e = 0; e < EP; ++e) {
-      z[e] = (((red[0][e] + red[1][e]) + red[2][e]) + red[3][e]) * inv;
-      sc[e] = z[e] + bias[e];  // bias is zero-padded to 64 entries
-    }
-    // top-k by descending score, exact ties to the lower index; NaN never wins
-    uint64_t taken = 0;
-    int chosen[8];
-    float zc[8];
+    const bool live = lane < E;
+    const int el = lane < EP ? lane : 0;
+    const float z = live ? (((red[0][el] + red[1][el]) + red[2][el]) + red[3][el]) * inv : 0.f;
+    const float sc = z + bias[lane < 64 ? lane : 0];  // bias is zero-padded to 64 entries
+    // top-k by descending score, exact ties to the lower index: each round
+    // takes the wave maximum of a 64-bit key (available flag, the score's
+    // order-preserving bits with NaN lowest, 63 - lane), unique per lane, so
+    // exactly one lane wins every round and only experts < E can
+    const uint32_t u = sc == 0.f ? 0u : __float_as_uint(sc);  // -0 ranks as +0
+    const uint32_t ord = sc != sc ? 0u : (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    bool avail = live;
+    int chosen = -1;  // this lane's rank j if chosen
     for (int j = 0; j < k; ++j) {
-      int best = -1;
-      float bs = 0.f, bz = 0.f;
+      uint64_t key = ((avail ? 1ull : 0ull) << 62) | ((uint64_t)ord << 6) | (uint64_t)(63 - lane);
 #pragma unroll
-      for (int e = 0; e < EP; ++e) {
-        const bool ok = e < E && !((taken >> e) & 1) && (best < 0 || sc[e] > bs);
-        best = ok ? e : best;
-        bs = ok ? sc[e] : bs;
-        bz = ok ? z[e] : bz;
+      for (int dl = 1; dl < 64; dl <<= 1) {
+        const uint64_t o = (uint64_t)__shfl_xor((unsigned long long)key, dl, kWave);
+        key = o > key ? o : key;
       }
-      chosen[j] = best;
-      zc[j] = bz;
-      taken |= 1ull << best;
+      if (lane == 63 - (int)(key & 63ull)) {
+        chosen = j;
+        avail = false;
+      }
     }
-    float zmax = -INFINITY, den = 0.f;
-    if (k == 1) {
+    // gates: k = 1 softmax over all E logits at the chosen expert; k >= 2
+    // softmax over the chosen logits
+    const bool in_set = k == 1 ? live : chosen >= 0;
+    float zm = in_set ? z : -INFINITY;
 #pragma unroll
-      for (int e = 0; e < EP; ++e) zmax = e < E ? fmaxf(zmax, z[e]) : zmax;
+    for (int dl = 1; dl < 64; dl <<= 1) zm = fmaxf(zm, __shfl_xor(zm, dl, kWave));
+    float ex = in_set ? expf(z - zm) : 0.f;
+    float den = ex;
 #pragma unroll
-      for (int e = 0; e < EP; ++e) den += e < E ? expf(z[e] - zmax) : 0.f;
-    } else {
-      for (int j = 0; j < k; ++j) zmax = fmaxf(zmax, zc[j]);
-      for (int j = 0; j < k; ++j) den += expf(zc[j] - zmax);
+    for (int dl = 1; dl < 64; dl <<= 1) den += __shfl_xor(den, dl, kWave);
+    if (chosen >= 0) {
+      sel[(size_t)t * k + chosen] = lane;
+      gate[(size_t)t * k + chosen] = ex / den;
     }
-    for (int j = 0; j < k; ++j) {
-      sel[(size_t)t * k + j] = chosen[j];
-      gate[(size_t)t * k + j] = expf(zc[j] - zmax) / den;
-    }
-    inv_out[t] = inv;
+    if (lane == 0) inv_out[t] = inv;
   }
 }
 
