@@ -26,7 +26,8 @@
 // its NW waves split the reduction axis into NW slices, and each wave issues
 // the loads of up to kRBatch k-steps at once.  One wave-wide token load reads
 // 64 contiguous bytes from each of 16 rows.  Partial logits of the waves meet
-// in LDS and are summed in a fixed order, one (token, expert) pair per thread.
+// in LDS and are summed in a fixed order, one (token, expert) pair per thread;
+// with 16 experts the top-k and gates run on 16 lanes per token.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -166,7 +167,55 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
   }
   __syncthreads();
 
-  if (tid < NTOK) {
+  if constexpr (EPAD == 16 && NTOK == 16) {
+    // 16 experts: 16 lanes per token (lane e owns expert e), top-k as k maxima
+    // of a unique key over the lane group (availability, the score's
+    // order-preserving bits with NaN lowest, 63 - e): the same choice as the
+    // one-thread loop below, ties to the lower index, one winner per round
+    if (tid < 16 * NTOK) {
+      const int tl = tid >> 4, e = tid & 15;
+      const int t = t0 + tl;
+      float sq = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        sq += (ssr[w][0][tl] + ssr[w][0][tl + 16]) + (ssr[w][0][tl + 32] + ssr[w][0][tl + 48]);
+      const float inv = 1.0f / sqrtf(sq / (float)d + eps);
+      const bool live = e < E;
+      const float z = zs[tl][e] * inv;
+      const float sc = z + bias[e];  // bias is padded with zeros to 64 entries
+      const uint32_t u = sc == 0.f ? 0u : __float_as_uint(sc);  // -0 ranks as +0
+      const uint32_t ord = sc != sc ? 0u : (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+      bool avail = live;
+      int chosen = -1;
+      for (int j = 0; j < k; ++j) {
+        uint64_t key = ((avail ? 1ull : 0ull) << 62) | ((uint64_t)ord << 6) | (uint64_t)(63 - e);
+#pragma unroll
+        for (int dl = 1; dl < 16; dl <<= 1) {
+          const uint64_t o = (uint64_t)__shfl_xor((unsigned long long)key, dl, 16);
+          key = o > key ? o : key;
+        }
+        if (e == 63 - (int)(key & 63ull)) {
+          chosen = j;
+          avail = false;
+        }
+      }
+      const bool in_set = k == 1 ? live : chosen >= 0;
+      float zm = in_set ? z : -INFINITY;
+#pragma unroll
+      for (int dl = 1; dl < 16; dl <<= 1) zm = fmaxf(zm, __shfl_xor(zm, dl, 16));
+      const float ex = in_set ? expf(z - zm) : 0.f;
+      float den = ex;
+#pragma unroll
+      for (int dl = 1; dl < 16; dl <<= 1) den += __shfl_xor(den, dl, 16);
+      if (t < T) {
+        if (chosen >= 0) {
+          sel[(size_t)t * k + chosen] = e;
+          gate[(size_t)t * k + chosen] = ex / den;
+        }
+        if (e == 0) inv_out[t] = inv;
+      }
+    }
+  } else if (tid < NTOK) {
     const int tt = tid >> 4, c = tid & 15;
     const int t = t0 + tid;
     float sq = 0.f;
