@@ -7,13 +7,14 @@
 //   MODE 1  y[slot, m]   = act[slot] W_down^T                                    K = d_ff
 //           k = 1: out[token] = bf16(gate * y); k > 1: y kept in fp32.
 //
-// Work unit: (expert, block of 128*RT weight rows, span of at most 160 of the
-// expert's slots).  An expert's slots are cut into the fewest spans of at most
-// five 32-token subtiles, split evenly; the spans of one weight block are
-// adjacent in the unit order, so they run together under one L2 and the block
-// comes from HBM once.
+// Work unit: (expert, block of 128*RT weight rows, span of at most 32*TTM of
+// the expert's slots; TTM = 5 by default).  An expert's slots are cut into the
+// fewest spans of at most TTM 32-token subtiles, split evenly; the spans of
+// one weight block are adjacent in the unit order, so they run together under
+// one L2 and the block comes from HBM once.
 //
-// Workgroup: four waves, one per SIMD, stacked along the weight rows; a wave
+// Workgroup (OCC per CU, 1 by default): four waves, one per SIMD, stacked
+// along the weight rows; a wave
 // owns RT 32-row tiles against the unit's TT token subtiles (RT*TT
 // accumulators of 32x32 fp32).  Both operands are stored as 1 KiB MFMA operand
 // blocks: the weights in the packed bank, the tokens in expert-ordered
@@ -31,7 +32,8 @@
 // Gate/up rows are packed as 32-row tiles of 16 gate rows followed by the 16
 // up rows of the same columns, so the lane that holds gate(f) in accumulator
 // element i holds up(f) in element i + 8 and the SiLU * up epilogue needs no
-// exchange between lanes.
+// exchange between lanes.  The activation tiles go out with non-temporal
+// stores (read back by the down launch, not kept dirty in this XCD's L2).
 //
 // fp8 (e4m3) expert weights: the GEMMs read a bank of the codes' exact bf16
 // values (every e4m3 value is a bf16 value), so the MFMA products are the
