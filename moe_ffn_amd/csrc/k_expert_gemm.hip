@@ -229,7 +229,8 @@ __device__ __forceinline__ void decode_unit(const int* __restrict__ counts,
   }
 }
 
-template <int MODE, int RT, int Q, int TT>
+// SC: fp8 weights (row scales in rsc); bf16 weights compile without them.
+template <int MODE, int RT, int Q, int TT, bool SC>
 __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16_t* __restrict__ wpk,
                                          const uint16_t* __restrict__ src,
                                          const int* __restrict__ gather,
@@ -289,16 +290,21 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
         for (int g = 0; g < 2; ++g) {
           // fp8 weights: per-row dequantisation scales of the gate rows
           // 16*gt + 8g + 4hi .. +3 and of the matching up rows
-          f32x4 sg = {1.f, 1.f, 1.f, 1.f}, su = sg;
-          if (rsc != nullptr) {
+          float gs[4] = {sc, sc, sc, sc}, us[4] = {sc, sc, sc, sc};
+          if constexpr (SC) {
             const float* rs = rsc + (size_t)u.e * 2 * F + 32 * gt + 8 * g + 4 * hi;
-            sg = *reinterpret_cast<const f32x4*>(rs);
-            su = *reinterpret_cast<const f32x4*>(rs + 16);
+            const f32x4 sg = *reinterpret_cast<const f32x4*>(rs);
+            const f32x4 su = *reinterpret_cast<const f32x4*>(rs + 16);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              gs[t] = sc * sg[t];
+              us[t] = sc * su[t];
+            }
           }
           float v4[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t)
-            v4[t] = silu(sc * sg[t] * acc[rt][j][4 * g + t]) * (sc * su[t] * acc[rt][j][4 * g + 8 + t]);
+            v4[t] = silu(gs[t] * acc[rt][j][4 * g + t]) * (us[t] * acc[rt][j][4 * g + 8 + t]);
           u32x2 v;
           v[0] = pack_bf16x2(v4[0], v4[1]);
           v[1] = pack_bf16x2(v4[2], v4[3]);
@@ -317,7 +323,7 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int m = m0 + 8 * q;
-          if (rsc != nullptr) {  // fp8 weights: per-row scales of output rows m .. m+3
+          if constexpr (SC) {  // fp8 weights: per-row scales of output rows m .. m+3
             const f32x4 s4 = *reinterpret_cast<const f32x4*>(rsc + (size_t)u.e * d + m);
 #pragma unroll
             for (int t = 0; t < 4; ++t) acc[rt][j][4 * q + t] *= s4[t];
@@ -341,7 +347,7 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
 
 namespace {
 // run_unit for the unit's subtile count (at most TTM)
-template <int MODE, int RT, int Q, int TTM>
+template <int MODE, int RT, int Q, int TTM, bool SC>
 __device__ __forceinline__ void run_any(const Unit& u, u32x4* lds, const uint16_t* __restrict__ wpk,
                                         const uint16_t* __restrict__ src,
                                         const int* __restrict__ gather,
@@ -351,7 +357,7 @@ __device__ __forceinline__ void run_any(const Unit& u, u32x4* lds, const uint16_
                                         const uint16_t* __restrict__ zrow,
                                         uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
                                         int d, int F) {
-#define MOE_RUN(TT) run_unit<MODE, RT, Q, TT>(u, lds, wpk, src, gather, gate, inv, rsc, k, zrow, dst16, ybuf, d, F)
+#define MOE_RUN(TT) run_unit<MODE, RT, Q, TT, SC>(u, lds, wpk, src, gather, gate, inv, rsc, k, zrow, dst16, ybuf, d, F)
   if constexpr (TTM >= 5) {
     if (u.nsub == 5) { MOE_RUN(5); return; }
   }
@@ -368,7 +374,7 @@ __device__ __forceinline__ void run_any(const Unit& u, u32x4* lds, const uint16_
 }  // namespace
 
 // OCC workgroups per CU; spans of at most TTM subtiles.
-template <int MODE, int RT, int Q, int OCC, int TTM>
+template <int MODE, int RT, int Q, int OCC, int TTM, bool SC>
 __global__ __launch_bounds__(256, OCC) void k_expert_gemm(
     const uint16_t* __restrict__ wpk, const uint16_t* __restrict__ src,
     const int* __restrict__ counts, const int* __restrict__ offsets,
@@ -389,7 +395,7 @@ __global__ __launch_bounds__(256, OCC) void k_expert_gemm(
     Unit u;
     decode_unit<TTM>(counts, offsets, E, nrb, L, u);
     __syncthreads();  // the previous unit's last LDS reads are done everywhere
-    run_any<MODE, RT, Q, TTM>(u, lds, wpk, src, gather, gate, inv, rsc, k, zrow, dst16, ybuf, d, F);
+    run_any<MODE, RT, Q, TTM, SC>(u, lds, wpk, src, gather, gate, inv, rsc, k, zrow, dst16, ybuf, d, F);
   }
 }
 
@@ -397,12 +403,15 @@ namespace {
 template <int MODE, int RT, int Q, int OCC, int TTM>
 hipError_t launch_gemm(const FwdArgs& a) {
   const int grid = (a.num_cu * OCC + 7) / 8 * 8;  // persistent: OCC workgroups per CU
-  return launch(k_expert_gemm<MODE, RT, Q, OCC, TTM>, dim3(grid), dim3(256), a.stream,
+  const float* rsc = MODE == 0 ? a.sgu : a.sd;
+  auto kern = rsc != nullptr ? k_expert_gemm<MODE, RT, Q, OCC, TTM, true>
+                             : k_expert_gemm<MODE, RT, Q, OCC, TTM, false>;
+  return launch(kern, dim3(grid), dim3(256), a.stream,
                 a.ev[MODE == 0 ? kSlotExpertsA : kSlotExpertsB],
                 (const uint16_t*)(MODE == 0 ? a.wgu : a.wd),
                 (const uint16_t*)(MODE == 0 ? a.xt : a.act), (const int*)a.counts,
                 (const int*)a.offsets, (const int*)a.gather, (const float*)a.gate,
-                (const float*)a.inv, MODE == 0 ? a.sgu : a.sd, a.dim.k, a.dim.E,
+                (const float*)a.inv, rsc, a.dim.k, a.dim.E,
                 (const uint16_t*)a.zrow,
                 (uint16_t*)(MODE == 0 ? a.act : a.out), a.ybuf, a.dim.d, a.dim.F);
 }
