@@ -3,7 +3,8 @@
 // Expert FFN y = W_down (SiLU(W_gate x) * (W_up x)) per routed assignment
 // (SwiGLU: GLU variants paper on the ZONOS2 report's "Builds on" list; 16
 // experts per layer, digest item 5).  Two launches:
-//   MODE 0  act[slot, f] = bf16( SiLU(inv * x W_gate^T) * (inv * x W_up^T) )   K = d_model
+//   MODE 0  act[slot, f] = bf16( SiLU(x W_gate^T) * (x W_up^T) )   K = d_model
+//           (x: the normalised rows, RMSNorm applied by the gather)
 //   MODE 1  y[slot, m]   = act[slot] W_down^T                                    K = d_ff
 //           k = 1: out[token] = bf16(gate * y); k > 1: y kept in fp32.
 //
@@ -235,7 +236,6 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
                                          const uint16_t* __restrict__ src,
                                          const int* __restrict__ gather,
                                          const float* __restrict__ gate,
-                                         const float* __restrict__ inv,
                                          const float* __restrict__ rsc, int k,
                                          const uint16_t* __restrict__ zrow,
                                          uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
@@ -281,7 +281,6 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
       // activations in the down projection's operand tiles: subtile sub0 + j,
       // k-step gt (16 columns of d_ff per gate/up tile); each wave store of a
       // (tile, subtile) pair fills one whole 1 KiB block
-      const float sc = r < u.nrows ? inv[gather[u.slot0 + r]] : 0.f;  // RMSNorm scale
       uint16_t* blk = dst16 + (size_t)(u.sub0 + j) * (F / kKStep) * kBlockElems;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
@@ -290,21 +289,19 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
         for (int g = 0; g < 2; ++g) {
           // fp8 weights: per-row dequantisation scales of the gate rows
           // 16*gt + 8g + 4hi .. +3 and of the matching up rows
-          float gs[4] = {sc, sc, sc, sc}, us[4] = {sc, sc, sc, sc};
+          float v4[4];
           if constexpr (SC) {
             const float* rs = rsc + (size_t)u.e * 2 * F + 32 * gt + 8 * g + 4 * hi;
             const f32x4 sg = *reinterpret_cast<const f32x4*>(rs);
             const f32x4 su = *reinterpret_cast<const f32x4*>(rs + 16);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              gs[t] = sc * sg[t];
-              us[t] = sc * su[t];
-            }
-          }
-          float v4[4];
+            for (int t = 0; t < 4; ++t)
+              v4[t] = silu(sg[t] * acc[rt][j][4 * g + t]) * (su[t] * acc[rt][j][4 * g + 8 + t]);
+          } else {
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            v4[t] = silu(gs[t] * acc[rt][j][4 * g + t]) * (us[t] * acc[rt][j][4 * g + 8 + t]);
+            for (int t = 0; t < 4; ++t)
+              v4[t] = silu(acc[rt][j][4 * g + t]) * acc[rt][j][4 * g + 8 + t];
+          }
           u32x2 v;
           v[0] = pack_bf16x2(v4[0], v4[1]);
           v[1] = pack_bf16x2(v4[2], v4[3]);
@@ -352,12 +349,11 @@ __device__ __forceinline__ void run_any(const Unit& u, u32x4* lds, const uint16_
                                         const uint16_t* __restrict__ src,
                                         const int* __restrict__ gather,
                                         const float* __restrict__ gate,
-                                        const float* __restrict__ inv,
                                         const float* __restrict__ rsc, int k,
                                         const uint16_t* __restrict__ zrow,
                                         uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
                                         int d, int F) {
-#define MOE_RUN(TT) run_unit<MODE, RT, Q, TT, SC>(u, lds, wpk, src, gather, gate, inv, rsc, k, zrow, dst16, ybuf, d, F)
+#define MOE_RUN(TT) run_unit<MODE, RT, Q, TT, SC>(u, lds, wpk, src, gather, gate, rsc, k, zrow, dst16, ybuf, d, F)
   if constexpr (TTM >= 5) {
     if (u.nsub == 5) { MOE_RUN(5); return; }
   }
@@ -379,7 +375,7 @@ __global__ __launch_bounds__(256, OCC) void k_expert_gemm(
     const uint16_t* __restrict__ wpk, const uint16_t* __restrict__ src,
     const int* __restrict__ counts, const int* __restrict__ offsets,
     const int* __restrict__ gather, const float* __restrict__ gate,
-    const float* __restrict__ inv, const float* __restrict__ rsc, int k, int E,
+    const float* __restrict__ rsc, int k, int E,
     const uint16_t* __restrict__ zrow, uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
     int d, int F) {
   __shared__ u32x4 lds[kBStages * kBStageEnt];
@@ -395,7 +391,7 @@ __global__ __launch_bounds__(256, OCC) void k_expert_gemm(
     Unit u;
     decode_unit<TTM>(counts, offsets, E, nrb, L, u);
     __syncthreads();  // the previous unit's last LDS reads are done everywhere
-    run_any<MODE, RT, Q, TTM, SC>(u, lds, wpk, src, gather, gate, inv, rsc, k, zrow, dst16, ybuf, d, F);
+    run_any<MODE, RT, Q, TTM, SC>(u, lds, wpk, src, gather, gate, rsc, k, zrow, dst16, ybuf, d, F);
   }
 }
 
@@ -411,7 +407,7 @@ hipError_t launch_gemm(const FwdArgs& a) {
                 (const uint16_t*)(MODE == 0 ? a.wgu : a.wd),
                 (const uint16_t*)(MODE == 0 ? a.xt : a.act), (const int*)a.counts,
                 (const int*)a.offsets, (const int*)a.gather, (const float*)a.gate,
-                (const float*)a.inv, rsc, a.dim.k, a.dim.E,
+                rsc, a.dim.k, a.dim.E,
                 (const uint16_t*)a.zrow,
                 (uint16_t*)(MODE == 0 ? a.act : a.out), a.ybuf, a.dim.d, a.dim.F);
 }

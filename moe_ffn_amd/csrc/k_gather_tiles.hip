@@ -3,9 +3,10 @@
 //
 // The dispatch step (telknet.cc article, section 2.1: each token's row goes to
 // the experts TopK chose for it) made explicit as a copy: slot p of expert e
-// holds the row x' = bf16(g * h) of token gather[p] (the RMSNorm gain applied
-// here, on the way from the hidden row to the tile, the same rounding the
-// router uses; 1/rms multiplies the GEMM's fp32 accumulators).  Rows are stored in
+// holds the normalised row x = bf16(inv_rms * (g * h)) of token gather[p]:
+// RMSNorm is applied here, on the way from the hidden row to the tile (g * h
+// is exact in fp32, times the router's inv_rms of the token, rounded once to
+// fp32 and once to bf16), so the grouped GEMM's epilogue has no per-row scale.  Rows are stored in
 // 32-slot subtiles, each expert's slots padded to a whole number of subtiles
 // (the expert owning ceil(count / 32) subtiles from psub[e], the running sum
 // of those numbers), and every subtile in the B-operand order of
@@ -24,6 +25,7 @@ namespace moe {
 
 __global__ __launch_bounds__(256) void k_gather_tiles(const uint16_t* __restrict__ hidden,
                                                       const uint16_t* __restrict__ gain,
+                                                      const float* __restrict__ inv,
                                                       const int* __restrict__ counts,
                                                       const int* __restrict__ offsets,
                                                       const int* __restrict__ gather, int E, int d,
@@ -42,21 +44,27 @@ __global__ __launch_bounds__(256) void k_gather_tiles(const uint16_t* __restrict
   const int lane = threadIdx.x & 63;
   uint16_t* dst = xt + (size_t)P * (d / kKStep) * kBlockElems;
   u32x4 v[4];
+  float s[4];
   const u32x4 gv = ldg16(gain + g * 64 + (lane & 7) * 8);  // chunk c = lane & 7 in every q
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int idx = q * 64 + lane;
     const int rr = idx >> 3, c = idx & 7;  // row of the subtile, 16-byte chunk of the 128 bytes
     v[q] = u32x4{0u, 0u, 0u, 0u};
-    if (r0 + rr < cnt) v[q] = ldg16(hidden + (size_t)gather[off + r0 + rr] * d + g * 64 + c * 8);
+    s[q] = 0.f;
+    if (r0 + rr < cnt) {
+      const int tok = gather[off + r0 + rr];
+      v[q] = ldg16(hidden + (size_t)tok * d + g * 64 + c * 8);
+      s[q] = inv[tok];
+    }
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {  // x' = bf16(g * h); padding rows stay +0
+  for (int q = 0; q < 4; ++q) {  // x = bf16(inv * (g * h)); padding rows stay +0
     const bool ok = r0 + ((q * 64 + lane) >> 3) < cnt;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t x = pack_bf16x2(bf16_lo(gv[i]) * bf16_lo(v[q][i]),
-                                     bf16_hi(gv[i]) * bf16_hi(v[q][i]));
+      const uint32_t x = pack_bf16x2(s[q] * (bf16_lo(gv[i]) * bf16_lo(v[q][i])),
+                                     s[q] * (bf16_hi(gv[i]) * bf16_hi(v[q][i])));
       v[q][i] = ok ? x : 0u;
     }
   }
@@ -75,7 +83,8 @@ int max_subtiles(int n, int E) { return (n + 31 * E) / 32; }
 hipError_t launch_gather_tiles(const FwdArgs& a) {
   const int waves = max_subtiles(a.n, a.dim.E) * (a.dim.d / 64);
   return launch(k_gather_tiles, dim3((waves + 3) / 4), dim3(256), a.stream, a.ev[kSlotGather],
-                (const uint16_t*)a.hidden, (const uint16_t*)a.gain16, (const int*)a.counts,
+                (const uint16_t*)a.hidden, (const uint16_t*)a.gain16, (const float*)a.inv,
+                (const int*)a.counts,
                 (const int*)a.offsets,
                 (const int*)a.gather, a.dim.E, a.dim.d, (uint16_t*)a.xt);
 }
