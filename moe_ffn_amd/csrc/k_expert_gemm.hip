@@ -154,11 +154,14 @@ __device__ __forceinline__ void bstage(const Ctx<RT, TT>& c, u32x4* lds, int& bu
   buf = b1;
 }
 
-// Q: depth of the weight queue in k-steps (kBK, or a multiple of 2 * kBK that
-// divides the k-steps of the reduction).
+// Q: depth of the weight queue in k-steps: kBK, 2 kBK or 4 kBK, so that one
+// loop iteration (two token stages, four at Q = 4 kBK) returns the queue to
+// its first slot; the token stages of the reduction are a multiple of that.
 template <int RT, int TT, int Q>
 __device__ __forceinline__ void mainloop(const Ctx<RT, TT>& c, u32x4* lds, f32x16 (&acc)[RT][TT]) {
   constexpr int NP = Q / kBK < 2 ? 2 : Q / kBK;  // token stages per loop iteration
+  static_assert(NP == 2 || NP == 4, "the loop body holds two or four token stages");
+  static_assert(Q == kBK || Q == 2 * kBK || Q == 4 * kBK, "queue depth must match the loop body");
   const int nsb = c.ksteps / kBK;                // token stages (a multiple of NP)
   u32x4 qa[Q][RT], rb0[TT], rb1[TT], bc[TT];
   load_b(c, 0, nsb, rb0);
