@@ -8,11 +8,12 @@
 //   MODE 1  y[slot, m]   = act[slot] W_down^T                                    K = d_ff
 //           k = 1: out[token] = bf16(gate * y); k > 1: y kept in fp32.
 //
-// Work unit: (expert, block of 128*RT weight rows, span of at most 32*TTM of
-// the expert's slots; TTM = 5 by default).  An expert's slots are cut into the
-// fewest spans of at most TTM 32-token subtiles, split evenly; the spans of
-// one weight block are adjacent in the unit order, so they run together under
-// one L2 and the block comes from HBM once.
+// Work unit: (expert, block of 128*RT weight rows, span of at most 32*cap of
+// the expert's slots; cap <= TTM, chosen per launch on the host, TTM = 5 for
+// gate/up and 6 for down).  An expert's slots are cut into the fewest spans of
+// at most cap 32-token subtiles, split evenly; the spans of one weight block
+// are adjacent in the unit order, so they run together under one L2 and the
+// block comes from HBM once.
 //
 // Workgroup (OCC per CU, 1 by default): four waves, one per SIMD, stacked
 // along the weight rows; a wave
@@ -23,9 +24,9 @@
 // activations, which the gate/up epilogue writes in that layout), so every
 // wave-wide load reads one contiguous KiB.
 //  * Weights go straight from HBM into each wave's operand registers through a
-//    queue Q k-steps deep (8 at RT = 3: 96 KiB in flight per CU; 16 at
-//    RT = 2: 128 KiB): the weight stream is what needs latency cover, and a
-//    register queue costs no LDS.
+//    queue Q k-steps deep (8: 96 KiB in flight per CU at RT = 3, 64 KiB at
+//    RT = 2): the weight stream is what needs latency cover, and a register
+//    queue costs no LDS.
 //  * Tokens, shared by the four waves, go through three LDS stages of 64 k
 //    (two staged in registers in flight); one barrier per stage, passed with
 //    the next stage's first operands already read.
@@ -41,6 +42,11 @@
 // codes' own; the per-row dequantisation scales multiply the fp32
 // accumulators in the epilogue (rsc: per gate/up row, or per output row of
 // the down projection; null for bf16 weights).
+#include <algorithm>
+#include <cstdint>
+#include <unordered_map>
+#include <vector>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -48,10 +54,11 @@ namespace moe {
 
 namespace {
 constexpr int kSub = 32;      // tokens per MFMA subtile
-constexpr int kTTMax = 5;     // token subtiles per work unit, at most
 constexpr int kBK = 4;        // k-steps (of 16) per token stage
 constexpr int kBStages = 3;   // LDS token stages
-constexpr int kBStageEnt = kTTMax * kBK * 64;  // 16-byte LDS entries per token stage
+// 16-byte LDS entries of one token stage of a unit with TT subtiles
+template <int TT>
+constexpr int stage_ent() { return TT * kBK * 64; }
 
 template <int RT>
 struct Geo {
@@ -119,17 +126,18 @@ __device__ __forceinline__ void bstage(const Ctx<RT, TT>& c, u32x4* lds, int& bu
   constexpr int NM = RT * TT;
   const int b1 = buf == kBStages - 1 ? 0 : buf + 1;
   const int b2 = b1 == kBStages - 1 ? 0 : b1 + 1;
-  const u32x4* cur = lds + buf * kBStageEnt;
+  constexpr int SE = stage_ent<TT>();
+  const u32x4* cur = lds + buf * SE;
 #pragma unroll
   for (int i = 0; i < kBK; ++i) {
     const int slot = (P * kBK + i) % Q;  // weight queue slot of this k-step
     u32x4 bn[TT];
     if (i < kBK - 1) read_b<TT>(cur, i + 1, c.lane, bn);
-    else read_b<TT>(lds + b1 * kBStageEnt, 0, c.lane, bn);
+    else read_b<TT>(lds + b1 * SE, 0, c.lane, bn);
     mac(qa[slot], bc, acc);
     load_a(c, (kb * kBK + i) + Q, qa[slot]);
     if (i == 1) {
-      store_b(c, lds + b2 * kBStageEnt, rb);
+      store_b(c, lds + b2 * SE, rb);
       load_b(c, kb + 4, nsb, rb);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
@@ -168,7 +176,7 @@ __device__ __forceinline__ void mainloop(const Ctx<RT, TT>& c, u32x4* lds, f32x1
   load_b(c, 1, nsb, rb1);
   store_b(c, lds, rb0);
   load_b(c, 2, nsb, rb0);
-  store_b(c, lds + kBStageEnt, rb1);
+  store_b(c, lds + stage_ent<TT>(), rb1);
   load_b(c, 3, nsb, rb1);
 #pragma unroll
   for (int i = 0; i < Q; ++i) load_a(c, i, qa[i]);
@@ -196,41 +204,67 @@ struct Unit {
   int e, rb, slot0, nrows, nsub;
   int sub0;  // first subtile of the unit in the padded, expert-ordered subtile list
 };
-template <int TTM>
-__device__ __forceinline__ int span_count(int cnt) {
-  const int nsub = (cnt + kSub - 1) / kSub;
-  return (nsub + TTM - 1) / TTM;
-}
-template <int TTM>
-__device__ __forceinline__ int unit_total(const int* __restrict__ counts, int E, int nrb) {
-  int U = 0;
-  for (int e = 0; e < E; ++e) U += nrb * span_count<TTM>(counts[e]);
-  return U;
-}
-template <int TTM>
-__device__ __forceinline__ void decode_unit(const int* __restrict__ counts,
-                                            const int* __restrict__ offsets, int E, int nrb, int L,
-                                            Unit& u) {
-  int base = 0, psub = 0;
-  for (int e = 0; e < E; ++e) {
-    const int cnt = counts[e];
-    const int ns = span_count<TTM>(cnt);
-    if (L < base + nrb * ns) {
-      const int r = L - base;
-      const int sp = r % ns;
-      const int nsub = (cnt + kSub - 1) / kSub;
-      const int s0 = sp * nsub / ns, s1 = (sp + 1) * nsub / ns;
-      u.e = e;
-      u.rb = r / ns;
-      u.slot0 = offsets[e] + s0 * kSub;
-      u.nrows = min(cnt, s1 * kSub) - s0 * kSub;
-      u.nsub = s1 - s0;
-      u.sub0 = psub + s0;
-      return;
-    }
-    base += nrb * ns;
-    psub += (cnt + kSub - 1) / kSub;
+// The launch's expert table in LDS (E <= 64), built once per workgroup so
+// that decoding a unit costs a few LDS reads and one ballot instead of a
+// dependent scan over the experts in global memory.
+struct ExpTab {
+  int cnt[64], off[64];  // assignments and first slot of each expert
+  int ns[64];            // 32-token subtiles of each expert
+  int psub[64];          // subtiles of the experts before it
+  int sp[64];            // spans of each expert under the launch's cap
+  int ubase[64];         // first unit of each expert
+};
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
   }
+  return v;
+}
+
+// Fill the table for span cap `cap` and return the launch's unit count.
+__device__ __forceinline__ int build_table(ExpTab& tab, const int* __restrict__ counts,
+                                           const int* __restrict__ offsets, int E, int nrb,
+                                           int cap) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int c = tid < E ? counts[tid] : 0;
+    const int ns = (c + kSub - 1) / kSub;
+    tab.cnt[tid] = c;
+    tab.off[tid] = tid < E ? offsets[tid] : 0;
+    tab.ns[tid] = ns;
+    tab.psub[tid] = wave_incl_scan(ns) - ns;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int n = nrb * ((tab.ns[tid] + cap - 1) / cap);  // 0 past the last expert
+    tab.sp[tid] = n / nrb;
+    tab.ubase[tid] = wave_incl_scan(n) - n;
+  }
+  __syncthreads();
+  return tab.ubase[63] + nrb * tab.sp[63];
+}
+
+// Unit L: the one lane whose expert's unit range holds L names the expert.
+__device__ __forceinline__ void decode_unit(const ExpTab& tab, int nrb, int L, Unit& u) {
+  const int lane = threadIdx.x & 63;
+  const int lo = tab.ubase[lane];
+  const unsigned long long m = __ballot(L >= lo && L < lo + nrb * tab.sp[lane]);
+  const int e = __builtin_amdgcn_readfirstlane(__ffsll((long long)m) - 1);
+  const int ns = __builtin_amdgcn_readfirstlane(tab.sp[e]);
+  const int nsub = __builtin_amdgcn_readfirstlane(tab.ns[e]);
+  const int r = L - __builtin_amdgcn_readfirstlane(tab.ubase[e]);
+  const int sp = r % ns;
+  const int s0 = sp * nsub / ns, s1 = (sp + 1) * nsub / ns;
+  u.e = e;
+  u.rb = r / ns;
+  u.slot0 = __builtin_amdgcn_readfirstlane(tab.off[e]) + s0 * kSub;
+  u.nrows = min(__builtin_amdgcn_readfirstlane(tab.cnt[e]), s1 * kSub) - s0 * kSub;
+  u.nsub = s1 - s0;
+  u.sub0 = __builtin_amdgcn_readfirstlane(tab.psub[e]) + s0;
 }
 
 // SC: fp8 weights (row scales in rsc); bf16 weights compile without them.
@@ -347,7 +381,7 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
 
 namespace {
 // run_unit for the unit's subtile count (at most TTM)
-template <int MODE, int RT, int Q, int TTM, bool SC>
+template <int MODE, int RT, int Q, int TT, bool SC>
 __device__ __forceinline__ void run_any(const Unit& u, u32x4* lds, const uint16_t* __restrict__ wpk,
                                         const uint16_t* __restrict__ src,
                                         const int* __restrict__ gather,
@@ -356,19 +390,14 @@ __device__ __forceinline__ void run_any(const Unit& u, u32x4* lds, const uint16_
                                         const uint16_t* __restrict__ zrow,
                                         uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
                                         int d, int F) {
-#define MOE_RUN(TT) run_unit<MODE, RT, Q, TT, SC>(u, lds, wpk, src, gather, gate, rsc, k, zrow, dst16, ybuf, d, F)
-  if constexpr (TTM >= 5) {
-    if (u.nsub == 5) { MOE_RUN(5); return; }
+  if constexpr (TT > 1) {
+    if (u.nsub != TT) {
+      run_any<MODE, RT, Q, TT - 1, SC>(u, lds, wpk, src, gather, gate, rsc, k, zrow, dst16, ybuf,
+                                       d, F);
+      return;
+    }
   }
-  if constexpr (TTM >= 4) {
-    if (u.nsub == 4) { MOE_RUN(4); return; }
-  }
-  if constexpr (TTM >= 3) {
-    if (u.nsub == 3) { MOE_RUN(3); return; }
-  }
-  if (u.nsub == 2) MOE_RUN(2);
-  else MOE_RUN(1);
-#undef MOE_RUN
+  run_unit<MODE, RT, Q, TT, SC>(u, lds, wpk, src, gather, gate, rsc, k, zrow, dst16, ybuf, d, F);
 }
 }  // namespace
 
@@ -378,12 +407,14 @@ __global__ __launch_bounds__(256, OCC) void k_expert_gemm(
     const uint16_t* __restrict__ wpk, const uint16_t* __restrict__ src,
     const int* __restrict__ counts, const int* __restrict__ offsets,
     const int* __restrict__ gather, const float* __restrict__ gate,
-    const float* __restrict__ rsc, int k, int E,
+    const float* __restrict__ rsc, int k, int E, int cap,
     const uint16_t* __restrict__ zrow, uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
     int d, int F) {
-  __shared__ u32x4 lds[kBStages * kBStageEnt];
+  static_assert(TTM >= 1 && TTM <= 8, "token subtiles per unit");
+  __shared__ u32x4 lds[kBStages * stage_ent<TTM>()];
   const int nrb = (MODE == 0 ? 2 * F : d) / Geo<RT>::kRows;
-  const int U = unit_total<TTM>(counts, E, nrb);
+  __shared__ ExpTab tab;
+  const int U = build_table(tab, counts, offsets, E, nrb, cap);
   const int per = (U + 7) >> 3;          // units per XCD range
   const int nw = gridDim.x >> 3;         // workgroups per XCD (the grid is a multiple of 8)
   const int x = blockIdx.x & 7, w = blockIdx.x >> 3;
@@ -392,16 +423,68 @@ __global__ __launch_bounds__(256, OCC) void k_expert_gemm(
     const int L = lo + ((r & 1) ? (r + 1) * nw - 1 - w : r * nw + w);
     if (L >= hi) continue;
     Unit u;
-    decode_unit<TTM>(counts, offsets, E, nrb, L, u);
+    decode_unit(tab, nrb, L, u);
     __syncthreads();  // the previous unit's last LDS reads are done everywhere
     run_any<MODE, RT, Q, TTM, SC>(u, lds, wpk, src, gather, gate, rsc, k, zrow, dst16, ybuf, d, F);
   }
 }
 
 namespace {
+// Span cap of a launch: the most token subtiles a unit holds (1..TTM).
+// Fewer, larger units save per-unit cost (the weight stream's start, the
+// epilogue), but the dealing can leave the grid's last round mostly idle.
+// Each cap from TTM - 2 to TTM is priced on the host by replaying the
+// kernel's dealing (ranges per XCD, snake order) for n assignments spread
+// evenly over the experts, a unit costing 2 + its token subtiles (a fit to
+// measured unit times of both GEMMs: a unit's fixed cost is about that of
+// two subtiles of MFMA work); the busiest workgroup's total decides, ties
+// to the larger cap.  The counts themselves are on the device; pricing them
+// there took longer than the choice saved.  Results are cached per shape.
+int span_cap(int n, int E, int nrb, int grid, int TTM) {
+  static thread_local std::unordered_map<uint64_t, int> memo;
+  const uint64_t key = (uint64_t)n << 32 ^ (uint64_t)E << 24 ^ (uint64_t)nrb << 12 ^
+                       (uint64_t)grid << 4 ^ (uint64_t)TTM;
+  if (auto it = memo.find(key); it != memo.end()) return it->second;
+  std::vector<int> ns(E);
+  for (int e = 0; e < E; ++e) ns[e] = (n / E + (e < n % E ? 1 : 0) + kSub - 1) / kSub;
+  const int nw = grid / 8;
+  int best = TTM;
+  long long best_cost = -1;
+  std::vector<uint8_t> cost;
+  for (int t = TTM; t >= 1 && t >= TTM - 2; --t) {
+    cost.clear();
+    for (int e = 0; e < E; ++e) {
+      const int sp = (ns[e] + t - 1) / t;
+      for (int rb = 0; rb < nrb; ++rb)
+        for (int q = 0; q < sp; ++q)
+          cost.push_back((uint8_t)(2 + (q + 1) * ns[e] / sp - q * ns[e] / sp));
+    }
+    const int U = (int)cost.size(), per = (U + 7) / 8;
+    long long mx = 0;
+    for (int b = 0; b < grid; ++b) {
+      const int x = b & 7, w = b >> 3, lo = x * per, hi = std::min(U, lo + per);
+      long long c = 0;
+      for (int r = 0; r * nw < per; ++r) {
+        const int L = lo + ((r & 1) ? (r + 1) * nw - 1 - w : r * nw + w);
+        if (L < hi) c += cost[L];
+      }
+      mx = std::max(mx, c);
+    }
+    if (best_cost < 0 || mx < best_cost) {
+      best_cost = mx;
+      best = t;
+    }
+  }
+  if (memo.size() > 4096) memo.clear();
+  memo.emplace(key, best);
+  return best;
+}
+
 template <int MODE, int RT, int Q, int OCC, int TTM>
 hipError_t launch_gemm(const FwdArgs& a) {
   const int grid = (a.num_cu * OCC + 7) / 8 * 8;  // persistent: OCC workgroups per CU
+  const int nrb = (MODE == 0 ? 2 * a.dim.F : a.dim.d) / Geo<RT>::kRows;
+  const int cap = span_cap(a.n, a.dim.E, nrb, grid, TTM);
   const float* rsc = MODE == 0 ? a.sgu : a.sd;
   auto kern = rsc != nullptr ? k_expert_gemm<MODE, RT, Q, OCC, TTM, true>
                              : k_expert_gemm<MODE, RT, Q, OCC, TTM, false>;
@@ -410,23 +493,25 @@ hipError_t launch_gemm(const FwdArgs& a) {
                 (const uint16_t*)(MODE == 0 ? a.wgu : a.wd),
                 (const uint16_t*)(MODE == 0 ? a.xt : a.act), (const int*)a.counts,
                 (const int*)a.offsets, (const int*)a.gather, (const float*)a.gate,
-                rsc, a.dim.k, a.dim.E,
+                rsc, a.dim.k, a.dim.E, cap,
                 (const uint16_t*)a.zrow,
                 (uint16_t*)(MODE == 0 ? a.act : a.out), a.ybuf, a.dim.d, a.dim.F);
 }
 }  // namespace
 
 // Gate/up on 384-row blocks (192 columns of d_ff) with an 8-k-step weight
-// queue where 2 * d_ff divides into them; the down projection, and gate/up
-// otherwise, on 256-row blocks with a 16-k-step queue where the reduction
-// divides into it (else 8).  On the prefill workloads the 384-row gate/up
-// units are faster (fewer re-reads of the token tiles per weight byte); the
-// deeper queue that fits the 256-row units' registers did not make up for it.
+// queue and spans of up to 5 subtiles where 2 * d_ff divides into them, else
+// on 256-row blocks; the down projection on 256-row blocks, an 8-k-step queue
+// and spans of up to 6 subtiles (the registers' limit at that queue; a
+// 16-k-step queue at 5 subtiles times the same).  On the prefill workloads the
+// 384-row gate/up units are faster (fewer re-reads of the token tiles per
+// weight byte); the deeper queue that fits the 256-row units' registers did
+// not make up for it.
 #ifndef MOE_GU_CFG
 #define MOE_GU_CFG 3, 8, 1, 5   // RT, Q, OCC, TTM of the gate/up GEMM (2 * d_ff % 384 == 0)
 #endif
 #ifndef MOE_DN_CFG
-#define MOE_DN_CFG 2, 16, 1, 5  // of the down GEMM (d_ff / 16 % 16 == 0)
+#define MOE_DN_CFG 2, 8, 1, 6   // of the down GEMM
 #endif
 namespace {
 template <int RT, int Q, int OCC, int TTM>
@@ -436,12 +521,12 @@ struct Cfg {
 }  // namespace
 
 hipError_t launch_experts_tile(const FwdArgs& a) {
-  const int ksd = a.dim.d / kKStep, ksf = a.dim.F / kKStep;
+  const int ksd = a.dim.d / kKStep;
   hipError_t err;
   if ((2 * a.dim.F) % Geo<Cfg<MOE_GU_CFG>::kRT>::kRows == 0) err = launch_gemm<0, MOE_GU_CFG>(a);
   else err = ksd % 16 == 0 ? launch_gemm<0, 2, 16, 1, 5>(a) : launch_gemm<0, 2, 8, 1, 5>(a);
   if (err != hipSuccess) return err;
-  return ksf % 16 == 0 ? launch_gemm<1, MOE_DN_CFG>(a) : launch_gemm<1, 2, 8, 1, 5>(a);
+  return launch_gemm<1, MOE_DN_CFG>(a);  // d_ff % 128 == 0: the k-steps fill whole loop bodies
 }
 
 }  // namespace moe
