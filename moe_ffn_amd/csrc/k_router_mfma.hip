@@ -14,14 +14,12 @@
 // therefore two bf16 MFMAs with fp32 accumulation: fp32-router precision at
 // matrix-core speed.  z = inv_rms * z_raw with inv_rms = 1/sqrt(mean(h^2)+eps).
 //
-// Outputs: inv_rms[T], sel[T,k], gate[T,k] and, with WX, xg = bf16(g * h)
-// for the experts (hi itself; inv_rms is applied to the experts' fp32
-// accumulators instead of to the activations).  The prefill path leaves xg
-// out: its gather kernel forms the same bf16(g * h) from the hidden rows it
-// copies, which saves the T*d*2-byte write and read of xg.
+// Outputs: inv_rms[T], sel[T,k], gate[T,k].  The normalised expert inputs
+// are formed by the gather kernel from the hidden rows it copies (with this
+// kernel's inv_rms), which saves writing and re-reading T*d*2 bytes here.
 //
-// The kernel moves T*d*2 bytes in and the same out, so it is sized for
-// memory-level parallelism: a workgroup owns 16*TT tokens (TT = 1; MFMA 16x16x32:
+// The kernel reads T*d*2 bytes, so it is sized for memory-level
+// parallelism: a workgroup owns 16*TT tokens (TT = 1; MFMA 16x16x32:
 // A = 16 router rows per tile, NA tiles; B = 16 tokens per tile, TT tiles),
 // its NW waves split the reduction axis into NW slices, and each wave issues
 // the loads of up to kRBatch k-steps at once.  One wave-wide token load reads
@@ -47,14 +45,16 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(const u32x4& a, const u32x4& b, c
 }
 }  // namespace
 
-template <int NA, int TT, int NW, bool WX>
+template <int NA, int TT, int NW>
 __global__ __launch_bounds__(NW * 64) void k_router_mfma(
     const uint16_t* __restrict__ hidden, int T, int d, const uint16_t* __restrict__ wr,
     const uint16_t* __restrict__ gain, const float* __restrict__ bias, int E, int k, float eps,
-    const uint16_t* __restrict__ zrow, uint16_t* __restrict__ sink, uint16_t* __restrict__ xg,
-    float* __restrict__ inv_out, int* __restrict__ sel, float* __restrict__ gate) {
+    const uint16_t* __restrict__ zrow, float* __restrict__ inv_out, int* __restrict__ sel,
+    float* __restrict__ gate) {
   constexpr int NTOK = 16 * TT;
   constexpr int EPAD = 16 * NA;
+  static_assert(EPAD != 16 || NTOK != 16 || NW * 64 >= 16 * NTOK,
+                "the 16-expert finish takes 16 lanes per token");
   __shared__ float red[NW][TT][NA][4][64];
   __shared__ float ssr[NW][TT][64];
   __shared__ float zs[NTOK][EPAD + 1];
@@ -72,13 +72,10 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
     ap[a] = (e < E ? wr + (size_t)e * d : zrow) + kgrp + k0;
   }
   const uint16_t* hp[TT];
-  uint16_t* xp[TT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) {
     const int t = t0 + tt * 16 + (lane & 15);
-    const bool valid = t < T;
-    hp[tt] = (valid ? hidden + (size_t)t * d : zrow) + kgrp + k0;
-    xp[tt] = (valid ? xg + (size_t)t * d : sink) + kgrp + k0;
+    hp[tt] = (t < T ? hidden + (size_t)t * d : zrow) + kgrp + k0;
   }
   const uint16_t* gp = gain + kgrp + k0;
 
@@ -92,7 +89,7 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
   }
 
   // one k-step: x' = g*h split into exact bf16 hi + lo, two MFMAs per tile pair
-  auto step = [&](const u32x4& gv, const u32x4 (&av)[NA], const u32x4 (&hv)[TT], int ko) {
+  auto step = [&](const u32x4& gv, const u32x4 (&av)[NA], const u32x4 (&hv)[TT]) {
     float g[8];
     unpack8(gv, g);
 #pragma unroll
@@ -109,7 +106,6 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
         bhi[i] = hi;
         blo[i] = pack_bf16x2(x0 - bf16_lo(hi), x1 - bf16_hi(hi));
       }
-      if constexpr (WX) stg16(xp[tt] + ko, bhi);
 #pragma unroll
       for (int a = 0; a < NA; ++a) {
         acc[tt][a] = mfma_16x16x32(av[a], bhi, acc[tt][a]);
@@ -132,7 +128,7 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the whole batch of loads in flight together
 #pragma unroll
-    for (int b = 0; b < kRBatch; ++b) step(gv[b], av[b], hv[b], (s + b) * kRK);
+    for (int b = 0; b < kRBatch; ++b) step(gv[b], av[b], hv[b]);
   }
   for (; s < kper; ++s) {
     const int ko = s * kRK;
@@ -141,7 +137,7 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
     for (int tt = 0; tt < TT; ++tt) hv[tt] = ldg16(hp[tt] + ko);
 #pragma unroll
     for (int a = 0; a < NA; ++a) av[a] = ldg16(ap[a] + ko);
-    step(ldg16(gp + ko), av, hv, ko);
+    step(ldg16(gp + ko), av, hv);
   }
 
 #pragma unroll
@@ -268,16 +264,18 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
 }
 
 namespace {
+// Four waves, one per SIMD, each owning a quarter of d_model: at 16384 tokens
+// eight waves (each with one batch of loads) took 28.3 us and four 22.6 us,
+// the same at 4096 tokens.
 template <int NA, int TT>
 hipError_t go(const FwdArgs& a) {
-  constexpr int NW = 8;
+  constexpr int NW = 4;
   if (a.dim.d % (kRK * NW) != 0) return hipErrorInvalidValue;
   const int grid = (a.T + 16 * TT - 1) / (16 * TT);
-  return launch(k_router_mfma<NA, TT, NW, false>, dim3(grid), dim3(NW * 64), a.stream,
+  return launch(k_router_mfma<NA, TT, NW>, dim3(grid), dim3(NW * 64), a.stream,
                 a.ev[kSlotNormRouter], (const uint16_t*)a.hidden, a.T, a.dim.d,
                 (const uint16_t*)a.wr16, (const uint16_t*)a.gain16, (const float*)a.bias, a.dim.E,
-                a.dim.k, a.dim.eps, (const uint16_t*)a.zrow, (uint16_t*)a.sink,
-                (uint16_t*)a.xn, a.inv, a.sel, a.gate);
+                a.dim.k, a.dim.eps, (const uint16_t*)a.zrow, a.inv, a.sel, a.gate);
 }
 }  // namespace
 
