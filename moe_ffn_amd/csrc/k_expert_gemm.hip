@@ -347,33 +347,69 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
         }
       }
     } else {
-      if (r >= u.nrows) continue;
-      const int slot = u.slot0 + r;
-      const int tok = k == 1 ? gather[slot] : 0;
-      const float gw = k == 1 ? gate[tok] : 0.f;
+      // Output rows leave through LDS as whole row pieces: the wave's 64
+      // output rows of the subtile's 32 tokens go to a wave-private LDS tile
+      // [32 tokens][64 rows] (its 16-byte chunks swizzled by token against
+      // bank conflicts; the token stages are free after the main loop), and
+      // come back 16 bytes per lane, so that one store instruction writes 8
+      // tokens' contiguous 128-byte bf16 pieces (4 tokens' 256-byte fp32
+      // pieces for k > 1) instead of 16 bytes of each of 32 tokens.
+      static_assert(MODE == 0 || RT == 2, "the down epilogue's LDS tile holds 64 rows");
+      char* wl = reinterpret_cast<char*>(lds) + wave * 8192;
+      const bool ok = r < u.nrows;
+      const int tok = k == 1 && ok ? gather[u.slot0 + r] : 0;
+      const float gw = k == 1 && ok ? gate[tok] : 0.f;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const int m0 = (tile0 + rt) * kTileRows + 4 * hi;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int m = m0 + 8 * q;
           if constexpr (SC) {  // fp8 weights: per-row scales of output rows m .. m+3
+            const int m = (tile0 + rt) * kTileRows + 4 * hi + 8 * q;
             const f32x4 s4 = *reinterpret_cast<const f32x4*>(rsc + (size_t)u.e * d + m);
 #pragma unroll
             for (int t = 0; t < 4; ++t) acc[rt][j][4 * q + t] *= s4[t];
           }
+          // local rows rt*32 + 8q + 4hi .. +3 of token col
           if (k == 1) {
             u32x2 v;
             v[0] = pack_bf16x2(gw * acc[rt][j][4 * q], gw * acc[rt][j][4 * q + 1]);
             v[1] = pack_bf16x2(gw * acc[rt][j][4 * q + 2], gw * acc[rt][j][4 * q + 3]);
-            *reinterpret_cast<u32x2*>(dst16 + (size_t)tok * d + m) = v;
+            const int ch = rt * 4 + q;
+            *reinterpret_cast<u32x2*>(wl + col * 128 + ((ch ^ (col & 7)) << 4) + 8 * hi) = v;
           } else {
-            f32x4 v = {acc[rt][j][4 * q], acc[rt][j][4 * q + 1], acc[rt][j][4 * q + 2],
-                       acc[rt][j][4 * q + 3]};
-            *reinterpret_cast<f32x4*>(ybuf + (size_t)slot * d + m) = v;
+            const f32x4 v = {acc[rt][j][4 * q], acc[rt][j][4 * q + 1], acc[rt][j][4 * q + 2],
+                             acc[rt][j][4 * q + 3]};
+            const int ch = rt * 8 + 2 * q + hi;
+            *reinterpret_cast<f32x4*>(wl + col * 256 + ((ch ^ (col & 15)) << 4)) = v;
           }
         }
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int mw = tile0 * kTileRows;  // the wave's first output row
+      if (k == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tl = (lane >> 3) + 8 * i, ch = lane & 7;
+          const int tr = __shfl(tok, tl, 64);
+          const u32x4 v = *reinterpret_cast<const u32x4*>(wl + tl * 128 + ((ch ^ (tl & 7)) << 4));
+          if (j * kSub + tl < u.nrows)
+            *reinterpret_cast<u32x4*>(dst16 + (size_t)tr * d + mw + ch * 8) = v;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int tl = (lane >> 4) + 4 * i, ch = lane & 15;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(wl + tl * 256 + ((ch ^ (tl & 15)) << 4));
+          if (j * kSub + tl < u.nrows)
+            *reinterpret_cast<f32x4*>(ybuf + (size_t)(u.slot0 + j * kSub + tl) * d + mw + ch * 4) =
+                v;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
 }
@@ -412,6 +448,7 @@ __global__ __launch_bounds__(256, OCC) void k_expert_gemm(
     int d, int F) {
   static_assert(TTM >= 1 && TTM <= 8, "token subtiles per unit");
   __shared__ u32x4 lds[kBStages * stage_ent<TTM>()];
+  static_assert(MODE == 0 || sizeof(lds) >= 4 * 8192, "the down epilogue's per-wave LDS tiles");
   const int nrb = (MODE == 0 ? 2 * F : d) / Geo<RT>::kRows;
   __shared__ ExpTab tab;
   const int U = build_table(tab, counts, offsets, E, nrb, cap);
