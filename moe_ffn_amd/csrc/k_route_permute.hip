@@ -5,14 +5,17 @@
 // a = t*k + j are counting-sorted by expert so that every expert sees its rows
 // contiguously, with slots inside an expert in increasing a.
 //
-// One workgroup of 16 waves.  The assignment array is cut into 16 contiguous
-// segments (one per wave) of 64-wide chunks.  Ranks never come from the order
-// of atomics: within a chunk, the lanes holding the same expert are found with
+// Two launches over P groups of consecutive 64-wide chunks (P at most
+// kPermuteMaxGroups, each group one workgroup of four waves, each wave a
+// contiguous run of the group's chunks).  Ranks never come from the order of
+// atomics: within a chunk, the lanes holding the same expert are found with
 // log2(E) ballots (one per bit of the expert id), and a lane's rank is the
-// number of such peers below it; across chunks a per-wave, per-expert running
-// base in LDS advances by the peer count; across waves the bases start from an
-// exclusive scan of the per-wave counts of a first pass.  The result is
-// deterministic and identical to a stable sort by expert.
+// number of such peers below it.  The first launch counts each group's
+// assignments per expert; the second gives every group its bases: the
+// expert's offset (from the totals of all groups) plus the counts of the
+// groups before it, then of the waves before it in the group, then a running
+// base per wave across its chunks.  The result is deterministic and identical
+// to a stable sort by expert.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -51,77 +54,120 @@ __device__ __forceinline__ uint64_t peers_of(int my) {
 }
 }  // namespace
 
+// The chunks of group g and wave w of it: [c0, c1).
+struct Part {
+  int c0, c1;
+};
+__device__ __forceinline__ Part wave_part(int nchunks, int cpg, int g, int w) {
+  const int cpw = (cpg + 3) / 4;
+  const int c0 = min(nchunks, g * cpg + w * cpw);
+  const int c1 = min(min(nchunks, (g + 1) * cpg), c0 + cpw);
+  return {c0, max(c0, c1)};
+}
+
+// This wave's counts per expert over its chunks, added into cnt[EP] (LDS) by
+// the lowest lane of each peer group.
 template <int EP>
-__global__ __launch_bounds__(1024) void k_route_permute(
-    const int* __restrict__ sel, int n, int k, int E, int* __restrict__ counts,
-    int* __restrict__ offsets, int* __restrict__ gather, int* __restrict__ scatter,
-    int* __restrict__ slot_expert) {
+__device__ __forceinline__ void count_part(const int* __restrict__ sel, int n, int E, Part pt,
+                                           int lane, int* cnt) {
   constexpr int NB = ilog2(EP);
-  __shared__ int wc[16][EP];  // per-wave counts, then per-wave running bases
-  __shared__ int cnt_s[EP];
-  __shared__ int off_s[EP + 1];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nchunks = (n + 63) / 64;
-  const int cpw = (nchunks + 15) / 16;
-  const int c_begin = wave * cpw;
-  const int c_end = min(nchunks, c_begin + cpw);
   const uint64_t below = (1ull << lane) - 1ull;
-
-  for (int i = tid; i < 16 * EP; i += 1024) wc[i / EP][i % EP] = 0;
-  __syncthreads();
-
-  // pass 1: per-wave counts, added by the lowest lane of each peer group.
-  // The expert ids of kPB chunks are loaded together.
-  for (int cb = c_begin; cb < c_end; cb += kPB) {
+  for (int cb = pt.c0; cb < pt.c1; cb += kPB) {
     int v[kPB];
     load_batch(sel, n, cb, lane, v);
 #pragma unroll
     for (int j = 0; j < kPB; ++j) {
-      if (cb + j >= c_end) break;
+      if (cb + j >= pt.c1) break;
       const int my = expert_of(v[j], cb + j, lane, n, E);
       const uint64_t peers = peers_of<NB>(my);
-      if (my >= 0 && (peers & below) == 0) atomicAdd(&wc[wave][my], __popcll(peers));
+      if (my >= 0 && (peers & below) == 0) atomicAdd(&cnt[my], __popcll(peers));
     }
   }
-  __syncthreads();
+}
 
-  // exclusive scan over waves (per expert), then over experts
-  if (tid < E) {
-    int run = 0;
-    for (int w = 0; w < 16; ++w) {
+// Launch 1: hist[g][e] = assignments of group g routed to expert e.
+template <int EP>
+__global__ __launch_bounds__(256) void k_route_hist(const int* __restrict__ sel, int n, int E,
+                                                    int cpg, int* __restrict__ hist) {
+  __shared__ int wc[4][EP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nchunks = (n + 63) / 64;
+  for (int i = tid; i < 4 * EP; i += 256) wc[i / EP][i % EP] = 0;
+  __syncthreads();
+  count_part<EP>(sel, n, E, wave_part(nchunks, cpg, blockIdx.x, wave), lane, wc[wave]);
+  __syncthreads();
+  if (tid < EP) hist[blockIdx.x * EP + tid] = wc[0][tid] + wc[1][tid] + wc[2][tid] + wc[3][tid];
+}
+
+// Launch 2: counts, offsets (group 0 writes them) and every assignment's slot.
+template <int EP>
+__global__ __launch_bounds__(256) void k_route_place(
+    const int* __restrict__ sel, int n, int k, int E, int cpg, const int* __restrict__ hist,
+    int* __restrict__ counts, int* __restrict__ offsets, int* __restrict__ gather,
+    int* __restrict__ scatter, int* __restrict__ slot_expert) {
+  constexpr int NB = ilog2(EP);
+  constexpr int G = 256 / EP;  // thread groups that split the group axis
+  __shared__ int part_tot[G][EP], part_pre[G][EP];
+  __shared__ int wc[4][EP];    // per-wave counts, then per-wave running bases
+  __shared__ int off_s[EP + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nchunks = (n + 63) / 64;
+  const int P = gridDim.x, g = blockIdx.x;
+  const uint64_t below = (1ull << lane) - 1ull;
+
+  {  // totals over all groups and over the groups before this one
+    const int e = tid % EP, gi = tid / EP;
+    int tot = 0, pre = 0;
+    for (int q = gi; q < P; q += G) {
+      const int v = hist[q * EP + e];
+      tot += v;
+      pre += q < g ? v : 0;
+    }
+    part_tot[gi][e] = tot;
+    part_pre[gi][e] = pre;
+  }
+  for (int i = tid; i < 4 * EP; i += 256) wc[i / EP][i % EP] = 0;
+  __syncthreads();
+  const Part pt = wave_part(nchunks, cpg, g, wave);
+  count_part<EP>(sel, n, E, pt, lane, wc[wave]);
+  if (wave == 0) {  // offsets: exclusive scan of the totals over the experts (EP <= 64)
+    int tot = 0;
+    if (lane < EP)
+      for (int gi = 0; gi < G; ++gi) tot += part_tot[gi][lane];
+    int inc = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += t;
+    }
+    if (lane < EP) off_s[lane] = inc - tot;
+    if (lane == EP - 1) off_s[EP] = inc;
+    if (g == 0 && lane < E) {
+      counts[lane] = tot;
+      offsets[lane] = inc - tot;
+    }
+    if (g == 0 && lane == E - 1) offsets[E] = inc;
+  }
+  __syncthreads();
+  if (tid < EP) {  // this group's first slot of each expert, then each wave's
+    int base = off_s[tid];
+    for (int gi = 0; gi < G; ++gi) base += part_pre[gi][tid];
+    for (int w = 0; w < 4; ++w) {
       const int v = wc[w][tid];
-      wc[w][tid] = run;
-      run += v;
+      wc[w][tid] = base;
+      base += v;
     }
-    cnt_s[tid] = run;
   }
   __syncthreads();
-  if (tid == 0) {
-    int o = 0;
-    for (int e = 0; e < E; ++e) {
-      off_s[e] = o;
-      o += cnt_s[e];
-    }
-    off_s[E] = o;
-  }
-  __syncthreads();
-  if (tid < E) {
-    counts[tid] = cnt_s[tid];
-    offsets[tid] = off_s[tid];
-  }
-  if (tid == 0) offsets[E] = off_s[E];
-  if (lane < E) wc[wave][lane] += off_s[lane];  // this wave's first slot of each expert
-
-  // pass 2: slots.  All lanes read their expert's base before the group's
-  // lowest lane advances it (the write depends on the value read; one wave's
-  // LDS operations complete in order).
-  for (int cb = c_begin; cb < c_end; cb += kPB) {
+  // slots.  All lanes read their expert's base before the group's lowest
+  // lane advances it (the write depends on the value read; one wave's LDS
+  // operations complete in order).
+  for (int cb = pt.c0; cb < pt.c1; cb += kPB) {
     int v[kPB];
     load_batch(sel, n, cb, lane, v);
 #pragma unroll
     for (int j = 0; j < kPB; ++j) {
-      if (cb + j >= c_end) break;
+      if (cb + j >= pt.c1) break;
       const int a = (cb + j) * 64 + lane;
       const int my = expert_of(v[j], cb + j, lane, n, E);
       const uint64_t peers = peers_of<NB>(my);
@@ -138,14 +184,26 @@ __global__ __launch_bounds__(1024) void k_route_permute(
 }
 
 namespace {
+// Groups of at least four chunks (one per wave), at most kPermuteMaxGroups.
 template <int EP>
 hipError_t launch_ep(const FwdArgs& a) {
-  return launch(k_route_permute<EP>, dim3(1), dim3(1024), a.stream, a.ev[kSlotPermute], a.sel, a.n,
-                a.dim.k, a.dim.E, a.counts, a.offsets, a.gather, a.scatter, a.slot_expert);
+  const int nchunks = (a.n + 63) / 64;
+  int cpg = 4;
+  if ((nchunks + cpg - 1) / cpg > kPermuteMaxGroups)
+    cpg = (nchunks + kPermuteMaxGroups - 1) / kPermuteMaxGroups;
+  const int P = (nchunks + cpg - 1) / cpg;
+  const KEv& ev = a.ev[kSlotPermute];
+  hipError_t he = launch(k_route_hist<EP>, dim3(P), dim3(256), a.stream, KEv{ev.start, nullptr},
+                         a.sel, a.n, a.dim.E, cpg, a.hist);
+  if (he != hipSuccess) return he;
+  return launch(k_route_place<EP>, dim3(P), dim3(256), a.stream, KEv{nullptr, ev.stop}, a.sel,
+                a.n, a.dim.k, a.dim.E, cpg, (const int*)a.hist, a.counts, a.offsets, a.gather,
+                a.scatter, a.slot_expert);
 }
 }  // namespace
 
 hipError_t launch_route_permute(const FwdArgs& a) {
+  if (a.n <= 0) return hipErrorInvalidValue;
   switch (a.dim.EP) {
     case 1: return launch_ep<1>(a);
     case 2: return launch_ep<2>(a);

@@ -81,6 +81,7 @@ struct FwdArgs {
   int* gather;         // [n]
   int* scatter;        // [n]
   int* slot_expert;    // [n]
+  int* hist;           // [kPermuteMaxGroups][64] per-group expert counts (permutation scratch)
   void* xt;            // bf16 prefill: gathered token rows in operand tiles (k_gather_tiles.hip)
   void* act;           // [n, F] SwiGLU activations (decode, f32); operand tiles (bf16 prefill)
   float* ybuf;         // [n, d] fp32 expert outputs (k >= 2 only)
@@ -104,6 +105,7 @@ hipError_t launch_experts_f32(const FwdArgs& a);
 hipError_t launch_combine(const FwdArgs& a);
 
 // balancing step on the router bias (between forwards)
+constexpr int kPermuteMaxGroups = 256;  // workgroups of the permutation, at most
 hipError_t launch_bias_update(const int* counts, int E, float rate, float* bias, hipStream_t s);
 
 // residual add of an FFN stack: out = h + y (n elements, dtype 1 = bf16, 0 = fp32)

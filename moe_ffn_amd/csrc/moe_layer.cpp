@@ -92,6 +92,7 @@ struct moe_layer {
   int* gather;
   int* scatter;
   int* slot_expert;
+  int* hist;
   void* xt;
   void* act;
   float* ybuf;
@@ -270,6 +271,7 @@ moe_status_t create_impl(const moe_layer_config_t* cfg, const moe_layer_weights_
   const size_t o_gat = wc.take(nmax * 4);
   const size_t o_sca = wc.take(nmax * 4);
   const size_t o_sle = wc.take(nmax * 4);
+  const size_t o_hist = wc.take((size_t)moe::kPermuteMaxGroups * 64 * 4);
   // bf16: slot-ordered activations (decode) or padded operand tiles (prefill)
   const size_t npad = bf16 ? (size_t)moe::max_subtiles((int)nmax, (int)E) * 32 : 0;
   const size_t o_xt = bf16 ? wc.take(npad * d * 2) : 0;
@@ -294,6 +296,7 @@ moe_status_t create_impl(const moe_layer_config_t* cfg, const moe_layer_weights_
   L->gather = at<int>(L->ws, o_gat);
   L->scatter = at<int>(L->ws, o_sca);
   L->slot_expert = at<int>(L->ws, o_sle);
+  L->hist = at<int>(L->ws, o_hist);
   L->xt = bf16 ? at<void>(L->ws, o_xt) : nullptr;
   L->act = at<void>(L->ws, o_act);
   L->ybuf = k > 1 ? at<float>(L->ws, o_y) : nullptr;
@@ -427,6 +430,7 @@ moe_status_t forward_impl(moe_layer_t* L, const void* hidden, int32_t T, void* o
   a.gather = (routing && routing->gather) ? routing->gather : L->gather;
   a.scatter = (routing && routing->scatter) ? routing->scatter : L->scatter;
   a.slot_expert = L->slot_expert;
+  a.hist = L->hist;
   a.xt = L->xt;
   a.act = L->act;
   a.ybuf = L->ybuf;
