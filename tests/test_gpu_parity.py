@@ -159,6 +159,21 @@ def test_expert_counts_and_top_k_up_to_the_limits(dtype, E, k, T):
     assert st["rows_compared"] == T
 
 
+@pytest.mark.parametrize("E,k,T", [
+    (16, 8, 9000),   # 72,000 assignments: 225 groups of 5 chunks, the last one ragged
+    (64, 2, 40000),  # 80,000 assignments over 64 experts: 250 groups
+    (8, 4, 16384),   # 65,536 assignments: exactly 256 groups of 4 chunks
+])
+def test_permutation_over_many_groups(E, k, T):
+    """The two-launch permutation at sizes where its groups grow past four
+    chunks each: dispatch arrays in full, output rows sampled."""
+    cfg = LayerConfig(93, f"groups_bf16_E{E}_k{k}_T{T}", T=T, d=256, E=E, F=256, k=k,
+                      dtype="bf16", bias="normal", family=f"groups_bf16_d256_E{E}_F256")
+    inp = make_inputs(cfg)
+    st = check_parity(inp, make_layer(inp, max_tokens=T), sample=256, label=cfg.name)
+    assert st["rows_compared"] >= 256
+
+
 def test_deterministic_bytes():
     inp = make_inputs(3, T=1000)
     layer = family_layer(3)
