@@ -7,9 +7,10 @@
 //   K3 weight-streaming gate/up and down kernels, each workgroup deriving its
 //      expert's dispatch from the routing choice (k_expert_stream.hip)
 // bf16 layers, larger batches:
-//   K1 RMSNorm + router on bf16 MFMA + top-k + gates (k_router_mfma.hip)
-//   K2 histogram + scan + stable permutation (k_route_permute.hip), then the
-//      routed rows gathered into expert-ordered operand tiles (k_gather_tiles.hip)
+//   K1 RMSNorm statistics + router on bf16 MFMA + top-k + gates (k_router_mfma.hip)
+//   K2 per-group expert histograms, then the stable permutation from their
+//      prefix (two launches, k_route_permute.hip); the routed rows normalised
+//      and gathered into expert-ordered operand tiles (k_gather_tiles.hip)
 //   K3 LDS-staged grouped GEMMs, gate/up with SiLU epilogue then down (k_expert_gemm.hip)
 // fp32 layers: VALU router (k_norm_router.hip), K2, VALU experts (k_expert_f32.hip)
 //   K4 gate-weighted combine (k >= 2; folded into K3 for k = 1)
