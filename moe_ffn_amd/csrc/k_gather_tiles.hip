@@ -6,7 +6,8 @@
 // holds the normalised row x = bf16(inv_rms * (g * h)) of token gather[p]:
 // RMSNorm is applied here, on the way from the hidden row to the tile (g * h
 // is exact in fp32, times the router's inv_rms of the token, rounded once to
-// fp32 and once to bf16), so the grouped GEMM's epilogue has no per-row scale.  Rows are stored in
+// fp32 and once to bf16), so the grouped GEMM's epilogue has no per-row
+// scale.  Rows are stored in
 // 32-slot subtiles, each expert's slots padded to a whole number of subtiles
 // (the expert owning ceil(count / 32) subtiles from psub[e], the running sum
 // of those numbers), and every subtile in the B-operand order of
