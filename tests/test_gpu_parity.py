@@ -94,6 +94,15 @@ def test_reduced_sizes_full_rows(cid, T, k):
     check_parity(inp, family_layer(cid, k=k), label=f"c{cid} T={T} k={k}")
 
 
+# Batch sizes at which the launches choose other spans per unit than at the
+# workloads above (the down projection takes at most 4 subtiles per unit at
+# 2048 assignments and 5 at 12288, 6 at 4096 and 16384).
+@pytest.mark.parametrize("T", [2048, 12288])
+def test_other_span_caps_sampled_rows(T):
+    inp = make_inputs(WORKLOADS[2], T=T)
+    check_parity(inp, family_layer(2), sample=384, label=f"c2 T={T}")
+
+
 def test_tiny_fp32_ragged_and_top2():
     for T, k in [(1, 1), (37, 1), (64, 2), (5, 3)]:
         inp = make_inputs(replace(WORKLOADS[0], k=k), T=T)
