@@ -25,11 +25,15 @@ state and TopK keeps a few of them)):
   O8  out_t = sum_{j<k} gate_{t,j} * y_{scatter[t*k+j]}       (no residual)
   O9  balancing step: b_e <- b_e + rate * sign(mean_load - c_e)  (between forwards)
   O10 FFN stack: h_{l+1} = h_l + FFN_l(h_l) over the backbone's layers
+  O11 depth averaging of the router logits over a stack's MoE layers:
+              z~_l = alpha * z~_{l-1} + (1 - alpha) * z_l   (optional)
 
 Readings where the pages are silent:
 the bias only steers selection and never enters a gate; the layer returns
 the FFN output without the residual; no capacity limit and no dropped
-tokens; no shared expert; a linear router (no EDA smoothing).
+tokens; no shared expert; a linear router, whose logits a stack may
+depth-average across its MoE layers (O11: the state averaged and the rate
+are readings, the rate the caller's).
 
 Every floating-point step runs in float64 on the exact values of the inputs
 (bf16 inputs are widened exactly).  Nothing is rounded.
@@ -199,13 +203,16 @@ def bias_update(b, counts, rate: float) -> np.ndarray:
 
 # whole layer ----------------------------------------------------------------
 def oracle_forward(vals: dict, k: int | None = None, forced_sel=None, tokens=None,
-                   eps: float | None = None) -> dict:
+                   eps: float | None = None, z_prev=None, eda_alpha: float | None = None) -> dict:
     """Run O1-O8 on exact input values (a dict as from ``synth.values_f32``).
 
     forced_sel : optional [T,k] expert ids that replace O3's choice (so the
                  expert path can be checked on the device's own routing).
     tokens     : optional token indices; the output is then computed for
                  those rows only (routing and permutation are always full).
+    eda_alpha  : optional depth averaging of the logits (O11) with the
+                 previous MoE layer's averaged logits z_prev (None: this is
+                 the first MoE layer); selection and gates then use them.
     Returns a dict with x, z, s, sel, margin, gate, counts, offsets, gather,
     scatter and out (float64; rows of ``tokens`` when given).
     """
@@ -218,6 +225,9 @@ def oracle_forward(vals: dict, k: int | None = None, forced_sel=None, tokens=Non
     E = np.asarray(vals["w_router"]).shape[0]
     x = rmsnorm(H, vals["gain"], eps)
     z, s = router_scores(x, vals["w_router"], vals["bias"])
+    if eda_alpha is not None:
+        z = depth_average(z_prev, z, eda_alpha)
+        s = z + _f64(vals["bias"])[None, :]
     sel_o, margin = select_topk(s, k)
     sel = sel_o if forced_sel is None else np.asarray(forced_sel, np.int32).reshape(-1, k)
     gate = gates(z, sel)
@@ -250,8 +260,26 @@ def oracle_forward(vals: dict, k: int | None = None, forced_sel=None, tokens=Non
             "scatter": scatter, "out": out, "tokens": tok}
 
 
+# O11 ------------------------------------------------------------------------
+def depth_average(z_prev, z, alpha: float) -> np.ndarray:
+    """Exponential depth averaging of the router state across layers.
+
+    The ZONOS2 digest (item 5) says the router follows ZAYA1 in smoothing its
+    state between layers by exponential depth averaging, and defines neither
+    the state nor the rate.  Reading: the state is the router's logits z (the
+    only state a linear router has), averaged over the stack's MoE layers in
+    order, z~_l = alpha * z~_{l-1} + (1 - alpha) * z_l, with z~ = z at the
+    first MoE layer; alpha in [0, 1) is the caller's (alpha = 0: no
+    smoothing).  The layer's bias b_l is added after the averaging (it steers
+    the choice only), and the gates come from z~."""
+    if z_prev is None:
+        return _f64(z)
+    return alpha * _f64(z_prev) + (1.0 - alpha) * _f64(z)
+
+
 # O10 ------------------------------------------------------------------------
-def stack_forward(layer_vals: list, H, ks: list, eps: float, forced_sels=None) -> dict:
+def stack_forward(layer_vals: list, H, ks: list, eps: float, forced_sels=None,
+                  eda_alpha: float | None = None) -> dict:
     """The FFN half of a stack of backbone layers with residual adds (digest
     item 5: a 28-layer stack whose first three and last layers are dense and
     whose middle layers are MoE, the last MoE layer top-2):
@@ -260,14 +288,22 @@ def stack_forward(layer_vals: list, H, ks: list, eps: float, forced_sels=None) -
 
     FFN_l is the layer of O1-O8 (a dense layer is its one-expert case).
     Everything stays in float64; forced_sels[l] optionally replaces layer l's
-    routing choice.  Returns the final h and every layer's routing.
+    routing choice.  eda_alpha: the MoE layers' (more than one expert) logits
+    are depth-averaged (O11) in stack order; dense layers carry no router
+    state.  Returns the final h and every layer's routing.
     """
     h = _f64(H)
     sels = []
+    zp = None
     for l, vals in enumerate(layer_vals):
         v = dict(vals, hidden=h)
         fs = None if forced_sels is None else forced_sels[l]
-        r = oracle_forward(v, k=ks[l], forced_sel=fs, eps=eps)
+        moe = np.asarray(vals["w_router"]).shape[0] > 1
+        if eda_alpha is not None and moe:
+            r = oracle_forward(v, k=ks[l], forced_sel=fs, eps=eps, z_prev=zp, eda_alpha=eda_alpha)
+            zp = r["z"]
+        else:
+            r = oracle_forward(v, k=ks[l], forced_sel=fs, eps=eps)
         h = h + r["out"]
         sels.append(r["sel"])
     return {"out": h, "sel": sels}

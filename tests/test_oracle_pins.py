@@ -373,6 +373,70 @@ def test_stack_of_zero_output_layers_is_identity():
     np.testing.assert_array_equal(O.stack_forward(layers, H, [1, 1], 1e-6)["out"], H)
 
 
+# ------------------------------------------- depth averaging of router logits
+def _moe_stack_layers(rng, d, F, shapes):
+    layers = []
+    for E, k in shapes:
+        L = _rand_layer(rng, 1, d, E, F)
+        L.pop("hidden")
+        layers.append(L)
+    return layers
+
+
+def test_depth_average_at_rate_zero_is_the_plain_stack():
+    rng = np.random.default_rng(21)
+    shapes = [(1, 1), (4, 1), (4, 1), (1, 1), (4, 2), (1, 1)]
+    layers = _moe_stack_layers(rng, 6, 5, shapes)
+    H = rng.standard_normal((9, 6))
+    ks = [k for _, k in shapes]
+    plain = O.stack_forward(layers, H, ks, 1e-6)
+    eda0 = O.stack_forward(layers, H, ks, 1e-6, eda_alpha=0.0)
+    np.testing.assert_array_equal(eda0["out"], plain["out"])
+    for a, b in zip(eda0["sel"], plain["sel"]):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_depth_average_recursion_closed_form():
+    # three MoE layers: z~_3 = a^2 z_1 + a(1-a) z_2 + (1-a) z_3 (dyadic values,
+    # exact in float64); a swapped weight or a missing term fails it
+    z1, z2, z3 = np.array([[4.0, -2.0]]), np.array([[1.0, 8.0]]), np.array([[-6.0, 2.0]])
+    a = 0.25
+    t = O.depth_average(O.depth_average(O.depth_average(None, z1, a), z2, a), z3, a)
+    np.testing.assert_array_equal(t, a * a * z1 + a * (1 - a) * z2 + (1 - a) * z3)
+    np.testing.assert_array_equal(O.depth_average(None, z2, a), z2)
+
+
+def test_depth_average_hand_worked_two_layers():
+    # d = 2, E = 2, k = 1, zero expert weights (h is the same at both layers):
+    # h = (1, 1), gain 1, inv = 1/sqrt(1 + eps); layer 1 logits (2 inv, 0),
+    # layer 2 logits (0, inv).  At alpha = 0.5 layer 2 averages to (inv,
+    # inv/2): expert 0 instead of 1, gate sigmoid(inv/2).  With a bias
+    # (0, 0.6) on layer 2 the choice is expert 1 (score inv/2 + 0.6 > inv)
+    # but the gate still comes from the averaged logits: sigmoid(-inv/2).
+    eps = 1e-6
+    inv = 1.0 / math.sqrt(1.0 + eps)
+    zero = np.zeros((2, 1, 2))
+
+    def layer(wr, b):
+        return {"gain": np.ones(2), "w_router": np.array(wr, float), "bias": np.array(b, float),
+                "w_gate": zero, "w_up": zero, "w_down": np.zeros((2, 2, 1))}
+    H = np.array([[1.0, 1.0]])
+    l1 = layer([[1, 1], [0, 0]], [0, 0])
+    for b2, want_sel, want_gate in [([0, 0], 0, 1 / (1 + math.exp(-inv / 2))),
+                                    ([0, 0.6], 1, 1 / (1 + math.exp(inv / 2)))]:
+        l2 = layer([[0, 0], [0.5, 0.5]], b2)
+        r1 = O.oracle_forward(dict(l1, hidden=H), k=1, eps=eps, z_prev=None, eda_alpha=0.5)
+        np.testing.assert_allclose(r1["z"], [[2 * inv, 0.0]], rtol=1e-15)
+        r2 = O.oracle_forward(dict(l2, hidden=H), k=1, eps=eps, z_prev=r1["z"], eda_alpha=0.5)
+        np.testing.assert_allclose(r2["z"], [[inv, inv / 2]], rtol=1e-15)
+        assert int(r2["sel"][0, 0]) == want_sel
+        assert abs(r2["gate"][0, 0] - want_gate) < 1e-14
+        plain = O.oracle_forward(dict(l2, hidden=H), k=1, eps=eps)
+        assert int(plain["sel"][0, 0]) == 1
+        st = O.stack_forward([l1, l2], H, [1, 1], eps, eda_alpha=0.5)
+        assert int(st["sel"][1][0, 0]) == want_sel
+
+
 # ------------------------------------------------------------- fp8 weights
 def test_e4m3_decoder_matches_torch_on_every_code():
     codes = np.arange(256, dtype=np.uint8)
