@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef struct moe_layer moe_layer_t; /* opaque; owned by the library */
 
@@ -212,9 +212,25 @@ typedef struct moe_stack moe_stack_t;
  * current device, all with the same d_model and dtype and max_tokens >=
  * max_tokens; BORROWED: they must outlive the stack, which never destroys
  * them.  The stack allocates two residual buffers and one FFN output buffer of
- * [max_tokens, d_model].  Errors: INVALID_ARG, OOM, HIP. */
+ * [max_tokens, d_model] and, for bf16 layers, the [max_tokens, 64] fp32 router
+ * state of moe_stack_set_eda.  Errors: INVALID_ARG, OOM, HIP. */
 moe_status_t moe_stack_create(int32_t n_layers, moe_layer_t* const* layers, int32_t max_tokens,
                               moe_stack_t** out);
+
+/* Exponential depth averaging of the router state across the stack's MoE
+ * layers (those with n_experts > 1), in stack order.  ZONOS2 digest (audio-
+ * paper-digest page, "Method overview and architecture", item 5): the router
+ * follows ZAYA1 in smoothing its state between layers by exponential depth
+ * averaging; the page defines neither the state nor the rate.  This library
+ * reads the state as the router logits z (before the bias) and applies, per
+ * token and expert, z~_l = alpha * z~_{l-1} + (1 - alpha) * z_l with z~ = z
+ * at the first MoE layer; selection uses z~ + b_l and the gates use z~.
+ * enable = 0 turns it off (the default); alpha in [0, 1) is the caller's
+ * (alpha = 0 gives the plain routing).  The state is a [max_tokens, 64] fp32
+ * buffer the stack allocated at create; a later moe_stack_forward or capture
+ * uses the setting current at that call.  Errors: INVALID_ARG (handle, alpha),
+ * UNSUPPORTED (fp32 layers). */
+moe_status_t moe_stack_set_eda(moe_stack_t* stack, int32_t enable, float alpha);
 
 /* One pass through the stack, enqueued on `stream` (no host synchronisation,
  * no allocation).  hidden_in / hidden_out: DEVICE [T, d_model] of the layers'

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
     const uint16_t* __restrict__ hidden, int T, int d, const uint16_t* __restrict__ wr,
     const uint16_t* __restrict__ gain, const float* __restrict__ bias, int E, int k, float eps,
     const uint16_t* __restrict__ zrow, float* __restrict__ inv_out, int* __restrict__ sel,
-    float* __restrict__ gate) {
+    float* __restrict__ gate, float* __restrict__ eda, float eda_alpha, int eda_first) {
   constexpr int NTOK = 16 * TT;
   constexpr int EPAD = 16 * NA;
   static_assert(EPAD != 16 || NTOK != 16 || NW * 64 >= 16 * NTOK,
@@ -177,7 +177,12 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
         sq += (ssr[w][0][tl] + ssr[w][0][tl + 16]) + (ssr[w][0][tl + 32] + ssr[w][0][tl + 48]);
       const float inv = 1.0f / sqrtf(sq / (float)d + eps);
       const bool live = e < E;
-      const float z = zs[tl][e] * inv;
+      float z = zs[tl][e] * inv;
+      if (eda != nullptr && live && t < T) {  // depth-averaged logits across MoE layers
+        float* st = eda + (size_t)t * 64 + e;
+        if (!eda_first) z = eda_alpha * *st + (1.0f - eda_alpha) * z;
+        *st = z;
+      }
       const float sc = z + bias[e];  // bias is padded with zeros to 64 entries
       const uint32_t u = sc == 0.f ? 0u : __float_as_uint(sc);  // -0 ranks as +0
       const uint32_t ord = sc != sc ? 0u : (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -223,6 +228,11 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
 #pragma unroll
     for (int e = 0; e < EPAD; ++e) {
       z[e] = zs[tid][e] * inv;
+      if (eda != nullptr && e < E && t < T) {  // depth-averaged logits across MoE layers
+        float* st = eda + (size_t)t * 64 + e;
+        if (!eda_first) z[e] = eda_alpha * *st + (1.0f - eda_alpha) * z[e];
+        *st = z[e];
+      }
       sc[e] = z[e] + bias[e];  // bias is padded with zeros to 64 entries
     }
     if (t < T) {
@@ -275,7 +285,8 @@ hipError_t go(const FwdArgs& a) {
   return launch(k_router_mfma<NA, TT, NW>, dim3(grid), dim3(NW * 64), a.stream,
                 a.ev[kSlotNormRouter], (const uint16_t*)a.hidden, a.T, a.dim.d,
                 (const uint16_t*)a.wr16, (const uint16_t*)a.gain16, (const float*)a.bias, a.dim.E,
-                a.dim.k, a.dim.eps, (const uint16_t*)a.zrow, a.inv, a.sel, a.gate);
+                a.dim.k, a.dim.eps, (const uint16_t*)a.zrow, a.inv, a.sel, a.gate, a.eda,
+                a.eda_alpha, a.eda_first);
 }
 }  // namespace
 

@@ -25,7 +25,8 @@ __global__ __launch_bounds__(256) void k_router_token(
     const uint16_t* __restrict__ hidden, int d, const uint16_t* __restrict__ wr,
     const uint16_t* __restrict__ gain, const float* __restrict__ bias, int E, int k, float eps,
     const uint16_t* __restrict__ zrow, uint16_t* __restrict__ xg, float* __restrict__ inv_out,
-    int* __restrict__ sel, float* __restrict__ gate) {
+    int* __restrict__ sel, float* __restrict__ gate, float* __restrict__ eda, float eda_alpha,
+    int eda_first) {
   constexpr int NV = EP;
   constexpr int R = NV >= 64 ? NV / 64 : 1;
   __shared__ float red[4][NV];
@@ -94,7 +95,12 @@ __global__ __launch_bounds__(256) void k_router_token(
     const float inv = 1.0f / sqrtf(sq / (float)d + eps);
     const bool live = lane < E;
     const int el = lane < EP ? lane : 0;
-    const float z = live ? (((red[0][el] + red[1][el]) + red[2][el]) + red[3][el]) * inv : 0.f;
+    float z = live ? (((red[0][el] + red[1][el]) + red[2][el]) + red[3][el]) * inv : 0.f;
+    if (eda != nullptr && live) {  // depth-averaged logits across the stack's MoE layers
+      float* st = eda + (size_t)t * 64 + lane;
+      if (!eda_first) z = eda_alpha * *st + (1.0f - eda_alpha) * z;
+      *st = z;
+    }
     const float sc = z + bias[lane < 64 ? lane : 0];  // bias is zero-padded to 64 entries
     // top-k by descending score, exact ties to the lower index: each round
     // takes the wave maximum of a 64-bit key (available flag, the score's
@@ -140,7 +146,8 @@ hipError_t go(const FwdArgs& a) {
   return launch(k_router_token<EP>, dim3(a.T), dim3(256), a.stream, a.ev[kSlotNormRouter],
                 (const uint16_t*)a.hidden, a.dim.d, (const uint16_t*)a.wr16,
                 (const uint16_t*)a.gain16, (const float*)a.bias, a.dim.E, a.dim.k, a.dim.eps,
-                (const uint16_t*)a.zrow, (uint16_t*)a.xn, a.inv, a.sel, a.gate);
+                (const uint16_t*)a.zrow, (uint16_t*)a.xn, a.inv, a.sel, a.gate, a.eda, a.eda_alpha,
+                a.eda_first);
 }
 }  // namespace
 

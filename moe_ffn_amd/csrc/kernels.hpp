@@ -87,6 +87,12 @@ struct FwdArgs {
   float* ybuf;         // [n, d] fp32 expert outputs (k >= 2 only)
   const void* zrow;    // max(d, F) zero elements (16-byte aligned), read-only
   void* sink;          // max(d, F) elements that absorb stores of lanes without a token
+  // depth averaging of the router logits across a stack's MoE layers (bf16
+  // routers): eda = [max_tokens][64] fp32 state or null, z~ = eda_alpha *
+  // state + (1 - eda_alpha) * z, the state read unless eda_first
+  float* eda = nullptr;
+  float eda_alpha = 0.f;
+  int eda_first = 0;
   int num_cu;          // compute units of the device (persistent grids)
   hipStream_t stream;
   KEv ev[kNumSlots];   // per-kernel timing events (null when not timing)

@@ -376,8 +376,11 @@ moe_status_t moe_layer_create_fp8(const moe_layer_config_t* cfg, const moe_layer
 namespace {
 // One forward; `allow_sync` is false inside a HIP graph capture, where the
 // MOE_DEBUG_SYNC synchronisation must not run.
+// eda: a stack's depth-averaging state for this layer's router (bf16 MoE
+// layers only; null otherwise), eda_first: the stack's first MoE layer.
 moe_status_t forward_impl(moe_layer_t* L, const void* hidden, int32_t T, void* out, void* stream,
-                          const moe_routing_out_t* routing, bool allow_sync) {
+                          const moe_routing_out_t* routing, bool allow_sync,
+                          float* eda = nullptr, float eda_alpha = 0.f, bool eda_first = false) {
   if (L == nullptr || L->magic != kMagic) return fail(MOE_ERR_INVALID_ARG, "invalid layer handle");
   if (T < 0 || T > L->max_tokens)
     return fail(MOE_ERR_INVALID_ARG, "T must be in [0, max_tokens] (max_tokens = " +
@@ -438,6 +441,9 @@ moe_status_t forward_impl(moe_layer_t* L, const void* hidden, int32_t T, void* o
   a.zrow = L->zrow;
   a.sink = L->sink;
   a.num_cu = L->num_cu;
+  a.eda = eda;
+  a.eda_alpha = eda_alpha;
+  a.eda_first = eda_first ? 1 : 0;
   a.stream = reinterpret_cast<hipStream_t>(stream);
   if (L->timing && L->t_used < L->t_max) {
     const hipEvent_t* ev = &L->tev[(size_t)L->t_used * kEventsPerForward];
@@ -607,6 +613,9 @@ struct moe_stack {
   void* y;
   hipGraphExec_t exec;
   hipStream_t exec_stream;
+  float* eda;       // [max_tokens][64] fp32 depth-averaging state of the router logits
+  bool eda_on;
+  float eda_alpha;
 };
 
 namespace {
@@ -616,6 +625,7 @@ void stack_release(moe_stack* S) {
   if (S == nullptr) return;
   if (S->exec) (void)hipGraphExecDestroy(S->exec);
   if (S->buf) (void)hipFree(S->buf);
+  if (S->eda) (void)hipFree(S->eda);
   S->magic = 0;
   delete S;
 }
@@ -645,8 +655,13 @@ moe_status_t stack_enqueue(moe_stack* S, const void* hin, int32_t T, void* hout,
   const size_t n = (size_t)T * S->d;
   const void* cur = hin;
   const int nl = (int)S->layers.size();
+  bool first_moe = true;
   for (int l = 0; l < nl; ++l) {
-    moe_status_t st = forward_impl(S->layers[l], cur, T, S->y, s, nullptr, allow_sync);
+    const bool moe = S->layers[l]->dim.E > 1;
+    float* eda = S->eda_on && moe ? S->eda : nullptr;
+    moe_status_t st = forward_impl(S->layers[l], cur, T, S->y, s, nullptr, allow_sync, eda,
+                                   S->eda_alpha, first_moe);
+    if (moe) first_moe = false;
     if (st != MOE_OK) return st;
     void* nxt = l == nl - 1 ? hout : ((l & 1) ? S->hB : S->hA);
     hipError_t he = moe::launch_residual(cur, S->y, nxt, n, S->dtype, s);
@@ -704,8 +719,29 @@ moe_status_t moe_stack_create(int32_t n_layers, moe_layer_t* const* layers, int3
   S->hA = S->buf;
   S->hB = at<void>(S->buf, one);
   S->y = at<void>(S->buf, 2 * one);
+  if (dtype == MOE_DTYPE_BF16) {
+    he = hipMalloc(&S->eda, (size_t)max_tokens * 64 * 4);
+    if (he != hipSuccess) {
+      S->eda = nullptr;
+      stack_release(S);
+      (void)hipGetLastError();
+      return fail(MOE_ERR_OOM, std::string("stack router state: ") + hipGetErrorString(he));
+    }
+  }
   S->magic = kStackMagic;
   *out = S;
+  return MOE_OK;
+}
+
+moe_status_t moe_stack_set_eda(moe_stack_t* S, int32_t enable, float alpha) {
+  g_err.clear();
+  if (S == nullptr || S->magic != kStackMagic) return fail(MOE_ERR_INVALID_ARG, "invalid stack handle");
+  if (enable && S->eda == nullptr)
+    return fail(MOE_ERR_UNSUPPORTED, "depth averaging needs bf16 layers");
+  if (enable && !(alpha >= 0.f && alpha < 1.f))
+    return fail(MOE_ERR_INVALID_ARG, "alpha must be in [0, 1)");
+  S->eda_on = enable != 0;
+  S->eda_alpha = enable ? alpha : 0.f;
   return MOE_OK;
 }
 

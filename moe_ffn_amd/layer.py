@@ -27,7 +27,7 @@ EXPORTS = ("moe_abi_version", "moe_last_error", "moe_layer_create", "moe_layer_c
            "moe_layer_set_bias", "moe_layer_get_bias", "moe_layer_update_bias",
            "moe_layer_timing_start",
            "moe_layer_timing_stop", "moe_layer_destroy", "moe_stack_create", "moe_stack_forward",
-           "moe_stack_capture", "moe_stack_replay", "moe_stack_destroy")
+           "moe_stack_capture", "moe_stack_replay", "moe_stack_destroy", "moe_stack_set_eda")
 TIMED_SLOTS = ("norm_router", "route_permute", "experts_gate_up", "experts_down", "combine",
                "gather")
 
@@ -114,6 +114,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.moe_stack_replay.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     lib.moe_stack_destroy.restype = None
     lib.moe_stack_destroy.argtypes = [ctypes.c_void_p]
+    lib.moe_stack_set_eda.restype = ctypes.c_int
+    lib.moe_stack_set_eda.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_float]
     if path is None:
         _lib = lib
     return lib
@@ -320,6 +322,12 @@ class MoEStack:
 
     def replay(self, stream=None):
         _check(self._lib, self._lib.moe_stack_replay(self.handle, ctypes.c_void_p(_stream_ptr(stream))))
+
+    def set_eda(self, alpha: float | None):
+        """Depth-average the router logits across the MoE layers at rate alpha
+        (None: off); see moe_stack_set_eda."""
+        _check(self._lib, self._lib.moe_stack_set_eda(self.handle, 0 if alpha is None else 1,
+                                                      0.0 if alpha is None else float(alpha)))
 
     def close(self):
         if self.handle is not None:

@@ -290,10 +290,10 @@ def stack_forward(layer_vals: list, H, ks: list, eps: float, forced_sels=None,
     Everything stays in float64; forced_sels[l] optionally replaces layer l's
     routing choice.  eda_alpha: the MoE layers' (more than one expert) logits
     are depth-averaged (O11) in stack order; dense layers carry no router
-    state.  Returns the final h and every layer's routing.
+    state.  Returns the final h and every layer's routing and top-k margins.
     """
     h = _f64(H)
-    sels = []
+    sels, margins = [], []
     zp = None
     for l, vals in enumerate(layer_vals):
         v = dict(vals, hidden=h)
@@ -306,7 +306,8 @@ def stack_forward(layer_vals: list, H, ks: list, eps: float, forced_sels=None,
             r = oracle_forward(v, k=ks[l], forced_sel=fs, eps=eps)
         h = h + r["out"]
         sels.append(r["sel"])
-    return {"out": h, "sel": sels}
+        margins.append(r["margin"])
+    return {"out": h, "sel": sels, "margin": margins}
 
 
 # fp8 expert weights ------------------------------------------------------------

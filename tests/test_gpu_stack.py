@@ -113,3 +113,75 @@ def test_full_width_stack_matches_layer_loop():
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref_loop.view(torch.int16))
     stack.close()
+
+
+# ------------------------------- depth averaging of the router logits (O11)
+def test_eda_at_rate_zero_equals_the_plain_stack():
+    from moe_ffn_amd import MoEStack
+    for T in (48, 300):
+        inps = _small_stack_inputs(T)
+        layers = [make_layer(inp, max_tokens=T) for inp in inps]
+        stack = MoEStack(layers, max_tokens=T)
+        h0 = to_torch(inps[0]["hidden"], "bf16")
+        plain = stack.forward(h0).clone()
+        stack.set_eda(0.0)
+        eda0 = stack.forward(h0).clone()
+        stack.set_eda(None)
+        again = stack.forward(h0)
+        torch.cuda.synchronize()
+        assert torch.equal(eda0.view(torch.int16), plain.view(torch.int16)), T
+        assert torch.equal(again.view(torch.int16), plain.view(torch.int16)), T
+        stack.close()
+
+
+@pytest.mark.parametrize("T,alpha", [(48, 0.5), (128, 0.5), (200, 0.5)])
+def test_eda_stack_matches_oracle(T, alpha):
+    """T = 48 routes the top-1 layers with the per-token router and the top-2
+    layer with the MFMA router; 128 and 200 take the MFMA router throughout.
+    The inputs are chosen so that no token of any MoE layer has a top-k margin
+    below 1e-3 in the oracle, so the routing must agree everywhere."""
+    from moe_ffn_amd import MoEStack
+    inps = _small_stack_inputs(T)
+    vals = [values_f32(inp) for inp in inps]
+    ks = [inp["cfg"].k for inp in inps]
+    ref = O.stack_forward(vals, vals[0]["hidden"], ks, inps[0]["cfg"].eps, eda_alpha=alpha)
+    plain = O.stack_forward(vals, vals[0]["hidden"], ks, inps[0]["cfg"].eps)
+    moe = [l for l, inp in enumerate(inps) if inp["cfg"].E > 1]
+    assert min(float(np.min(ref["margin"][l])) for l in moe) >= O.MARGIN_TOL
+    assert any(np.any(ref["sel"][l] != plain["sel"][l]) for l in moe)  # the averaging matters
+    layers = [make_layer(inp, max_tokens=T) for inp in inps]
+    stack = MoEStack(layers, max_tokens=T)
+    stack.set_eda(alpha)
+    h0 = to_torch(inps[0]["hidden"], "bf16")
+    out = stack.forward(h0).clone()
+    # a captured graph of the same pass replays to the same bytes
+    side = torch.cuda.Stream()
+    buf_out = torch.empty_like(h0)
+    torch.cuda.synchronize()
+    stack.capture(h0, buf_out, side)
+    for _ in range(2):
+        buf_out.zero_()
+        torch.cuda.synchronize()
+        stack.replay(side)
+        side.synchronize()
+        assert torch.equal(buf_out.view(torch.int16), out.view(torch.int16))
+    err = np.abs(out_to_f64(out) - ref["out"]).max()
+    assert err <= TOL["bf16"] * np.abs(ref["out"]).max(), (err, np.abs(ref["out"]).max())
+    stack.close()
+
+
+def test_eda_rejects_bad_rates_and_fp32_stacks():
+    from moe_ffn_amd import MoEStack
+    from moe_ffn_amd.layer import MoELayerError
+    inps = _small_stack_inputs(48)
+    layers = [make_layer(inp, max_tokens=48) for inp in inps[:3]]
+    stack = MoEStack(layers, max_tokens=48)
+    for bad in (1.0, -0.1, float("nan")):
+        with pytest.raises(MoELayerError):
+            stack.set_eda(bad)
+    stack.close()
+    f32 = make_inputs(WORKLOADS[0], T=16)
+    s32 = MoEStack([make_layer(f32, max_tokens=16)], max_tokens=16)
+    with pytest.raises(MoELayerError):
+        s32.set_eda(0.5)
+    s32.close()
