@@ -400,6 +400,20 @@ def run_stack(args):
     e1.record(side)
     side.synchronize()
     ms_graph = e0.elapsed_time(e1) / K
+    eda = None
+    if args.eda is not None:  # the same pass with the router logits depth-averaged
+        stack.set_eda(args.eda)
+        for _ in range(W):
+            stack.forward(h0, out=out)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(K):
+            stack.forward(h0, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        eda = {"alpha": args.eda, "us_per_frame_eager": round(e0.elapsed_time(e1) / K * 1e3, 2)}
+        log(f"[bench] with depth-averaged router logits (alpha {args.eda}): "
+            f"eager {eda['us_per_frame_eager']:.1f} us per frame")
     log(f"[bench] stack of {len(layers)} FFN layers: eager {ms_eager * 1e3:.1f} us, "
         f"graph {ms_graph * 1e3:.1f} us per frame of {T} tokens; experts touched per layer "
         f"{touched}; stack equals layer loop: {same_as_loop}, graph equals eager: {graph_same}")
@@ -416,7 +430,7 @@ def run_stack(args):
                       "weight_bytes_per_frame": wbytes,
                       "weight_GBps": round(wbytes / (ms_graph * 1e-3) / 1e9, 1),
                       "experts_touched": touched, "stack_equals_layer_loop": same_as_loop,
-                      "graph_equals_eager": graph_same}}
+                      "graph_equals_eager": graph_same, "depth_averaged_router": eda}}
     stack.close()
     for L in layers:
         L.close()
@@ -441,6 +455,8 @@ def main():
                     help="expert weights as E4M3 codes with per-row scales")
     ap.add_argument("--stack", action="store_true",
                     help="time the FFN half of the full 28-layer backbone at decode instead")
+    ap.add_argument("--eda", type=float, default=None, metavar="ALPHA",
+                    help="with --stack: also time the pass with the router logits depth-averaged")
     ap.add_argument("--ingest-counters", metavar="DIR",
                     help="no GPU: write profiles/traffic.json from rocprofv3 --pmc runs in DIR")
     args = ap.parse_args()
