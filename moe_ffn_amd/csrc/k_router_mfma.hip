@@ -14,7 +14,11 @@
 // therefore two bf16 MFMAs with fp32 accumulation: fp32-router precision at
 // matrix-core speed.  z = inv_rms * z_raw with inv_rms = 1/sqrt(mean(h^2)+eps).
 //
-// Outputs: inv_rms[T], sel[T,k], gate[T,k].  The normalised expert inputs
+// Outputs: inv_rms[T], sel[T,k], gate[T,k].  In a stack that depth-averages
+// the router state (the digest's item 5 names exponential depth averaging
+// after ZAYA1 without defining it; read as z~ = alpha * z~_prev + (1 - alpha)
+// * z on the logits), eda holds each token's averaged logits of the previous
+// MoE layer, which selection and gates then use in place of z.  The normalised expert inputs
 // are formed by the gather kernel from the hidden rows it copies (with this
 // kernel's inv_rms), which saves writing and re-reading T*d*2 bytes here.
 //

@@ -12,9 +12,11 @@
 //   z_raw[e] = sum_i W_r[e][i] * x'_i     (every product exact in fp32).
 // The E partial sums are reduced by a spreading butterfly inside each wave and
 // across the four waves in LDS (fixed order); then the lanes of wave 0, one per
-// expert, apply inv_rms = 1/sqrt(mean(h^2) + eps), add the bias, pick the
-// top-k by wave-wide maximum reductions and write the gates.  The dispatch of
-// decode batches happens in the expert kernels.
+// expert, apply inv_rms = 1/sqrt(mean(h^2) + eps) (and, when a stack passes
+// its depth-averaging state eda, replace the logits z by z~ = alpha * z~_prev
+// + (1 - alpha) * z; the first MoE layer only writes the state), add the
+// bias, pick the top-k by wave-wide maximum reductions and write the gates.
+// The dispatch of decode batches happens in the expert kernels.
 #include "common.hpp"
 #include "kernels.hpp"
 
