@@ -12,12 +12,17 @@ consecutive MoE layers of the backbone would not.
 Prints ONE JSON line: the metric, the step time, a roofline entry for the
 dominant kernel (its algorithmic bytes or flops per launch over its average
 duration, from HIP events recorded by the library on the forward's stream)
-and the fp64 CPU oracle's throughput on a bounded sample of the same workload.
+and the fp64 CPU oracle's throughput on a bounded sample of the same workload,
+with the oracle's routing of every benched batch checked against the GPU's
+(near-ties counted and reported).  The default line (the decode workload)
+also carries `prefill`: the T=4096 and T=16384 prefill workloads' step time,
+tokens/s, whole-layer fraction of the bf16 MFMA peak and their gate/up
+grouped GEMM's time and fraction.
 
 With --fp8 the expert weights are E4M3 codes with per-row fp32 scales
 (moe_layer_create_fp8): decode streams half the weight bytes.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config {1,2,3,4}] [--fp8]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config {0,1,2,3,4}] [--fp8]
 """
 
 from __future__ import annotations
@@ -46,6 +51,7 @@ def log(*a):
 # sources that decide the dominant kernel's memory traffic (its counters are
 # void once any of them changes)
 DOMINANT_SOURCES = {"k_gateup_stream": ["k_expert_stream.hip", "common.hpp", "kernels.hpp"],
+                    "k_gateup_f32": ["k_expert_f32.hip", "common.hpp", "kernels.hpp"],
                     "k_expert_gemm<0>": ["k_expert_gemm.hip", "common.hpp", "kernels.hpp"]}
 
 
@@ -59,6 +65,8 @@ def kernel_source_hash(kernel: str) -> str:
 
 
 def dominant_kernel_name(cfg) -> str:
+    if cfg.dtype == "f32":
+        return "k_gateup_f32"
     return "k_gateup_stream" if cfg.T * cfg.k <= 64 else "k_expert_gemm<0>"
 
 
@@ -116,7 +124,7 @@ def ingest_counters(pmc_dir: str) -> None:
     out = {"_calibration": {"copy_bytes_each_way": copy_bytes, "fetch_counter_bytes": cf,
                             "write_counter_bytes": cw, "fetch_factor": round(ffac, 5),
                             "write_factor": round(wfac, 5)}}
-    for cid, tag in [(c, t) for c in (1, 2, 3, 4) for t in ("", "fp8")]:
+    for cid, tag in [(c, t) for c in (0, 1, 2, 3, 4) for t in ("", "fp8")]:
         fd, wd = (os.path.join(pmc_dir, f"c{cid}{tag}_{x}") for x in ("fetch", "write"))
         if not (os.path.isdir(fd) and os.path.isdir(wd)):
             continue
@@ -149,6 +157,13 @@ def dominant_kernel(cfg, counts, fp8: bool = False):
     d, F, k, T = cfg.d, cfg.F, cfg.k, cfg.T
     n = T * k
     touched = int((counts > 0).sum())
+    if cfg.dtype == "f32":
+        # fp32 layers: gate and up rows of each touched expert, 4 bytes each
+        per_expert = 2 * F * d * 4
+        return {"slot": "experts_gate_up", "kernel": "k_gateup_f32", "bound": "hbm",
+                "unit": "GB/s", "units": touched, "per_unit": per_expert,
+                "unit_name": "touched expert (fp32 W_gate + W_up bytes)",
+                "work": touched * per_expert, "work_unit": "bytes"}
     if n <= 64:
         # W_gate + W_up bytes of one expert
         per_expert = 2 * F * d + 2 * F * 4 if fp8 else 2 * F * d * 2
@@ -168,10 +183,31 @@ def dominant_kernel(cfg, counts, fp8: bool = False):
 def layer_work(cfg, counts, fp8: bool = False):
     touched = int((counts > 0).sum())
     d, F, n = cfg.d, cfg.F, cfg.T * cfg.k
-    wexp = 3 * F * d + (2 * F + d) * 4 if fp8 else 3 * F * d * 2  # expert weight bytes
-    bytes_ = touched * wexp + 2 * cfg.T * d * 2 + cfg.E * d * 2 + cfg.E * 4 + d * 2
+    es = 4 if cfg.dtype == "f32" else 2
+    wexp = 3 * F * d + (2 * F + d) * 4 if fp8 else 3 * F * d * es  # expert weight bytes
+    bytes_ = touched * wexp + 2 * cfg.T * d * es + cfg.E * d * es + cfg.E * 4 + d * es
     flops = n * 6 * F * d + 2 * cfg.T * d * cfg.E
     return bytes_, flops, touched
+
+
+def routing_check(inputs, sel_gpu) -> dict:
+    """The oracle's routing (O1-O3, every token) of a benched batch against the
+    GPU's: tokens whose top-k margin is below 1e-3 (near-ties, either route
+    is correct), how many of them the GPU routed differently, and how many
+    other tokens it routed differently (must be 0)."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    from synth import gen
+    cfg = inputs["cfg"]
+    vals = gen.values_f32(inputs)
+    x = O.rmsnorm(vals["hidden"], vals["gain"], cfg.eps)
+    _, sc = O.router_scores(x, vals["w_router"], vals["bias"])
+    sel_o, margin = O.select_topk(sc, cfg.k)
+    firm = margin >= O.MARGIN_TOL
+    same = (np.asarray(sel_gpu) == sel_o).all(axis=1)
+    return {"workload": cfg.name, "tokens": int(cfg.T), "near_ties": int(np.sum(~firm)),
+            "near_tie_flips": int(np.sum(~same & ~firm)),
+            "firm_mismatches": int(np.sum(~same & firm))}
 
 
 def cpu_baseline(inputs, seconds: float, fp8: dict | None = None):
@@ -223,14 +259,12 @@ def cpu_baseline(inputs, seconds: float, fp8: dict | None = None):
             "host_cpus": ncores}
 
 
-def hw_context(dev, cus: int) -> dict:
-    """Measured ceilings of this part, as context for the roofline fractions:
-    a 1 GiB device copy (HBM read + write), the MFMA rate probe of
-    libmoe_probe.so (register operands only) and a vendor bf16 GEMM
-    (torch.matmul) of the prefill gate/up shape."""
-    import ctypes
+def hw_context(dev) -> dict:
+    """Measured rates of this part, as context for the roofline fractions
+    (which use the published peaks): a 1 GiB device copy (HBM read + write)
+    and a vendor bf16 GEMM (torch.matmul, hipBLASLt) of the prefill gate/up
+    shape."""
     import torch
-    from moe_ffn_amd.build import PROBE_LIB
 
     def best_ms(fn, reps=5):
         ts = []
@@ -251,23 +285,6 @@ def hw_context(dev, cus: int) -> dict:
     ms = best_ms(lambda: dst.copy_(src))
     out["hbm_copy_GBps"] = round(2 * n / (ms * 1e-3) / 1e9, 1)
     del src, dst
-    if os.path.exists(PROBE_LIB):
-        lib = ctypes.CDLL(PROBE_LIB)
-        lib.moe_probe_mfma.restype = ctypes.c_int32
-        lib.moe_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
-                                       ctypes.c_void_p]
-        lib.moe_probe_mfma_flops.restype = ctypes.c_double
-        lib.moe_probe_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
-        blocks, iters = 2 * cus, 20000
-        sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
-        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-
-        def probe():
-            if lib.moe_probe_mfma(blocks, iters, ctypes.c_void_p(sink.data_ptr()), stream) != 0:
-                raise RuntimeError("MFMA probe launch failed")
-        probe()
-        ms = best_ms(probe, 3)
-        out["mfma_probe_TFLOPs"] = round(lib.moe_probe_mfma_flops(blocks, iters) / (ms * 1e-3) / 1e12, 1)
     a = torch.randn(4096, 2048, device=dev).to(torch.bfloat16)
     b = torch.randn(2048, 6144, device=dev).to(torch.bfloat16)
     c = torch.matmul(a, b)
@@ -437,17 +454,152 @@ def run_stack(args):
     print(json.dumps(line), flush=True)
 
 
+def make_layers(inp, n: int, fp8: bool, dev):
+    """n independently allocated copies of the workload's layer (fp8: E4M3
+    expert weights with row scales) and the fp8 codes used (or None)."""
+    import numpy as np
+    import torch
+    from moe_ffn_amd import MoELayer
+    cfg = inp["cfg"]
+    q8 = None
+    if fp8:
+        from synth.gen import fp8_expert_weights
+        q8 = fp8_expert_weights(inp)
+
+    def tt(a, bf16=True):
+        if bf16 and a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+    w = {"rms_gain": tt(inp["gain"]), "w_router": tt(inp["w_router"]),
+         "b_router": tt(inp["bias"], False)}
+    scales = None
+    if q8 is None:
+        w.update({n_: tt(inp[n_]) for n_ in ("w_gate", "w_up", "w_down")})
+    else:
+        w.update({n_: torch.from_numpy(q8[n_]).to(dev) for n_ in ("w_gate", "w_up", "w_down")})
+        scales = {n_: tt(q8["s_" + n_], False) for n_ in ("gate", "up", "down")}
+    layers = [MoELayer(cfg.d, cfg.F, cfg.E, cfg.k, cfg.dtype, w, cfg.T, rms_eps=cfg.eps,
+                       fp8_scales=scales)
+              for _ in range(n)]
+    del w, scales
+    hidden = tt(inp["hidden"])
+    torch.cuda.synchronize()
+    return layers, hidden, q8
+
+
+def time_steps(layers, hidden, outs, K: int, per_kernel: bool):
+    """K forwards rotating over the layer copies, bracketed by synchronisations
+    and HIP events on the forwards' stream.  Returns (ms per step, per-kernel
+    ms per forward from the events the library attaches to each kernel's own
+    dispatch, or None)."""
+    import torch
+    nl = len(layers)
+    if per_kernel:
+        for L in layers:
+            L.timing_start((K + nl - 1) // nl)
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for i in range(K):
+        layers[i % nl].forward(hidden, out=outs[i % nl])
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    slots = None
+    if per_kernel:
+        slots, nf = {}, 0
+        for L in layers:
+            sl, n = L.timing_stop()
+            nf += n
+            for k_, v in sl.items():
+                slots[k_] = slots.get(k_, 0.0) + v
+        slots = {k_: v / nf for k_, v in slots.items()}
+    return ms / K, slots
+
+
+def roofline_entry(dom: dict, dom_ms: float, traffic) -> dict:
+    if dom["work_unit"] == "bytes":
+        achieved, peak = dom["work"] / (dom_ms * 1e-3) / 1e9, PEAK_HBM_GBPS
+    else:
+        achieved, peak = dom["work"] / (dom_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS
+    return {"bound": dom["bound"], "achieved": round(achieved, 2), "peak": peak,
+            "unit": dom["unit"], "frac": round(achieved / peak, 4), "traffic": traffic,
+            "kernel": dom["kernel"], "avg_launch_us": round(dom_ms * 1e3, 3),
+            "per_unit": dom["per_unit"], "units_per_launch": dom["units"],
+            "unit_name": dom["unit_name"]}
+
+
+def counter_traffic(wname: str, kernel: str):
+    """HBM bytes per launch of the kernel from profiles/traffic.json, if the
+    kernel's sources still hash to the value recorded with the counters."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f).get(wname, {})
+        if tr.get("kernel") == kernel and tr.get("source_hash") == kernel_source_hash(kernel):
+            return tr.get("bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+    return None
+
+
+def prefill_summary(cid: int, args, dev) -> tuple[dict, dict, object]:
+    """Step time, whole-layer MFMA fraction and the gate/up GEMM's time and
+    fraction of one prefill workload (a sub-object of the default line).
+    Returns (summary, inputs, GPU routing choice)."""
+    import torch
+    from synth import make_inputs
+    inp = make_inputs(cid)
+    cfg = inp["cfg"]
+    layers, hidden, _ = make_layers(inp, args.instances, False, dev)
+    outs = [torch.empty_like(hidden) for _ in layers]
+    _, r = layers[0].forward(hidden, routing=True)
+    sel = r["sel"].cpu().numpy()
+    counts = r["counts"].cpu().numpy()
+    dom = dominant_kernel(cfg, counts)
+    lbytes, lflops, touched = layer_work(cfg, counts)
+    K = args.prefill_steps
+    for i in range(max(5, K // 10)):
+        layers[i % len(layers)].forward(hidden, out=outs[i % len(layers)])
+    ms, _ = time_steps(layers, hidden, outs, K, False)
+    ms_ev, slots = time_steps(layers, hidden, outs, K, True)
+    rl = roofline_entry(dom, slots[dom["slot"]], counter_traffic(cfg.name, dom["kernel"]))
+    for L in layers:
+        L.close()
+    out = {"workload": cfg.name, "T": cfg.T, "top_k": cfg.k, "steps": K,
+           "tokens_per_s": round(cfg.T / (ms * 1e-3), 1), "us_per_step": round(ms * 1e3, 3),
+           "mfma_frac_layer": round(lflops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "algorithmic_flops": lflops, "algorithmic_bytes": lbytes,
+           "experts_touched": touched,
+           "gemm_gate_up": {"kernel": dom["kernel"], "us": rl["avg_launch_us"],
+                            "TFLOPs": rl["achieved"], "frac": rl["frac"],
+                            "traffic": rl["traffic"]},
+           "kernel_us": {k_: round(v * 1e3, 3) for k_, v in slots.items()},
+           "us_per_step_with_kernel_events": round(ms_ev * 1e3, 3)}
+    log(f"[bench] {cfg.name}: {out['us_per_step']:.1f} us/step, {out['tokens_per_s'] / 1e6:.2f} M "
+        f"tokens/s, layer {100 * out['mfma_frac_layer']:.1f}% of bf16 peak; gate/up GEMM "
+        f"{rl['avg_launch_us']:.1f} us = {100 * rl['frac']:.1f}%")
+    return out, inp, sel
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4])
+    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--instances", type=int, default=3)
+    ap.add_argument("--prefill-steps", type=int, default=200,
+                    help="steps of each prefill workload in the default line's `prefill` entry")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="leave the prefill workloads out of the decode line")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
-                    help="skip the copy / MFMA-probe / vendor-GEMM context measurements")
+                    help="skip the copy / vendor-GEMM context measurements")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy (dst = -src, MIB MiB read and MIB MiB\n"
                          "written) five times, to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -476,14 +628,15 @@ def main():
         run_stack(args)
         return
 
-    import numpy as np
     import torch
     from synth import make_inputs
-    from moe_ffn_amd import MoELayer, load_library
+    from moe_ffn_amd import load_library
 
     load_library()  # fails loudly if the HIP library is not built
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
+    if args.fp8 and args.config == 0:
+        raise SystemExit("--fp8 needs a bf16 workload (--config 1..4)")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
@@ -503,36 +656,14 @@ def main():
     t_gen = time.perf_counter()
     inp = make_inputs(args.config)
     cfg = inp["cfg"]
-    q8 = None
-    if args.fp8:
-        from synth.gen import fp8_expert_weights
-        q8 = fp8_expert_weights(inp)
     wname = cfg.name + ("_fp8w" if args.fp8 else "")
-    log(f"[bench] inputs for {wname} in {time.perf_counter() - t_gen:.1f} s")
-
-    def tt(a, bf16=True):
-        if bf16 and a.dtype == np.uint16:
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
-
-    w = {"rms_gain": tt(inp["gain"]), "w_router": tt(inp["w_router"]),
-         "b_router": tt(inp["bias"], False)}
-    scales = None
-    if q8 is None:
-        w.update({n_: tt(inp[n_]) for n_ in ("w_gate", "w_up", "w_down")})
-    else:
-        w.update({n_: torch.from_numpy(q8[n_]).to(dev) for n_ in ("w_gate", "w_up", "w_down")})
-        scales = {n_: tt(q8["s_" + n_], False) for n_ in ("gate", "up", "down")}
-    layers = [MoELayer(cfg.d, cfg.F, cfg.E, cfg.k, cfg.dtype, w, cfg.T, rms_eps=cfg.eps,
-                       fp8_scales=scales)
-              for _ in range(args.instances)]
-    del w, scales
-    hidden = tt(inp["hidden"])
+    layers, hidden, q8 = make_layers(inp, args.instances, args.fp8, dev)
     outs = [torch.empty_like(hidden) for _ in layers]
-    torch.cuda.synchronize()
+    log(f"[bench] inputs and {len(layers)} layers for {wname} in {time.perf_counter() - t_gen:.1f} s")
 
     _, r = layers[0].forward(hidden, routing=True)
     counts = r["counts"].cpu().numpy()
+    sel_gpu = r["sel"].cpu().numpy()
     dom = dominant_kernel(cfg, counts, args.fp8)
     lbytes, lflops, touched = layer_work(cfg, counts, args.fp8)
     log(f"[bench] {touched} experts touched; dominant kernel {dom['kernel']}")
@@ -543,64 +674,26 @@ def main():
         layers[i % nl].forward(hidden, out=outs[i % nl])
     torch.cuda.synchronize()
 
-    def timed(per_kernel: bool):
-        if per_kernel:
-            for L in layers:
-                L.timing_start((K + nl - 1) // nl)
-        s = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(s)
-        for i in range(K):
-            layers[i % nl].forward(hidden, out=outs[i % nl])
-        e1.record(s)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
-        slots = None
-        if per_kernel:
-            slots, nf = {}, 0
-            for L in layers:
-                sl, n = L.timing_stop()
-                nf += n
-                for k_, v in sl.items():
-                    slots[k_] = slots.get(k_, 0.0) + v
-            slots = {k_: v / nf for k_, v in slots.items()}
-        return ms / K, slots
-
-    ms_step, _ = timed(False)
+    ms_step, _ = time_steps(layers, hidden, outs, K, False)
     log(f"[bench] {K} steps: {ms_step * 1e3:.2f} us/step")
     pf = per_forward(layers, hidden, outs, min(K, 1000))
     log(f"[bench] per forward: p10 {pf['p10']} median {pf['median']} p90 {pf['p90']} us")
     gr = graph_timing(layers, hidden, outs, K)
     log(f"[bench] HIP graph of {nl} forwards: {gr['ms_per_step'] * 1e3:.2f} us/step, "
         f"replay equals eager: {gr['matches_eager']}")
-    ms_step_ev, slots = timed(True)
+    ms_step_ev, slots = time_steps(layers, hidden, outs, K, True)
     log(f"[bench] with per-kernel events: {ms_step_ev * 1e3:.2f} us/step; "
         + ", ".join(f"{k_} {v * 1e3:.2f} us" for k_, v in slots.items()))
-
-    dom_ms = slots[dom["slot"]]
-    if dom["work_unit"] == "bytes":
-        achieved = dom["work"] / (dom_ms * 1e-3) / 1e9
-        peak = PEAK_HBM_GBPS
-    else:
-        achieved = dom["work"] / (dom_ms * 1e-3) / 1e12
-        peak = PEAK_BF16_TFLOPS
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        try:
-            with open(TRAFFIC_FILE) as f:
-                tr = json.load(f).get(wname, {})
-            if tr.get("kernel") == dom["kernel"] and \
-                    tr.get("source_hash") == kernel_source_hash(dom["kernel"]):
-                traffic = tr.get("bytes_per_launch")
-        except (OSError, ValueError):
-            traffic = None
+    for L in layers:
+        L.close()
+    del layers, outs
 
     value = cfg.T / (ms_step * 1e-3)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": K, "warmup": W, "ms_per_step": round(ms_step, 6), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if cfg.dtype == "f32" else "bf16",
         "data": "synthetic: seeded N(0,1) hidden states and random-init weights of the stated "
                 "distributions (no checkpoint or dataset)",
         "config": {"workload": wname, "T": cfg.T, "d_model": cfg.d, "d_ff": cfg.F,
@@ -608,11 +701,7 @@ def main():
                    "expert_weights": "fp8_e4m3_row_scaled" if args.fp8 else cfg.dtype,
                    "experts_touched": touched, "layer_instances": nl,
                    "device": props.name, "compute_units": props.multi_processor_count},
-        "roofline": {"bound": dom["bound"], "achieved": round(achieved, 2), "peak": peak,
-                     "unit": dom["unit"], "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": dom["kernel"], "avg_launch_us": round(dom_ms * 1e3, 3),
-                     "per_unit": dom["per_unit"], "units_per_launch": dom["units"],
-                     "unit_name": dom["unit_name"]},
+        "roofline": roofline_entry(dom, slots[dom["slot"]], counter_traffic(wname, dom["kernel"])),
         "layer": {"algorithmic_bytes": lbytes, "algorithmic_flops": lflops,
                   "hbm_GBps": round(lbytes / (ms_step * 1e-3) / 1e9, 1),
                   "mfma_frac": round(lflops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -622,15 +711,22 @@ def main():
                             "forwards_per_graph": nl, "replay_equals_eager": gr["matches_eager"]},
                   "kernel_us": {k_: round(v * 1e3, 3) for k_, v in slots.items()}},
     }
-    for L in layers:
-        L.close()
+    checked = [(inp, sel_gpu)]
+    if args.config == 1 and not args.fp8 and not args.no_prefill:
+        line["prefill"] = {}
+        for cid in (2, 4):
+            summ, pinp, psel = prefill_summary(cid, args, dev)
+            line["prefill"][f"T{pinp['cfg'].T}"] = summ
+            checked.append((pinp, psel))
     if not args.no_context:
         torch.cuda.synchronize()
-        line["context"] = hw_context(dev, props.multi_processor_count)
+        line["context"] = hw_context(dev)
         log(f"[bench] context: {line['context']}")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, q8)
+        line["cpu_baseline"]["routing_check"] = [routing_check(i, s_) for i, s_ in checked]
+        log(f"[bench] routing against the oracle: {line['cpu_baseline']['routing_check']}")
     print(json.dumps(line), flush=True)
 
 

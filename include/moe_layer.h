@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef struct moe_layer moe_layer_t; /* opaque; owned by the library */
 
@@ -228,8 +228,11 @@ moe_status_t moe_stack_create(int32_t n_layers, moe_layer_t* const* layers, int3
  * enable = 0 turns it off (the default); alpha in [0, 1) is the caller's
  * (alpha = 0 gives the plain routing).  The state is a [max_tokens, 64] fp32
  * buffer the stack allocated at create; a later moe_stack_forward or capture
- * uses the setting current at that call.  Errors: INVALID_ARG (handle, alpha),
- * UNSUPPORTED (fp32 layers). */
+ * uses the setting current at that call.  The averaged logit of expert e
+ * passes from one MoE layer to the next, so every MoE layer of the stack must
+ * have the same n_experts.  Errors: INVALID_ARG (handle, alpha, MoE layers
+ * with different n_experts; moe_stack_forward and moe_stack_capture check the
+ * last again), UNSUPPORTED (fp32 layers). */
 moe_status_t moe_stack_set_eda(moe_stack_t* stack, int32_t enable, float alpha);
 
 /* One pass through the stack, enqueued on `stream` (no host synchronisation,
@@ -239,6 +242,17 @@ moe_status_t moe_stack_set_eda(moe_stack_t* stack, int32_t enable, float alpha);
  * calls that overlap (on two streams) race.  Errors: INVALID_ARG, HIP. */
 moe_status_t moe_stack_forward(moe_stack_t* stack, const void* hidden_in, int32_t T,
                                void* hidden_out, void* stream);
+
+/* As moe_stack_forward, and also writes each layer's routing of this pass:
+ * routing points to n_layers moe_routing_out_t structs in HOST memory, the
+ * l-th naming (as for moe_layer_forward) DEVICE buffers for layer l, each
+ * member NULL or sized for T tokens and that layer's top_k and n_experts.
+ * Meant for checking a stack's routing layer by layer (for instance with
+ * depth averaging on).  Errors: as moe_stack_forward; INVALID_ARG for a NULL
+ * `routing` or a misaligned routing buffer. */
+moe_status_t moe_stack_forward_routing(moe_stack_t* stack, const void* hidden_in, int32_t T,
+                                       void* hidden_out, void* stream,
+                                       const moe_routing_out_t* routing);
 
 /* Record the launch sequence of moe_stack_forward(stack, hidden_in, T,
  * hidden_out) on `stream` (a created stream, not NULL) into a HIP graph owned

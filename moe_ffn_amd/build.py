@@ -3,9 +3,7 @@
 Usage: python -m moe_ffn_amd.build [--jobs N]
 
 Every source under csrc/ is compiled to an object in _build/ (in parallel),
-then linked into moe_ffn_amd/libmoe_layer.so.  The measurement probe under
-probe/ is linked separately into moe_ffn_amd/libmoe_probe.so (bench.py only).
-Both libraries are always rebuilt.
+then linked into moe_ffn_amd/libmoe_layer.so.  The library is always rebuilt.
 """
 
 from __future__ import annotations
@@ -22,8 +20,6 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe_layer.so")
-PROBE_LIB = os.path.join(HERE, "libmoe_probe.so")
-PROBE_SRC = os.path.join(HERE, "probe")
 ARCH = "gfx950"
 
 CFLAGS = [
@@ -72,17 +68,8 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
-    psrcs = sorted(os.path.join(PROBE_SRC, f) for f in os.listdir(PROBE_SRC) if f.endswith(".hip"))
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        pobjs = list(ex.map(_compile, psrcs))
-    tmp = PROBE_LIB + ".tmp"
-    r = subprocess.run([_hipcc(), "-shared", f"--offload-arch={ARCH}", "-o", tmp, *pobjs],
-                       capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, PROBE_LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources, {PROBE_LIB} from {len(psrcs)}")
+        print(f"built {LIB} from {len(srcs)} sources")
     return LIB
 
 

@@ -538,32 +538,18 @@ hipError_t launch_gemm(const FwdArgs& a) {
 
 // Gate/up on 384-row blocks (192 columns of d_ff) with an 8-k-step weight
 // queue and spans of up to 5 subtiles where 2 * d_ff divides into them, else
-// on 256-row blocks; the down projection on 256-row blocks, an 8-k-step queue
+// on 256-row blocks with a 16-k-step queue (d_model % 256 == 0 makes d/16 a
+// multiple of 16); the down projection on 256-row blocks, an 8-k-step queue
 // and spans of up to 6 subtiles (the registers' limit at that queue; a
 // 16-k-step queue at 5 subtiles times the same).  On the prefill workloads the
 // 384-row gate/up units are faster (fewer re-reads of the token tiles per
 // weight byte); the deeper queue that fits the 256-row units' registers did
 // not make up for it.
-#ifndef MOE_GU_CFG
-#define MOE_GU_CFG 3, 8, 1, 5   // RT, Q, OCC, TTM of the gate/up GEMM (2 * d_ff % 384 == 0)
-#endif
-#ifndef MOE_DN_CFG
-#define MOE_DN_CFG 2, 8, 1, 6   // of the down GEMM
-#endif
-namespace {
-template <int RT, int Q, int OCC, int TTM>
-struct Cfg {
-  static constexpr int kRT = RT;
-};
-}  // namespace
-
 hipError_t launch_experts_tile(const FwdArgs& a) {
-  const int ksd = a.dim.d / kKStep;
-  hipError_t err;
-  if ((2 * a.dim.F) % Geo<Cfg<MOE_GU_CFG>::kRT>::kRows == 0) err = launch_gemm<0, MOE_GU_CFG>(a);
-  else err = ksd % 16 == 0 ? launch_gemm<0, 2, 16, 1, 5>(a) : launch_gemm<0, 2, 8, 1, 5>(a);
+  hipError_t err = (2 * a.dim.F) % Geo<3>::kRows == 0 ? launch_gemm<0, 3, 8, 1, 5>(a)
+                                                      : launch_gemm<0, 2, 16, 1, 5>(a);
   if (err != hipSuccess) return err;
-  return launch_gemm<1, MOE_DN_CFG>(a);  // d_ff % 128 == 0: the k-steps fill whole loop bodies
+  return launch_gemm<1, 2, 8, 1, 6>(a);  // d_ff % 128 == 0: the k-steps fill whole loop bodies
 }
 
 }  // namespace moe

@@ -36,51 +36,18 @@
 namespace moe {
 
 namespace {
-#ifndef MOE_GU_SPLIT
-#define MOE_GU_SPLIT 8
-#endif
-constexpr int kSplit = MOE_GU_SPLIT;  // waves per gate/up weight tile (split of the reduction axis)
-#ifndef MOE_GU_TILES
-#define MOE_GU_TILES 1
-#endif
-constexpr int kGuTiles = MOE_GU_TILES;  // interleaved gate/up tiles (16 columns each) per workgroup
-#ifndef MOE_DOWN_SPLIT
-#define MOE_DOWN_SPLIT 8
-#endif
-constexpr int kSplitD = MOE_DOWN_SPLIT;  // waves per down-projection tile
-#ifndef MOE_GU_TILES_FP8
-#define MOE_GU_TILES_FP8 1
-#endif
-#ifndef MOE_GU_SPLIT_FP8
-#define MOE_GU_SPLIT_FP8 4
-#endif
-#ifndef MOE_DOWN_SPLIT_FP8
-#define MOE_DOWN_SPLIT_FP8 8
-#endif
+constexpr int kSplit = 8;     // waves per gate/up weight tile (split of the reduction axis)
+constexpr int kGuTiles = 1;   // interleaved gate/up tiles (16 columns each) per workgroup
+constexpr int kSplitD = 8;    // waves per down-projection tile
 // fp8 weights: tiles and waves per workgroup of the two streams
-constexpr int kGuTiles8 = MOE_GU_TILES_FP8, kSplit8 = MOE_GU_SPLIT_FP8;
-constexpr int kSplitD8 = MOE_DOWN_SPLIT_FP8;
-#ifndef MOE_STREAM_NT
-#define MOE_STREAM_NT 1
-#endif
-#ifndef MOE_STREAM_WAVES_EU
-#define MOE_STREAM_WAVES_EU 1  // waves per SIMD the register budget must allow
-#endif
+constexpr int kGuTiles8 = 1, kSplit8 = 4;
+constexpr int kSplitD8 = 8;
+// prefetch depth of the weight queues (k-steps; k-step pairs for fp8), at most
+constexpr int kStreamDepth = 4;
+constexpr int kStreamDepth8 = 4;
 
-__device__ __forceinline__ u32x4 ldw8(const uint8_t* p) {
-#if MOE_STREAM_NT
-  return ldg16_stream(p);
-#else
-  return ldg16(p);
-#endif
-}
-__device__ __forceinline__ u32x4 ldw(const uint16_t* p) {
-#if MOE_STREAM_NT
-  return ldg16_stream(p);
-#else
-  return ldg16(p);
-#endif
-}
+__device__ __forceinline__ u32x4 ldw8(const uint8_t* p) { return ldg16_stream(p); }
+__device__ __forceinline__ u32x4 ldw(const uint16_t* p) { return ldg16_stream(p); }
 
 // Split-K reduction spread over the waves: every wave parks its NACC
 // accumulator tiles in LDS; after a barrier, element i of tile q summed over
@@ -221,7 +188,7 @@ __device__ __forceinline__ void stream_mac_fp8(const uint8_t* const (&w)[NW], co
 // (NT interleaved tiles, S waves splitting the reduction axis).
 // The workgroups with ft == 0 also write the routing outputs of their expert.
 template <int D, bool FP8, int NT, int S>
-__global__ __launch_bounds__(64 * S, MOE_STREAM_WAVES_EU) void k_gateup_stream(
+__global__ __launch_bounds__(64 * S, 1) void k_gateup_stream(
     const uint16_t* __restrict__ wgu, const uint8_t* __restrict__ wgu8,
     const float* __restrict__ sgu, const uint16_t* __restrict__ xn,
     const int* __restrict__ sel, int n, int k, int E, int* __restrict__ counts,
@@ -294,7 +261,7 @@ __global__ __launch_bounds__(64 * S, MOE_STREAM_WAVES_EU) void k_gateup_stream(
 // output row of the token, k > 1 writes y (fp32) for the combine kernel.
 // SD waves split the reduction axis.
 template <int D, bool FP8, int SD>
-__global__ __launch_bounds__(64 * SD, MOE_STREAM_WAVES_EU) void k_down_stream(
+__global__ __launch_bounds__(64 * SD, 1) void k_down_stream(
     const uint16_t* __restrict__ wd, const uint8_t* __restrict__ wd8,
     const float* __restrict__ sd, const uint16_t* __restrict__ act,
     const int* __restrict__ sel, int n, int k, int E, const float* __restrict__ gate,
@@ -351,12 +318,6 @@ __global__ __launch_bounds__(64 * SD, MOE_STREAM_WAVES_EU) void k_down_stream(
 }
 
 namespace {
-#ifndef MOE_STREAM_DEPTH
-#define MOE_STREAM_DEPTH 4
-#endif
-#ifndef MOE_STREAM_DEPTH_FP8
-#define MOE_STREAM_DEPTH_FP8 4
-#endif
 // Largest prefetch depth (k-steps, or k-step pairs for fp8) up to dmax that
 // divides a wave's share.
 int pick_depth(int kper, int dmax) {
@@ -371,7 +332,7 @@ template <bool FP8, int NT, int S, int SD>
 hipError_t launch_streams(const FwdArgs& a) {
   const int d = a.dim.d, F = a.dim.F, E = a.dim.E;
   // queue depth: k-steps (bf16) or k-step pairs (fp8) in flight per wave
-  const int dmax = FP8 ? MOE_STREAM_DEPTH_FP8 : MOE_STREAM_DEPTH;
+  const int dmax = FP8 ? kStreamDepth8 : kStreamDepth;
   const int Da = pick_depth(d / kKStep / S / (FP8 ? 2 : 1), dmax);
   const int Db = pick_depth(F / kKStep / SD / (FP8 ? 2 : 1), dmax);
   auto gu = Da == 8 ? k_gateup_stream<8, FP8, NT, S> : Da == 4 ? k_gateup_stream<4, FP8, NT, S>

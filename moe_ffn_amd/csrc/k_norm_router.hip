@@ -9,7 +9,7 @@
 // One workgroup (256 threads) handles TOK consecutive tokens.  Each thread owns
 // 16-byte chunks of the d_model axis and accumulates, in one pass over h, the
 // sum of squares and the E dot products with the gain-folded router rows
-// (W_r[e][i] * g[i], exact in fp32 for bf16 operands):  z_e = inv_rms * sum_i
+// (W_r[e][i] * g[i], each product rounded once to fp32):  z_e = inv_rms * sum_i
 // (W_r g)_{e,i} h_i.  The TOK x E partial sums are reduced by a butterfly that
 // spreads the totals over the lanes, then across the four waves through LDS.
 // A second pass writes x' = g * h for the experts and inv_rms per token; the
@@ -19,7 +19,7 @@
 
 namespace moe {
 
-template <bool BF16, int EP, int TOK>
+template <int EP, int TOK>
 __global__ __launch_bounds__(256) void k_norm_router(const void* __restrict__ hidden, int T, int d,
                                                      const float* __restrict__ wrg,
                                                      const float* __restrict__ gain,
@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void k_norm_router(const void* __restrict__ hi
                                                      float eps, void* __restrict__ xn,
                                                      float* __restrict__ inv_out,
                                                      int* __restrict__ sel, float* __restrict__ gate) {
-  constexpr int VEC = BF16 ? 8 : 4;  // elements per 16-byte chunk
+  constexpr int VEC = 4;  // fp32 elements per 16-byte chunk
   constexpr int NV = TOK * EP;
   constexpr int R = NV >= 64 ? NV / 64 : 1;
   __shared__ float red[4][NV];
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void k_norm_router(const void* __restrict__ hi
   const int t0 = blockIdx.x * TOK;
   const int nch = d / VEC;
   const char* hb = reinterpret_cast<const char*>(hidden);
-  const size_t row_bytes = (size_t)d * (BF16 ? 2 : 4);
+  const size_t row_bytes = (size_t)d * 4;
 
   float acc[NV];
   float ss[TOK];
@@ -54,12 +54,8 @@ __global__ __launch_bounds__(256) void k_norm_router(const void* __restrict__ hi
     for (int t = 0; t < TOK; ++t) {
       if (t0 + t < T) {
         const u32x4 v = ldg16(hb + (size_t)(t0 + t) * row_bytes + (size_t)c * 16);
-        if constexpr (BF16) {
-          unpack8(v, h[t]);
-        } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) h[t][i] = __uint_as_float(v[i]);
-        }
+        for (int i = 0; i < 4; ++i) h[t][i] = __uint_as_float(v[i]);
       } else {
 #pragma unroll
         for (int i = 0; i < VEC; ++i) h[t][i] = 0.f;
@@ -168,16 +164,8 @@ __global__ __launch_bounds__(256) void k_norm_router(const void* __restrict__ hi
       if (t0 + t >= T) break;
       const u32x4 v = ldg16(hb + (size_t)(t0 + t) * row_bytes + (size_t)c * 16);
       u32x4 o;
-      if constexpr (BF16) {
-        float h[8];
-        unpack8(v, h);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          o[i] = pack_bf16x2(h[2 * i] * g[2 * i], h[2 * i + 1] * g[2 * i + 1]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(__uint_as_float(v[i]) * g[i]);
-      }
+      for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(__uint_as_float(v[i]) * g[i]);
       stg16(reinterpret_cast<char*>(xn) + (size_t)(t0 + t) * row_bytes + (size_t)c * 16, o);
     }
   }
@@ -186,7 +174,7 @@ __global__ __launch_bounds__(256) void k_norm_router(const void* __restrict__ hi
 namespace {
 constexpr int tok_big(int ep) { return ep >= 64 ? 2 : (128 / ep > 16 ? 16 : 128 / ep); }
 
-template <bool BF16, int EP>
+template <int EP>
 hipError_t launch_ep(const FwdArgs& a) {
   constexpr int TB = tok_big(EP);
   constexpr int TS = TB < 2 ? TB : 2;
@@ -194,29 +182,28 @@ hipError_t launch_ep(const FwdArgs& a) {
   const bool small = (T + TB - 1) / TB < 256;
   const KEv& ev = a.ev[kSlotNormRouter];
   if (small)
-    return launch(k_norm_router<BF16, EP, TS>, dim3((T + TS - 1) / TS), dim3(256), a.stream, ev,
+    return launch(k_norm_router<EP, TS>, dim3((T + TS - 1) / TS), dim3(256), a.stream, ev,
                   a.hidden, T, a.dim.d, a.wrg, a.gain, a.bias, a.dim.E, a.dim.k, a.dim.eps, a.xn,
                   a.inv, a.sel, a.gate);
-  return launch(k_norm_router<BF16, EP, TB>, dim3((T + TB - 1) / TB), dim3(256), a.stream, ev,
+  return launch(k_norm_router<EP, TB>, dim3((T + TB - 1) / TB), dim3(256), a.stream, ev,
                 a.hidden, T, a.dim.d, a.wrg, a.gain, a.bias, a.dim.E, a.dim.k, a.dim.eps, a.xn,
                 a.inv, a.sel, a.gate);
 }
 
-template <bool BF16>
-hipError_t launch_dtype(const FwdArgs& a) {
+hipError_t launch_by_experts(const FwdArgs& a) {
   switch (a.dim.EP) {
-    case 1: return launch_ep<BF16, 1>(a);
-    case 2: return launch_ep<BF16, 2>(a);
-    case 4: return launch_ep<BF16, 4>(a);
-    case 8: return launch_ep<BF16, 8>(a);
-    case 16: return launch_ep<BF16, 16>(a);
-    case 32: return launch_ep<BF16, 32>(a);
-    case 64: return launch_ep<BF16, 64>(a);
+    case 1: return launch_ep<1>(a);
+    case 2: return launch_ep<2>(a);
+    case 4: return launch_ep<4>(a);
+    case 8: return launch_ep<8>(a);
+    case 16: return launch_ep<16>(a);
+    case 32: return launch_ep<32>(a);
+    case 64: return launch_ep<64>(a);
     default: return hipErrorInvalidValue;
   }
 }
 }  // namespace
 
-hipError_t launch_norm_router(const FwdArgs& a) { return launch_dtype<false>(a); }
+hipError_t launch_norm_router(const FwdArgs& a) { return launch_by_experts(a); }
 
 }  // namespace moe

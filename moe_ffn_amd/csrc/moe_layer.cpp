@@ -630,6 +630,18 @@ void stack_release(moe_stack* S) {
   delete S;
 }
 
+// Depth averaging carries one expert's logit from a MoE layer to the next, so
+// every MoE layer (n_experts > 1) of the stack must have the same n_experts.
+bool stack_moe_experts_agree(const moe_stack* S) {
+  int E = 0;
+  for (const moe_layer_t* L : S->layers) {
+    if (L->dim.E <= 1) continue;
+    if (E != 0 && L->dim.E != E) return false;
+    E = L->dim.E;
+  }
+  return true;
+}
+
 moe_status_t stack_check(moe_stack* S, const void* hin, int32_t T, void* hout) {
   if (S == nullptr || S->magic != kStackMagic) return fail(MOE_ERR_INVALID_ARG, "invalid stack handle");
   if (T < 0 || T > S->max_tokens)
@@ -645,12 +657,16 @@ moe_status_t stack_check(moe_stack* S, const void* hin, int32_t T, void* hout) {
   if (dev != S->device) return fail(MOE_ERR_INVALID_ARG, "the current device is not the stack's device");
   for (moe_layer_t* L : S->layers)
     if (L == nullptr || L->magic != kMagic) return fail(MOE_ERR_INVALID_ARG, "a layer of the stack was destroyed");
+  if (S->eda_on && !stack_moe_experts_agree(S))
+    return fail(MOE_ERR_INVALID_ARG,
+                "depth averaging needs the same n_experts in every MoE layer of the stack");
   return MOE_OK;
 }
 
 // The launch sequence of one stack forward (no validation, no synchronisation).
+// routing: null, or one routing-output struct per layer.
 moe_status_t stack_enqueue(moe_stack* S, const void* hin, int32_t T, void* hout, hipStream_t s,
-                           bool allow_sync) {
+                           bool allow_sync, const moe_routing_out_t* routing = nullptr) {
   if (T == 0) return MOE_OK;
   const size_t n = (size_t)T * S->d;
   const void* cur = hin;
@@ -659,7 +675,8 @@ moe_status_t stack_enqueue(moe_stack* S, const void* hin, int32_t T, void* hout,
   for (int l = 0; l < nl; ++l) {
     const bool moe = S->layers[l]->dim.E > 1;
     float* eda = S->eda_on && moe ? S->eda : nullptr;
-    moe_status_t st = forward_impl(S->layers[l], cur, T, S->y, s, nullptr, allow_sync, eda,
+    moe_status_t st = forward_impl(S->layers[l], cur, T, S->y, s,
+                                   routing != nullptr ? &routing[l] : nullptr, allow_sync, eda,
                                    S->eda_alpha, first_moe);
     if (moe) first_moe = false;
     if (st != MOE_OK) return st;
@@ -727,6 +744,13 @@ moe_status_t moe_stack_create(int32_t n_layers, moe_layer_t* const* layers, int3
       (void)hipGetLastError();
       return fail(MOE_ERR_OOM, std::string("stack router state: ") + hipGetErrorString(he));
     }
+    // never read before the first MoE layer of a pass writes it; cleared so
+    // that no path can see uninitialised memory
+    he = hipMemset(S->eda, 0, (size_t)max_tokens * 64 * 4);
+    if (he != hipSuccess) {
+      stack_release(S);
+      return hip_fail(he, "stack router state");
+    }
   }
   S->magic = kStackMagic;
   *out = S;
@@ -740,6 +764,9 @@ moe_status_t moe_stack_set_eda(moe_stack_t* S, int32_t enable, float alpha) {
     return fail(MOE_ERR_UNSUPPORTED, "depth averaging needs bf16 layers");
   if (enable && !(alpha >= 0.f && alpha < 1.f))
     return fail(MOE_ERR_INVALID_ARG, "alpha must be in [0, 1)");
+  if (enable && !stack_moe_experts_agree(S))
+    return fail(MOE_ERR_INVALID_ARG,
+                "depth averaging needs the same n_experts in every MoE layer of the stack");
   S->eda_on = enable != 0;
   S->eda_alpha = enable ? alpha : 0.f;
   return MOE_OK;
@@ -751,6 +778,17 @@ moe_status_t moe_stack_forward(moe_stack_t* S, const void* hidden_in, int32_t T,
   moe_status_t st = stack_check(S, hidden_in, T, hidden_out);
   if (st != MOE_OK) return st;
   return stack_enqueue(S, hidden_in, T, hidden_out, reinterpret_cast<hipStream_t>(stream), true);
+}
+
+moe_status_t moe_stack_forward_routing(moe_stack_t* S, const void* hidden_in, int32_t T,
+                                       void* hidden_out, void* stream,
+                                       const moe_routing_out_t* routing) {
+  g_err.clear();
+  moe_status_t st = stack_check(S, hidden_in, T, hidden_out);
+  if (st != MOE_OK) return st;
+  if (routing == nullptr) return fail(MOE_ERR_INVALID_ARG, "routing is NULL");
+  return stack_enqueue(S, hidden_in, T, hidden_out, reinterpret_cast<hipStream_t>(stream), true,
+                       routing);
 }
 
 moe_status_t moe_stack_capture(moe_stack_t* S, const void* hidden_in, int32_t T, void* hidden_out,

@@ -27,7 +27,8 @@ EXPORTS = ("moe_abi_version", "moe_last_error", "moe_layer_create", "moe_layer_c
            "moe_layer_set_bias", "moe_layer_get_bias", "moe_layer_update_bias",
            "moe_layer_timing_start",
            "moe_layer_timing_stop", "moe_layer_destroy", "moe_stack_create", "moe_stack_forward",
-           "moe_stack_capture", "moe_stack_replay", "moe_stack_destroy", "moe_stack_set_eda")
+           "moe_stack_capture", "moe_stack_replay", "moe_stack_destroy", "moe_stack_set_eda",
+           "moe_stack_forward_routing")
 TIMED_SLOTS = ("norm_router", "route_permute", "experts_gate_up", "experts_down", "combine",
                "gather")
 
@@ -110,6 +111,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                       ctypes.c_void_p]
+    lib.moe_stack_forward_routing.restype = ctypes.c_int
+    lib.moe_stack_forward_routing.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                              ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.POINTER(RoutingOut)]
     lib.moe_stack_replay.restype = ctypes.c_int
     lib.moe_stack_replay.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     lib.moe_stack_destroy.restype = None
@@ -209,15 +214,7 @@ class MoELayer:
         r = None
         rp = None
         if routing:
-            dev = hidden.device
-            n = T * self.k
-            r = {"sel": torch.empty((T, self.k), dtype=torch.int32, device=dev),
-                 "gate": torch.empty((T, self.k), dtype=torch.float32, device=dev),
-                 "counts": torch.empty(self.E, dtype=torch.int32, device=dev),
-                 "offsets": torch.empty(self.E + 1, dtype=torch.int32, device=dev),
-                 "gather": torch.empty(n, dtype=torch.int32, device=dev),
-                 "scatter": torch.empty(n, dtype=torch.int32, device=dev)}
-            rp = RoutingOut(**{k: v.data_ptr() for k, v in r.items()})
+            r, rp = self.routing_buffers(T, hidden.device)
         st = self._lib.moe_layer_forward(self.handle, ctypes.c_void_p(hidden.data_ptr()), T,
                                          ctypes.c_void_p(out.data_ptr()),
                                          ctypes.c_void_p(_stream_ptr(stream)),
@@ -226,6 +223,17 @@ class MoELayer:
         return (out, r) if routing else out
 
     __call__ = forward
+
+    def routing_buffers(self, T: int, dev) -> tuple[dict, RoutingOut]:
+        """Fresh routing outputs for a forward over T tokens, and their struct."""
+        n = T * self.k
+        r = {"sel": torch.empty((T, self.k), dtype=torch.int32, device=dev),
+             "gate": torch.empty((T, self.k), dtype=torch.float32, device=dev),
+             "counts": torch.empty(self.E, dtype=torch.int32, device=dev),
+             "offsets": torch.empty(self.E + 1, dtype=torch.int32, device=dev),
+             "gather": torch.empty(n, dtype=torch.int32, device=dev),
+             "scatter": torch.empty(n, dtype=torch.int32, device=dev)}
+        return r, RoutingOut(**{k: v.data_ptr() for k, v in r.items()})
 
     def set_bias(self, b: torch.Tensor, stream=None):
         if not (b.is_cuda and b.dtype == torch.float32 and b.numel() == self.E and b.is_contiguous()):
@@ -312,6 +320,18 @@ class MoEStack:
         return out
 
     __call__ = forward
+
+    def forward_routing(self, hidden: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+        """One pass that also returns every layer's routing (a list of dicts as
+        from MoELayer.forward(routing=True)); see moe_stack_forward_routing."""
+        out = self._io(hidden, out)
+        T = hidden.shape[0]
+        bufs = [L.routing_buffers(T, hidden.device) for L in self.layers]
+        arr = (RoutingOut * len(bufs))(*[b[1] for b in bufs])
+        _check(self._lib, self._lib.moe_stack_forward_routing(
+            self.handle, ctypes.c_void_p(hidden.data_ptr()), T, ctypes.c_void_p(out.data_ptr()),
+            ctypes.c_void_p(_stream_ptr(stream)), arr))
+        return out, [b[0] for b in bufs]
 
     def capture(self, hidden: torch.Tensor, out: torch.Tensor, stream):
         """Record one pass (these pointers, this T) into the stack's HIP graph."""

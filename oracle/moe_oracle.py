@@ -271,9 +271,14 @@ def depth_average(z_prev, z, alpha: float) -> np.ndarray:
     order, z~_l = alpha * z~_{l-1} + (1 - alpha) * z_l, with z~ = z at the
     first MoE layer; alpha in [0, 1) is the caller's (alpha = 0: no
     smoothing).  The layer's bias b_l is added after the averaging (it steers
-    the choice only), and the gates come from z~."""
+    the choice only), and the gates come from z~.  The average runs per
+    (token, expert), so it is defined only between layers with the same
+    experts: logits of different widths raise ValueError."""
     if z_prev is None:
         return _f64(z)
+    if np.shape(z_prev) != np.shape(z):
+        raise ValueError(f"depth averaging needs logits of one shape, got {np.shape(z_prev)} "
+                         f"and {np.shape(z)}")
     return alpha * _f64(z_prev) + (1.0 - alpha) * _f64(z)
 
 
@@ -290,10 +295,16 @@ def stack_forward(layer_vals: list, H, ks: list, eps: float, forced_sels=None,
     Everything stays in float64; forced_sels[l] optionally replaces layer l's
     routing choice.  eda_alpha: the MoE layers' (more than one expert) logits
     are depth-averaged (O11) in stack order; dense layers carry no router
-    state.  Returns the final h and every layer's routing and top-k margins.
+    state.  Returns the final h and every layer's routing (the forced one
+    where given), the oracle's own choice and the top-k margins.
     """
     h = _f64(H)
-    sels, margins = [], []
+    sels, own, margins = [], [], []
+    if eda_alpha is not None:
+        widths = {np.asarray(v["w_router"]).shape[0] for v in layer_vals}
+        if len(widths - {1}) > 1:
+            raise ValueError(f"depth averaging needs one expert count over the MoE layers, "
+                             f"got {sorted(widths - {1})}")
     zp = None
     for l, vals in enumerate(layer_vals):
         v = dict(vals, hidden=h)
@@ -306,8 +317,9 @@ def stack_forward(layer_vals: list, H, ks: list, eps: float, forced_sels=None,
             r = oracle_forward(v, k=ks[l], forced_sel=fs, eps=eps)
         h = h + r["out"]
         sels.append(r["sel"])
+        own.append(r["sel_oracle"])
         margins.append(r["margin"])
-    return {"out": h, "sel": sels, "margin": margins}
+    return {"out": h, "sel": sels, "sel_oracle": own, "margin": margins}
 
 
 # fp8 expert weights ------------------------------------------------------------

@@ -53,6 +53,33 @@ def test_dominant_kernel_work():
     assert lbytes == 16 * 3 * F * d * 2 + 2 * 4096 * d * 2 + 16 * d * 2 + 16 * 4 + d * 2
 
 
+def test_dominant_kernel_of_the_fp32_layer():
+    d, F = 256, 512
+    c0 = bench.dominant_kernel(WORKLOADS[0], np.array([20, 0, 30, 14]))
+    assert c0["kernel"] == "k_gateup_f32" and c0["bound"] == "hbm"
+    assert c0["units"] == 3 and c0["work"] == 3 * 2 * F * d * 4
+    lbytes, lflops, touched = bench.layer_work(WORKLOADS[0], np.array([20, 0, 30, 14]))
+    assert touched == 3 and lbytes == 3 * 3 * F * d * 4 + 2 * 64 * d * 4 + 4 * d * 4 + 4 * 4 + d * 4
+    assert bench.kernel_source_hash("k_gateup_f32")
+
+
+def test_routing_check_counts_near_ties_and_mismatches():
+    from oracle import moe_oracle as O
+    from synth import make_inputs, gen
+    inp = make_inputs(0)
+    vals = gen.values_f32(inp)
+    x = O.rmsnorm(vals["hidden"], vals["gain"], 1e-6)
+    _, sc = O.router_scores(x, vals["w_router"], vals["bias"])
+    sel, margin = O.select_topk(sc, 1)
+    r = bench.routing_check(inp, sel)
+    assert r["firm_mismatches"] == 0 and r["near_tie_flips"] == 0
+    assert r["near_ties"] == int(np.sum(margin < O.MARGIN_TOL)) and r["tokens"] == 64
+    bad = sel.copy()
+    t = int(np.argmax(margin))          # the firmest token, routed elsewhere
+    bad[t, 0] = (bad[t, 0] + 1) % 4
+    assert bench.routing_check(inp, bad)["firm_mismatches"] == 1
+
+
 def _write_run(dirname, rows):
     os.makedirs(dirname)
     with open(os.path.join(dirname, "run_counter_collection.csv"), "w", newline="") as f:

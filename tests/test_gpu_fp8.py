@@ -5,7 +5,7 @@ The layer is built with moe_layer_create_fp8 from codes and per-row scales
 weights value(code) * scale (oracle.fp8_weights), so the comparison measures
 the kernels' arithmetic, not the quantisation.  Covers the decode streams
 (k-step-pair fp8 loads) and the tile GEMMs (bf16 code values, scales in the
-epilogue) at full size and at ragged reduced sizes, top-1 and top-2.
+epilogue) at full size (every output row) and at ragged reduced sizes, top-1 and top-2.
 """
 
 from dataclasses import replace
@@ -74,10 +74,10 @@ def family_fp8_layer(cid: int, k: int):
     (1, None, 1, None),   # decode T = 32: fp8 streams, full rows
     (1, 7, 1, None),      # decode, ragged
     (3, 32, 2, None),     # decode + combine (64 assignments)
-    (2, None, 1, 512),    # prefill T = 4096: tile GEMMs, sampled rows
+    (2, None, 1, None),   # prefill T = 4096: tile GEMMs, every row
     (2, 300, 1, None),    # tile GEMMs, ragged tails
     (3, 200, 2, None),    # tile GEMMs + combine
-    (3, None, 2, 512),    # top-2 T = 4096
+    (3, None, 2, None),   # top-2 T = 4096, every row
 ])
 def test_fp8_parity(cid, T, k, sample):
     base = replace(WORKLOADS[cid], k=k)
@@ -85,6 +85,7 @@ def test_fp8_parity(cid, T, k, sample):
     st = check_parity(inp, family_fp8_layer(cid, k), sample=sample, vals=fp8_vals(inp),
                       label=f"fp8 c{cid} T={inp['cfg'].T} k={k}")
     assert st["rms_err_rel"] < 5e-3
+    assert st["rows_compared"] == inp["cfg"].T
 
 
 def test_fp8_matches_bf16_layer_on_code_values():

@@ -1,11 +1,12 @@
 """Parity of the HIP layer (through the C ABI) with the fp64 oracle.
 
-Covers the five workloads at full size (routing and dispatch in full, output
-rows in full or on a sample the oracle computes one by one), reduced sizes that
-span several tiles with ragged tails on both expert paths, and the edge cases:
-T = 0, T = 1, T = max_tokens, every token on one expert, a single-expert
-(dense) layer, expert counts from 5 to 64 and top-k up to 8 on both paths and
-both dtypes, NaN rows, bias updates, determinism and bad arguments.
+Covers the five workloads at full size (routing, dispatch and every output
+row), reduced sizes that span several tiles with ragged tails on both expert
+paths, and the edge cases: T = 0, T = 1, T = max_tokens, every token on one
+expert, exact score ties (the lower expert index wins on every router), a
+single-expert (dense) layer, expert counts from 5 to 64 and top-k up to 8 on
+both paths and both dtypes, NaN rows, bias updates, determinism and bad
+arguments.
 """
 
 from dataclasses import replace
@@ -55,21 +56,23 @@ def test_decode_bf16_T32_full():
     check_parity(inp, family_layer(1), label="c1 decode T=32")
 
 
-def test_prefill_bf16_T4096_full_routing_sampled_rows():
+def test_prefill_bf16_T4096_full():
     inp = make_inputs(2)
-    check_parity(inp, family_layer(2), sample=512, label="c2 prefill T=4096")
+    st = check_parity(inp, family_layer(2), label="c2 prefill T=4096")
+    assert st["rows_compared"] == 4096
 
 
-def test_top2_bf16_T4096_full_routing_sampled_rows():
+def test_top2_bf16_T4096_full():
     inp = make_inputs(3)
-    check_parity(inp, family_layer(3), sample=512, label="c3 top-2 T=4096")
+    st = check_parity(inp, family_layer(3), label="c3 top-2 T=4096")
+    assert st["rows_compared"] == 4096
 
 
-def test_skewed_bf16_T16384_full_routing_sampled_rows():
+def test_skewed_bf16_T16384_full():
     inp = make_inputs(4)
     layer = family_layer(4)
-    st = check_parity(inp, layer, sample=512, label="c4 skewed T=16384")
-    assert st["rows_compared"] >= 500
+    st = check_parity(inp, layer, label="c4 skewed T=16384")
+    assert st["rows_compared"] == 16384
     _, r = layer.forward(to_torch(inp["hidden"], "bf16"), routing=True)
     counts = r["counts"].cpu().numpy()
     assert counts.sum() == 16384 and (counts == 0).sum() >= 1
@@ -98,9 +101,10 @@ def test_reduced_sizes_full_rows(cid, T, k):
 # workloads above (the down projection takes at most 4 subtiles per unit at
 # 2048 assignments and 5 at 12288, 6 at 4096 and 16384).
 @pytest.mark.parametrize("T", [2048, 12288])
-def test_other_span_caps_sampled_rows(T):
+def test_other_span_caps(T):
     inp = make_inputs(WORKLOADS[2], T=T)
-    check_parity(inp, family_layer(2), sample=384, label=f"c2 T={T}")
+    st = check_parity(inp, family_layer(2), label=f"c2 T={T}")
+    assert st["rows_compared"] == T
 
 
 def test_tiny_fp32_ragged_and_top2():
@@ -133,6 +137,40 @@ def test_every_token_on_one_expert():
         assert c[5] == T and c.sum() == T
         assert np.array_equal(r["gather"].cpu().numpy(), np.arange(T))
         assert st["near_ties"] == 0
+
+
+@pytest.mark.parametrize("dtype,T,k", [
+    ("bf16", 32, 1),    # per-token router (decode path)
+    ("bf16", 16, 2),
+    ("bf16", 300, 1),   # MFMA router (tile path)
+    ("bf16", 300, 2),
+    ("f32", 40, 1),     # fp32 router
+    ("f32", 40, 2),
+])
+def test_exact_score_tie_goes_to_the_lower_expert(dtype, T, k):
+    """Two experts with the same router row and the same bias score every
+    token identically.  The tie is exact, so the near-tie exemption does not
+    apply: the lower index must come first (and for top-2 the pair must be
+    (lower, higher) with equal gates)."""
+    base = WORKLOADS[1] if dtype == "bf16" else WORKLOADS[0]
+    lo, hi = (3, 9) if dtype == "bf16" else (1, 3)
+    inp = make_inputs(replace(base, k=k), T=T)
+    wr = inp["w_router"].copy()
+    wr[hi] = wr[lo]
+    b = np.asarray(inp["bias"], np.float32).copy()
+    b[lo] = b[hi] = 8.0   # both far above every other score
+    inp = dict(inp, w_router=wr, bias=b)
+    layer = make_layer(inp, max_tokens=T)
+    st = check_parity(inp, layer, label=f"tie {dtype} T={T} k={k}")
+    assert st["near_ties"] == T   # margin 0 on every token
+    _, r = layer.forward(to_torch(inp["hidden"], dtype), routing=True)
+    sel = r["sel"].cpu().numpy()
+    assert np.all(sel[:, 0] == lo), np.unique(sel[:, 0])
+    if k == 2:
+        assert np.all(sel[:, 1] == hi)
+        g = r["gate"].cpu().numpy()
+        assert np.all(g == 0.5)   # softmax of two equal logits
+    layer.close()
 
 
 @pytest.mark.parametrize("dtype,d,F", [("bf16", 256, 128), ("f32", 64, 96)])
@@ -175,12 +213,12 @@ def test_expert_counts_and_top_k_up_to_the_limits(dtype, E, k, T):
 ])
 def test_permutation_over_many_groups(E, k, T):
     """The two-launch permutation at sizes where its groups grow past four
-    chunks each: dispatch arrays in full, output rows sampled."""
+    chunks each: dispatch arrays and output rows in full."""
     cfg = LayerConfig(93, f"groups_bf16_E{E}_k{k}_T{T}", T=T, d=256, E=E, F=256, k=k,
                       dtype="bf16", bias="normal", family=f"groups_bf16_d256_E{E}_F256")
     inp = make_inputs(cfg)
-    st = check_parity(inp, make_layer(inp, max_tokens=T), sample=256, label=cfg.name)
-    assert st["rows_compared"] >= 256
+    st = check_parity(inp, make_layer(inp, max_tokens=T), label=cfg.name)
+    assert st["rows_compared"] == T
 
 
 def test_deterministic_bytes():

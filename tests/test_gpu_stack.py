@@ -4,8 +4,10 @@ A stack h_{l+1} = h_l + FFN_l(h_l) over dense (one-expert), top-1 and top-2
 layers must equal, bit for bit, the same layers run one by one through the
 layer ABI with the bf16 residual add done in torch; it must follow the fp64
 oracle's stack (O10, on the GPU's own routing of every layer) to the layer
-tolerance; and its captured HIP graph must reproduce eager runs on every
-replay, also after the input buffer's contents change.
+tolerance, at d_model = 256 and at the full width d_model = 2048; and its
+captured HIP graph must reproduce eager runs on every replay, also after the
+input buffer's contents change.  With the router logits depth-averaged (O11)
+every MoE layer's routing is compared with the oracle's, layer by layer.
 """
 
 from dataclasses import replace
@@ -31,23 +33,53 @@ def _need_gpu():
     load_library()
 
 
-def _small_stack_inputs(T):
+def _small_stack_inputs(T, E=4):
     """Six layers at d=256, F=512: dense, dense, MoE top-1 (x2), MoE top-2, dense."""
-    moe = LayerConfig(80, "stack_moe_bf16_d256_E4_F512", T=T, d=256, E=4, F=512, k=1,
-                      dtype="bf16", bias="normal", family="stack_moe_d256")
+    moe = LayerConfig(80, f"stack_moe_bf16_d256_E{E}_F512", T=T, d=256, E=E, F=512, k=1,
+                      dtype="bf16", bias="normal", family=f"stack_moe_d256_E{E}")
     dense = LayerConfig(81, "stack_dense_bf16_d256_F512", T=T, d=256, E=1, F=512, k=1,
                         dtype="bf16", bias="zero", family="stack_dense_d256")
     plan = [(dense, 1), (dense, 1), (moe, 1), (moe, 1), (moe, 2), (dense, 1)]
     return [make_inputs(replace(cfg, k=k), T=T, layer=l) for l, (cfg, k) in enumerate(plan)]
 
 
-def _loop(layers, h):
+def _loop(layers, h, inputs=None):
+    """The stack as a loop of layer forwards with the bf16 residual add in
+    torch; `inputs`, if a list, receives every layer's input (as float64)."""
     sels = []
     for L in layers:
+        if inputs is not None:
+            inputs.append(out_to_f64(h))
         y, r = L.forward(h, routing=True)
         sels.append(r["sel"].cpu().numpy())
         h = (h.float() + y.float()).to(torch.bfloat16)
     return h, sels
+
+
+def _check_layer_routing(vals, h_in, sels, ks, eps, alpha=None, label=""):
+    """Each layer's routing against the oracle's router (O1-O3, with O11's
+    depth averaging when alpha is given) run on the input that layer really
+    received on the GPU (the bf16 residual stream): bit-exact for every token
+    whose top-k margin is at least 1e-3.  The fp64 stack of O10 carries an
+    unrounded residual, so its own later-layer choices are not comparable
+    token by token.  Returns (near-ties, flips) summed over the layers."""
+    near = flips = 0
+    zp = None
+    none = np.zeros(0, np.int64)
+    for l, v in enumerate(vals):
+        moe = np.asarray(v["w_router"]).shape[0] > 1
+        if alpha is not None and moe:
+            r = O.oracle_forward(dict(v, hidden=h_in[l]), k=ks[l], eps=eps, tokens=none,
+                                 z_prev=zp, eda_alpha=alpha)
+            zp = r["z"]
+        else:
+            r = O.oracle_forward(dict(v, hidden=h_in[l]), k=ks[l], eps=eps, tokens=none)
+        firm = r["margin"] >= O.MARGIN_TOL
+        same = (sels[l] == r["sel_oracle"]).all(axis=1)
+        assert np.all(same | ~firm), (label, l, np.nonzero(~same & firm)[0][:5])
+        near += int(np.sum(~firm))
+        flips += int(np.sum(~same & ~firm))
+    return near, flips
 
 
 @pytest.mark.parametrize("T", [48, 300])
@@ -58,12 +90,14 @@ def test_small_stack_matches_layer_loop_and_oracle(T):
     stack = MoEStack(layers, max_tokens=T)
     h0 = to_torch(inps[0]["hidden"], "bf16")
     out = stack.forward(h0)
-    ref_loop, sels = _loop(layers, h0)
+    h_in = []
+    ref_loop, sels = _loop(layers, h0, h_in)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref_loop.view(torch.int16))
     vals = [values_f32(inp) for inp in inps]
-    ref = O.stack_forward(vals, vals[0]["hidden"], [inp["cfg"].k for inp in inps],
-                          inps[0]["cfg"].eps, forced_sels=sels)["out"]
+    ks = [inp["cfg"].k for inp in inps]
+    _check_layer_routing(vals, h_in, sels, ks, inps[0]["cfg"].eps, label=f"d256 T={T}")
+    ref = O.stack_forward(vals, vals[0]["hidden"], ks, inps[0]["cfg"].eps, forced_sels=sels)["out"]
     err = np.abs(out_to_f64(out) - ref).max()
     assert err <= TOL["bf16"] * np.abs(ref).max(), (err, np.abs(ref).max())
     stack.close()
@@ -97,22 +131,37 @@ def test_stack_graph_replays_match_eager():
     stack.close()
 
 
-def test_full_width_stack_matches_layer_loop():
-    """d=2048, F=3072: dense, MoE top-1, MoE top-2 (16 experts), dense; T=32."""
-    from moe_ffn_amd import MoEStack
-    T = 32
+def _full_width_inputs(T):
+    """d=2048, F=3072: dense, MoE top-1, MoE top-2 (16 experts), dense."""
     dense = LayerConfig(82, "stack_dense_bf16_d2048_F3072", T=T, d=2048, E=1, F=3072, k=1,
                         dtype="bf16", bias="zero", family="stack_dense_d2048")
-    inps = [make_inputs(dense, T=T, layer=0), make_inputs(WORKLOADS[1], T=T),
+    return [make_inputs(dense, T=T, layer=0), make_inputs(WORKLOADS[1], T=T),
             make_inputs(replace(WORKLOADS[1], k=2), T=T), make_inputs(dense, T=T, layer=1)]
+
+
+@pytest.mark.parametrize("T", [32, 200])
+def test_full_width_stack_matches_layer_loop_and_oracle(T):
+    """Four layers at the backbone's width; T = 32 runs the decode path of
+    every layer, T = 200 the tiled one."""
+    from moe_ffn_amd import MoEStack
+    inps = _full_width_inputs(T)
     layers = [make_layer(inp, max_tokens=T) for inp in inps]
     stack = MoEStack(layers, max_tokens=T)
     h0 = to_torch(inps[1]["hidden"], "bf16")
     out = stack.forward(h0)
-    ref_loop, _ = _loop(layers, h0)
+    h_in = []
+    ref_loop, sels = _loop(layers, h0, h_in)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref_loop.view(torch.int16))
+    vals = [values_f32(inp) for inp in inps]
+    ks = [inp["cfg"].k for inp in inps]
+    _check_layer_routing(vals, h_in, sels, ks, inps[0]["cfg"].eps, label=f"d2048 T={T}")
+    ref = O.stack_forward(vals, vals[1]["hidden"], ks, inps[0]["cfg"].eps, forced_sels=sels)
+    err = np.abs(out_to_f64(out) - ref["out"]).max()
+    assert err <= TOL["bf16"] * np.abs(ref["out"]).max(), (err, np.abs(ref["out"]).max())
     stack.close()
+    for L in layers:
+        L.close()
 
 
 # ------------------------------- depth averaging of the router logits (O11)
@@ -134,6 +183,56 @@ def test_eda_at_rate_zero_equals_the_plain_stack():
         stack.close()
 
 
+def _eda_parity(inps, T, alpha, label):
+    """One depth-averaged pass with every layer's routing: each MoE layer's
+    choice equals the oracle's (O1-O3 with O11 on the layer inputs the GPU
+    computed) for every token whose top-k margin is at least 1e-3, the
+    dispatch arrays equal O5-O6 of the GPU's choice, and the output follows
+    the oracle's stack (O10 with O11 on the GPU's routing) to the layer
+    tolerance.  Returns (near-ties, flips) over the layers."""
+    from moe_ffn_amd import MoEStack
+    vals = [values_f32(inp) for inp in inps]
+    ks = [inp["cfg"].k for inp in inps]
+    layers = [make_layer(inp, max_tokens=T) for inp in inps]
+    stack = MoEStack(layers, max_tokens=T)
+    stack.set_eda(alpha)
+    h0 = to_torch(inps[0]["hidden"], "bf16")
+    out, routs = stack.forward_routing(h0)
+    torch.cuda.synchronize()
+    sels = [r["sel"].cpu().numpy() for r in routs]
+    # every layer's input on the GPU: the output of the stack of the layers
+    # before it, depth averaging on (the same launches as the full pass)
+    h_in = [out_to_f64(h0)]
+    for l in range(1, len(layers)):
+        pre = MoEStack(layers[:l], max_tokens=T)
+        if any(L.E > 1 for L in layers[:l]):
+            pre.set_eda(alpha)
+        h_in.append(out_to_f64(pre.forward(h0)))
+        pre.close()
+    torch.cuda.synchronize()
+    near, flips = _check_layer_routing(vals, h_in, sels, ks, inps[0]["cfg"].eps, alpha, label)
+    ref = O.stack_forward(vals, vals[0]["hidden"], ks, inps[0]["cfg"].eps, forced_sels=sels,
+                          eda_alpha=alpha)
+    for l, inp in enumerate(inps):
+        c, o = O.histogram(sels[l], inp["cfg"].E)
+        g, sc = O.permutation(sels[l])
+        np.testing.assert_array_equal(routs[l]["counts"].cpu().numpy(), c)
+        np.testing.assert_array_equal(routs[l]["offsets"].cpu().numpy(), o)
+        np.testing.assert_array_equal(routs[l]["gather"].cpu().numpy(), g)
+        np.testing.assert_array_equal(routs[l]["scatter"].cpu().numpy(), sc)
+    err = np.abs(out_to_f64(out) - ref["out"]).max()
+    assert err <= TOL["bf16"] * np.abs(ref["out"]).max(), (label, err, np.abs(ref["out"]).max())
+    # the plain pass of the same stack matches the routing-less forward
+    again = stack.forward(h0)
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(torch.int16), out.view(torch.int16))
+    print(f"[eda] {label}: near-ties {near}, flips {flips}", flush=True)
+    stack.close()
+    for L in layers:
+        L.close()
+    return near, flips
+
+
 @pytest.mark.parametrize("T,alpha", [(48, 0.5), (128, 0.5), (200, 0.5)])
 def test_eda_stack_matches_oracle(T, alpha):
     """T = 48 routes the top-1 layers with the per-token router and the top-2
@@ -149,6 +248,8 @@ def test_eda_stack_matches_oracle(T, alpha):
     moe = [l for l, inp in enumerate(inps) if inp["cfg"].E > 1]
     assert min(float(np.min(ref["margin"][l])) for l in moe) >= O.MARGIN_TOL
     assert any(np.any(ref["sel"][l] != plain["sel"][l]) for l in moe)  # the averaging matters
+    near, _ = _eda_parity(inps, T, alpha, f"d256 E4 T={T}")
+    assert near == 0
     layers = [make_layer(inp, max_tokens=T) for inp in inps]
     stack = MoEStack(layers, max_tokens=T)
     stack.set_eda(alpha)
@@ -168,6 +269,46 @@ def test_eda_stack_matches_oracle(T, alpha):
     err = np.abs(out_to_f64(out) - ref["out"]).max()
     assert err <= TOL["bf16"] * np.abs(ref["out"]).max(), (err, np.abs(ref["out"]).max())
     stack.close()
+
+
+@pytest.mark.parametrize("E,T", [(32, 48), (32, 200), (64, 300)])
+def test_eda_wide_routers_match_oracle(E, T):
+    """More than 16 experts: the MFMA router's generic branch (and the
+    per-token router at T = 48 for the top-1 layers)."""
+    _eda_parity(_small_stack_inputs(T, E=E), T, 0.5, f"d256 E{E} T={T}")
+
+
+@pytest.mark.parametrize("T", [32, 200])
+def test_eda_full_width_matches_oracle(T):
+    """d_model = 2048 with 16 experts: the decode routers at T = 32, the MFMA
+    router at T = 200."""
+    _eda_parity(_full_width_inputs(T), T, 0.5, f"d2048 E16 T={T}")
+
+
+def test_eda_rejects_mixed_expert_counts():
+    """Depth averaging passes expert e's logit to the next MoE layer, so a
+    stack whose MoE layers differ in n_experts cannot turn it on (the oracle
+    refuses the same stack)."""
+    from moe_ffn_amd import MoEStack, MOE_ERR_INVALID_ARG
+    from moe_ffn_amd.layer import MoELayerError
+    T = 48
+    a = _small_stack_inputs(T, E=4)
+    b = _small_stack_inputs(T, E=8)
+    inps = [a[0], a[2], b[3], a[5]]   # dense, MoE E=4, MoE E=8, dense
+    layers = [make_layer(inp, max_tokens=T) for inp in inps]
+    stack = MoEStack(layers, max_tokens=T)
+    with pytest.raises(MoELayerError) as ei:
+        stack.set_eda(0.5)
+    assert ei.value.status == MOE_ERR_INVALID_ARG
+    h0 = to_torch(inps[0]["hidden"], "bf16")
+    stack.forward(h0)   # without averaging the stack runs
+    torch.cuda.synchronize()
+    vals = [values_f32(inp) for inp in inps]
+    with pytest.raises(ValueError):
+        O.stack_forward(vals, vals[0]["hidden"], [1, 1, 1, 1], 1e-6, eda_alpha=0.5)
+    stack.close()
+    for L in layers:
+        L.close()
 
 
 def test_eda_rejects_bad_rates_and_fp32_stacks():

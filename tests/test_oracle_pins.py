@@ -437,6 +437,22 @@ def test_depth_average_hand_worked_two_layers():
         assert int(st["sel"][1][0, 0]) == want_sel
 
 
+def test_depth_average_needs_one_expert_count():
+    # averaging expert e's logit from a 4-expert layer into a 6-expert layer
+    # has no meaning: the oracle refuses it rather than pad or truncate
+    rng = np.random.default_rng(22)
+    layers = _moe_stack_layers(rng, 6, 5, [(1, 1), (4, 1), (6, 1), (1, 1)])
+    H = rng.standard_normal((3, 6))
+    with pytest.raises(ValueError):
+        O.stack_forward(layers, H, [1, 1, 1, 1], 1e-6, eda_alpha=0.5)
+    with pytest.raises(ValueError):
+        O.depth_average(np.zeros((3, 4)), np.zeros((3, 6)), 0.5)
+    # without the averaging the same stack is fine, and dense layers never count
+    O.stack_forward(layers, H, [1, 1, 1, 1], 1e-6)
+    same = _moe_stack_layers(rng, 6, 5, [(1, 1), (6, 1), (6, 2), (1, 1)])
+    O.stack_forward(same, H, [1, 1, 2, 1], 1e-6, eda_alpha=0.5)
+
+
 # ------------------------------------------------------------- fp8 weights
 def test_e4m3_decoder_matches_torch_on_every_code():
     codes = np.arange(256, dtype=np.uint8)
