@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef struct moe_layer moe_layer_t; /* opaque; owned by the library */
 
@@ -152,6 +152,23 @@ moe_status_t moe_layer_create_fp8(const moe_layer_config_t* cfg, const moe_layer
  * or overlapping buffers), HIP (launch failure). */
 moe_status_t moe_layer_forward(moe_layer_t* layer, const void* hidden, int32_t T, void* out,
                                void* stream, const moe_routing_out_t* routing);
+
+/* As moe_layer_forward, for callers that cannot allocate device memory at the
+ * time of the call (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the forward's per-call buffers (router
+ * outputs, dispatch arrays, token and activation tiles) come from one static
+ * 16 MiB device array of the library instead of the layer's workspace, and
+ * nothing is allocated or freed.  The array is per device and shared by every
+ * call on that device: it keeps the last call's contents, the parts that must
+ * start at zero are cleared by a kernel at the start of each call, and calls
+ * that overlap on one device (on two streams, or with two host threads) race.
+ * Sizes: the buffers needed for T tokens must fit in 16 MiB (at d_model 2048,
+ * d_ff 3072 and 16 experts: T up to 815 with top-1, 286 with top-2); larger T
+ * is rejected with INVALID_ARG and a message giving the bytes needed.  Outputs and routing are
+ * those moe_layer_forward gives for the same arguments.
+ * Errors: as moe_layer_forward; INVALID_ARG also when T needs more scratch. */
+moe_status_t moe_layer_forward_static(moe_layer_t* layer, const void* hidden, int32_t T,
+                                      void* out, void* stream, const moe_routing_out_t* routing);
 
 /* Replace the router bias b with n_experts fp32 values from DEVICE memory,
  * enqueued on `stream` (the update is ordered with forwards on that stream).

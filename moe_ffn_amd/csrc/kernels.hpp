@@ -118,6 +118,9 @@ hipError_t launch_bias_update(const int* counts, int E, float rate, float* bias,
 hipError_t launch_residual(const void* h, const void* y, void* out, size_t n, int dtype,
                            hipStream_t s);
 
+// zero fill by a kernel (graph-capturable): bytes a multiple of 16, p 16-byte aligned
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
 // create-time packing
 hipError_t launch_pack_gateup(const uint16_t* w_gate, const uint16_t* w_up, uint16_t* packed, int E,
                               int F, int d, hipStream_t s);

@@ -20,6 +20,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -58,6 +59,114 @@ struct Carver {
   }
 };
 
+// Per-call buffers of one forward (device memory): the layer's workspace, or
+// the library's static scratch array for moe_layer_forward_static.
+struct Work {
+  void* xn;
+  float* inv;
+  int* sel;
+  float* gate;
+  int* counts;
+  int* offsets;
+  int* gather;
+  int* scatter;
+  int* slot_expert;
+  int* hist;
+  void* xt;
+  void* act;
+  float* ybuf;
+  void* zrow;  // max(d, F) zero elements: must hold zeros before a forward runs
+  void* sink;
+  size_t zbytes;
+  bool clear_zrow;  // zero zrow at the start of the forward (shared static scratch)
+};
+
+// Lay out the buffers of a forward over up to `tokens` tokens from `base`
+// (nullptr: only measure); returns the bytes needed.
+size_t carve_work(const moe::LayerDims& dim, size_t tokens, char* base, Work* w) {
+  const size_t d = dim.d, F = dim.F, E = dim.E, k = dim.k;
+  const bool bf16 = dim.dtype == MOE_DTYPE_BF16;
+  const size_t es = bf16 ? 2 : 4;
+  const size_t nmax = tokens * k;
+  Carver wc;
+  const size_t o_xn = wc.take(tokens * d * es);
+  const size_t o_inv = wc.take(tokens * 4);
+  const size_t o_sel = wc.take(nmax * 4);
+  const size_t o_gate = wc.take(nmax * 4);
+  const size_t o_cnt = wc.take(E * 4);
+  const size_t o_off = wc.take((E + 1) * 4);
+  const size_t o_gat = wc.take(nmax * 4);
+  const size_t o_sca = wc.take(nmax * 4);
+  const size_t o_sle = wc.take(nmax * 4);
+  const size_t o_hist = wc.take((size_t)moe::kPermuteMaxGroups * 64 * 4);
+  // bf16: slot-ordered activations (decode) or padded operand tiles (prefill)
+  const size_t npad = bf16 ? (size_t)moe::max_subtiles((int)nmax, (int)E) * 32 : 0;
+  const size_t o_xt = bf16 ? wc.take(npad * d * 2) : 0;
+  const size_t o_act = wc.take((nmax > npad ? nmax : npad) * F * es);
+  const size_t o_y = k > 1 ? wc.take(nmax * d * 4) : 0;
+  const size_t zbytes = (d > F ? d : F) * 4;
+  const size_t o_z = wc.take(zbytes);
+  const size_t o_sink = wc.take(zbytes);
+  if (base != nullptr) {
+    w->xn = base + o_xn;
+    w->inv = reinterpret_cast<float*>(base + o_inv);
+    w->sel = reinterpret_cast<int*>(base + o_sel);
+    w->gate = reinterpret_cast<float*>(base + o_gate);
+    w->counts = reinterpret_cast<int*>(base + o_cnt);
+    w->offsets = reinterpret_cast<int*>(base + o_off);
+    w->gather = reinterpret_cast<int*>(base + o_gat);
+    w->scatter = reinterpret_cast<int*>(base + o_sca);
+    w->slot_expert = reinterpret_cast<int*>(base + o_sle);
+    w->hist = reinterpret_cast<int*>(base + o_hist);
+    w->xt = bf16 ? base + o_xt : nullptr;
+    w->act = base + o_act;
+    w->ybuf = k > 1 ? reinterpret_cast<float*>(base + o_y) : nullptr;
+    w->zrow = base + o_z;
+    w->sink = base + o_sink;
+    w->zbytes = zbytes;
+    w->clear_zrow = false;
+  }
+  return wc.off;
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch for moe_layer_forward_static: a forward's per-call buffers
+// for callers that cannot allocate device memory.  Every device the library
+// runs on holds its own copy of this array until the process ends; on the
+// host `scratch` names a host-side stand-in, so the device address of each
+// device's copy is looked up once (with that device current) and kept.
+constexpr size_t kScratchBytes = size_t(16) << 20;  // 16 MiB
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device (null: not looked up)
+
+// Looks up this device's copy of `scratch` if not done yet; `dev` must be the
+// current device.
+moe_status_t scratch_setup(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] != nullptr) return MOE_OK;
+  void* p = nullptr;
+  const hipError_t he = hipGetSymbolAddress((void**)&p, HIP_SYMBOL(scratch));
+  if (he != hipSuccess || p == nullptr) {
+    (void)hipGetLastError();
+    return hip_fail(he != hipSuccess ? he : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+  }
+  g_scratch_ptr[dev] = p;
+  return MOE_OK;
+}
+
+void* scratch_base(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 struct moe_layer {
@@ -82,23 +191,9 @@ struct moe_layer {
   void* wd8;
   float* sgu;
   float* sd;
-  // workspace (one allocation)
+  // workspace (one allocation) and its buffers
   void* ws;
-  void* xn;
-  float* inv;
-  int* sel;
-  float* gate;
-  int* counts;
-  int* offsets;
-  int* gather;
-  int* scatter;
-  int* slot_expert;
-  int* hist;
-  void* xt;
-  void* act;
-  float* ybuf;
-  void* zrow;
-  void* sink;
+  Work w;
   // optional per-kernel event timing (start/stop per kernel of a recorded forward)
   std::vector<hipEvent_t> tev;
   std::vector<uint8_t> tslots;  // per recorded forward: bit i set if slot i ran
@@ -206,6 +301,8 @@ moe_status_t create_impl(const moe_layer_config_t* cfg, const moe_layer_weights_
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(MOE_ERR_UNSUPPORTED, std::string("device is ") + prop.gcnArchName +
                                          ", the kernels are built for gfx950");
+  st = scratch_setup(dev);  // the device's static scratch, for moe_layer_forward_static
+  if (st != MOE_OK) return st;
 
   moe_layer* L = new (std::nothrow) moe_layer();
   if (L == nullptr) return fail(MOE_ERR_OOM, "host allocation failed");
@@ -222,9 +319,8 @@ moe_status_t create_impl(const moe_layer_config_t* cfg, const moe_layer_weights_
   const char* dbg = std::getenv("MOE_DEBUG_SYNC");
   L->debug_sync = dbg != nullptr && dbg[0] == '1';
 
-  const size_t d = L->dim.d, F = L->dim.F, E = L->dim.E, EP = L->dim.EP, k = L->dim.k;
+  const size_t d = L->dim.d, F = L->dim.F, E = L->dim.E, EP = L->dim.EP;
   const size_t es = cfg->dtype == MOE_DTYPE_BF16 ? 2 : 4;
-  const size_t nmax = (size_t)L->max_tokens * k;
 
   // parameters
   Carver pc;
@@ -262,47 +358,15 @@ moe_status_t create_impl(const moe_layer_config_t* cfg, const moe_layer_weights_
   L->sd = fp8 ? at<float>(L->params, o_sd) : nullptr;
 
   // workspace
-  Carver wc;
-  const size_t o_xn = wc.take((size_t)L->max_tokens * d * es);
-  const size_t o_inv = wc.take((size_t)L->max_tokens * 4);
-  const size_t o_sel = wc.take(nmax * 4);
-  const size_t o_gate = wc.take(nmax * 4);
-  const size_t o_cnt = wc.take(E * 4);
-  const size_t o_off = wc.take((E + 1) * 4);
-  const size_t o_gat = wc.take(nmax * 4);
-  const size_t o_sca = wc.take(nmax * 4);
-  const size_t o_sle = wc.take(nmax * 4);
-  const size_t o_hist = wc.take((size_t)moe::kPermuteMaxGroups * 64 * 4);
-  // bf16: slot-ordered activations (decode) or padded operand tiles (prefill)
-  const size_t npad = bf16 ? (size_t)moe::max_subtiles((int)nmax, (int)E) * 32 : 0;
-  const size_t o_xt = bf16 ? wc.take(npad * d * 2) : 0;
-  const size_t o_act = wc.take((nmax > npad ? nmax : npad) * F * es);
-  const size_t o_y = k > 1 ? wc.take(nmax * d * 4) : 0;
-  const size_t zbytes = (d > F ? d : F) * 4;
-  const size_t o_z = wc.take(zbytes);
-  const size_t o_sink = wc.take(zbytes);
-  he = hipMalloc(&L->ws, wc.off);
+  const size_t ws_bytes = carve_work(L->dim, (size_t)L->max_tokens, nullptr, nullptr);
+  he = hipMalloc(&L->ws, ws_bytes);
   if (he != hipSuccess) {
     L->ws = nullptr;
     release(L);
     (void)hipGetLastError();
     return fail(MOE_ERR_OOM, std::string("workspace allocation: ") + hipGetErrorString(he));
   }
-  L->xn = at<void>(L->ws, o_xn);
-  L->inv = at<float>(L->ws, o_inv);
-  L->sel = at<int>(L->ws, o_sel);
-  L->gate = at<float>(L->ws, o_gate);
-  L->counts = at<int>(L->ws, o_cnt);
-  L->offsets = at<int>(L->ws, o_off);
-  L->gather = at<int>(L->ws, o_gat);
-  L->scatter = at<int>(L->ws, o_sca);
-  L->slot_expert = at<int>(L->ws, o_sle);
-  L->hist = at<int>(L->ws, o_hist);
-  L->xt = bf16 ? at<void>(L->ws, o_xt) : nullptr;
-  L->act = at<void>(L->ws, o_act);
-  L->ybuf = k > 1 ? at<float>(L->ws, o_y) : nullptr;
-  L->zrow = at<void>(L->ws, o_z);
-  L->sink = at<void>(L->ws, o_sink);
+  carve_work(L->dim, (size_t)L->max_tokens, static_cast<char*>(L->ws), &L->w);
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   he = moe::launch_prep_router(w->w_router, w->rms_gain, cfg->dtype, (int)E, (int)EP, (int)d,
@@ -310,7 +374,7 @@ moe_status_t create_impl(const moe_layer_config_t* cfg, const moe_layer_weights_
   if (he == hipSuccess) he = hipMemsetAsync(L->bias, 0, 64 * 4, s);
   if (he == hipSuccess)
     he = hipMemcpyAsync(L->bias, w->b_router, E * 4, hipMemcpyDeviceToDevice, s);
-  if (he == hipSuccess) he = hipMemsetAsync(L->zrow, 0, zbytes, s);
+  if (he == hipSuccess) he = hipMemsetAsync(L->w.zrow, 0, L->w.zbytes, s);
   if (he == hipSuccess && bf16)
     he = hipMemcpyAsync(L->wr16, w->w_router, E * d * 2, hipMemcpyDeviceToDevice, s);
   if (he == hipSuccess && bf16)
@@ -378,9 +442,11 @@ namespace {
 // MOE_DEBUG_SYNC synchronisation must not run.
 // eda: a stack's depth-averaging state for this layer's router (bf16 MoE
 // layers only; null otherwise), eda_first: the stack's first MoE layer.
+// wk: the per-call buffers (null: the layer's workspace).
 moe_status_t forward_impl(moe_layer_t* L, const void* hidden, int32_t T, void* out, void* stream,
                           const moe_routing_out_t* routing, bool allow_sync,
-                          float* eda = nullptr, float eda_alpha = 0.f, bool eda_first = false) {
+                          float* eda = nullptr, float eda_alpha = 0.f, bool eda_first = false,
+                          const Work* wk = nullptr) {
   if (L == nullptr || L->magic != kMagic) return fail(MOE_ERR_INVALID_ARG, "invalid layer handle");
   if (T < 0 || T > L->max_tokens)
     return fail(MOE_ERR_INVALID_ARG, "T must be in [0, max_tokens] (max_tokens = " +
@@ -425,21 +491,22 @@ moe_status_t forward_impl(moe_layer_t* L, const void* hidden, int32_t T, void* o
   a.wd8 = L->wd8;
   a.sgu = L->sgu;
   a.sd = L->sd;
-  a.xn = L->xn;
-  a.inv = L->inv;
-  a.sel = (routing && routing->sel) ? routing->sel : L->sel;
-  a.gate = (routing && routing->gate) ? routing->gate : L->gate;
-  a.counts = (routing && routing->counts) ? routing->counts : L->counts;
-  a.offsets = (routing && routing->offsets) ? routing->offsets : L->offsets;
-  a.gather = (routing && routing->gather) ? routing->gather : L->gather;
-  a.scatter = (routing && routing->scatter) ? routing->scatter : L->scatter;
-  a.slot_expert = L->slot_expert;
-  a.hist = L->hist;
-  a.xt = L->xt;
-  a.act = L->act;
-  a.ybuf = L->ybuf;
-  a.zrow = L->zrow;
-  a.sink = L->sink;
+  const Work& w = wk != nullptr ? *wk : L->w;
+  a.xn = w.xn;
+  a.inv = w.inv;
+  a.sel = (routing && routing->sel) ? routing->sel : w.sel;
+  a.gate = (routing && routing->gate) ? routing->gate : w.gate;
+  a.counts = (routing && routing->counts) ? routing->counts : w.counts;
+  a.offsets = (routing && routing->offsets) ? routing->offsets : w.offsets;
+  a.gather = (routing && routing->gather) ? routing->gather : w.gather;
+  a.scatter = (routing && routing->scatter) ? routing->scatter : w.scatter;
+  a.slot_expert = w.slot_expert;
+  a.hist = w.hist;
+  a.xt = w.xt;
+  a.act = w.act;
+  a.ybuf = w.ybuf;
+  a.zrow = w.zrow;
+  a.sink = w.sink;
   a.num_cu = L->num_cu;
   a.eda = eda;
   a.eda_alpha = eda_alpha;
@@ -459,6 +526,10 @@ moe_status_t forward_impl(moe_layer_t* L, const void* hidden, int32_t T, void* o
     L->tslots[L->t_used - 1] = (uint8_t)(0x0d | (decode ? 0 : 0x02) | (L->dim.k > 1 ? 0x10 : 0) |
                                          (bf16 && !decode ? 0x20 : 0));
 
+  if (wk != nullptr && wk->clear_zrow) {
+    he = moe::launch_zero(wk->zrow, wk->zbytes, a.stream);
+    if (he != hipSuccess) return hip_fail(he, "scratch clear launch");
+  }
   if (decode) {
     he = moe::launch_router_token(a);
     if (he != hipSuccess) return hip_fail(he, "router launch");
@@ -495,6 +566,27 @@ moe_status_t moe_layer_forward(moe_layer_t* L, const void* hidden, int32_t T, vo
   return forward_impl(L, hidden, T, out, stream, routing, true);
 }
 
+moe_status_t moe_layer_forward_static(moe_layer_t* L, const void* hidden, int32_t T, void* out,
+                                      void* stream, const moe_routing_out_t* routing) {
+  g_err.clear();
+  if (L == nullptr || L->magic != kMagic) return fail(MOE_ERR_INVALID_ARG, "invalid layer handle");
+  if (T < 0 || T > L->max_tokens)
+    return fail(MOE_ERR_INVALID_ARG, "T must be in [0, max_tokens] (max_tokens = " +
+                                         std::to_string(L->max_tokens) + ")");
+  const size_t need = carve_work(L->dim, (size_t)T, nullptr, nullptr);
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_INVALID_ARG,
+                "T = " + std::to_string(T) + " needs " + std::to_string(need) +
+                    " bytes of per-call buffers; the static scratch holds " +
+                    std::to_string(kScratchBytes) + " (use moe_layer_forward)");
+  char* base = static_cast<char*>(scratch_base(L->device));
+  if (base == nullptr) return fail(MOE_ERR_HIP, "static scratch of the layer's device not set up");
+  Work w;
+  carve_work(L->dim, (size_t)T, base, &w);
+  w.clear_zrow = true;  // the array keeps whatever the previous call left there
+  return forward_impl(L, hidden, T, out, stream, routing, true, nullptr, 0.f, false, &w);
+}
+
 moe_status_t moe_layer_set_bias(moe_layer_t* L, const float* b_router, void* stream) {
   g_err.clear();
   if (L == nullptr || L->magic != kMagic) return fail(MOE_ERR_INVALID_ARG, "invalid layer handle");
@@ -524,7 +616,7 @@ moe_status_t moe_layer_update_bias(moe_layer_t* L, const int32_t* counts, float 
   if (!std::isfinite(rate)) return fail(MOE_ERR_INVALID_ARG, "rate must be finite");
   if (counts != nullptr && !aligned(counts, 4))
     return fail(MOE_ERR_INVALID_ARG, "counts must be 4-byte aligned");
-  const int* c = counts != nullptr ? counts : L->counts;
+  const int* c = counts != nullptr ? counts : L->w.counts;
   hipError_t he = moe::launch_bias_update(c, L->dim.E, rate, L->bias,
                                           reinterpret_cast<hipStream_t>(stream));
   if (he != hipSuccess) return hip_fail(he, "bias update launch");

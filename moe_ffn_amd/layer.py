@@ -28,7 +28,7 @@ EXPORTS = ("moe_abi_version", "moe_last_error", "moe_layer_create", "moe_layer_c
            "moe_layer_timing_start",
            "moe_layer_timing_stop", "moe_layer_destroy", "moe_stack_create", "moe_stack_forward",
            "moe_stack_capture", "moe_stack_replay", "moe_stack_destroy", "moe_stack_set_eda",
-           "moe_stack_forward_routing")
+           "moe_stack_forward_routing", "moe_layer_forward_static")
 TIMED_SLOTS = ("norm_router", "route_permute", "experts_gate_up", "experts_down", "combine",
                "gather")
 
@@ -89,6 +89,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.moe_layer_forward.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                       ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.POINTER(RoutingOut)]
+    lib.moe_layer_forward_static.restype = ctypes.c_int
+    lib.moe_layer_forward_static.argtypes = lib.moe_layer_forward.argtypes
     lib.moe_layer_set_bias.restype = ctypes.c_int
     lib.moe_layer_set_bias.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.moe_layer_get_bias.restype = ctypes.c_int
@@ -200,9 +202,13 @@ class MoELayer:
         self.handle = h
 
     def forward(self, hidden: torch.Tensor, out: torch.Tensor | None = None,
-                routing: bool = False, stream=None):
+                routing: bool = False, stream=None, static_scratch: bool = False):
         """hidden [T, d] -> out [T, d]; with routing=True also returns a dict of
-        sel, gate, counts, offsets, gather, scatter (int32 / fp32 CUDA tensors)."""
+        sel, gate, counts, offsets, gather, scatter (int32 / fp32 CUDA tensors).
+        static_scratch=True calls moe_layer_forward_static (the per-call
+        buffers in the library's static scratch array instead of the layer's
+        workspace; `out` and the routing buffers should then be allocated by
+        the caller beforehand when nothing may be allocated)."""
         if self.handle is None:
             raise RuntimeError("layer is closed")
         if not (hidden.is_cuda and hidden.dtype == self.torch_dtype and hidden.dim() == 2
@@ -215,10 +221,10 @@ class MoELayer:
         rp = None
         if routing:
             r, rp = self.routing_buffers(T, hidden.device)
-        st = self._lib.moe_layer_forward(self.handle, ctypes.c_void_p(hidden.data_ptr()), T,
-                                         ctypes.c_void_p(out.data_ptr()),
-                                         ctypes.c_void_p(_stream_ptr(stream)),
-                                         ctypes.byref(rp) if rp is not None else None)
+        fwd = self._lib.moe_layer_forward_static if static_scratch else self._lib.moe_layer_forward
+        st = fwd(self.handle, ctypes.c_void_p(hidden.data_ptr()), T,
+                 ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(_stream_ptr(stream)),
+                 ctypes.byref(rp) if rp is not None else None)
         _check(self._lib, st)
         return (out, r) if routing else out
 

@@ -34,7 +34,8 @@ def test_header_declares_the_abi():
                             "moe_layer_timing_start", "moe_layer_timing_stop",
                             "moe_layer_destroy", "moe_stack_create", "moe_stack_forward",
                             "moe_stack_capture", "moe_stack_replay", "moe_stack_destroy",
-                            "moe_stack_set_eda", "moe_stack_forward_routing"])
+                            "moe_stack_set_eda", "moe_stack_forward_routing",
+                            "moe_layer_forward_static"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), f"missing export {name}"
     assert set(layer.EXPORTS) == set(declared_functions())
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
 
 
 def test_abi_structs_match_header_sizes():
