@@ -27,16 +27,23 @@ state and TopK keeps a few of them)):
   O10 FFN stack: h_{l+1} = h_l + FFN_l(h_l) over the backbone's layers
   O11 depth averaging of the router logits over a stack's MoE layers:
               z~_l = alpha * z~_{l-1} + (1 - alpha) * z_l   (optional)
+  O12 fp8 activations (optional): O7 with its two GEMM inputs, u and
+              SiLU(W_gate u) * (W_up u), quantised to E4M3 per row with the
+              dynamic scale max|row| / 448 (fp8_activation)
 
 Readings where the pages are silent:
 the bias only steers selection and never enters a gate; the layer returns
 the FFN output without the residual; no capacity limit and no dropped
 tokens; no shared expert; a linear router, whose logits a stack may
 depth-average across its MoE layers (O11: the state averaged and the rate
-are readings, the rate the caller's).
+are readings, the rate the caller's); "fp8" read as fp8 weights and fp8
+activations with per-row dynamic scales (O12, a reading of the cookbook
+page's "fp8").
 
 Every floating-point step runs in float64 on the exact values of the inputs
-(bf16 inputs are widened exactly).  Nothing is rounded.
+(bf16 inputs are widened exactly).  Nothing is rounded, except where O12
+quantises: there the bf16 value of a row is quantised in float32, the
+precision in which the device takes that integer decision.
 """
 
 from __future__ import annotations
@@ -203,7 +210,8 @@ def bias_update(b, counts, rate: float) -> np.ndarray:
 
 # whole layer ----------------------------------------------------------------
 def oracle_forward(vals: dict, k: int | None = None, forced_sel=None, tokens=None,
-                   eps: float | None = None, z_prev=None, eda_alpha: float | None = None) -> dict:
+                   eps: float | None = None, z_prev=None, eda_alpha: float | None = None,
+                   fp8_act: bool = False) -> dict:
     """Run O1-O8 on exact input values (a dict as from ``synth.values_f32``).
 
     forced_sel : optional [T,k] expert ids that replace O3's choice (so the
@@ -213,6 +221,9 @@ def oracle_forward(vals: dict, k: int | None = None, forced_sel=None, tokens=Non
     eda_alpha  : optional depth averaging of the logits (O11) with the
                  previous MoE layer's averaged logits z_prev (None: this is
                  the first MoE layer); selection and gates then use them.
+    fp8_act    : the experts quantise their activations to E4M3 per row
+                 (swiglu_expert_fp8act); the weights in vals are then the
+                 dequantised fp8 weights (fp8_weights).
     Returns a dict with x, z, s, sel, margin, gate, counts, offsets, gather,
     scatter and out (float64; rows of ``tokens`` when given).
     """
@@ -247,7 +258,8 @@ def oracle_forward(vals: dict, k: int | None = None, forced_sel=None, tokens=Non
         ps = slots_needed[(slots_needed >= lo) & (slots_needed < hi)]
         if ps.size == 0:
             continue
-        Y[ps] = swiglu_expert(Wg[e], Wu[e], Wd[e], x[gather[ps]])
+        expert = swiglu_expert_fp8act if fp8_act else swiglu_expert
+        Y[ps] = expert(Wg[e], Wu[e], Wd[e], x[gather[ps]])
     if tokens is None:
         out = combine(Y, gate, scatter, k)
     else:
@@ -340,3 +352,100 @@ def fp8_weights(codes, scale) -> np.ndarray:
     """Expert weights stored as E4M3 codes with one float32 scale per output
     row: W[e, r, :] = value(codes[e, r, :]) * scale[e, r] (exact in float64)."""
     return e4m3_value(codes) * np.asarray(scale, np.float64)[..., None]
+
+
+# fp8 activations ----------------------------------------------------------------
+# The SGLang-Omni cookbook page ("Benchmark Results") serves ZONOS2 with "fp8"
+# and says nothing more.  Read as fp8 weights AND fp8 activations (both
+# operands of the expert GEMMs in E4M3): the expert input of each routed row
+# and the SwiGLU intermediate of each row are quantised on the fly with one
+# float32 scale per row, scale = max|row| / 448 (dynamic per-token scales);
+# the weights keep their per-output-row scales (fp8_weights).  The device
+# stores both quantised vectors in bf16 before quantising them (the expert
+# input as bf16 rows, the intermediate as bf16 SwiGLU outputs), and a
+# quantisation decides integer codes, so this reading quantises the bf16
+# value of each vector and takes the scale and the division in float32, as
+# the device does.  Everything else stays in float64.
+
+def bf16_round(v) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value (8 significant bits,
+    float32's exponent range), ties to even; returned as float64.  Zeros,
+    infinities and NaN pass through."""
+    v = _f64(v)
+    e = np.maximum(np.frexp(v)[1], -125)  # |v| in [2^(e-1), 2^e); bf16 subnormals below 2^-126
+    r = np.ldexp(np.rint(np.ldexp(v, 8 - e)), e - 8)   # 8 significant bits, spacing 2^(e-8)
+    return np.where(np.isfinite(v), r, v)
+
+
+_E4M3_POS = None
+
+
+def _e4m3_table():
+    """The 127 finite non-negative E4M3 values in increasing order with their
+    codes (code 0x00 .. 0x7e: the order of the codes is the order of the
+    values)."""
+    global _E4M3_POS
+    if _E4M3_POS is None:
+        codes = np.arange(0x7F, dtype=np.uint8)
+        _E4M3_POS = (e4m3_value(codes), codes)
+    return _E4M3_POS
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """E4M3 code of the nearest E4M3 value to each float64 v, ties to the even
+    code (the one whose last mantissa bit is 0), saturating at +-448 (the
+    largest finite value); the sign bit follows v's sign (-0.0 -> 0x80).
+    NaN gives 0x7f."""
+    v = _f64(v)
+    vals, codes = _e4m3_table()
+    a = np.minimum(np.abs(v), 448.0)
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 1, vals.size - 1)
+    lo = hi - 1                            # vals[lo] <= a <= vals[hi]
+    dlo, dhi = a - vals[lo], vals[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (codes[hi] % 2 == 0))
+    c = np.where(pick_hi, codes[hi], codes[lo]).astype(np.uint8)
+    c = np.where(a == 0.0, 0, c).astype(np.uint8)
+    c = np.where(np.signbit(v), c | 0x80, c).astype(np.uint8)
+    return np.where(np.isnan(v), 0x7F, c).astype(np.uint8)
+
+
+def quantize_rows_e4m3(V):
+    """Dynamic per-row E4M3 quantisation of V [R, K] (values that float32
+    holds exactly; the layer passes bf16 values): with amax the largest |v| of
+    a row, the row's scale is a = float32(amax / 448) and its codes are
+    e4m3_encode(float32(v / a)), both divisions correctly rounded in float32.
+    A row of zeros gets a = 0 and all codes 0.  Returns (codes uint8 [R, K],
+    a float32 [R]); the row's values are then a * e4m3_value(codes)."""
+    V32 = np.asarray(V, np.float64).astype(np.float32)
+    if not np.array_equal(V32.astype(np.float64), _f64(V)):
+        raise ValueError("quantize_rows_e4m3 takes values that float32 holds exactly")
+    amax = np.max(np.abs(V32), axis=-1)
+    a = (amax / np.float32(448.0)).astype(np.float32)
+    safe = np.where(a > 0, a, np.float32(1.0)).astype(np.float32)
+    q = (V32 / safe[..., None]).astype(np.float32)
+    codes = e4m3_encode(q.astype(np.float64))
+    codes = np.where((a > 0)[..., None], codes, 0).astype(np.uint8)
+    return codes, a
+
+
+def dequantize_rows(codes, a) -> np.ndarray:
+    """a[r] * value(codes[r, :]) in float64 (exact)."""
+    return e4m3_value(codes) * np.asarray(a, np.float64)[..., None]
+
+
+def fp8_activation(U) -> np.ndarray:
+    """What an expert GEMM multiplies under fp8 activations: each row of U
+    rounded to bf16, quantised per row (quantize_rows_e4m3) and dequantised,
+    in float64."""
+    return dequantize_rows(*quantize_rows_e4m3(bf16_round(U)))
+
+
+def swiglu_expert_fp8act(Wg, Wu, Wd, U) -> np.ndarray:
+    """O7 with fp8 activations (the reading above): G and V are the exact
+    products of fp8_activation(u) with the (dequantised fp8) weights, and
+    y = W_down fp8_activation(SiLU(G) * V).  Float64 throughout, apart from
+    the bf16 roundings and the float32 quantisation steps the reading names."""
+    X = fp8_activation(U)
+    G = X @ _f64(Wg).T
+    V = X @ _f64(Wu).T
+    return fp8_activation(silu(G) * V) @ _f64(Wd).T

@@ -470,3 +470,192 @@ def test_fp8_weights_scale_rows_exactly():
     codes = np.array([[[0x38, 0x40], [0xb8, 0x00]]], np.uint8)   # 1, 2 / -1, 0
     scale = np.array([[0.5, 3.0]], np.float32)
     np.testing.assert_array_equal(O.fp8_weights(codes, scale), [[[0.5, 1.0], [-3.0, 0.0]]])
+
+
+# ------------------------------------------------------------- fp8 activations
+def test_bf16_round_matches_torch_on_float32_values():
+    rng = np.random.default_rng(30)
+    x = rng.standard_normal(20000) * np.exp2(rng.integers(-30, 30, 20000))
+    x32 = x.astype(np.float32)
+    # exact midpoints between neighbouring bf16 values (float32 holds them)
+    b = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float32).numpy()
+    mid = (b.view(np.uint32) | np.uint32(0x8000)).view(np.float32)
+    for v in (x32, mid):
+        ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+        np.testing.assert_array_equal(O.bf16_round(v.astype(np.float64)), ref)
+    # by hand: a tie goes to the even significand; just above a tie rounds up;
+    # a float64 just below the midpoint -2776 rounds to -2768 (a detour
+    # through float32 would land on the midpoint and round to -2784)
+    assert O.bf16_round(1 + 2.0 ** -8) == 1.0
+    assert O.bf16_round(1 + 3 * 2.0 ** -8) == 1 + 2.0 ** -6
+    assert O.bf16_round(1 + 2.0 ** -8 + 2.0 ** -30) == 1 + 2.0 ** -7
+    assert O.bf16_round(-2775.99990387) == -2768.0
+
+
+def test_e4m3_encode_round_trips_every_code_and_matches_torch():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    np.testing.assert_array_equal(O.e4m3_encode(O.e4m3_value(codes)), codes)
+    rng = np.random.default_rng(31)
+    v = rng.uniform(-1, 1, 30000) * np.exp2(rng.integers(-12, 9, 30000))
+    v = np.clip(v, -448, 448)
+    vals = O.e4m3_value(np.arange(0x7F, dtype=np.uint8))
+    mids = (vals[1:] + vals[:-1]) / 2
+    for x in (v, mids, -mids):
+        ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        np.testing.assert_array_equal(O.e4m3_encode(x), ref)
+
+
+def test_e4m3_encode_is_the_nearest_value_ties_to_even():
+    allc = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    allv = O.e4m3_value(allc)
+    rng = np.random.default_rng(32)
+    v = rng.uniform(-1, 1, 3000) * np.exp2(rng.integers(-11, 9, 3000))
+    v = np.clip(v, -448, 448)
+    got = O.e4m3_value(O.e4m3_encode(v))
+    best = np.min(np.abs(v[:, None] - allv[None, :]), axis=1)   # brute force over all values
+    np.testing.assert_array_equal(np.abs(v - got), best)
+    vals = O.e4m3_value(np.arange(0x7F, dtype=np.uint8))
+    mids = (vals[1:] + vals[:-1]) / 2
+    c = O.e4m3_encode(mids)
+    assert np.all(c % 2 == 0)                                     # even last mantissa bit
+    assert np.all((O.e4m3_value(c) == vals[1:]) | (O.e4m3_value(c) == vals[:-1]))
+    # saturation, zero signs, NaN
+    np.testing.assert_array_equal(O.e4m3_encode([450.0, -1e6, 0.0, -0.0, np.nan]),
+                                  [0x7E, 0xFE, 0x00, 0x80, 0x7F])
+
+
+def test_quantize_rows_hand_examples():
+    # scale exactly 1: 1.0625 is the tie between 1 (0x38) and 1.125 (0x39);
+    # 2^-8 is the subnormal 2 * 2^-9
+    c, a = O.quantize_rows_e4m3(np.array([[448.0, 1.0625, -2.0 ** -8, 0.0]]))
+    assert a[0] == np.float32(1.0)
+    np.testing.assert_array_equal(c[0], [0x7E, 0x38, 0x82, 0x00])
+    # [3, 1]: a = float32(3/448); 1/a = 149.33.. lies between 144 and 160
+    c, a = O.quantize_rows_e4m3(np.array([[3.0, 1.0]]))
+    assert a[0] == np.float32(3.0) / np.float32(448.0)
+    np.testing.assert_array_equal(c[0], [0x7E, 0x71])
+    assert O.e4m3_value([0x71])[0] == 144.0
+    # a zero row: scale 0, codes 0
+    c, a = O.quantize_rows_e4m3(np.zeros((2, 5)))
+    assert np.all(a == 0) and np.all(c == 0)
+    with pytest.raises(ValueError):
+        O.quantize_rows_e4m3(np.array([[1.0 + 2.0 ** -40]]))
+
+
+def test_quantize_rows_error_bound_and_scale_invariance():
+    rng = np.random.default_rng(33)
+    V = O.bf16_round(rng.standard_normal((64, 200)) * np.exp2(rng.integers(-6, 6, (64, 1))))
+    V[3] = 0.0
+    V[5, :7] = 0.0
+    c, a = O.quantize_rows_e4m3(V)
+    ok = a > 0
+    # the largest |v| of each row lands on +-448
+    arg = np.argmax(np.abs(V), axis=1)
+    assert np.all(np.abs(O.e4m3_value(c[np.arange(64), arg]))[ok] == 448.0)
+    assert np.all(a[ok] == (np.max(np.abs(V), axis=1)[ok] / 448.0).astype(np.float32))
+    # every code is within half an E4M3 spacing of v / a (spacing 2^(E-3) for
+    # |t| in [2^E, 2^(E+1)), E >= -6; 2^-9 below 2^-6), plus the float32
+    # rounding of the quotient
+    t = V[ok] / a[ok].astype(np.float64)[:, None]
+    E = np.floor(np.log2(np.maximum(np.abs(t), 2.0 ** -6)))
+    half = np.exp2(E - 3) / 2
+    err = np.abs(O.e4m3_value(c[ok]) - t)
+    assert np.all(err <= half + np.abs(t) * 2.0 ** -23)
+    # dequantised rows against the input: relative 2^-4 plus the subnormal floor
+    D = O.dequantize_rows(c, a)
+    assert np.all(np.abs(D - V) <= np.abs(V) * (2.0 ** -4 + 2.0 ** -22) + a[:, None] * 2.0 ** -10)
+    # powers of two commute with the quantisation
+    c2, a2 = O.quantize_rows_e4m3(V * 2.0 ** 5)
+    np.testing.assert_array_equal(c2, c)
+    np.testing.assert_array_equal(a2, a * np.float32(32.0))
+
+
+def _silu_slope_max():
+    x = np.linspace(-20, 20, 400001)
+    s = scipy.special.expit(x)
+    return float(np.max(np.abs(s * (1 + x * (1 - s)))))
+
+
+def test_swiglu_fp8act_within_the_quantisation_bound():
+    # the fp8-activation expert against the exact expert on the same bf16
+    # input: every output differs by no more than the a-priori bound that the
+    # two per-row quantisations (relative 2^-4 each, plus the subnormal floor)
+    # and the bf16 rounding of the intermediate (2^-9) allow; a dropped scale,
+    # a transposed operand or a missing quantisation step breaks it
+    rng = np.random.default_rng(34)
+    d, F, R = 64, 96, 40
+    Wg = rng.standard_normal((F, d)) / 8
+    Wu = rng.standard_normal((F, d)) / 8
+    Wd = rng.standard_normal((d, F)) / 10
+    U = O.bf16_round(rng.standard_normal((R, d)))
+    Y8 = O.swiglu_expert_fp8act(Wg, Wu, Wd, U)
+    G, V = U @ Wg.T, U @ Wu.T
+    sg = scipy.special.expit(G) * G
+    M = sg * V
+    Y = M @ Wd.T
+    ax = np.max(np.abs(U), axis=1, keepdims=True) / 448 * (1 + 2.0 ** -22)
+    ex = np.abs(U) * (2.0 ** -4 + 2.0 ** -22) + ax * 2.0 ** -10
+    dG, dV = ex @ np.abs(Wg).T, ex @ np.abs(Wu).T
+    L = _silu_slope_max()
+    dM1 = L * dG * (np.abs(V) + dV) + np.abs(sg) * dV          # SiLU(G~) V~ - SiLU(G) V
+    Mb = (np.abs(M) + dM1) * (1 + 2.0 ** -9)                   # bound on |bf16(M~)|
+    am = np.max(Mb, axis=1, keepdims=True) / 448 * (1 + 2.0 ** -22)
+    dM = dM1 + (np.abs(M) + dM1) * 2.0 ** -9 + Mb * (2.0 ** -4 + 2.0 ** -22) + am * 2.0 ** -10
+    bound = dM @ np.abs(Wd).T + 1e-12 * (np.abs(M) @ np.abs(Wd).T)
+    err = np.abs(Y8 - Y)
+    assert np.all(err <= bound)
+    # and the quantisation is really there: errors of the order of 2^-5
+    rel = np.max(err) / np.max(np.abs(Y))
+    assert 1e-3 < rel < 0.1
+
+
+def test_fp8act_layer_with_one_expert_is_the_dense_fp8act_ffn():
+    rng = np.random.default_rng(35)
+    T, d, F = 24, 32, 64
+    vals = _rand_layer(rng, T, d, 1, F)
+    r = O.oracle_forward(vals, k=1, eps=1e-6, fp8_act=True)
+    x = O.rmsnorm(vals["hidden"], vals["gain"], 1e-6)
+    want = O.swiglu_expert_fp8act(vals["w_gate"][0], vals["w_up"][0], vals["w_down"][0], x)
+    np.testing.assert_array_equal(r["gate"], 1.0)
+    np.testing.assert_allclose(r["out"], want, rtol=0, atol=0)
+    # a planted mistake in the plain path would not pass for this one: the
+    # fp8 path differs from it by the quantisation
+    plain = O.oracle_forward(vals, k=1, eps=1e-6)
+    assert np.max(np.abs(plain["out"] - r["out"])) > 1e-4 * np.max(np.abs(want))
+
+
+def test_swiglu_fp8act_on_exact_fp8_inputs_quantises_the_intermediate():
+    # rows that are E4M3 values times 2^j with a +-448 * 2^j entry quantise
+    # exactly (scale 2^j), so the whole difference to the exact expert comes
+    # from the bf16 rounding and the quantisation of SiLU(G) * V: it is of
+    # the order of 2^-5 relative and within that step's bound
+    rng = np.random.default_rng(36)
+    d, F, R = 64, 96, 32
+    Wg = rng.standard_normal((F, d)) / 8
+    Wu = rng.standard_normal((F, d)) / 8
+    Wd = rng.standard_normal((d, F)) / 10
+    codes = rng.integers(0, 0x7F, (R, d)).astype(np.uint8) | (rng.integers(0, 2, (R, d)) << 7).astype(np.uint8)
+    codes[:, 0] = 0x7E
+    U = O.e4m3_value(codes) * np.exp2(rng.integers(-12, -6, (R, 1)))
+    c, a = O.quantize_rows_e4m3(U)
+    np.testing.assert_array_equal(O.dequantize_rows(c, a), U)
+    M = scipy.special.expit(U @ Wg.T) * (U @ Wg.T) * (U @ Wu.T)
+    Y8 = O.swiglu_expert_fp8act(Wg, Wu, Wd, U)
+    Mb = np.abs(M) * (1 + 2.0 ** -9)
+    am = np.max(Mb, axis=1, keepdims=True) / 448 * (1 + 2.0 ** -22)
+    dM = np.abs(M) * 2.0 ** -9 + Mb * (2.0 ** -4 + 2.0 ** -22) + am * 2.0 ** -10
+    err = np.abs(Y8 - M @ Wd.T)
+    assert np.all(err <= dM @ np.abs(Wd).T + 1e-12 * (np.abs(M) @ np.abs(Wd).T))
+    assert np.max(err) > 4e-3 * np.max(np.abs(M @ Wd.T))   # bf16 alone would give ~2^-9
+
+
+def test_fp8_activation_quantises_the_bf16_value():
+    # 1.0625 + 2^-20 rounds to the bf16 value 1.0625, the tie between the
+    # E4M3 values 1 and 1.125, which goes to 1 (even); quantising the float64
+    # value directly would give 1.125
+    X = O.fp8_activation(np.array([[448.0, 1.0625 + 2.0 ** -20, -3.0 - 2.0 ** -12]]))
+    np.testing.assert_array_equal(X, [[448.0, 1.0, -3.0]])
+    # a scaled row: amax 3 -> scale float32(3/448); 1 -> 144 * scale
+    X = O.fp8_activation(np.array([[3.0, 1.0]]))
+    a = np.float64(np.float32(3.0) / np.float32(448.0))
+    np.testing.assert_array_equal(X, [[448.0 * a, 144.0 * a]])
