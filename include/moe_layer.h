@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 typedef struct moe_layer moe_layer_t; /* opaque; owned by the library */
 
@@ -141,6 +141,40 @@ moe_status_t moe_layer_create_fp8(const moe_layer_config_t* cfg, const moe_layer
                                   const moe_fp8_scales_t* scales, void* stream,
                                   moe_layer_t** out);
 
+/* fp8 weights AND fp8 activations (the cookbook page's "fp8" read as both GEMM
+ * operands in E4M3, so the expert products run on gfx950's fp8 MFMA,
+ * v_mfma_f32_32x32x64_f8f6f4).  Weights and scales as for
+ * moe_layer_create_fp8.  In every forward, each routed row u of the expert
+ * input (the bf16 RMSNorm output) and each row m = SiLU(G) * V of the SwiGLU
+ * intermediate (rounded to bf16) is quantised to E4M3 with one dynamic fp32
+ * scale per row, exactly as moe_fp8_quantize_rows does; the weight scales and
+ * the row scales multiply the fp32 accumulators:
+ *   G[r, f] = a_u[r] * s_gate[f] * sum_i code(u_r)_i * code(W_gate[f])_i   (V likewise)
+ *   y[r, m] = a_m[r] * s_down[m] * sum_f code(m_r)_f * code(W_down[m])_f
+ * Router, gates, dispatch and combine are those of the bf16 layer.  Every
+ * batch size runs the tiled path (router, permutation, gather, the two
+ * quantisations and the two fp8 GEMMs).  The layer keeps only the fp8 banks:
+ * 1 byte per expert weight plus the row scales.  Shape limits and errors as
+ * moe_layer_create_fp8. */
+moe_status_t moe_layer_create_w8a8(const moe_layer_config_t* cfg, const moe_layer_weights_t* w,
+                                   const moe_fp8_scales_t* scales, void* stream,
+                                   moe_layer_t** out);
+
+/* Per-row E4M3 quantisation with a dynamic scale, the step that layers made by
+ * moe_layer_create_w8a8 apply to their expert inputs and SwiGLU intermediates
+ * (for callers that quantise activations themselves, and to check the step).
+ * x: DEVICE bf16 [R, K] (16-byte aligned, K a multiple of 8); codes: DEVICE
+ * uint8 [R, K] (8-byte aligned) receives OCP E4M3 codes; scales: DEVICE fp32
+ * [R] (4-byte aligned).  Row r: a = max_i |x[r,i]| / 448 in fp32 (correctly
+ * rounded), code(x) = the E4M3 value nearest to fl32(x / a) (correctly rounded
+ * division; ties to the even code; |x / a| is at most 448 up to rounding and
+ * is clamped to +-448); a row of zeros gives a = 0 and codes 0.  Then
+ * x[r,i] ~= a * value(code).  Enqueued on `stream`; R == 0 does nothing.
+ * NaN or Inf inputs give undefined codes.  Errors: INVALID_ARG (NULL or
+ * misaligned pointers, R < 0, K not a positive multiple of 8), HIP. */
+moe_status_t moe_fp8_quantize_rows(const void* x, int32_t R, int32_t K, void* codes,
+                                   float* scales, void* stream);
+
 /* One forward over T tokens: hidden [T, d_model] -> out [T, d_model], both
  * DEVICE memory in the layer's dtype; `out` must not overlap `hidden`.
  * Asynchronous on `stream`: no host synchronisation and no allocation.
@@ -207,10 +241,13 @@ moe_status_t moe_layer_update_bias(moe_layer_t* layer, const int32_t* counts, fl
  * with T*top_k <= 64, whose expert kernels dispatch), 2 first expert kernel
  * (gate/up), 3 second expert kernel (down), 4 combine (0 when top_k = 1, where
  * the combine is part of slot 3), 5 gather of the routed rows into expert
- * order (bf16 layers with T*top_k > 64 only; it runs between slots 1 and 2).
+ * order (bf16 layers with T*top_k > 64 and fp8-activation layers; it runs
+ * between slots 1 and 2), 6 quantisation of the gathered rows and 7 of the
+ * SwiGLU intermediate (fp8-activation layers only; before slot 2 and before
+ * slot 3).
  * Errors: INVALID_ARG (bad handle, max_forwards outside [1, 65536], stop
  * without start), HIP. */
-#define MOE_TIMED_SLOTS 6
+#define MOE_TIMED_SLOTS 8
 moe_status_t moe_layer_timing_start(moe_layer_t* layer, int32_t max_forwards);
 moe_status_t moe_layer_timing_stop(moe_layer_t* layer, float* ms_sum, int32_t* n_forwards);
 

@@ -61,6 +61,22 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(const u32x4& a, const u32x4& b, 
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+// D = A * B + C on a 32x32 output tile with K = 64, both operands OCP E4M3
+// (v_mfma_f32_32x32x64_f8f6f4; the scaled form with zero scale operands is the
+// plain instruction), fp32 accumulation.  Each operand is 32 bytes per lane,
+// given as two 16-byte halves; A and B use the same lane order, so any fixed
+// assignment of k to (lane / 32, byte) that both operands share gives the
+// same sums.  The output lane layout is that of mfma_32x32x16.
+__device__ __forceinline__ f32x16 mfma_32x32x64_fp8(const u32x4& a0, const u32x4& a1,
+                                                    const u32x4& b0, const u32x4& b1,
+                                                    const f32x16& c) {
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                   (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                   (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
 __device__ __forceinline__ int c32_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
 // SiLU(v) = v * sigmoid(v), the reciprocal from v_rcp_f32 (1 ulp) instead of an
@@ -131,6 +147,28 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   o[2] = e4m3_pair_to_bf16x2<false>(hi);
   o[3] = e4m3_pair_to_bf16x2<true>(hi);
   return o;
+}
+
+// Per-row E4M3 quantisation with a dynamic scale (fp8 activations): with a
+// = max|row| / 448 in fp32, the code of v is the E4M3 nearest to v / a (fp32
+// division, correctly rounded; v_cvt_pk_fp8_f32 rounds to nearest even),
+// clamped to +-448 first (|v / a| exceeds 448 by at most one rounding, which
+// the clamp takes back to the value round-to-nearest gives); a = 0 (a zero
+// row) gives code 0.
+__device__ __forceinline__ float e4m3_quotient(float v, float a) {
+  return a > 0.f ? fminf(fmaxf(v / a, -448.f), 448.f) : 0.f;
+}
+// four bf16 values (two bf16x2 words) -> four codes, in order, in one word
+__device__ __forceinline__ uint32_t quant4_e4m3(uint32_t w0, uint32_t w1, float a) {
+  uint32_t r = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_quotient(bf16_lo(w0), a),
+                                               e4m3_quotient(bf16_hi(w0), a), 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_quotient(bf16_lo(w1), a),
+                                         e4m3_quotient(bf16_hi(w1), a), (int)r, true);
+}
+__device__ __forceinline__ float absmax8_bf16(const u32x4& v, float m) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[i])), fabsf(bf16_hi(v[i]))));
+  return m;
 }
 
 }  // namespace moe

@@ -42,6 +42,17 @@
 // codes' own; the per-row dequantisation scales multiply the fp32
 // accumulators in the epilogue (rsc: per gate/up row, or per output row of
 // the down projection; null for bf16 weights).
+//
+// fp8 weights and fp8 activations (F8): both operands are E4M3 codes and the
+// products run on v_mfma_f32_32x32x64_f8f6f4.  The weights come from the
+// layer's fp8 bank and the tokens from E4M3 operand tiles (k_quant_tiles.hip),
+// both as 1 KiB blocks of 32 rows x 32 k (lane l: 16 codes of row l % 32);
+// one MFMA takes two consecutive blocks (64 k, 32 bytes per lane).  A block
+// carries as many bytes as a bf16 block, so the token stages, the LDS ring
+// and the weight queue are the same, counted in blocks: a stage holds two
+// MFMA steps instead of four.  The epilogues multiply the accumulators by
+// the weight row's scale and the token row's activation scale (asc, one per
+// padded slot).
 #include <algorithm>
 #include <cstdint>
 #include <unordered_map>
@@ -102,6 +113,16 @@ __device__ __forceinline__ void read_b(const u32x4* buf, int s, int lane, u32x4 
   for (int j = 0; j < TT; ++j) bv[j] = buf[(j * kBK + s) * 64 + lane];
 }
 
+// fp8 token operands of MFMA step m of a stage: blocks 2m and 2m+1
+template <int TT>
+__device__ __forceinline__ void read_b8(const u32x4* buf, int m, int lane, u32x4 (&bv)[TT][2]) {
+#pragma unroll
+  for (int j = 0; j < TT; ++j) {
+    bv[j][0] = buf[(j * kBK + 2 * m) * 64 + lane];
+    bv[j][1] = buf[(j * kBK + 2 * m + 1) * 64 + lane];
+  }
+}
+
 template <int RT, int TT>
 __device__ __forceinline__ void mac(const u32x4 (&a)[RT], const u32x4 (&bv)[TT],
                                     f32x16 (&acc)[RT][TT]) {
@@ -109,6 +130,32 @@ __device__ __forceinline__ void mac(const u32x4 (&a)[RT], const u32x4 (&bv)[TT],
   for (int j = 0; j < TT; ++j)
 #pragma unroll
     for (int r = 0; r < RT; ++r) acc[r][j] = mfma_32x32x16(a[r], bv[j], acc[r][j]);
+}
+
+template <int RT, int TT>
+__device__ __forceinline__ void mac8(const u32x4 (&a0)[RT], const u32x4 (&a1)[RT],
+                                     const u32x4 (&bv)[TT][2], f32x16 (&acc)[RT][TT]) {
+#pragma unroll
+  for (int j = 0; j < TT; ++j)
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+      acc[r][j] = mfma_32x32x64_fp8(a0[r], a1[r], bv[j][0], bv[j][1], acc[r][j]);
+}
+
+// After each of the NM MFMAs of a step, up to two of the step's other
+// instructions, in this order: R DS reads, W DS writes, V global loads.
+template <int NM, int R, int W, int V>
+__device__ __forceinline__ void sched_pairs() {
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+    for (int t = 2 * m; t < 2 * m + 2; ++t) {
+      if (t < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      else if (t < R + W) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      else if (t < R + W + V) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+  }
 }
 
 // One token stage kb (k-steps 4kb .. 4kb+3).  Per k-step: the token operands
@@ -162,16 +209,57 @@ __device__ __forceinline__ void bstage(const Ctx<RT, TT>& c, u32x4* lds, int& bu
   buf = b1;
 }
 
+// The fp8 form of bstage: the stage's four blocks are two MFMA steps, each
+// taking two weight queue slots (refilled Q blocks ahead) and two token
+// blocks per subtile; the second step copies token stage kb+2 to LDS and
+// issues the loads of stage kb+4, as the second k-step of bstage does.
+template <int RT, int TT, int Q, int P>
+__device__ __forceinline__ void bstage8(const Ctx<RT, TT>& c, u32x4* lds, int& buf, int kb,
+                                        int nsb, u32x4 (&qa)[Q][RT], u32x4 (&rb)[TT],
+                                        u32x4 (&bc)[TT][2], f32x16 (&acc)[RT][TT]) {
+  constexpr int NM = RT * TT;
+  const int b1 = buf == kBStages - 1 ? 0 : buf + 1;
+  const int b2 = b1 == kBStages - 1 ? 0 : b1 + 1;
+  constexpr int SE = stage_ent<TT>();
+  const u32x4* cur = lds + buf * SE;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int s0 = (P * kBK + 2 * m) % Q;  // weight queue slots of this step: s0, s0 + 1
+    u32x4 bn[TT][2];
+    if (m == 0) read_b8<TT>(cur, 1, c.lane, bn);
+    else read_b8<TT>(lds + b1 * SE, 0, c.lane, bn);
+    mac8(qa[s0], qa[s0 + 1], bc, acc);
+    load_a(c, kb * kBK + 2 * m + Q, qa[s0]);
+    load_a(c, kb * kBK + 2 * m + 1 + Q, qa[s0 + 1]);
+    if (m == 1) {
+      store_b(c, lds + b2 * SE, rb);
+      load_b(c, kb + 4, nsb, rb);
+      sched_pairs<NM, 2 * TT, TT, TT + 2 * RT>();
+    } else {
+      sched_pairs<NM, 2 * TT, 0, 2 * RT>();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < TT; ++j) {
+      bc[j][0] = bn[j][0];
+      bc[j][1] = bn[j][1];
+    }
+  }
+  __syncthreads();
+  buf = b1;
+}
+
 // Q: depth of the weight queue in k-steps: kBK, 2 kBK or 4 kBK, so that one
 // loop iteration (two token stages, four at Q = 4 kBK) returns the queue to
 // its first slot; the token stages of the reduction are a multiple of that.
-template <int RT, int TT, int Q>
+// (F8: k-steps are 1 KiB blocks of 32 k; two make one MFMA step.)
+template <int RT, int TT, int Q, bool F8>
 __device__ __forceinline__ void mainloop(const Ctx<RT, TT>& c, u32x4* lds, f32x16 (&acc)[RT][TT]) {
   constexpr int NP = Q / kBK < 2 ? 2 : Q / kBK;  // token stages per loop iteration
   static_assert(NP == 2 || NP == 4, "the loop body holds two or four token stages");
   static_assert(Q == kBK || Q == 2 * kBK || Q == 4 * kBK, "queue depth must match the loop body");
   const int nsb = c.ksteps / kBK;                // token stages (a multiple of NP)
-  u32x4 qa[Q][RT], rb0[TT], rb1[TT], bc[TT];
+  u32x4 qa[Q][RT], rb0[TT], rb1[TT];
   load_b(c, 0, nsb, rb0);
   load_b(c, 1, nsb, rb1);
   store_b(c, lds, rb0);
@@ -181,14 +269,29 @@ __device__ __forceinline__ void mainloop(const Ctx<RT, TT>& c, u32x4* lds, f32x1
 #pragma unroll
   for (int i = 0; i < Q; ++i) load_a(c, i, qa[i]);
   __syncthreads();
-  read_b<TT>(lds, 0, c.lane, bc);
   int buf = 0;
-  for (int kb = 0; kb < nsb; kb += NP) {
-    bstage<RT, TT, Q, 0>(c, lds, buf, kb, nsb, qa, rb0, bc, acc);
-    bstage<RT, TT, Q, 1>(c, lds, buf, kb + 1, nsb, qa, rb1, bc, acc);
-    if constexpr (NP == 4) {
-      bstage<RT, TT, Q, 2>(c, lds, buf, kb + 2, nsb, qa, rb0, bc, acc);
-      bstage<RT, TT, Q, 3>(c, lds, buf, kb + 3, nsb, qa, rb1, bc, acc);
+  if constexpr (F8) {
+    static_assert(Q % 2 == 0, "an fp8 MFMA step takes two queue slots");
+    u32x4 bc[TT][2];
+    read_b8<TT>(lds, 0, c.lane, bc);
+    for (int kb = 0; kb < nsb; kb += NP) {
+      bstage8<RT, TT, Q, 0>(c, lds, buf, kb, nsb, qa, rb0, bc, acc);
+      bstage8<RT, TT, Q, 1>(c, lds, buf, kb + 1, nsb, qa, rb1, bc, acc);
+      if constexpr (NP == 4) {
+        bstage8<RT, TT, Q, 2>(c, lds, buf, kb + 2, nsb, qa, rb0, bc, acc);
+        bstage8<RT, TT, Q, 3>(c, lds, buf, kb + 3, nsb, qa, rb1, bc, acc);
+      }
+    }
+  } else {
+    u32x4 bc[TT];
+    read_b<TT>(lds, 0, c.lane, bc);
+    for (int kb = 0; kb < nsb; kb += NP) {
+      bstage<RT, TT, Q, 0>(c, lds, buf, kb, nsb, qa, rb0, bc, acc);
+      bstage<RT, TT, Q, 1>(c, lds, buf, kb + 1, nsb, qa, rb1, bc, acc);
+      if constexpr (NP == 4) {
+        bstage<RT, TT, Q, 2>(c, lds, buf, kb + 2, nsb, qa, rb0, bc, acc);
+        bstage<RT, TT, Q, 3>(c, lds, buf, kb + 3, nsb, qa, rb1, bc, acc);
+      }
     }
   }
 }
@@ -268,12 +371,14 @@ __device__ __forceinline__ void decode_unit(const ExpTab& tab, int nrb, int L, U
 }
 
 // SC: fp8 weights (row scales in rsc); bf16 weights compile without them.
-template <int MODE, int RT, int Q, int TT, bool SC>
+// F8: fp8 weights and activations (row scales in rsc, activation scales in asc).
+template <int MODE, int RT, int Q, int TT, bool SC, bool F8>
 __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16_t* __restrict__ wpk,
                                          const uint16_t* __restrict__ src,
                                          const int* __restrict__ gather,
                                          const float* __restrict__ gate,
-                                         const float* __restrict__ rsc, int k,
+                                         const float* __restrict__ rsc,
+                                         const float* __restrict__ asc, int k,
                                          const uint16_t* __restrict__ zrow,
                                          uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
                                          int d, int F) {
@@ -286,7 +391,7 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
   Ctx<RT, TT> c;
   c.wave = wave;
   c.lane = lane;
-  c.ksteps = K / kKStep;
+  c.ksteps = K / (F8 ? 2 * kKStep : kKStep);  // 1 KiB blocks along K
   c.tile_elems = (size_t)c.ksteps * kBlockElems;
   c.wa = wpk + ((size_t)u.e * (rows_e / kTileRows) + tile0) * c.tile_elems + lane * 8;
 #pragma unroll
@@ -307,7 +412,7 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[r][j][q] = 0.f;
 
-  mainloop<RT, TT, Q>(c, lds, acc);
+  mainloop<RT, TT, Q, F8>(c, lds, acc);
 
   // epilogue
   const int col = lane & 31, hi = lane >> 5;
@@ -327,7 +432,16 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
           // fp8 weights: per-row dequantisation scales of the gate rows
           // 16*gt + 8g + 4hi .. +3 and of the matching up rows
           float v4[4];
-          if constexpr (SC) {
+          if constexpr (F8) {  // weight row scales times the token's activation scale
+            const float* rs = rsc + (size_t)u.e * 2 * F + 32 * gt + 8 * g + 4 * hi;
+            const f32x4 sg = *reinterpret_cast<const f32x4*>(rs);
+            const f32x4 su = *reinterpret_cast<const f32x4*>(rs + 16);
+            const float xs = asc[(size_t)(u.sub0 + j) * kSub + col];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              v4[t] = silu((sg[t] * xs) * acc[rt][j][4 * g + t]) *
+                      ((su[t] * xs) * acc[rt][j][4 * g + 8 + t]);
+          } else if constexpr (SC) {
             const float* rs = rsc + (size_t)u.e * 2 * F + 32 * gt + 8 * g + 4 * hi;
             const f32x4 sg = *reinterpret_cast<const f32x4*>(rs);
             const f32x4 su = *reinterpret_cast<const f32x4*>(rs + 16);
@@ -359,11 +473,18 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
       const bool ok = r < u.nrows;
       const int tok = k == 1 && ok ? gather[u.slot0 + r] : 0;
       const float gw = k == 1 && ok ? gate[tok] : 0.f;
+      float ms = 1.f;  // F8: the token row's activation scale
+      if constexpr (F8) ms = asc[(size_t)(u.sub0 + j) * kSub + col];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          if constexpr (SC) {  // fp8 weights: per-row scales of output rows m .. m+3
+          if constexpr (F8) {  // per-row weight scales times the activation scale
+            const int m = (tile0 + rt) * kTileRows + 4 * hi + 8 * q;
+            const f32x4 s4 = *reinterpret_cast<const f32x4*>(rsc + (size_t)u.e * d + m);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[rt][j][4 * q + t] *= s4[t] * ms;
+          } else if constexpr (SC) {  // fp8 weights: per-row scales of output rows m .. m+3
             const int m = (tile0 + rt) * kTileRows + 4 * hi + 8 * q;
             const f32x4 s4 = *reinterpret_cast<const f32x4*>(rsc + (size_t)u.e * d + m);
 #pragma unroll
@@ -417,33 +538,35 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
 
 namespace {
 // run_unit for the unit's subtile count (at most TTM)
-template <int MODE, int RT, int Q, int TT, bool SC>
+template <int MODE, int RT, int Q, int TT, bool SC, bool F8>
 __device__ __forceinline__ void run_any(const Unit& u, u32x4* lds, const uint16_t* __restrict__ wpk,
                                         const uint16_t* __restrict__ src,
                                         const int* __restrict__ gather,
                                         const float* __restrict__ gate,
-                                        const float* __restrict__ rsc, int k,
+                                        const float* __restrict__ rsc,
+                                        const float* __restrict__ asc, int k,
                                         const uint16_t* __restrict__ zrow,
                                         uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
                                         int d, int F) {
   if constexpr (TT > 1) {
     if (u.nsub != TT) {
-      run_any<MODE, RT, Q, TT - 1, SC>(u, lds, wpk, src, gather, gate, rsc, k, zrow, dst16, ybuf,
-                                       d, F);
+      run_any<MODE, RT, Q, TT - 1, SC, F8>(u, lds, wpk, src, gather, gate, rsc, asc, k, zrow,
+                                           dst16, ybuf, d, F);
       return;
     }
   }
-  run_unit<MODE, RT, Q, TT, SC>(u, lds, wpk, src, gather, gate, rsc, k, zrow, dst16, ybuf, d, F);
+  run_unit<MODE, RT, Q, TT, SC, F8>(u, lds, wpk, src, gather, gate, rsc, asc, k, zrow, dst16, ybuf,
+                                    d, F);
 }
 }  // namespace
 
 // OCC workgroups per CU; spans of at most TTM subtiles.
-template <int MODE, int RT, int Q, int OCC, int TTM, bool SC>
+template <int MODE, int RT, int Q, int OCC, int TTM, bool SC, bool F8>
 __global__ __launch_bounds__(256, OCC) void k_expert_gemm(
     const uint16_t* __restrict__ wpk, const uint16_t* __restrict__ src,
     const int* __restrict__ counts, const int* __restrict__ offsets,
     const int* __restrict__ gather, const float* __restrict__ gate,
-    const float* __restrict__ rsc, int k, int E, int cap,
+    const float* __restrict__ rsc, const float* __restrict__ asc, int k, int E, int cap,
     const uint16_t* __restrict__ zrow, uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
     int d, int F) {
   static_assert(TTM >= 1 && TTM <= 8, "token subtiles per unit");
@@ -462,7 +585,8 @@ __global__ __launch_bounds__(256, OCC) void k_expert_gemm(
     Unit u;
     decode_unit(tab, nrb, L, u);
     __syncthreads();  // the previous unit's last LDS reads are done everywhere
-    run_any<MODE, RT, Q, TTM, SC>(u, lds, wpk, src, gather, gate, rsc, k, zrow, dst16, ybuf, d, F);
+    run_any<MODE, RT, Q, TTM, SC, F8>(u, lds, wpk, src, gather, gate, rsc, asc, k, zrow, dst16, ybuf,
+                                      d, F);
   }
 }
 
@@ -517,20 +641,25 @@ int span_cap(int n, int E, int nrb, int grid, int TTM) {
   return best;
 }
 
-template <int MODE, int RT, int Q, int OCC, int TTM>
+// F8: fp8 weights and activations (the fp8 banks, the E4M3 token tiles and
+// their scales).
+template <int MODE, int RT, int Q, int OCC, int TTM, bool F8 = false>
 hipError_t launch_gemm(const FwdArgs& a) {
   const int grid = (a.num_cu * OCC + 7) / 8 * 8;  // persistent: OCC workgroups per CU
   const int nrb = (MODE == 0 ? 2 * a.dim.F : a.dim.d) / Geo<RT>::kRows;
   const int cap = span_cap(a.n, a.dim.E, nrb, grid, TTM);
   const float* rsc = MODE == 0 ? a.sgu : a.sd;
-  auto kern = rsc != nullptr ? k_expert_gemm<MODE, RT, Q, OCC, TTM, true>
-                             : k_expert_gemm<MODE, RT, Q, OCC, TTM, false>;
+  auto kern = F8 ? k_expert_gemm<MODE, RT, Q, OCC, TTM, true, F8>
+                 : rsc != nullptr ? k_expert_gemm<MODE, RT, Q, OCC, TTM, true, false>
+                                  : k_expert_gemm<MODE, RT, Q, OCC, TTM, false, false>;
+  const void* wsrc = F8 ? (MODE == 0 ? a.wgu8 : a.wd8) : (MODE == 0 ? a.wgu : a.wd);
+  const void* tsrc = F8 ? (MODE == 0 ? a.xq : a.actq) : (MODE == 0 ? a.xt : a.act);
+  const float* asc = F8 ? (MODE == 0 ? a.sx : a.sm) : nullptr;
   return launch(kern, dim3(grid), dim3(256), a.stream,
                 a.ev[MODE == 0 ? kSlotExpertsA : kSlotExpertsB],
-                (const uint16_t*)(MODE == 0 ? a.wgu : a.wd),
-                (const uint16_t*)(MODE == 0 ? a.xt : a.act), (const int*)a.counts,
+                (const uint16_t*)wsrc, (const uint16_t*)tsrc, (const int*)a.counts,
                 (const int*)a.offsets, (const int*)a.gather, (const float*)a.gate,
-                rsc, a.dim.k, a.dim.E, cap,
+                rsc, asc, a.dim.k, a.dim.E, cap,
                 (const uint16_t*)a.zrow,
                 (uint16_t*)(MODE == 0 ? a.act : a.out), a.ybuf, a.dim.d, a.dim.F);
 }
@@ -550,6 +679,18 @@ hipError_t launch_experts_tile(const FwdArgs& a) {
                                                       : launch_gemm<0, 2, 16, 1, 5>(a);
   if (err != hipSuccess) return err;
   return launch_gemm<1, 2, 8, 1, 6>(a);  // d_ff % 128 == 0: the k-steps fill whole loop bodies
+}
+
+// fp8 weights and activations: the gate/up GEMM over the E4M3 token tiles,
+// then (after k_quant_tiles has quantised its activations) the down GEMM.
+// Blocks of 32 k: d_model % 256 == 0 and d_ff % 256 == 0 fill whole loop
+// bodies of two stages (8 blocks) with an 8-block weight queue.
+hipError_t launch_experts_tile_fp8_gateup(const FwdArgs& a) {
+  return (2 * a.dim.F) % Geo<3>::kRows == 0 ? launch_gemm<0, 3, 8, 1, 5, true>(a)
+                                            : launch_gemm<0, 2, 8, 1, 5, true>(a);
+}
+hipError_t launch_experts_tile_fp8_down(const FwdArgs& a) {
+  return launch_gemm<1, 2, 8, 1, 6, true>(a);
 }
 
 }  // namespace moe

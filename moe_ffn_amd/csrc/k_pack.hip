@@ -112,6 +112,9 @@ hipError_t launch_prep_router(const void* w_router, const void* gain, int dtype,
 // (k-group l / 32 of each k-step), and the bf16 banks above holding the code
 // values themselves (every E4M3 value is exact in bf16) for the prefill GEMM.
 // The scales are applied to the fp32 accumulators, so no weight is rounded.
+// Layers with fp8 activations keep only the fp8 banks, which the fp8 MFMA
+// GEMMs read as they are (a 16-byte piece is one lane's share of a 1 KiB
+// block of 32 rows x 32 k).
 // gate/up or down codes -> bf16 bank in the layout of k_pack_gateup / k_pack_down
 __global__ void k_pack_gateup_fp8_bf16(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
                                        uint16_t* __restrict__ packed, int E, int F, int d) {
@@ -217,8 +220,10 @@ hipError_t launch_pack_fp8(const uint8_t* w_gate, const uint8_t* w_up, const uin
   auto grid = [](size_t n) { return dim3((unsigned)((n + 255) / 256)); };
   const size_t n_gu16 = (size_t)E * (2 * F / kTileRows) * (d / kKStep) * 64;
   const size_t n_d16 = (size_t)E * (d / kTileRows) * (F / kKStep) * 64;
-  hipLaunchKernelGGL(k_pack_gateup_fp8_bf16, grid(n_gu16), dim3(256), 0, s, w_gate, w_up, wgu16, E, F, d);
-  hipLaunchKernelGGL(k_pack_down_fp8_bf16, grid(n_d16), dim3(256), 0, s, w_down, wd16, E, d, F);
+  if (wgu16 != nullptr)
+    hipLaunchKernelGGL(k_pack_gateup_fp8_bf16, grid(n_gu16), dim3(256), 0, s, w_gate, w_up, wgu16, E, F, d);
+  if (wd16 != nullptr)
+    hipLaunchKernelGGL(k_pack_down_fp8_bf16, grid(n_d16), dim3(256), 0, s, w_down, wd16, E, d, F);
   hipLaunchKernelGGL(k_pack_gateup_fp8, grid(n_gu16 / 2), dim3(256), 0, s, w_gate, w_up, wgu8, E, F, d);
   hipLaunchKernelGGL(k_pack_down_fp8, grid(n_d16 / 2), dim3(256), 0, s, w_down, wd8, E, d, F);
   hipLaunchKernelGGL(k_pack_gateup_scales, grid((size_t)E * 2 * F), dim3(256), 0, s, s_gate, s_up, sgu, E, F);

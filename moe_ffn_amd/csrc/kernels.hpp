@@ -8,9 +8,12 @@
 namespace moe {
 
 // Kernel slots of one forward (per-kernel timing).  Launch order: router,
-// permutation, gather (bf16 prefill only), gate/up, down, combine.
+// permutation, gather (bf16 prefill only), [quantisation of the gathered rows],
+// gate/up, [quantisation of the activations], down, combine; the bracketed
+// ones run for fp8 activations only.
 enum Slot { kSlotNormRouter = 0, kSlotPermute = 1, kSlotExpertsA = 2, kSlotExpertsB = 3,
-            kSlotCombine = 4, kSlotGather = 5, kNumSlots = 6 };
+            kSlotCombine = 4, kSlotGather = 5, kSlotQuantX = 6, kSlotQuantAct = 7,
+            kNumSlots = 8 };
 
 // Optional start/stop events carried by a kernel's own dispatch packet.
 struct KEv {
@@ -48,6 +51,7 @@ struct LayerDims {
   int d, F, E, k, EP;  // EP = n_experts rounded up to a power of two
   float eps;
   int dtype;           // 0 = f32, 1 = bf16
+  int act8 = 0;        // fp8 weights and fp8 activations (bf16 layers with fp8 banks)
 };
 
 struct FwdArgs {
@@ -71,6 +75,12 @@ struct FwdArgs {
   const void* wd8;
   const float* sgu;
   const float* sd;
+  // fp8 activations (dim.act8): E4M3 token and activation tiles in the fp8
+  // banks' block order, and their per-row scales (one per padded slot)
+  void* xq = nullptr;
+  void* actq = nullptr;
+  float* sx = nullptr;
+  float* sm = nullptr;
   // per-call buffers (workspace or caller-provided routing outputs)
   void* xn;            // [T, d] gain-scaled activations g * h (bf16 or f32)
   float* inv;          // [T] 1 / rms of each token's hidden state
@@ -107,6 +117,14 @@ hipError_t launch_gather_tiles(const FwdArgs& a);
 int max_subtiles(int n, int E);
 hipError_t launch_experts_stream(const FwdArgs& a);
 hipError_t launch_experts_tile(const FwdArgs& a);
+hipError_t launch_experts_tile_fp8_gateup(const FwdArgs& a);  // dim.act8 layers
+hipError_t launch_experts_tile_fp8_down(const FwdArgs& a);
+// per-row E4M3 quantisation of bf16 operand tiles: which = 0 the gathered rows
+// (xt -> xq, sx), 1 the activations (act -> actq, sm)
+hipError_t launch_quant_tiles(const FwdArgs& a, int which);
+// the same on row-major bf16 rows [R][K] (K % 8 == 0)
+hipError_t launch_quant_rows(const void* x, int R, int K, void* codes, float* scale,
+                             hipStream_t s);
 hipError_t launch_experts_f32(const FwdArgs& a);
 hipError_t launch_combine(const FwdArgs& a);
 
@@ -126,6 +144,7 @@ hipError_t launch_pack_gateup(const uint16_t* w_gate, const uint16_t* w_up, uint
                               int F, int d, hipStream_t s);
 hipError_t launch_pack_down(const uint16_t* w_down, uint16_t* packed, int E, int d, int F,
                             hipStream_t s);
+// wgu16 / wd16 null: only the fp8 banks and the gate/up scales
 hipError_t launch_pack_fp8(const uint8_t* w_gate, const uint8_t* w_up, const uint8_t* w_down,
                            const float* s_gate, const float* s_up, int E, int F, int d,
                            uint16_t* wgu16, uint16_t* wd16, uint8_t* wgu8, uint8_t* wd8,

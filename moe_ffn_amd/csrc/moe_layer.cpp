@@ -74,6 +74,10 @@ struct Work {
   int* hist;
   void* xt;
   void* act;
+  void* xq;    // fp8 activations: E4M3 token tiles, activation tiles, their row scales
+  void* actq;
+  float* sx;
+  float* sm;
   float* ybuf;
   void* zrow;  // max(d, F) zero elements: must hold zeros before a forward runs
   void* sink;
@@ -103,6 +107,11 @@ size_t carve_work(const moe::LayerDims& dim, size_t tokens, char* base, Work* w)
   const size_t npad = bf16 ? (size_t)moe::max_subtiles((int)nmax, (int)E) * 32 : 0;
   const size_t o_xt = bf16 ? wc.take(npad * d * 2) : 0;
   const size_t o_act = wc.take((nmax > npad ? nmax : npad) * F * es);
+  const bool a8 = dim.act8 != 0;
+  const size_t o_xq = a8 ? wc.take(npad * d) : 0;
+  const size_t o_actq = a8 ? wc.take(npad * F) : 0;
+  const size_t o_sx = a8 ? wc.take(npad * 4) : 0;
+  const size_t o_sm = a8 ? wc.take(npad * 4) : 0;
   const size_t o_y = k > 1 ? wc.take(nmax * d * 4) : 0;
   const size_t zbytes = (d > F ? d : F) * 4;
   const size_t o_z = wc.take(zbytes);
@@ -120,6 +129,10 @@ size_t carve_work(const moe::LayerDims& dim, size_t tokens, char* base, Work* w)
     w->hist = reinterpret_cast<int*>(base + o_hist);
     w->xt = bf16 ? base + o_xt : nullptr;
     w->act = base + o_act;
+    w->xq = a8 ? base + o_xq : nullptr;
+    w->actq = a8 ? base + o_actq : nullptr;
+    w->sx = a8 ? reinterpret_cast<float*>(base + o_sx) : nullptr;
+    w->sm = a8 ? reinterpret_cast<float*>(base + o_sm) : nullptr;
     w->ybuf = k > 1 ? reinterpret_cast<float*>(base + o_y) : nullptr;
     w->zrow = base + o_z;
     w->sink = base + o_sink;
@@ -264,9 +277,10 @@ const char* moe_last_error(void) { return g_err.c_str(); }
 }  // extern "C"
 
 namespace {
-// sc != nullptr: expert weights are E4M3 codes with per-row scales.
+// sc != nullptr: expert weights are E4M3 codes with per-row scales; act8:
+// activations in E4M3 too (only the fp8 banks are kept).
 moe_status_t create_impl(const moe_layer_config_t* cfg, const moe_layer_weights_t* w,
-                         const moe_fp8_scales_t* sc, void* stream, moe_layer_t** out) {
+                         const moe_fp8_scales_t* sc, bool act8, void* stream, moe_layer_t** out) {
   if (out == nullptr) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   if (cfg == nullptr || w == nullptr) return fail(MOE_ERR_INVALID_ARG, "cfg or weights is NULL");
@@ -313,6 +327,7 @@ moe_status_t create_impl(const moe_layer_config_t* cfg, const moe_layer_weights_
   L->dim.EP = next_pow2(cfg->n_experts);
   L->dim.eps = cfg->rms_eps;
   L->dim.dtype = cfg->dtype;
+  L->dim.act8 = fp8 && act8 ? 1 : 0;
   L->max_tokens = cfg->max_tokens;
   L->device = dev;
   L->num_cu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
@@ -330,9 +345,10 @@ moe_status_t create_impl(const moe_layer_config_t* cfg, const moe_layer_weights_
   const bool bf16 = cfg->dtype == MOE_DTYPE_BF16;
   const size_t o_wr16 = bf16 ? pc.take(E * d * 2) : 0;
   const size_t o_g16 = bf16 ? pc.take(d * 2) : 0;
-  const size_t o_wgu = pc.take(E * F * d * es * (cfg->dtype == MOE_DTYPE_BF16 ? 2 : 1));
+  const bool banks16 = !L->dim.act8;  // bf16 (or fp8-valued bf16) banks
+  const size_t o_wgu = banks16 ? pc.take(E * F * d * es * (cfg->dtype == MOE_DTYPE_BF16 ? 2 : 1)) : 0;
   const size_t o_wup = cfg->dtype == MOE_DTYPE_F32 ? pc.take(E * F * d * es) : 0;
-  const size_t o_wd = pc.take(E * d * F * es);
+  const size_t o_wd = banks16 ? pc.take(E * d * F * es) : 0;
   const size_t o_wgu8 = fp8 ? pc.take(E * 2 * F * d) : 0;
   const size_t o_wd8 = fp8 ? pc.take(E * d * F) : 0;
   const size_t o_sgu = fp8 ? pc.take(E * 2 * F * 4) : 0;
@@ -349,9 +365,9 @@ moe_status_t create_impl(const moe_layer_config_t* cfg, const moe_layer_weights_
   L->bias = at<float>(L->params, o_bias);
   L->wr16 = bf16 ? at<void>(L->params, o_wr16) : nullptr;
   L->gain16 = bf16 ? at<void>(L->params, o_g16) : nullptr;
-  L->wgu = at<void>(L->params, o_wgu);
+  L->wgu = banks16 ? at<void>(L->params, o_wgu) : nullptr;
   L->wup = cfg->dtype == MOE_DTYPE_F32 ? at<void>(L->params, o_wup) : nullptr;
-  L->wd = at<void>(L->params, o_wd);
+  L->wd = banks16 ? at<void>(L->params, o_wd) : nullptr;
   L->wgu8 = fp8 ? at<void>(L->params, o_wgu8) : nullptr;
   L->wd8 = fp8 ? at<void>(L->params, o_wd8) : nullptr;
   L->sgu = fp8 ? at<float>(L->params, o_sgu) : nullptr;
@@ -384,7 +400,7 @@ moe_status_t create_impl(const moe_layer_config_t* cfg, const moe_layer_weights_
       he = moe::launch_pack_fp8(static_cast<const uint8_t*>(w->w_gate),
                                 static_cast<const uint8_t*>(w->w_up),
                                 static_cast<const uint8_t*>(w->w_down), sc->gate, sc->up, (int)E,
-                                (int)F, (int)d, static_cast<uint16_t*>(L->wgu),
+                                (int)F, (int)d, static_cast<uint16_t*>(L->wgu),  // null for act8
                                 static_cast<uint16_t*>(L->wd), static_cast<uint8_t*>(L->wgu8),
                                 static_cast<uint8_t*>(L->wd8), L->sgu, s);
       if (he == hipSuccess)
@@ -421,7 +437,7 @@ extern "C" {
 moe_status_t moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* w,
                               void* stream, moe_layer_t** out) {
   g_err.clear();
-  return create_impl(cfg, w, nullptr, stream, out);
+  return create_impl(cfg, w, nullptr, false, stream, out);
 }
 
 moe_status_t moe_layer_create_fp8(const moe_layer_config_t* cfg, const moe_layer_weights_t* w,
@@ -432,7 +448,34 @@ moe_status_t moe_layer_create_fp8(const moe_layer_config_t* cfg, const moe_layer
     if (out != nullptr) *out = nullptr;
     return fail(MOE_ERR_INVALID_ARG, "scales is NULL");
   }
-  return create_impl(cfg, w, scales, stream, out);
+  return create_impl(cfg, w, scales, false, stream, out);
+}
+
+moe_status_t moe_layer_create_w8a8(const moe_layer_config_t* cfg, const moe_layer_weights_t* w,
+                                   const moe_fp8_scales_t* scales, void* stream,
+                                   moe_layer_t** out) {
+  g_err.clear();
+  if (scales == nullptr) {
+    if (out != nullptr) *out = nullptr;
+    return fail(MOE_ERR_INVALID_ARG, "scales is NULL");
+  }
+  return create_impl(cfg, w, scales, true, stream, out);
+}
+
+moe_status_t moe_fp8_quantize_rows(const void* x, int32_t R, int32_t K, void* codes,
+                                   float* scales, void* stream) {
+  g_err.clear();
+  if (R < 0 || K <= 0 || K % 8 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "R must be >= 0 and K a positive multiple of 8");
+  if (R == 0) return MOE_OK;
+  if (x == nullptr || codes == nullptr || scales == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "x, codes or scales is NULL");
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(scales, 4))
+    return fail(MOE_ERR_INVALID_ARG, "x must be 16-byte, codes 8-byte and scales 4-byte aligned");
+  const hipError_t he = moe::launch_quant_rows(x, R, K, codes, scales,
+                                               reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "quantize launch");
+  return MOE_OK;
 }
 
 }  // extern "C"
@@ -504,6 +547,10 @@ moe_status_t forward_impl(moe_layer_t* L, const void* hidden, int32_t T, void* o
   a.hist = w.hist;
   a.xt = w.xt;
   a.act = w.act;
+  a.xq = w.xq;
+  a.actq = w.actq;
+  a.sx = w.sx;
+  a.sm = w.sm;
   a.ybuf = w.ybuf;
   a.zrow = w.zrow;
   a.sink = w.sink;
@@ -521,10 +568,11 @@ moe_status_t forward_impl(moe_layer_t* L, const void* hidden, int32_t T, void* o
     ++L->t_used;
   }
   const bool bf16 = L->dim.dtype == MOE_DTYPE_BF16;
-  const bool decode = bf16 && a.n <= moe::kStreamMaxAssign;
+  const bool act8 = L->dim.act8 != 0;  // fp8 activations: the tile path at every T
+  const bool decode = bf16 && !act8 && a.n <= moe::kStreamMaxAssign;
   if (L->timing && L->t_used > 0 && a.ev[0].start != nullptr)
     L->tslots[L->t_used - 1] = (uint8_t)(0x0d | (decode ? 0 : 0x02) | (L->dim.k > 1 ? 0x10 : 0) |
-                                         (bf16 && !decode ? 0x20 : 0));
+                                         (bf16 && !decode ? 0x20 : 0) | (act8 ? 0xc0 : 0));
 
   if (wk != nullptr && wk->clear_zrow) {
     he = moe::launch_zero(wk->zrow, wk->zbytes, a.stream);
@@ -543,7 +591,14 @@ moe_status_t forward_impl(moe_layer_t* L, const void* hidden, int32_t T, void* o
       he = moe::launch_gather_tiles(a);
       if (he != hipSuccess) return hip_fail(he, "gather launch");
     }
-    he = bf16 ? moe::launch_experts_tile(a) : moe::launch_experts_f32(a);
+    if (act8) {
+      he = moe::launch_quant_tiles(a, 0);
+      if (he == hipSuccess) he = moe::launch_experts_tile_fp8_gateup(a);
+      if (he == hipSuccess) he = moe::launch_quant_tiles(a, 1);
+      if (he == hipSuccess) he = moe::launch_experts_tile_fp8_down(a);
+    } else {
+      he = bf16 ? moe::launch_experts_tile(a) : moe::launch_experts_f32(a);
+    }
   }
   if (he != hipSuccess) return hip_fail(he, "expert launch");
   if (L->dim.k > 1) {

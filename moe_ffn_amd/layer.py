@@ -23,14 +23,14 @@ MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 
 # Symbols declared in include/moe_layer.h.
 EXPORTS = ("moe_abi_version", "moe_last_error", "moe_layer_create", "moe_layer_create_fp8",
-           "moe_layer_forward",
+           "moe_layer_create_w8a8", "moe_fp8_quantize_rows", "moe_layer_forward",
            "moe_layer_set_bias", "moe_layer_get_bias", "moe_layer_update_bias",
            "moe_layer_timing_start",
            "moe_layer_timing_stop", "moe_layer_destroy", "moe_stack_create", "moe_stack_forward",
            "moe_stack_capture", "moe_stack_replay", "moe_stack_destroy", "moe_stack_set_eda",
            "moe_stack_forward_routing", "moe_layer_forward_static")
 TIMED_SLOTS = ("norm_router", "route_permute", "experts_gate_up", "experts_down", "combine",
-               "gather")
+               "gather", "quant_x", "quant_act")
 
 
 class LayerConfig(ctypes.Structure):
@@ -81,10 +81,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.moe_layer_create.restype = ctypes.c_int
     lib.moe_layer_create.argtypes = [ctypes.POINTER(LayerConfig), ctypes.POINTER(LayerWeights),
                                      ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
-    lib.moe_layer_create_fp8.restype = ctypes.c_int
-    lib.moe_layer_create_fp8.argtypes = [ctypes.POINTER(LayerConfig), ctypes.POINTER(LayerWeights),
-                                         ctypes.POINTER(Fp8Scales), ctypes.c_void_p,
-                                         ctypes.POINTER(ctypes.c_void_p)]
+    for f in (lib.moe_layer_create_fp8, lib.moe_layer_create_w8a8):
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.POINTER(LayerConfig), ctypes.POINTER(LayerWeights),
+                      ctypes.POINTER(Fp8Scales), ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
+    lib.moe_fp8_quantize_rows.restype = ctypes.c_int
+    lib.moe_fp8_quantize_rows.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.moe_layer_forward.restype = ctypes.c_int
     lib.moe_layer_forward.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                       ctypes.c_void_p, ctypes.c_void_p,
@@ -138,6 +141,22 @@ def _stream_ptr(stream) -> int:
     return int(s.cuda_stream)
 
 
+def fp8_quantize_rows(x: torch.Tensor, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """moe_fp8_quantize_rows: x [R, K] contiguous CUDA bf16 (K % 8 == 0) ->
+    (codes [R, K] uint8 E4M3, scales [R] float32), per-row dynamic scales."""
+    lib = load_library()
+    if not (x.is_cuda and x.dtype == torch.bfloat16 and x.dim() == 2 and x.is_contiguous()):
+        raise ValueError("x: need a contiguous CUDA bfloat16 tensor [R, K]")
+    R, K = x.shape
+    codes = torch.empty((R, K), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((R,), dtype=torch.float32, device=x.device)
+    _check(lib, lib.moe_fp8_quantize_rows(ctypes.c_void_p(x.data_ptr()), R, K,
+                                          ctypes.c_void_p(codes.data_ptr()),
+                                          ctypes.c_void_p(scales.data_ptr()),
+                                          ctypes.c_void_p(_stream_ptr(stream))))
+    return codes, scales
+
+
 _TORCH_DTYPE = {MOE_DTYPE_F32: torch.float32, MOE_DTYPE_BF16: torch.bfloat16}
 
 
@@ -151,11 +170,13 @@ class MoELayer:
       gate [E, F], up [E, F], down [E, d]; then w_gate, w_up and w_down hold
       E4M3 codes (torch.uint8 or torch.float8_e4m3fn) and dtype must be "bf16"
       (moe_layer_create_fp8).
+    fp8_act: with fp8_scales, quantise the activations to E4M3 as well
+      (moe_layer_create_w8a8: both GEMM operands fp8, per-row dynamic scales).
     """
 
     def __init__(self, d_model: int, d_ff: int, n_experts: int, top_k: int, dtype: str,
                  weights: dict, max_tokens: int, rms_eps: float = 1e-6, stream=None,
-                 fp8_scales: dict | None = None):
+                 fp8_scales: dict | None = None, fp8_act: bool = False):
         self._lib = load_library()
         self.handle = None
         self.dtype_code = MOE_DTYPE_BF16 if dtype == "bf16" else MOE_DTYPE_F32
@@ -166,6 +187,9 @@ class MoELayer:
                   "b_router": (n_experts,), "w_gate": (n_experts, d_ff, d_model),
                   "w_up": (n_experts, d_ff, d_model), "w_down": (n_experts, d_model, d_ff)}
         self.fp8 = fp8_scales is not None
+        if fp8_act and not self.fp8:
+            raise ValueError("fp8_act needs fp8 weights (fp8_scales)")
+        self.fp8_act = fp8_act
         ptrs = {}
         for name, shp in shapes.items():
             t = weights[name]
@@ -193,9 +217,10 @@ class MoELayer:
                                      f"of shape {shp}")
                 sptrs[name] = t.data_ptr()
             sc = Fp8Scales(**sptrs)
-            _check(self._lib, self._lib.moe_layer_create_fp8(ctypes.byref(cfg), ctypes.byref(w),
-                                                             ctypes.byref(sc), stream_p,
-                                                             ctypes.byref(h)))
+            create = (self._lib.moe_layer_create_w8a8 if fp8_act
+                      else self._lib.moe_layer_create_fp8)
+            _check(self._lib, create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(sc),
+                                     stream_p, ctypes.byref(h)))
         else:
             _check(self._lib, self._lib.moe_layer_create(ctypes.byref(cfg), ctypes.byref(w),
                                                          stream_p, ctypes.byref(h)))

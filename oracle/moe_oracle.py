@@ -53,6 +53,14 @@ import numpy as np
 # Tokens whose top-k decision has a margin below this (absolute, on the biased
 # scores) may legitimately route either way in finite precision.
 MARGIN_TOL = 1e-3
+# fp8 activations (O12): a row's quantisation scale is a discrete decision
+# (the bf16 value of the row's largest element).  Rows whose scale changes
+# when every element moves by this much (relative) may legitimately be scaled
+# either way: the expert input carries the RMSNorm's float32 rounding; the
+# SwiGLU intermediate carries that of the fp8 dot products, which gfx950's
+# fp8 MFMA forms to about 5e-5 relative (rms) rather than to float32.
+FP8_SCALE_REL_U = 1e-5
+FP8_SCALE_REL_M = 3e-4
 
 
 def _f64(a) -> np.ndarray:
@@ -252,14 +260,19 @@ def oracle_forward(vals: dict, k: int | None = None, forced_sel=None, tokens=Non
         need[tok * k + j] = True
     slots_needed = np.sort(scatter[need])
     Y = np.zeros((T * k, x.shape[1]))
+    undecided = np.zeros(T * k, bool)   # fp8_act: slots whose quantisation scales are undecided
     Wg, Wu, Wd = vals["w_gate"], vals["w_up"], vals["w_down"]
     for e in range(E):
         lo, hi = offsets[e], offsets[e + 1]
         ps = slots_needed[(slots_needed >= lo) & (slots_needed < hi)]
         if ps.size == 0:
             continue
-        expert = swiglu_expert_fp8act if fp8_act else swiglu_expert
-        Y[ps] = expert(Wg[e], Wu[e], Wd[e], x[gather[ps]])
+        if fp8_act:
+            Y[ps], M = swiglu_expert_fp8act(Wg[e], Wu[e], Wd[e], x[gather[ps]], inner=True)
+            undecided[ps] = (scale_undecided(x[gather[ps]], FP8_SCALE_REL_U)
+                             | scale_undecided(M, FP8_SCALE_REL_M))
+        else:
+            Y[ps] = swiglu_expert(Wg[e], Wu[e], Wd[e], x[gather[ps]])
     if tokens is None:
         out = combine(Y, gate, scatter, k)
     else:
@@ -267,9 +280,11 @@ def oracle_forward(vals: dict, k: int | None = None, forced_sel=None, tokens=Non
         out = np.zeros((tok.size, x.shape[1]))
         for j in range(k):
             out += gate[tok, j:j + 1] * Y[sc[:, j]]
+    # a token is undecided when one of its assignments is
+    scale_tie = undecided[scatter.reshape(T, k)].any(axis=1)[tok]
     return {"x": x, "z": z, "s": s, "sel": sel, "sel_oracle": sel_o, "margin": margin,
             "gate": gate, "counts": counts, "offsets": offsets, "gather": gather,
-            "scatter": scatter, "out": out, "tokens": tok}
+            "scatter": scatter, "out": out, "tokens": tok, "scale_tie": scale_tie}
 
 
 # O11 ------------------------------------------------------------------------
@@ -440,12 +455,24 @@ def fp8_activation(U) -> np.ndarray:
     return dequantize_rows(*quantize_rows_e4m3(bf16_round(U)))
 
 
-def swiglu_expert_fp8act(Wg, Wu, Wd, U) -> np.ndarray:
+def swiglu_expert_fp8act(Wg, Wu, Wd, U, inner: bool = False):
     """O7 with fp8 activations (the reading above): G and V are the exact
     products of fp8_activation(u) with the (dequantised fp8) weights, and
     y = W_down fp8_activation(SiLU(G) * V).  Float64 throughout, apart from
-    the bf16 roundings and the float32 quantisation steps the reading names."""
+    the bf16 roundings and the float32 quantisation steps the reading names.
+    inner=True also returns the intermediate SiLU(G) * V before its rounding."""
     X = fp8_activation(U)
     G = X @ _f64(Wg).T
     V = X @ _f64(Wu).T
-    return fp8_activation(silu(G) * V) @ _f64(Wd).T
+    M = silu(G) * V
+    Y = fp8_activation(M) @ _f64(Wd).T
+    return (Y, M) if inner else Y
+
+
+def scale_undecided(V, rel: float) -> np.ndarray:
+    """Rows of V whose fp8 quantisation scale is not fixed under a relative
+    change of at most `rel` in each element: the scale is amax / 448 with
+    amax the largest |bf16(v)|, and bf16 rounding is monotone, so the row is
+    undecided when bf16(max|v| (1 - rel)) != bf16(max|v| (1 + rel))."""
+    amax = np.max(np.abs(_f64(V)), axis=-1)
+    return bf16_round(amax * (1.0 - rel)) != bf16_round(amax * (1.0 + rel))

@@ -56,13 +56,19 @@ def out_to_f64(t: torch.Tensor) -> np.ndarray:
 
 
 def check_parity(inputs: dict, layer, sample: int | None = None, seed: int = 0,
-                 label: str = "", vals: dict | None = None) -> dict:
+                 label: str = "", vals: dict | None = None, fp8_act: bool = False) -> dict:
     """Run the layer on ``inputs`` and assert the parity protocol.
 
     sample: number of tokens whose output rows are compared (all when None);
     routing and dispatch are always compared in full.
     vals: the exact values the oracle runs on (default: those of ``inputs``;
-    fp8 layers pass their dequantised expert weights)."""
+    fp8 layers pass their dequantised expert weights).
+    fp8_act: the oracle quantises the expert activations (O12).  Tokens whose
+    quantisation scale the oracle reports undecided (scale_tie: the device's
+    finite-precision value may round the row's largest element either way,
+    re-deciding every code of the row) are held to validity only (a row rms
+    error under 10%), counted and reported, like routing near-ties; every
+    other row meets the output bar."""
     cfg = inputs["cfg"]
     if vals is None:
         vals = gen.values_f32(inputs)
@@ -80,7 +86,7 @@ def check_parity(inputs: dict, layer, sample: int | None = None, seed: int = 0,
     else:
         rng = np.random.default_rng(seed)
         tokens = np.unique(np.concatenate([[0, T - 1], rng.choice(T, size=sample, replace=False)]))
-    ref = O.oracle_forward(vals, forced_sel=sel, tokens=tokens)
+    ref = O.oracle_forward(vals, forced_sel=sel, tokens=tokens, fp8_act=fp8_act)
     # 1. routing against the oracle's own choice
     margin = ref["margin"]
     firm = margin >= O.MARGIN_TOL
@@ -101,14 +107,23 @@ def check_parity(inputs: dict, layer, sample: int | None = None, seed: int = 0,
     if tokens is not None:
         got = got[tokens]
     want = ref["out"]
-    scale = float(np.max(np.abs(want)))
-    err = float(np.max(np.abs(got - want)))
     assert np.all(np.isfinite(got)), f"{label}: non-finite output"
+    tie = ref["scale_tie"] if fp8_act else np.zeros(got.shape[0], bool)
+    scale = float(np.max(np.abs(want)))
+    d = got - want
+    err = float(np.max(np.abs(d[~tie]))) if np.any(~tie) else 0.0
     assert err <= TOL[cfg.dtype] * scale, (
         f"{label}: max|err| {err:.3e} > {TOL[cfg.dtype]} * max|ref| {scale:.3e}")
+    row_rms = np.sqrt(np.mean(d ** 2, axis=1)) / np.maximum(np.sqrt(np.mean(want ** 2, axis=1)), 1e-300)
+    assert np.all(row_rms[tie] <= 0.1), f"{label}: a row with an undecided fp8 scale is off by {row_rms[tie].max():.3f}"
+    strict_rms = (float(np.sqrt(np.mean(d[~tie] ** 2)) / max(np.sqrt(np.mean(want[~tie] ** 2)), 1e-300))
+                  if np.any(~tie) else 0.0)
     stats = {"label": label, "T": T, "k": k, "near_ties": int(np.sum(~firm)),
              "near_tie_flips": int(np.sum(mism & ~firm)), "max_err_rel": err / max(scale, 1e-300),
-             "rms_err_rel": float(np.sqrt(np.mean((got - want) ** 2)) / max(np.sqrt(np.mean(want ** 2)), 1e-300)),
-             "gate_err": gerr, "rows_compared": int(got.shape[0])}
+             "rms_err_rel": strict_rms, "gate_err": gerr, "rows_compared": int(got.shape[0])}
+    if fp8_act:
+        stats["scale_ties"] = int(np.sum(tie))
+        stats["scale_tie_max_row_rms"] = float(row_rms[tie].max()) if np.any(tie) else 0.0
+        stats["max_row_rms_decided"] = float(row_rms[~tie].max()) if np.any(~tie) else 0.0
     print(f"[parity] {stats}", flush=True)
     return stats

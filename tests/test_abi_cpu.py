@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["moe_abi_version", "moe_last_error", "moe_layer_create",
-                            "moe_layer_create_fp8",
+                            "moe_layer_create_fp8", "moe_layer_create_w8a8",
+                            "moe_fp8_quantize_rows",
                             "moe_layer_forward", "moe_layer_set_bias", "moe_layer_get_bias",
                             "moe_layer_update_bias",
                             "moe_layer_timing_start", "moe_layer_timing_stop",
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), f"missing export {name}"
     assert set(layer.EXPORTS) == set(declared_functions())
-    assert lib.moe_abi_version() == 5
+    assert lib.moe_abi_version() == 6
 
 
 def test_abi_structs_match_header_sizes():
@@ -113,6 +114,27 @@ def test_create_fp8_rejects_bad_scales_and_dtype_on_host():
     assert lib.moe_layer_create_fp8(ctypes.byref(cfg32), ctypes.byref(w), ctypes.byref(sc), None,
                                     ctypes.byref(h)) == layer.MOE_ERR_INVALID_ARG
     assert b"BF16" in lib.moe_last_error()
+
+
+def test_create_w8a8_and_quantize_rows_reject_bad_arguments_on_host():
+    lib, layer = _lib()
+    cfg = _cfg(layer)
+    w = layer.LayerWeights(16, 16, 16, 16, 16, 16)
+    h = ctypes.c_void_p(123)
+    assert lib.moe_layer_create_w8a8(ctypes.byref(cfg), ctypes.byref(w), None, None,
+                                     ctypes.byref(h)) == layer.MOE_ERR_INVALID_ARG
+    assert h.value is None and b"scales" in lib.moe_last_error()
+    sc = layer.Fp8Scales(16, 16, 16)
+    cfg32 = _cfg(layer, dtype=0)
+    assert lib.moe_layer_create_w8a8(ctypes.byref(cfg32), ctypes.byref(w), ctypes.byref(sc),
+                                     None, ctypes.byref(h)) == layer.MOE_ERR_INVALID_ARG
+    q = lib.moe_fp8_quantize_rows
+    assert q(16, 4, 12, 16, 16, None) == layer.MOE_ERR_INVALID_ARG      # K % 8 != 0
+    assert q(16, -1, 8, 16, 16, None) == layer.MOE_ERR_INVALID_ARG      # R < 0
+    assert q(None, 4, 8, 16, 16, None) == layer.MOE_ERR_INVALID_ARG     # NULL x
+    assert q(24, 4, 8, 16, 16, None) == layer.MOE_ERR_INVALID_ARG       # x not 16-byte aligned
+    assert b"aligned" in lib.moe_last_error()
+    assert q(None, 0, 8, None, None, None) == layer.MOE_OK              # nothing to do
 
 
 def test_entry_points_reject_bad_handles_and_destroy_is_null_safe():

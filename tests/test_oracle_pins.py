@@ -659,3 +659,22 @@ def test_fp8_activation_quantises_the_bf16_value():
     X = O.fp8_activation(np.array([[3.0, 1.0]]))
     a = np.float64(np.float32(3.0) / np.float32(448.0))
     np.testing.assert_array_equal(X, [[448.0 * a, 144.0 * a]])
+
+
+def test_scale_undecided_marks_rows_near_a_bf16_rounding_boundary():
+    # amax 1 + 2^-8 (+-) is the midpoint between the bf16 values 1 and
+    # 1 + 2^-7: any perturbation decides it; 1.25 is a bf16 value far from
+    # every boundary; a row's other elements do not matter
+    V = np.array([[1 + 2.0 ** -8, 0.5], [1.25, -1.0], [-(1 + 2.0 ** -8 + 2.0 ** -20), 0.0],
+                  [0.0, 0.0]])
+    np.testing.assert_array_equal(O.scale_undecided(V, 1e-4), [True, False, True, False])
+    np.testing.assert_array_equal(O.scale_undecided(V, 1e-8), [True, False, False, False])
+    # the flag is the only difference the perturbation can make to the scale
+    rng = np.random.default_rng(37)
+    M = rng.standard_normal((400, 50))
+    und = O.scale_undecided(M, 1e-3)
+    a0 = O.quantize_rows_e4m3(O.bf16_round(M))[1]
+    for f in (1 - 1e-3, 1 + 1e-3):
+        a1 = O.quantize_rows_e4m3(O.bf16_round(M * f))[1]
+        assert np.all(a1[~und] == a0[~und])
+    assert 0 < und.sum() < 400
