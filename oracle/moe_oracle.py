@@ -379,8 +379,8 @@ def fp8_weights(codes, scale) -> np.ndarray:
 # stores both quantised vectors in bf16 before quantising them (the expert
 # input as bf16 rows, the intermediate as bf16 SwiGLU outputs), and a
 # quantisation decides integer codes, so this reading quantises the bf16
-# value of each vector and takes the scale and the division in float32, as
-# the device does.  Everything else stays in float64.
+# value of each vector and takes the scale, its reciprocal and the product
+# in float32, as the device does.  Everything else stays in float64.
 
 def bf16_round(v) -> np.ndarray:
     """Round float64 values to the nearest bfloat16 value (8 significant bits,
@@ -427,17 +427,19 @@ def e4m3_encode(v) -> np.ndarray:
 def quantize_rows_e4m3(V):
     """Dynamic per-row E4M3 quantisation of V [R, K] (values that float32
     holds exactly; the layer passes bf16 values): with amax the largest |v| of
-    a row, the row's scale is a = float32(amax / 448) and its codes are
-    e4m3_encode(float32(v / a)), both divisions correctly rounded in float32.
-    A row of zeros gets a = 0 and all codes 0.  Returns (codes uint8 [R, K],
-    a float32 [R]); the row's values are then a * e4m3_value(codes)."""
+    a row, the row's scale is a = float32(amax / 448), its reciprocal
+    r = float32(1 / a) (both correctly rounded divisions in float32), and its
+    codes are e4m3_encode(float32(v * r)).  A row of zeros gets a = 0 and all
+    codes 0.  Returns (codes uint8 [R, K], a float32 [R]); the row's values
+    are then a * e4m3_value(codes)."""
     V32 = np.asarray(V, np.float64).astype(np.float32)
     if not np.array_equal(V32.astype(np.float64), _f64(V)):
         raise ValueError("quantize_rows_e4m3 takes values that float32 holds exactly")
     amax = np.max(np.abs(V32), axis=-1)
     a = (amax / np.float32(448.0)).astype(np.float32)
     safe = np.where(a > 0, a, np.float32(1.0)).astype(np.float32)
-    q = (V32 / safe[..., None]).astype(np.float32)
+    r = (np.float32(1.0) / safe).astype(np.float32)
+    q = (V32 * r[..., None]).astype(np.float32)
     codes = e4m3_encode(q.astype(np.float64))
     codes = np.where((a > 0)[..., None], codes, 0).astype(np.uint8)
     return codes, a

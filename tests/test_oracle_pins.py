@@ -530,7 +530,7 @@ def test_quantize_rows_hand_examples():
     c, a = O.quantize_rows_e4m3(np.array([[448.0, 1.0625, -2.0 ** -8, 0.0]]))
     assert a[0] == np.float32(1.0)
     np.testing.assert_array_equal(c[0], [0x7E, 0x38, 0x82, 0x00])
-    # [3, 1]: a = float32(3/448); 1/a = 149.33.. lies between 144 and 160
+    # [3, 1]: a = float32(3/448); 1 * float32(1/a) = 149.33.. lies between 144 and 160
     c, a = O.quantize_rows_e4m3(np.array([[3.0, 1.0]]))
     assert a[0] == np.float32(3.0) / np.float32(448.0)
     np.testing.assert_array_equal(c[0], [0x7E, 0x71])
@@ -555,12 +555,16 @@ def test_quantize_rows_error_bound_and_scale_invariance():
     assert np.all(a[ok] == (np.max(np.abs(V), axis=1)[ok] / 448.0).astype(np.float32))
     # every code is within half an E4M3 spacing of v / a (spacing 2^(E-3) for
     # |t| in [2^E, 2^(E+1)), E >= -6; 2^-9 below 2^-6), plus the float32
-    # rounding of the quotient
+    # roundings of the reciprocal and of the product
     t = V[ok] / a[ok].astype(np.float64)[:, None]
     E = np.floor(np.log2(np.maximum(np.abs(t), 2.0 ** -6)))
     half = np.exp2(E - 3) / 2
     err = np.abs(O.e4m3_value(c[ok]) - t)
-    assert np.all(err <= half + np.abs(t) * 2.0 ** -23)
+    assert np.all(err <= half + np.abs(t) * 2.0 ** -22)
+    # the quotient is the float32 product with the float32 reciprocal
+    r = (np.float32(1) / a[ok]).astype(np.float32)
+    q = (V[ok].astype(np.float32) * r[:, None]).astype(np.float32)
+    np.testing.assert_array_equal(c[ok], O.e4m3_encode(q.astype(np.float64)))
     # dequantised rows against the input: relative 2^-4 plus the subnormal floor
     D = O.dequantize_rows(c, a)
     assert np.all(np.abs(D - V) <= np.abs(V) * (2.0 ** -4 + 2.0 ** -22) + a[:, None] * 2.0 ** -10)
