@@ -20,9 +20,12 @@ tokens/s, whole-layer fraction of the bf16 MFMA peak and their gate/up
 grouped GEMM's time and fraction.
 
 With --fp8 the expert weights are E4M3 codes with per-row fp32 scales
-(moe_layer_create_fp8): decode streams half the weight bytes.
+(moe_layer_create_fp8): decode streams half the weight bytes.  With --w8a8
+the activations are quantised to E4M3 as well (moe_layer_create_w8a8) and the
+expert GEMMs run on the fp8 MFMA, priced against the dense fp8 peak.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config {0,1,2,3,4}] [--fp8]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config {0,1,2,3,4}]
+                       [--fp8 | --w8a8]
 """
 
 from __future__ import annotations
@@ -40,6 +43,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 METRIC = "MoE-layer tokens/s at 1 GPU; HBM GB/s (decode) and MFMA % of peak (prefill)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -147,13 +151,15 @@ def ingest_counters(pmc_dir: str) -> None:
     print(json.dumps(out, indent=1))
 
 
-def dominant_kernel(cfg, counts, fp8: bool = False):
+def dominant_kernel(cfg, counts, fp8: bool = False, act8: bool = False):
     """Dominant kernel of a forward and its algorithmic work per launch.
 
     Decode-sized batches (T*k <= 64) take the weight-streaming path whose
     gate/up kernel moves 2/3 of the bytes; larger batches take the tiled
     grouped GEMM whose gate/up launch does 2/3 of the flops.  fp8 weights:
-    one byte per weight plus one fp32 scale per row."""
+    one byte per weight plus one fp32 scale per row.  fp8 activations (act8):
+    the tiled path at every batch size, its gate/up GEMM priced by weight
+    bytes at decode sizes and against the fp8 MFMA peak above them."""
     d, F, k, T = cfg.d, cfg.F, cfg.k, cfg.T
     n = T * k
     touched = int((counts > 0).sum())
@@ -168,7 +174,8 @@ def dominant_kernel(cfg, counts, fp8: bool = False):
         # W_gate + W_up bytes of one expert
         per_expert = 2 * F * d + 2 * F * 4 if fp8 else 2 * F * d * 2
         work = touched * per_expert + n * d * 2 + n * F * 2
-        return {"slot": "experts_gate_up", "kernel": "k_gateup_stream", "bound": "hbm",
+        return {"slot": "experts_gate_up",
+                "kernel": "k_expert_gemm<0>" if act8 else "k_gateup_stream", "bound": "hbm",
                 "unit": "GB/s", "units": touched, "per_unit": per_expert,
                 "unit_name": "touched expert (W_gate + W_up bytes%s)" % (
                     ": E4M3 codes + row scales" if fp8 else ""), "work": work,
@@ -176,6 +183,7 @@ def dominant_kernel(cfg, counts, fp8: bool = False):
     per_assign = 2 * 2 * F * d                      # gate and up: 2 flops x F x d each
     work = n * per_assign
     return {"slot": "experts_gate_up", "kernel": "k_expert_gemm<0>", "bound": "mfma",
+            "peak": PEAK_FP8_TFLOPS if act8 else PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "units": n, "per_unit": per_assign,
             "unit_name": "routed assignment (gate+up flops)", "work": work, "work_unit": "flops"}
 
@@ -210,7 +218,7 @@ def routing_check(inputs, sel_gpu) -> dict:
             "firm_mismatches": int(np.sum(~same & firm))}
 
 
-def cpu_baseline(inputs, seconds: float, fp8: dict | None = None):
+def cpu_baseline(inputs, seconds: float, fp8: dict | None = None, act8: bool = False):
     """The fp64 oracle as it stands, on the host cores, over a bounded sample."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
@@ -229,7 +237,7 @@ def cpu_baseline(inputs, seconds: float, fp8: dict | None = None):
         threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
         reps, t0 = 0, time.perf_counter()
         while True:
-            O.oracle_forward(vals, tokens=sample)
+            O.oracle_forward(vals, tokens=sample, fp8_act=act8)
             reps += 1
             el = time.perf_counter() - t0
             if el >= seconds or reps >= 10000:
@@ -237,7 +245,7 @@ def cpu_baseline(inputs, seconds: float, fp8: dict | None = None):
     with threadpool_limits(limits=1):
         reps1, t1 = 0, time.perf_counter()
         while True:
-            O.oracle_forward(vals, tokens=sample)
+            O.oracle_forward(vals, tokens=sample, fp8_act=act8)
             reps1 += 1
             el1 = time.perf_counter() - t1
             if el1 >= seconds / 3 or reps1 >= 10000:
@@ -454,9 +462,10 @@ def run_stack(args):
     print(json.dumps(line), flush=True)
 
 
-def make_layers(inp, n: int, fp8: bool, dev):
+def make_layers(inp, n: int, fp8: bool, dev, act8: bool = False):
     """n independently allocated copies of the workload's layer (fp8: E4M3
-    expert weights with row scales) and the fp8 codes used (or None)."""
+    expert weights with row scales; act8: and E4M3 activations) and the fp8
+    codes used (or None)."""
     import numpy as np
     import torch
     from moe_ffn_amd import MoELayer
@@ -480,7 +489,7 @@ def make_layers(inp, n: int, fp8: bool, dev):
         w.update({n_: torch.from_numpy(q8[n_]).to(dev) for n_ in ("w_gate", "w_up", "w_down")})
         scales = {n_: tt(q8["s_" + n_], False) for n_ in ("gate", "up", "down")}
     layers = [MoELayer(cfg.d, cfg.F, cfg.E, cfg.k, cfg.dtype, w, cfg.T, rms_eps=cfg.eps,
-                       fp8_scales=scales)
+                       fp8_scales=scales, fp8_act=act8)
               for _ in range(n)]
     del w, scales
     hidden = tt(inp["hidden"])
@@ -523,7 +532,7 @@ def roofline_entry(dom: dict, dom_ms: float, traffic) -> dict:
     if dom["work_unit"] == "bytes":
         achieved, peak = dom["work"] / (dom_ms * 1e-3) / 1e9, PEAK_HBM_GBPS
     else:
-        achieved, peak = dom["work"] / (dom_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS
+        achieved, peak = dom["work"] / (dom_ms * 1e-3) / 1e12, dom.get("peak", PEAK_BF16_TFLOPS)
     return {"bound": dom["bound"], "achieved": round(achieved, 2), "peak": peak,
             "unit": dom["unit"], "frac": round(achieved / peak, 4), "traffic": traffic,
             "kernel": dom["kernel"], "avg_launch_us": round(dom_ms * 1e3, 3),
@@ -605,6 +614,8 @@ def main():
                          "written) five times, to scale the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--fp8", action="store_true",
                     help="expert weights as E4M3 codes with per-row scales")
+    ap.add_argument("--w8a8", action="store_true",
+                    help="E4M3 weights and E4M3 activations (fp8 MFMA GEMMs)")
     ap.add_argument("--stack", action="store_true",
                     help="time the FFN half of the full 28-layer backbone at decode instead")
     ap.add_argument("--eda", type=float, default=None, metavar="ALPHA",
@@ -635,8 +646,10 @@ def main():
     load_library()  # fails loudly if the HIP library is not built
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
+    if args.w8a8:
+        args.fp8 = True
     if args.fp8 and args.config == 0:
-        raise SystemExit("--fp8 needs a bf16 workload (--config 1..4)")
+        raise SystemExit("--fp8 and --w8a8 need a bf16 workload (--config 1..4)")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
@@ -656,15 +669,15 @@ def main():
     t_gen = time.perf_counter()
     inp = make_inputs(args.config)
     cfg = inp["cfg"]
-    wname = cfg.name + ("_fp8w" if args.fp8 else "")
-    layers, hidden, q8 = make_layers(inp, args.instances, args.fp8, dev)
+    wname = cfg.name + ("_w8a8" if args.w8a8 else "_fp8w" if args.fp8 else "")
+    layers, hidden, q8 = make_layers(inp, args.instances, args.fp8, dev, args.w8a8)
     outs = [torch.empty_like(hidden) for _ in layers]
     log(f"[bench] inputs and {len(layers)} layers for {wname} in {time.perf_counter() - t_gen:.1f} s")
 
     _, r = layers[0].forward(hidden, routing=True)
     counts = r["counts"].cpu().numpy()
     sel_gpu = r["sel"].cpu().numpy()
-    dom = dominant_kernel(cfg, counts, args.fp8)
+    dom = dominant_kernel(cfg, counts, args.fp8, args.w8a8)
     lbytes, lflops, touched = layer_work(cfg, counts, args.fp8)
     log(f"[bench] {touched} experts touched; dominant kernel {dom['kernel']}")
 
@@ -693,18 +706,21 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": K, "warmup": W, "ms_per_step": round(ms_step, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32" if cfg.dtype == "f32" else "bf16",
+        "dtype": "f32" if cfg.dtype == "f32" else "fp8e4m3" if args.w8a8 else "bf16",
         "data": "synthetic: seeded N(0,1) hidden states and random-init weights of the stated "
                 "distributions (no checkpoint or dataset)",
         "config": {"workload": wname, "T": cfg.T, "d_model": cfg.d, "d_ff": cfg.F,
                    "n_experts": cfg.E, "top_k": cfg.k, "router_bias": cfg.bias,
                    "expert_weights": "fp8_e4m3_row_scaled" if args.fp8 else cfg.dtype,
+                   "expert_activations": "fp8_e4m3_row_scaled" if args.w8a8 else cfg.dtype,
                    "experts_touched": touched, "layer_instances": nl,
                    "device": props.name, "compute_units": props.multi_processor_count},
         "roofline": roofline_entry(dom, slots[dom["slot"]], counter_traffic(wname, dom["kernel"])),
         "layer": {"algorithmic_bytes": lbytes, "algorithmic_flops": lflops,
                   "hbm_GBps": round(lbytes / (ms_step * 1e-3) / 1e9, 1),
-                  "mfma_frac": round(lflops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                  "mfma_frac": round(lflops / (ms_step * 1e-3) / 1e12 /
+                                     (PEAK_FP8_TFLOPS if args.w8a8 else PEAK_BF16_TFLOPS), 4),
+                  "mfma_peak_TFLOPs": PEAK_FP8_TFLOPS if args.w8a8 else PEAK_BF16_TFLOPS,
                   "us_per_step_with_kernel_events": round(ms_step_ev * 1e3, 3),
                   "per_forward_us": pf,
                   "graph": {"us_per_step": round(gr["ms_per_step"] * 1e3, 3),
@@ -724,7 +740,7 @@ def main():
         log(f"[bench] context: {line['context']}")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
-        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, q8)
+        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, q8, args.w8a8)
         line["cpu_baseline"]["routing_check"] = [routing_check(i, s_) for i, s_ in checked]
         log(f"[bench] routing against the oracle: {line['cpu_baseline']['routing_check']}")
     print(json.dumps(line), flush=True)

@@ -165,10 +165,10 @@ moe_status_t moe_layer_create_w8a8(const moe_layer_config_t* cfg, const moe_laye
  * (for callers that quantise activations themselves, and to check the step).
  * x: DEVICE bf16 [R, K] (16-byte aligned, K a multiple of 8); codes: DEVICE
  * uint8 [R, K] (8-byte aligned) receives OCP E4M3 codes; scales: DEVICE fp32
- * [R] (4-byte aligned).  Row r: a = max_i |x[r,i]| / 448 in fp32 (correctly
- * rounded), code(x) = the E4M3 value nearest to fl32(x / a) (correctly rounded
- * division; ties to the even code; |x / a| is at most 448 up to rounding and
- * is clamped to +-448); a row of zeros gives a = 0 and codes 0.  Then
+ * [R] (4-byte aligned).  Row r: a = max_i |x[r,i]| / 448 and its reciprocal
+ * q = 1 / a in fp32 (correctly rounded divisions), code(x) = the E4M3 value
+ * nearest to fl32(x * q) (ties to the even code; |x * q| is at most 448 up to
+ * rounding and is clamped to +-448); a row of zeros gives a = 0 and codes 0.  Then
  * x[r,i] ~= a * value(code).  Enqueued on `stream`; R == 0 does nothing.
  * NaN or Inf inputs give undefined codes.  Errors: INVALID_ARG (NULL or
  * misaligned pointers, R < 0, K not a positive multiple of 8), HIP. */
@@ -241,13 +241,13 @@ moe_status_t moe_layer_update_bias(moe_layer_t* layer, const int32_t* counts, fl
  * with T*top_k <= 64, whose expert kernels dispatch), 2 first expert kernel
  * (gate/up), 3 second expert kernel (down), 4 combine (0 when top_k = 1, where
  * the combine is part of slot 3), 5 gather of the routed rows into expert
- * order (bf16 layers with T*top_k > 64 and fp8-activation layers; it runs
- * between slots 1 and 2), 6 quantisation of the gathered rows and 7 of the
- * SwiGLU intermediate (fp8-activation layers only; before slot 2 and before
- * slot 3).
+ * order (bf16 layers with T*top_k > 64 and fp8-activation layers, whose
+ * gather also quantises the rows; it runs between slots 1 and 2), 6
+ * quantisation of the SwiGLU intermediate (fp8-activation layers only; between
+ * slots 2 and 3).
  * Errors: INVALID_ARG (bad handle, max_forwards outside [1, 65536], stop
  * without start), HIP. */
-#define MOE_TIMED_SLOTS 8
+#define MOE_TIMED_SLOTS 7
 moe_status_t moe_layer_timing_start(moe_layer_t* layer, int32_t max_forwards);
 moe_status_t moe_layer_timing_stop(moe_layer_t* layer, float* ms_sum, int32_t* n_forwards);
 

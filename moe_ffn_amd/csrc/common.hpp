@@ -150,20 +150,22 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 }
 
 // Per-row E4M3 quantisation with a dynamic scale (fp8 activations): with a
-// = max|row| / 448 in fp32, the code of v is the E4M3 nearest to v / a (fp32
-// division, correctly rounded; v_cvt_pk_fp8_f32 rounds to nearest even),
-// clamped to +-448 first (|v / a| exceeds 448 by at most one rounding, which
-// the clamp takes back to the value round-to-nearest gives); a = 0 (a zero
-// row) gives code 0.
-__device__ __forceinline__ float e4m3_quotient(float v, float a) {
-  return a > 0.f ? fminf(fmaxf(v / a, -448.f), 448.f) : 0.f;
+// = max|row| / 448 and r = 1 / a (fp32, correctly rounded divisions, once per
+// row: e4m3_recip), the code of v is the E4M3 nearest to fl32(v * r)
+// (v_cvt_pk_fp8_f32 rounds to nearest even), clamped to +-448 first (|v * r|
+// exceeds 448 by at most a few roundings, which the clamp takes back to the
+// value round-to-nearest gives); a = 0 (a zero row) gives code 0.
+__device__ __forceinline__ float e4m3_recip(float a) { return a > 0.f ? 1.f / a : 0.f; }
+__device__ __forceinline__ float e4m3_quotient(float v, float r) {
+  return r > 0.f ? fminf(fmaxf(v * r, -448.f), 448.f) : 0.f;
 }
-// four bf16 values (two bf16x2 words) -> four codes, in order, in one word
-__device__ __forceinline__ uint32_t quant4_e4m3(uint32_t w0, uint32_t w1, float a) {
-  uint32_t r = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_quotient(bf16_lo(w0), a),
-                                               e4m3_quotient(bf16_hi(w0), a), 0, false);
-  return __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_quotient(bf16_lo(w1), a),
-                                         e4m3_quotient(bf16_hi(w1), a), (int)r, true);
+// four bf16 values (two bf16x2 words) -> four codes, in order, in one word;
+// r = e4m3_recip(a)
+__device__ __forceinline__ uint32_t quant4_e4m3(uint32_t w0, uint32_t w1, float r) {
+  uint32_t c = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_quotient(bf16_lo(w0), r),
+                                               e4m3_quotient(bf16_hi(w0), r), 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_quotient(bf16_lo(w1), r),
+                                         e4m3_quotient(bf16_hi(w1), r), (int)c, true);
 }
 __device__ __forceinline__ float absmax8_bf16(const u32x4& v, float m) {
 #pragma unroll

@@ -378,8 +378,8 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
                                          const int* __restrict__ gather,
                                          const float* __restrict__ gate,
                                          const float* __restrict__ rsc,
-                                         const float* __restrict__ asc, int k,
-                                         const uint16_t* __restrict__ zrow,
+                                         const float* __restrict__ asc, float* __restrict__ pmax,
+                                         int k, const uint16_t* __restrict__ zrow,
                                          uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
                                          int d, int F) {
   using G = Geo<RT>;
@@ -424,6 +424,7 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
       // k-step gt (16 columns of d_ff per gate/up tile); each wave store of a
       // (tile, subtile) pair fills one whole 1 KiB block
       uint16_t* blk = dst16 + (size_t)(u.sub0 + j) * (F / kKStep) * kBlockElems;
+      float amax = 0.f;  // F8: the token's largest |activation| over this wave's columns
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const int gt = tile0 + rt;  // 16 gate rows + 16 up rows: columns 16*gt ..
@@ -438,9 +439,11 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
             const f32x4 su = *reinterpret_cast<const f32x4*>(rs + 16);
             const float xs = asc[(size_t)(u.sub0 + j) * kSub + col];
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < 4; ++t) {
               v4[t] = silu((sg[t] * xs) * acc[rt][j][4 * g + t]) *
                       ((su[t] * xs) * acc[rt][j][4 * g + 8 + t]);
+              amax = fmaxf(amax, fabsf(v4[t]));
+            }
           } else if constexpr (SC) {
             const float* rs = rsc + (size_t)u.e * 2 * F + 32 * gt + 8 * g + 4 * hi;
             const f32x4 sg = *reinterpret_cast<const f32x4*>(rs);
@@ -459,6 +462,14 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
           // operand lane g*32 + col holds columns 8g .. 8g+7 of the k-step
           stg8_stream(blk + ((size_t)gt * 64 + g * 32 + col) * 8 + 4 * hi, v);
         }
+      }
+      if constexpr (F8) {
+        // the two lanes of a token hold different rows; bf16 rounding is
+        // monotone, so the bf16 value of the max is the max of the bf16 values
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        if (hi == 0)
+          pmax[((size_t)(u.sub0 + j) * (F / (16 * RT)) + tile0 / RT) * kSub + col] =
+              bf16_lo(f32_to_bf16(amax));
       }
     } else {
       // Output rows leave through LDS as whole row pieces: the wave's 64
@@ -544,19 +555,19 @@ __device__ __forceinline__ void run_any(const Unit& u, u32x4* lds, const uint16_
                                         const int* __restrict__ gather,
                                         const float* __restrict__ gate,
                                         const float* __restrict__ rsc,
-                                        const float* __restrict__ asc, int k,
-                                        const uint16_t* __restrict__ zrow,
+                                        const float* __restrict__ asc, float* __restrict__ pmax,
+                                        int k, const uint16_t* __restrict__ zrow,
                                         uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
                                         int d, int F) {
   if constexpr (TT > 1) {
     if (u.nsub != TT) {
-      run_any<MODE, RT, Q, TT - 1, SC, F8>(u, lds, wpk, src, gather, gate, rsc, asc, k, zrow,
-                                           dst16, ybuf, d, F);
+      run_any<MODE, RT, Q, TT - 1, SC, F8>(u, lds, wpk, src, gather, gate, rsc, asc, pmax, k,
+                                           zrow, dst16, ybuf, d, F);
       return;
     }
   }
-  run_unit<MODE, RT, Q, TT, SC, F8>(u, lds, wpk, src, gather, gate, rsc, asc, k, zrow, dst16, ybuf,
-                                    d, F);
+  run_unit<MODE, RT, Q, TT, SC, F8>(u, lds, wpk, src, gather, gate, rsc, asc, pmax, k, zrow, dst16,
+                                    ybuf, d, F);
 }
 }  // namespace
 
@@ -566,7 +577,8 @@ __global__ __launch_bounds__(256, OCC) void k_expert_gemm(
     const uint16_t* __restrict__ wpk, const uint16_t* __restrict__ src,
     const int* __restrict__ counts, const int* __restrict__ offsets,
     const int* __restrict__ gather, const float* __restrict__ gate,
-    const float* __restrict__ rsc, const float* __restrict__ asc, int k, int E, int cap,
+    const float* __restrict__ rsc, const float* __restrict__ asc, float* __restrict__ pmax, int k,
+    int E, int cap,
     const uint16_t* __restrict__ zrow, uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
     int d, int F) {
   static_assert(TTM >= 1 && TTM <= 8, "token subtiles per unit");
@@ -585,8 +597,8 @@ __global__ __launch_bounds__(256, OCC) void k_expert_gemm(
     Unit u;
     decode_unit(tab, nrb, L, u);
     __syncthreads();  // the previous unit's last LDS reads are done everywhere
-    run_any<MODE, RT, Q, TTM, SC, F8>(u, lds, wpk, src, gather, gate, rsc, asc, k, zrow, dst16, ybuf,
-                                      d, F);
+    run_any<MODE, RT, Q, TTM, SC, F8>(u, lds, wpk, src, gather, gate, rsc, asc, pmax, k, zrow, dst16,
+                                      ybuf, d, F);
   }
 }
 
@@ -659,7 +671,7 @@ hipError_t launch_gemm(const FwdArgs& a) {
                 a.ev[MODE == 0 ? kSlotExpertsA : kSlotExpertsB],
                 (const uint16_t*)wsrc, (const uint16_t*)tsrc, (const int*)a.counts,
                 (const int*)a.offsets, (const int*)a.gather, (const float*)a.gate,
-                rsc, asc, a.dim.k, a.dim.E, cap,
+                rsc, asc, F8 && MODE == 0 ? a.pmm : nullptr, a.dim.k, a.dim.E, cap,
                 (const uint16_t*)a.zrow,
                 (uint16_t*)(MODE == 0 ? a.act : a.out), a.ybuf, a.dim.d, a.dim.F);
 }
@@ -686,8 +698,8 @@ hipError_t launch_experts_tile(const FwdArgs& a) {
 // Blocks of 32 k: d_model % 256 == 0 and d_ff % 256 == 0 fill whole loop
 // bodies of two stages (8 blocks) with an 8-block weight queue.
 hipError_t launch_experts_tile_fp8_gateup(const FwdArgs& a) {
-  return (2 * a.dim.F) % Geo<3>::kRows == 0 ? launch_gemm<0, 3, 8, 1, 5, true>(a)
-                                            : launch_gemm<0, 2, 8, 1, 5, true>(a);
+  return fp8_gateup_rt(a.dim.F) == 3 ? launch_gemm<0, 3, 8, 1, 5, true>(a)
+                                     : launch_gemm<0, 2, 8, 1, 5, true>(a);
 }
 hipError_t launch_experts_tile_fp8_down(const FwdArgs& a) {
   return launch_gemm<1, 2, 8, 1, 6, true>(a);

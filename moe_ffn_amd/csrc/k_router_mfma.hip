@@ -14,7 +14,10 @@
 // therefore two bf16 MFMAs with fp32 accumulation: fp32-router precision at
 // matrix-core speed.  z = inv_rms * z_raw with inv_rms = 1/sqrt(mean(h^2)+eps).
 //
-// Outputs: inv_rms[T], sel[T,k], gate[T,k].  In a stack that depth-averages
+// Outputs: inv_rms[T], sel[T,k], gate[T,k]; with fp8 activations also each
+// token's quantisation scale xs[T] = max_i |bf16(inv_rms * x'_i)| / 448, which
+// is bf16(inv_rms * max_i |x'_i|) / 448 because both roundings are monotone,
+// so the gather can write E4M3 rows in one pass.  In a stack that depth-averages
 // the router state (the digest's item 5 names exponential depth averaging
 // after ZAYA1 without defining it; read as z~ = alpha * z~_prev + (1 - alpha)
 // * z on the logits), eda holds each token's averaged logits of the previous
@@ -54,13 +57,15 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
     const uint16_t* __restrict__ hidden, int T, int d, const uint16_t* __restrict__ wr,
     const uint16_t* __restrict__ gain, const float* __restrict__ bias, int E, int k, float eps,
     const uint16_t* __restrict__ zrow, float* __restrict__ inv_out, int* __restrict__ sel,
-    float* __restrict__ gate, float* __restrict__ eda, float eda_alpha, int eda_first) {
+    float* __restrict__ gate, float* __restrict__ eda, float eda_alpha, int eda_first,
+    float* __restrict__ xs_out) {
   constexpr int NTOK = 16 * TT;
   constexpr int EPAD = 16 * NA;
   static_assert(EPAD != 16 || NTOK != 16 || NW * 64 >= 16 * NTOK,
                 "the 16-expert finish takes 16 lanes per token");
   __shared__ float red[NW][TT][NA][4][64];
   __shared__ float ssr[NW][TT][64];
+  __shared__ float mxr[NW][TT][64];
   __shared__ float zs[NTOK][EPAD + 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -84,10 +89,11 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
   const uint16_t* gp = gain + kgrp + k0;
 
   f32x4 acc[TT][NA];
-  float ss[TT];
+  float ss[TT], mx[TT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) {
     ss[tt] = 0.f;
+    mx[tt] = 0.f;
 #pragma unroll
     for (int a = 0; a < NA; ++a) acc[tt][a] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -106,6 +112,7 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
         const float x0 = g[2 * i] * h[2 * i], x1 = g[2 * i + 1] * h[2 * i + 1];
         ss[tt] = fmaf(h[2 * i], h[2 * i], ss[tt]);
         ss[tt] = fmaf(h[2 * i + 1], h[2 * i + 1], ss[tt]);
+        mx[tt] = fmaxf(mx[tt], fmaxf(fabsf(x0), fabsf(x1)));
         const uint32_t hi = pack_bf16x2(x0, x1);
         bhi[i] = hi;
         blo[i] = pack_bf16x2(x0 - bf16_lo(hi), x1 - bf16_hi(hi));
@@ -147,6 +154,7 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) {
     ssr[wave][tt][lane] = ss[tt];
+    mxr[wave][tt][lane] = mx[tt];
 #pragma unroll
     for (int a = 0; a < NA; ++a)
 #pragma unroll
@@ -218,6 +226,14 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
           gate[(size_t)t * k + chosen] = ex / den;
         }
         if (e == 0) inv_out[t] = inv;
+        if (e == 1 && xs_out != nullptr) {
+          float m = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w)
+            m = fmaxf(m, fmaxf(fmaxf(mxr[w][0][tl], mxr[w][0][tl + 16]),
+                               fmaxf(mxr[w][0][tl + 32], mxr[w][0][tl + 48])));
+          xs_out[t] = bf16_lo(f32_to_bf16(inv * m)) / 448.f;
+        }
       }
     }
   } else if (tid < NTOK) {
@@ -273,6 +289,14 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
         gate[(size_t)t * k + j] = expf(zc[j] - zmax) / den;
       }
       inv_out[t] = inv;
+      if (xs_out != nullptr) {
+        float m = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+          m = fmaxf(m, fmaxf(fmaxf(mxr[w][tt][c], mxr[w][tt][c + 16]),
+                             fmaxf(mxr[w][tt][c + 32], mxr[w][tt][c + 48])));
+        xs_out[t] = bf16_lo(f32_to_bf16(inv * m)) / 448.f;
+      }
     }
   }
 }
@@ -290,7 +314,7 @@ hipError_t go(const FwdArgs& a) {
                 a.ev[kSlotNormRouter], (const uint16_t*)a.hidden, a.T, a.dim.d,
                 (const uint16_t*)a.wr16, (const uint16_t*)a.gain16, (const float*)a.bias, a.dim.E,
                 a.dim.k, a.dim.eps, (const uint16_t*)a.zrow, a.inv, a.sel, a.gate, a.eda,
-                a.eda_alpha, a.eda_first);
+                a.eda_alpha, a.eda_first, a.dim.act8 ? a.xs_tok : nullptr);
 }
 }  // namespace
 

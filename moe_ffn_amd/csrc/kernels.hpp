@@ -8,12 +8,10 @@
 namespace moe {
 
 // Kernel slots of one forward (per-kernel timing).  Launch order: router,
-// permutation, gather (bf16 prefill only), [quantisation of the gathered rows],
-// gate/up, [quantisation of the activations], down, combine; the bracketed
-// ones run for fp8 activations only.
+// permutation, gather (bf16 prefill only), gate/up, [quantisation of the
+// activations: fp8 activations only], down, combine.
 enum Slot { kSlotNormRouter = 0, kSlotPermute = 1, kSlotExpertsA = 2, kSlotExpertsB = 3,
-            kSlotCombine = 4, kSlotGather = 5, kSlotQuantX = 6, kSlotQuantAct = 7,
-            kNumSlots = 8 };
+            kSlotCombine = 4, kSlotGather = 5, kSlotQuantAct = 6, kNumSlots = 7 };
 
 // Optional start/stop events carried by a kernel's own dispatch packet.
 struct KEv {
@@ -76,11 +74,16 @@ struct FwdArgs {
   const float* sgu;
   const float* sd;
   // fp8 activations (dim.act8): E4M3 token and activation tiles in the fp8
-  // banks' block order, and their per-row scales (one per padded slot)
+  // banks' block order, and their per-row scales (one per padded slot); the
+  // router's per-token scales of the gathered rows; the activations' per-row
+  // partial maxima that the fp8 gate/up epilogue leaves for the quantiser,
+  // [subtile][group][32 rows], groups of 16 * fp8_gateup_rt(F) columns
   void* xq = nullptr;
   void* actq = nullptr;
   float* sx = nullptr;
   float* sm = nullptr;
+  float* xs_tok = nullptr;
+  float* pmm = nullptr;
   // per-call buffers (workspace or caller-provided routing outputs)
   void* xn;            // [T, d] gain-scaled activations g * h (bf16 or f32)
   float* inv;          // [T] 1 / rms of each token's hidden state
@@ -117,11 +120,12 @@ hipError_t launch_gather_tiles(const FwdArgs& a);
 int max_subtiles(int n, int E);
 hipError_t launch_experts_stream(const FwdArgs& a);
 hipError_t launch_experts_tile(const FwdArgs& a);
+// weight tiles per wave of the fp8 gate/up GEMM (its activation column group is 16 * this)
+inline int fp8_gateup_rt(int F) { return (2 * F) % 384 == 0 ? 3 : 2; }
 hipError_t launch_experts_tile_fp8_gateup(const FwdArgs& a);  // dim.act8 layers
 hipError_t launch_experts_tile_fp8_down(const FwdArgs& a);
-// per-row E4M3 quantisation of bf16 operand tiles: which = 0 the gathered rows
-// (xt -> xq, sx), 1 the activations (act -> actq, sm)
-hipError_t launch_quant_tiles(const FwdArgs& a, int which);
+// per-row E4M3 quantisation of the bf16 activation tiles (act -> actq, sm)
+hipError_t launch_quant_act(const FwdArgs& a);
 // the same on row-major bf16 rows [R][K] (K % 8 == 0)
 hipError_t launch_quant_rows(const void* x, int R, int K, void* codes, float* scale,
                              hipStream_t s);

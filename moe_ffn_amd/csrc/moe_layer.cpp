@@ -78,6 +78,8 @@ struct Work {
   void* actq;
   float* sx;
   float* sm;
+  float* xs_tok;  // per-token quantisation scales of the gathered rows (router)
+  float* pmm;     // partial row maxima of the activations (fp8 gate/up epilogue)
   float* ybuf;
   void* zrow;  // max(d, F) zero elements: must hold zeros before a forward runs
   void* sink;
@@ -105,13 +107,15 @@ size_t carve_work(const moe::LayerDims& dim, size_t tokens, char* base, Work* w)
   const size_t o_hist = wc.take((size_t)moe::kPermuteMaxGroups * 64 * 4);
   // bf16: slot-ordered activations (decode) or padded operand tiles (prefill)
   const size_t npad = bf16 ? (size_t)moe::max_subtiles((int)nmax, (int)E) * 32 : 0;
-  const size_t o_xt = bf16 ? wc.take(npad * d * 2) : 0;
+  const bool a8 = dim.act8 != 0;  // fp8 activations: E4M3 token tiles instead of bf16 ones
+  const size_t o_xt = bf16 && !a8 ? wc.take(npad * d * 2) : 0;
   const size_t o_act = wc.take((nmax > npad ? nmax : npad) * F * es);
-  const bool a8 = dim.act8 != 0;
   const size_t o_xq = a8 ? wc.take(npad * d) : 0;
   const size_t o_actq = a8 ? wc.take(npad * F) : 0;
   const size_t o_sx = a8 ? wc.take(npad * 4) : 0;
   const size_t o_sm = a8 ? wc.take(npad * 4) : 0;
+  const size_t o_xst = a8 ? wc.take(tokens * 4) : 0;
+  const size_t o_pmm = a8 ? wc.take(npad * (F / 32) * 4) : 0;  // groups of 32 or 48 columns
   const size_t o_y = k > 1 ? wc.take(nmax * d * 4) : 0;
   const size_t zbytes = (d > F ? d : F) * 4;
   const size_t o_z = wc.take(zbytes);
@@ -127,12 +131,14 @@ size_t carve_work(const moe::LayerDims& dim, size_t tokens, char* base, Work* w)
     w->scatter = reinterpret_cast<int*>(base + o_sca);
     w->slot_expert = reinterpret_cast<int*>(base + o_sle);
     w->hist = reinterpret_cast<int*>(base + o_hist);
-    w->xt = bf16 ? base + o_xt : nullptr;
+    w->xt = bf16 && !a8 ? base + o_xt : nullptr;
     w->act = base + o_act;
     w->xq = a8 ? base + o_xq : nullptr;
     w->actq = a8 ? base + o_actq : nullptr;
     w->sx = a8 ? reinterpret_cast<float*>(base + o_sx) : nullptr;
     w->sm = a8 ? reinterpret_cast<float*>(base + o_sm) : nullptr;
+    w->xs_tok = a8 ? reinterpret_cast<float*>(base + o_xst) : nullptr;
+    w->pmm = a8 ? reinterpret_cast<float*>(base + o_pmm) : nullptr;
     w->ybuf = k > 1 ? reinterpret_cast<float*>(base + o_y) : nullptr;
     w->zrow = base + o_z;
     w->sink = base + o_sink;
@@ -551,6 +557,8 @@ moe_status_t forward_impl(moe_layer_t* L, const void* hidden, int32_t T, void* o
   a.actq = w.actq;
   a.sx = w.sx;
   a.sm = w.sm;
+  a.xs_tok = w.xs_tok;
+  a.pmm = w.pmm;
   a.ybuf = w.ybuf;
   a.zrow = w.zrow;
   a.sink = w.sink;
@@ -572,7 +580,7 @@ moe_status_t forward_impl(moe_layer_t* L, const void* hidden, int32_t T, void* o
   const bool decode = bf16 && !act8 && a.n <= moe::kStreamMaxAssign;
   if (L->timing && L->t_used > 0 && a.ev[0].start != nullptr)
     L->tslots[L->t_used - 1] = (uint8_t)(0x0d | (decode ? 0 : 0x02) | (L->dim.k > 1 ? 0x10 : 0) |
-                                         (bf16 && !decode ? 0x20 : 0) | (act8 ? 0xc0 : 0));
+                                         (bf16 && !decode ? 0x20 : 0) | (act8 ? 0x40 : 0));
 
   if (wk != nullptr && wk->clear_zrow) {
     he = moe::launch_zero(wk->zrow, wk->zbytes, a.stream);
@@ -592,9 +600,8 @@ moe_status_t forward_impl(moe_layer_t* L, const void* hidden, int32_t T, void* o
       if (he != hipSuccess) return hip_fail(he, "gather launch");
     }
     if (act8) {
-      he = moe::launch_quant_tiles(a, 0);
-      if (he == hipSuccess) he = moe::launch_experts_tile_fp8_gateup(a);
-      if (he == hipSuccess) he = moe::launch_quant_tiles(a, 1);
+      he = moe::launch_experts_tile_fp8_gateup(a);
+      if (he == hipSuccess) he = moe::launch_quant_act(a);
       if (he == hipSuccess) he = moe::launch_experts_tile_fp8_down(a);
     } else {
       he = bf16 ? moe::launch_experts_tile(a) : moe::launch_experts_f32(a);

@@ -30,7 +30,7 @@ EXPORTS = ("moe_abi_version", "moe_last_error", "moe_layer_create", "moe_layer_c
            "moe_stack_capture", "moe_stack_replay", "moe_stack_destroy", "moe_stack_set_eda",
            "moe_stack_forward_routing", "moe_layer_forward_static")
 TIMED_SLOTS = ("norm_router", "route_permute", "experts_gate_up", "experts_down", "combine",
-               "gather", "quant_x", "quant_act")
+               "gather", "quant_act")
 
 
 class LayerConfig(ctypes.Structure):
