@@ -68,10 +68,10 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def dominant_kernel_name(cfg) -> str:
+def dominant_kernel_name(cfg, act8: bool = False) -> str:
     if cfg.dtype == "f32":
         return "k_gateup_f32"
-    return "k_gateup_stream" if cfg.T * cfg.k <= 64 else "k_expert_gemm<0>"
+    return "k_gateup_stream" if cfg.T * cfg.k <= 64 and not act8 else "k_expert_gemm<0>"
 
 
 def kernel_short_name(name: str) -> str:
@@ -117,7 +117,8 @@ def ingest_counters(pmc_dir: str) -> None:
     Expects pmc_dir/copy_fetch and pmc_dir/copy_write (bench.py
     --copy-calibration 1024 under --pmc FETCH_SIZE, resp. WRITE_SIZE) and
     pmc_dir/c<N>_fetch, pmc_dir/c<N>_write for each --config N profiled
-    (c<N>fp8_fetch, c<N>fp8_write for --config N --fp8).  Each
+    (c<N>fp8_fetch, c<N>fp8_write for --config N --fp8; c<N>w8a8_* for
+    --w8a8).  Each
     counter is scaled by the bytes the copy kernel really moves over what the
     same counter reads for it."""
     from synth.configs import WORKLOADS
@@ -128,12 +129,12 @@ def ingest_counters(pmc_dir: str) -> None:
     out = {"_calibration": {"copy_bytes_each_way": copy_bytes, "fetch_counter_bytes": cf,
                             "write_counter_bytes": cw, "fetch_factor": round(ffac, 5),
                             "write_factor": round(wfac, 5)}}
-    for cid, tag in [(c, t) for c in (0, 1, 2, 3, 4) for t in ("", "fp8")]:
+    for cid, tag in [(c, t) for c in (0, 1, 2, 3, 4) for t in ("", "fp8", "w8a8")]:
         fd, wd = (os.path.join(pmc_dir, f"c{cid}{tag}_{x}") for x in ("fetch", "write"))
         if not (os.path.isdir(fd) and os.path.isdir(wd)):
             continue
         cfg = WORKLOADS[cid]
-        wname = cfg.name + ("_fp8w" if tag else "")
+        wname = cfg.name + {"": "", "fp8": "_fp8w", "w8a8": "_w8a8"}[tag]
         fm, wm = _counter_means(fd), _counter_means(wd)
         kernels = {}
         for kname in fm:
@@ -141,7 +142,7 @@ def ingest_counters(pmc_dir: str) -> None:
                     not kname.startswith(("k_pack", "k_prep", "k_mfma_rate")):
                 kernels[kname] = {"fetch_bytes": round(fm[kname] * 1024 * ffac),
                                   "write_bytes": round(wm[kname] * 1024 * wfac)}
-        dom = dominant_kernel_name(cfg)
+        dom = dominant_kernel_name(cfg, act8=tag == "w8a8")
         dk = next(k for k in kernels if _matches(k, dom))
         out[wname] = {"kernel": dom, "source_hash": kernel_source_hash(dom),
                       "bytes_per_launch": kernels[dk]["fetch_bytes"] + kernels[dk]["write_bytes"],

@@ -142,3 +142,17 @@ def test_w8a8_static_and_repeat_are_byte_identical():
     c = layer.forward(h, static_scratch=True)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(a, c)
+
+
+@pytest.mark.parametrize("E,k,T", [(4, 1, 100), (40, 3, 1000), (16, 2, 333)])
+def test_w8a8_small_shapes(E, k, T):
+    # d_ff = 256: 2 * d_ff is not a multiple of 384, so the gate/up GEMM takes
+    # its two-tile (RT = 2) fp8 form; many experts and top-3 as well
+    from synth.configs import LayerConfig
+    cfg = LayerConfig(94, f"w8a8_small_E{E}_k{k}_T{T}", T=T, d=256, E=E, F=256, k=k,
+                      dtype="bf16", bias="normal", family=f"w8a8_small_d256_E{E}_F256")
+    inp = make_inputs(cfg)
+    print(f"[case] {cfg.name}", flush=True)
+    st = check_parity(inp, w8a8_layer(inp, T), vals=fp8_vals(inp), fp8_act=True, label=cfg.name)
+    assert st["rows_compared"] == T
+    assert st["rms_err_rel"] < 5e-3
