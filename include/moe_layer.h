@@ -151,11 +151,14 @@ moe_status_t moe_layer_create_fp8(const moe_layer_config_t* cfg, const moe_layer
  * the row scales multiply the fp32 accumulators:
  *   G[r, f] = a_u[r] * s_gate[f] * sum_i code(u_r)_i * code(W_gate[f])_i   (V likewise)
  *   y[r, m] = a_m[r] * s_down[m] * sum_f code(m_r)_f * code(W_down[m])_f
- * Router, gates, dispatch and combine are those of the bf16 layer.  Every
- * batch size runs the tiled path (router, permutation, gather, the two
- * quantisations and the two fp8 GEMMs).  The layer keeps only the fp8 banks:
- * 1 byte per expert weight plus the row scales.  Shape limits and errors as
- * moe_layer_create_fp8. */
+ * Router, gates, dispatch and combine are those of the bf16 layer.  Batches
+ * with T * top_k > 64 run the tiled path (router, permutation, the gather that
+ * quantises the rows, the fp8 gate/up GEMM, the quantisation of the
+ * intermediate, the fp8 down GEMM); decode-sized batches stream the fp8
+ * weights against the exact E4M3 values of the quantised rows (bf16 matrix
+ * operands; the same products), with the same scales.  The layer keeps only
+ * the fp8 banks: 1 byte per expert weight plus the row scales.  Shape limits
+ * and errors as moe_layer_create_fp8. */
 moe_status_t moe_layer_create_w8a8(const moe_layer_config_t* cfg, const moe_layer_weights_t* w,
                                    const moe_fp8_scales_t* scales, void* stream,
                                    moe_layer_t** out);

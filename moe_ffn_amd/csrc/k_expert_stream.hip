@@ -23,6 +23,13 @@
 // workload, gate/up 48.0 -> 43.8 us (two tiles, four waves before) and down
 // 28.0 -> 22.8 us (four waves before), 6.3 and 6.1 TB/s.
 //
+// fp8 weights and fp8 activations (decode batches of layers made by
+// moe_layer_create_w8a8): the router leaves the E4M3 values of the expert
+// inputs (exact in bf16) and their row scales, which the gate/up stream takes
+// in place of inv_rms; the activation rows are quantised in place between the
+// two streams, and the down stream also multiplies its sums by their scales
+// (asc), so both streams multiply exact E4M3 values.
+//
 // fp8 (E4M3) weights: a second bank holds the codes of two consecutive k-steps
 // per lane and 16-byte load (1 KiB per wave-wide load, as in bf16); they are
 // widened exactly to bf16 operands in registers and the per-row scales
@@ -265,8 +272,8 @@ __global__ __launch_bounds__(64 * SD, 1) void k_down_stream(
     const uint16_t* __restrict__ wd, const uint8_t* __restrict__ wd8,
     const float* __restrict__ sd, const uint16_t* __restrict__ act,
     const int* __restrict__ sel, int n, int k, int E, const float* __restrict__ gate,
-    const uint16_t* __restrict__ zrow, uint16_t* __restrict__ out, float* __restrict__ ybuf, int d,
-    int F) {
+    const float* __restrict__ asc, const uint16_t* __restrict__ zrow, uint16_t* __restrict__ out,
+    float* __restrict__ ybuf, int d, int F) {
   __shared__ float red[SD * 16 * 64];
   __shared__ int list[64];
   __shared__ int sh[2];
@@ -307,7 +314,10 @@ __global__ __launch_bounds__(64 * SD, 1) void k_down_stream(
     for (int i = wave; i < 16; i += SD) {
       const int r = c32_row(i, lane);
       float y = split_sum<1, SD>(red, 0, i, lane);
-      if constexpr (FP8) y *= sd[(size_t)e * d + m0 + r];
+      if constexpr (FP8) {
+        y *= sd[(size_t)e * d + m0 + r];
+        if (asc != nullptr) y *= asc[slot];  // fp8 activations: the row's scale
+      }
       if (valid) {
         if (k == 1) out[(size_t)tok * d + m0 + r] = (uint16_t)f32_to_bf16(gw * y);
         else ybuf[(size_t)slot * d + m0 + r] = y;
@@ -339,16 +349,23 @@ hipError_t launch_streams(const FwdArgs& a) {
           : Da == 2 ? k_gateup_stream<2, FP8, NT, S> : k_gateup_stream<1, FP8, NT, S>;
   auto dn = Db == 8 ? k_down_stream<8, FP8, SD> : Db == 4 ? k_down_stream<4, FP8, SD>
           : Db == 2 ? k_down_stream<2, FP8, SD> : k_down_stream<1, FP8, SD>;
+  // fp8 activations: the router's row scales take inv_rms's place
+  const float* rs = a.dim.act8 ? a.xs_tok : a.inv;
   hipError_t err = launch(gu, dim3(F / (16 * NT), E), dim3(64 * S), a.stream,
                           a.ev[kSlotExpertsA], (const uint16_t*)a.wgu, (const uint8_t*)a.wgu8,
                           a.sgu, (const uint16_t*)a.xn, (const int*)a.sel, a.n, a.dim.k, E,
-                          a.counts, a.offsets, a.gather, a.scatter, (const float*)a.inv,
+                          a.counts, a.offsets, a.gather, a.scatter, rs,
                           (const uint16_t*)a.zrow, (uint16_t*)a.act, d, F);
   if (err != hipSuccess) return err;
+  if (a.dim.act8) {
+    err = launch_quant_act_rows(a);
+    if (err != hipSuccess) return err;
+  }
   return launch(dn, dim3(d / kTileRows, E), dim3(64 * SD), a.stream, a.ev[kSlotExpertsB],
                 (const uint16_t*)a.wd, (const uint8_t*)a.wd8, a.sd, (const uint16_t*)a.act,
                 (const int*)a.sel, a.n, a.dim.k, E, (const float*)a.gate,
-                (const uint16_t*)a.zrow, (uint16_t*)a.out, a.ybuf, d, F);
+                (const float*)(a.dim.act8 ? a.sm : nullptr), (const uint16_t*)a.zrow,
+                (uint16_t*)a.out, a.ybuf, d, F);
 }
 }  // namespace
 

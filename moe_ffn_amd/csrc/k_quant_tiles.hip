@@ -20,7 +20,10 @@
 // that the fp8 gate/up epilogue left, so the subtile is read once.
 //
 // k_quant_rows: the same quantisation on row-major bf16 rows [R][K] ->
-// codes [R][K] and scales [R], one wave per row (moe_fp8_quantize_rows).
+// codes [R][K] and scales [R], one wave per row (moe_fp8_quantize_rows); with
+// VALS the rows are overwritten by the codes' values (exact in bf16) instead:
+// the activation rows of decode batches, which the fp8 down stream multiplies
+// as they are before it scales its sums by the row's scale.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -97,7 +100,8 @@ __global__ __launch_bounds__(512) void k_quant_tiles(const uint16_t* __restrict_
   }
 }
 
-__global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ x, int R, int K,
+template <bool VALS>
+__global__ __launch_bounds__(256) void k_quant_rows(uint16_t* __restrict__ x, int R, int K,
                                                     uint8_t* __restrict__ codes,
                                                     float* __restrict__ scale) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -112,10 +116,20 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
   const float r = e4m3_recip(a);
   for (int c = lane * 8; c < K; c += 512) {
     const u32x4 v = ldg16(xr + c);
-    u32x2 o;
-    o[0] = quant4_e4m3(v[0], v[1], r);
-    o[1] = quant4_e4m3(v[2], v[3], r);
-    *reinterpret_cast<u32x2*>(codes + (size_t)row * K + c) = o;
+    const uint32_t c0 = quant4_e4m3(v[0], v[1], r), c1 = quant4_e4m3(v[2], v[3], r);
+    if constexpr (VALS) {  // each lane rewrites only the 16 bytes it read
+      u32x4 o;
+      o[0] = e4m3_pair_to_bf16x2<false>(c0);
+      o[1] = e4m3_pair_to_bf16x2<true>(c0);
+      o[2] = e4m3_pair_to_bf16x2<false>(c1);
+      o[3] = e4m3_pair_to_bf16x2<true>(c1);
+      stg16(x + (size_t)row * K + c, o);
+    } else {
+      u32x2 o;
+      o[0] = c0;
+      o[1] = c1;
+      *reinterpret_cast<u32x2*>(codes + (size_t)row * K + c) = o;
+    }
   }
 }
 
@@ -130,9 +144,14 @@ hipError_t launch_quant_act(const FwdArgs& a) {
 
 hipError_t launch_quant_rows(const void* x, int R, int K, void* codes, float* scale,
                              hipStream_t s) {
-  hipLaunchKernelGGL(k_quant_rows, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, s,
-                     (const uint16_t*)x, R, K, (uint8_t*)codes, scale);
+  hipLaunchKernelGGL(k_quant_rows<false>, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, s,
+                     (uint16_t*)const_cast<void*>(x), R, K, (uint8_t*)codes, scale);
   return hipGetLastError();
+}
+
+hipError_t launch_quant_act_rows(const FwdArgs& a) {
+  return launch(k_quant_rows<true>, dim3((unsigned)((a.n + 3) / 4)), dim3(256), a.stream,
+                a.ev[kSlotQuantAct], (uint16_t*)a.act, a.n, a.dim.F, (uint8_t*)nullptr, a.sm);
 }
 
 }  // namespace moe

@@ -17,6 +17,13 @@
 // + (1 - alpha) * z; the first MoE layer only writes the state), add the
 // bias, pick the top-k by wave-wide maximum reductions and write the gates.
 // The dispatch of decode batches happens in the expert kernels.
+//
+// Layers with fp8 activations (xs != null) get the quantised expert input
+// instead of x': the row's scale a = max_i |u_i| / 448 of u = bf16(inv_rms *
+// x') is bf16(inv_rms * max_i |x'_i|) / 448 (both roundings are monotone), so
+// the first pass also tracks max |x'|; a second pass over the row (in cache)
+// writes the E4M3 values of u (quant4_e4m3, exact in bf16) and xs[t] = a.  The
+// weight streams then multiply exact code values and scale the sums by a.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,11 +35,12 @@ __global__ __launch_bounds__(256) void k_router_token(
     const uint16_t* __restrict__ gain, const float* __restrict__ bias, int E, int k, float eps,
     const uint16_t* __restrict__ zrow, uint16_t* __restrict__ xg, float* __restrict__ inv_out,
     int* __restrict__ sel, float* __restrict__ gate, float* __restrict__ eda, float eda_alpha,
-    int eda_first) {
+    int eda_first, float* __restrict__ xs) {
   constexpr int NV = EP;
   constexpr int R = NV >= 64 ? NV / 64 : 1;
   __shared__ float red[4][NV];
-  __shared__ float ssr[4];
+  __shared__ float ssr[4], mxr[4];
+  __shared__ float s_inv, s_r;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.x;
@@ -45,7 +53,7 @@ __global__ __launch_bounds__(256) void k_router_token(
   float acc[NV];
 #pragma unroll
   for (int e = 0; e < NV; ++e) acc[e] = 0.f;
-  float ss = 0.f;
+  float ss = 0.f, mx = 0.f;
   constexpr int G = EP < 16 ? EP : 16;  // router rows loaded together
   for (int c = tid * 8; c < d; c += 256 * 8) {
     u32x4 wv[G];
@@ -59,10 +67,13 @@ __global__ __launch_bounds__(256) void k_router_token(
     for (int i = 0; i < 8; ++i) {
       ss = fmaf(h[i], h[i], ss);
       x[i] = g[i] * h[i];
+      mx = fmaxf(mx, fabsf(x[i]));
     }
+    if (xs == nullptr) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-    stg16(xrow + c, o);
+      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+      stg16(xrow + c, o);
+    }
 #pragma unroll
     for (int e0 = 0; e0 < EP; e0 += G) {
       if (e0 > 0) {
@@ -82,12 +93,18 @@ __global__ __launch_bounds__(256) void k_router_token(
   }
   WaveSpread<NV, 32>::run(acc, lane);
 #pragma unroll
-  for (int dlt = 32; dlt >= 1; dlt >>= 1) ss += __shfl_xor(ss, dlt, kWave);
+  for (int dlt = 32; dlt >= 1; dlt >>= 1) {
+    ss += __shfl_xor(ss, dlt, kWave);
+    mx = fmaxf(mx, __shfl_xor(mx, dlt, kWave));
+  }
   if (spread_owner<NV>(lane)) {
 #pragma unroll
     for (int i = 0; i < R; ++i) red[wave][spread_index<NV>(lane, i)] = acc[i];
   }
-  if (lane == 0) ssr[wave] = ss;
+  if (lane == 0) {
+    ssr[wave] = ss;
+    mxr[wave] = mx;
+  }
   __syncthreads();
 
   if (wave == 0) {
@@ -139,6 +156,33 @@ __global__ __launch_bounds__(256) void k_router_token(
       gate[(size_t)t * k + chosen] = ex / den;
     }
     if (lane == 0) inv_out[t] = inv;
+    if (xs != nullptr && lane == 0) {
+      const float m = fmaxf(fmaxf(mxr[0], mxr[1]), fmaxf(mxr[2], mxr[3]));
+      const float a = bf16_lo(f32_to_bf16(inv * m)) / 448.f;
+      xs[t] = a;
+      s_inv = inv;
+      s_r = e4m3_recip(a);
+    }
+  }
+  if (xs != nullptr) {  // second pass: the E4M3 values of u = bf16(inv * x')
+    __syncthreads();
+    const float inv = s_inv, r = s_r;
+    for (int c = tid * 8; c < d; c += 256 * 8) {
+      float h[8], g[8];
+      unpack8(ldg16(hrow + c), h);
+      unpack8(ldg16(gain + c), g);
+      uint32_t uw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        uw[i] = pack_bf16x2(inv * (g[2 * i] * h[2 * i]), inv * (g[2 * i + 1] * h[2 * i + 1]));
+      const uint32_t c0 = quant4_e4m3(uw[0], uw[1], r), c1 = quant4_e4m3(uw[2], uw[3], r);
+      u32x4 o;
+      o[0] = e4m3_pair_to_bf16x2<false>(c0);
+      o[1] = e4m3_pair_to_bf16x2<true>(c0);
+      o[2] = e4m3_pair_to_bf16x2<false>(c1);
+      o[3] = e4m3_pair_to_bf16x2<true>(c1);
+      stg16(xrow + c, o);
+    }
   }
 }
 
@@ -149,7 +193,7 @@ hipError_t go(const FwdArgs& a) {
                 (const uint16_t*)a.hidden, a.dim.d, (const uint16_t*)a.wr16,
                 (const uint16_t*)a.gain16, (const float*)a.bias, a.dim.E, a.dim.k, a.dim.eps,
                 (const uint16_t*)a.zrow, (uint16_t*)a.xn, a.inv, a.sel, a.gate, a.eda, a.eda_alpha,
-                a.eda_first);
+                a.eda_first, a.dim.act8 ? a.xs_tok : nullptr);
 }
 }  // namespace
 

@@ -126,6 +126,8 @@ hipError_t launch_experts_tile_fp8_gateup(const FwdArgs& a);  // dim.act8 layers
 hipError_t launch_experts_tile_fp8_down(const FwdArgs& a);
 // per-row E4M3 quantisation of the bf16 activation tiles (act -> actq, sm)
 hipError_t launch_quant_act(const FwdArgs& a);
+// the decode path's activation rows [n][F] in place: the E4M3 values as bf16, scales in sm
+hipError_t launch_quant_act_rows(const FwdArgs& a);
 // the same on row-major bf16 rows [R][K] (K % 8 == 0)
 hipError_t launch_quant_rows(const void* x, int R, int K, void* codes, float* scale,
                              hipStream_t s);

@@ -576,8 +576,8 @@ moe_status_t forward_impl(moe_layer_t* L, const void* hidden, int32_t T, void* o
     ++L->t_used;
   }
   const bool bf16 = L->dim.dtype == MOE_DTYPE_BF16;
-  const bool act8 = L->dim.act8 != 0;  // fp8 activations: the tile path at every T
-  const bool decode = bf16 && !act8 && a.n <= moe::kStreamMaxAssign;
+  const bool act8 = L->dim.act8 != 0;  // fp8 activations
+  const bool decode = bf16 && a.n <= moe::kStreamMaxAssign;
   if (L->timing && L->t_used > 0 && a.ev[0].start != nullptr)
     L->tslots[L->t_used - 1] = (uint8_t)(0x0d | (decode ? 0 : 0x02) | (L->dim.k > 1 ? 0x10 : 0) |
                                          (bf16 && !decode ? 0x20 : 0) | (act8 ? 0x40 : 0));
