@@ -71,7 +71,7 @@ def kernel_source_hash(kernel: str) -> str:
 def dominant_kernel_name(cfg, act8: bool = False) -> str:
     if cfg.dtype == "f32":
         return "k_gateup_f32"
-    return "k_gateup_stream" if cfg.T * cfg.k <= 64 and not act8 else "k_expert_gemm<0>"
+    return "k_gateup_stream" if cfg.T * cfg.k <= 64 else "k_expert_gemm<0>"
 
 
 def kernel_short_name(name: str) -> str:
@@ -159,8 +159,8 @@ def dominant_kernel(cfg, counts, fp8: bool = False, act8: bool = False):
     gate/up kernel moves 2/3 of the bytes; larger batches take the tiled
     grouped GEMM whose gate/up launch does 2/3 of the flops.  fp8 weights:
     one byte per weight plus one fp32 scale per row.  fp8 activations (act8):
-    the tiled path at every batch size, its gate/up GEMM priced by weight
-    bytes at decode sizes and against the fp8 MFMA peak above them."""
+    decode sizes stream the fp8 weights as above; larger batches run the fp8
+    MFMA GEMMs, priced against the fp8 peak."""
     d, F, k, T = cfg.d, cfg.F, cfg.k, cfg.T
     n = T * k
     touched = int((counts > 0).sum())
@@ -175,8 +175,7 @@ def dominant_kernel(cfg, counts, fp8: bool = False, act8: bool = False):
         # W_gate + W_up bytes of one expert
         per_expert = 2 * F * d + 2 * F * 4 if fp8 else 2 * F * d * 2
         work = touched * per_expert + n * d * 2 + n * F * 2
-        return {"slot": "experts_gate_up",
-                "kernel": "k_expert_gemm<0>" if act8 else "k_gateup_stream", "bound": "hbm",
+        return {"slot": "experts_gate_up", "kernel": "k_gateup_stream", "bound": "hbm",
                 "unit": "GB/s", "units": touched, "per_unit": per_expert,
                 "unit_name": "touched expert (W_gate + W_up bytes%s)" % (
                     ": E4M3 codes + row scales" if fp8 else ""), "work": work,
@@ -556,42 +555,47 @@ def counter_traffic(wname: str, kernel: str):
     return None
 
 
-def prefill_summary(cid: int, args, dev) -> tuple[dict, dict, object]:
+def prefill_summary(cid: int, args, dev, w8a8: bool = False) -> tuple[dict, dict, object]:
     """Step time, whole-layer MFMA fraction and the gate/up GEMM's time and
-    fraction of one prefill workload (a sub-object of the default line).
+    fraction of one prefill workload (a sub-object of the default line);
+    w8a8: the layer with fp8 weights and activations, its fractions against
+    the fp8 peak (at decode sizes: its weight stream against HBM).
     Returns (summary, inputs, GPU routing choice)."""
     import torch
     from synth import make_inputs
     inp = make_inputs(cid)
     cfg = inp["cfg"]
-    layers, hidden, _ = make_layers(inp, args.instances, False, dev)
+    layers, hidden, _ = make_layers(inp, args.instances, w8a8, dev, w8a8)
     outs = [torch.empty_like(hidden) for _ in layers]
     _, r = layers[0].forward(hidden, routing=True)
     sel = r["sel"].cpu().numpy()
     counts = r["counts"].cpu().numpy()
-    dom = dominant_kernel(cfg, counts)
-    lbytes, lflops, touched = layer_work(cfg, counts)
+    dom = dominant_kernel(cfg, counts, w8a8, w8a8)
+    lbytes, lflops, touched = layer_work(cfg, counts, w8a8)
+    peak = PEAK_FP8_TFLOPS if w8a8 else PEAK_BF16_TFLOPS
     K = args.prefill_steps
     for i in range(max(5, K // 10)):
         layers[i % len(layers)].forward(hidden, out=outs[i % len(layers)])
     ms, _ = time_steps(layers, hidden, outs, K, False)
     ms_ev, slots = time_steps(layers, hidden, outs, K, True)
-    rl = roofline_entry(dom, slots[dom["slot"]], counter_traffic(cfg.name, dom["kernel"]))
+    wname = cfg.name + ("_w8a8" if w8a8 else "")
+    rl = roofline_entry(dom, slots[dom["slot"]], counter_traffic(wname, dom["kernel"]))
     for L in layers:
         L.close()
-    out = {"workload": cfg.name, "T": cfg.T, "top_k": cfg.k, "steps": K,
+    out = {"workload": wname, "T": cfg.T, "top_k": cfg.k, "steps": K,
            "tokens_per_s": round(cfg.T / (ms * 1e-3), 1), "us_per_step": round(ms * 1e3, 3),
-           "mfma_frac_layer": round(lflops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "mfma_frac_layer": round(lflops / (ms * 1e-3) / 1e12 / peak, 4),
+           "mfma_peak_TFLOPs": peak,
            "algorithmic_flops": lflops, "algorithmic_bytes": lbytes,
            "experts_touched": touched,
            "gemm_gate_up": {"kernel": dom["kernel"], "us": rl["avg_launch_us"],
-                            "TFLOPs": rl["achieved"], "frac": rl["frac"],
+                            "achieved": rl["achieved"], "unit": rl["unit"], "frac": rl["frac"],
                             "traffic": rl["traffic"]},
            "kernel_us": {k_: round(v * 1e3, 3) for k_, v in slots.items()},
            "us_per_step_with_kernel_events": round(ms_ev * 1e3, 3)}
-    log(f"[bench] {cfg.name}: {out['us_per_step']:.1f} us/step, {out['tokens_per_s'] / 1e6:.2f} M "
-        f"tokens/s, layer {100 * out['mfma_frac_layer']:.1f}% of bf16 peak; gate/up GEMM "
-        f"{rl['avg_launch_us']:.1f} us = {100 * rl['frac']:.1f}%")
+    log(f"[bench] {wname}: {out['us_per_step']:.1f} us/step, {out['tokens_per_s'] / 1e6:.2f} M "
+        f"tokens/s, layer {100 * out['mfma_frac_layer']:.1f}% of the {'fp8' if w8a8 else 'bf16'} "
+        f"peak; gate/up {rl['avg_launch_us']:.1f} us = {100 * rl['frac']:.1f}% of its roofline")
     return out, inp, sel
 
 
@@ -605,7 +609,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=200,
                     help="steps of each prefill workload in the default line's `prefill` entry")
     ap.add_argument("--no-prefill", action="store_true",
-                    help="leave the prefill workloads out of the decode line")
+                    help="leave the prefill and fp8-activation workloads out of the decode line")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
@@ -735,6 +739,12 @@ def main():
             summ, pinp, psel = prefill_summary(cid, args, dev)
             line["prefill"][f"T{pinp['cfg'].T}"] = summ
             checked.append((pinp, psel))
+        # the same workloads with fp8 weights and activations (R20): the same
+        # router, so the routing checked above covers them
+        line["w8a8"] = {}
+        for cid in (1, 2, 4):
+            summ, pinp, _ = prefill_summary(cid, args, dev, w8a8=True)
+            line["w8a8"][f"T{pinp['cfg'].T}"] = summ
     if not args.no_context:
         torch.cuda.synchronize()
         line["context"] = hw_context(dev)
