@@ -363,6 +363,8 @@ def run_stack(args):
     d_ff=3072, T=32 (32 streams x one frame).  Weights are drawn on the GPU
     (seeded torch generator, the layer distributions of the workloads); no
     oracle runs here (the stack's parity is in tests/test_gpu_stack.py).
+    --fp8 / --w8a8: every layer's expert weights quantised per row on the GPU
+    (E4M3, scale max|row| / 448), with bf16 or fp8 activations.
     """
     import torch
     from moe_ffn_amd import MoELayer, MoEStack, load_library
@@ -384,8 +386,17 @@ def run_stack(args):
              else torch.zeros(1, device=dev),
              "w_gate": rnd(ne, F, d, std=d ** -0.5), "w_up": rnd(ne, F, d, std=d ** -0.5),
              "w_down": rnd(ne, d, F, std=F ** -0.5)}
-        layers.append(MoELayer(d, F, ne, k, "bf16", w, T))
-        del w
+        sc = None
+        if args.fp8:
+            sc = {}
+            for name, sname in (("w_gate", "gate"), ("w_up", "up"), ("w_down", "down")):
+                w32 = w[name].float()
+                amax = w32.abs().amax(dim=-1)
+                s_ = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+                w[name] = (w32 / s_[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
+                sc[sname] = s_.contiguous()
+        layers.append(MoELayer(d, F, ne, k, "bf16", w, T, fp8_scales=sc, fp8_act=args.w8a8))
+        del w, sc
     torch.cuda.synchronize()
     log(f"[bench] {len(layers)} layers created in {time.perf_counter() - t0:.1f} s")
     g.manual_seed(7)
@@ -400,7 +411,7 @@ def run_stack(args):
     out = stack.forward(h0)
     torch.cuda.synchronize()
     same_as_loop = bool(torch.equal(out.view(torch.int16), h.view(torch.int16)))
-    per_expert = 3 * F * d * 2
+    per_expert = 3 * F * d + (2 * F + d) * 4 if args.fp8 else 3 * F * d * 2
     wbytes = sum(t * per_expert for t in touched)
     K, W = args.steps, args.warmup
     for _ in range(W):
@@ -445,9 +456,10 @@ def run_stack(args):
     line = {"metric": "FFN-stack frames of 32 tokens per second (28 layers, decode)",
             "value": round(1e3 / ms_graph, 2), "unit": "frames/s", "n_gpus": 1, "steps": K,
             "warmup": W, "ms_per_step": round(ms_graph, 6), "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3" if args.w8a8 else "bf16",
             "data": "synthetic: random-init weights drawn on the GPU (seeded), N(0,1) hidden states",
-            "config": {"workload": "ffn_stack_28_layers_decode_T32_d2048_E16_F3072",
+            "config": {"workload": "ffn_stack_28_layers_decode_T32_d2048_E16_F3072" +
+                                   ("_w8a8" if args.w8a8 else "_fp8w" if args.fp8 else ""),
                        "layers": "3 dense, 23 MoE top-1, 1 MoE top-2, 1 dense", "T": T},
             "stack": {"us_per_frame_graph": round(ms_graph * 1e3, 2),
                       "us_per_frame_eager": round(ms_eager * 1e3, 2),
@@ -638,6 +650,8 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.w8a8:
+        args.fp8 = True
     if args.stack:
         if args.steps == 2000:
             args.steps = 100
@@ -651,8 +665,6 @@ def main():
     load_library()  # fails loudly if the HIP library is not built
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
-    if args.w8a8:
-        args.fp8 = True
     if args.fp8 and args.config == 0:
         raise SystemExit("--fp8 and --w8a8 need a bf16 workload (--config 1..4)")
     dev = torch.device("cuda:0")

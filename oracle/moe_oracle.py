@@ -311,7 +311,7 @@ def depth_average(z_prev, z, alpha: float) -> np.ndarray:
 
 # O10 ------------------------------------------------------------------------
 def stack_forward(layer_vals: list, H, ks: list, eps: float, forced_sels=None,
-                  eda_alpha: float | None = None) -> dict:
+                  eda_alpha: float | None = None, fp8_act: bool = False) -> dict:
     """The FFN half of a stack of backbone layers with residual adds (digest
     item 5: a 28-layer stack whose first three and last layers are dense and
     whose middle layers are MoE, the last MoE layer top-2):
@@ -322,7 +322,8 @@ def stack_forward(layer_vals: list, H, ks: list, eps: float, forced_sels=None,
     Everything stays in float64; forced_sels[l] optionally replaces layer l's
     routing choice.  eda_alpha: the MoE layers' (more than one expert) logits
     are depth-averaged (O11) in stack order; dense layers carry no router
-    state.  Returns the final h and every layer's routing (the forced one
+    state.  fp8_act: every layer quantises its expert activations (O12).
+    Returns the final h and every layer's routing (the forced one
     where given), the oracle's own choice and the top-k margins.
     """
     h = _f64(H)
@@ -338,10 +339,11 @@ def stack_forward(layer_vals: list, H, ks: list, eps: float, forced_sels=None,
         fs = None if forced_sels is None else forced_sels[l]
         moe = np.asarray(vals["w_router"]).shape[0] > 1
         if eda_alpha is not None and moe:
-            r = oracle_forward(v, k=ks[l], forced_sel=fs, eps=eps, z_prev=zp, eda_alpha=eda_alpha)
+            r = oracle_forward(v, k=ks[l], forced_sel=fs, eps=eps, z_prev=zp, eda_alpha=eda_alpha,
+                               fp8_act=fp8_act)
             zp = r["z"]
         else:
-            r = oracle_forward(v, k=ks[l], forced_sel=fs, eps=eps)
+            r = oracle_forward(v, k=ks[l], forced_sel=fs, eps=eps, fp8_act=fp8_act)
         h = h + r["out"]
         sels.append(r["sel"])
         own.append(r["sel_oracle"])

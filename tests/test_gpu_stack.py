@@ -326,3 +326,42 @@ def test_eda_rejects_bad_rates_and_fp32_stacks():
     with pytest.raises(MoELayerError):
         s32.set_eda(0.5)
     s32.close()
+
+
+@pytest.mark.parametrize("T", [40, 300])
+def test_w8a8_stack_matches_layer_loop_and_oracle(T):
+    """A stack of layers with fp8 weights and fp8 activations (moe_layer_create_w8a8;
+    T=40 streams the weights, T=300 runs the fp8 MFMA GEMMs): the stack equals
+    the layer loop bit for bit, and every layer, on the input it received on
+    the GPU and the GPU's routing, matches the oracle's fp8-activation step
+    (O12) with undecided quantisation scales held to validity only."""
+    from moe_ffn_amd import MoEStack
+    from tests.test_gpu_fp8 import fp8_vals
+    from tests.test_gpu_w8a8 import w8a8_layer
+    inps = _small_stack_inputs(T)
+    layers = [w8a8_layer(inp, T) for inp in inps]
+    stack = MoEStack(layers, max_tokens=T)
+    h = to_torch(inps[0]["hidden"], "bf16")
+    out = stack.forward(h)
+    ties = 0
+    for l, (L, inp) in enumerate(zip(layers, inps)):
+        h_in = out_to_f64(h)
+        y, r = L.forward(h, routing=True)
+        torch.cuda.synchronize()
+        sel = r["sel"].cpu().numpy()
+        vals = dict(fp8_vals(inp), hidden=h_in)
+        ref = O.oracle_forward(vals, k=inp["cfg"].k, eps=inp["cfg"].eps, forced_sel=sel,
+                               fp8_act=True)
+        got = out_to_f64(y)
+        tie = ref["scale_tie"]
+        scale = np.abs(ref["out"]).max()
+        err = np.abs(got - ref["out"])[~tie].max()
+        assert err <= TOL["bf16"] * scale, (l, err, scale)
+        row = np.sqrt(np.mean((got - ref["out"]) ** 2, axis=1) / np.mean(ref["out"] ** 2, axis=1))
+        assert np.all(row[tie] <= 0.1), (l, row[tie].max())
+        ties += int(tie.sum())
+        h = (h.float() + y.float()).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), h.view(torch.int16))
+    print(f"[w8a8 stack] T={T}: {len(layers)} layers, undecided scales {ties}", flush=True)
+    stack.close()

@@ -682,3 +682,19 @@ def test_scale_undecided_marks_rows_near_a_bf16_rounding_boundary():
         a1 = O.quantize_rows_e4m3(O.bf16_round(M * f))[1]
         assert np.all(a1[~und] == a0[~und])
     assert 0 < und.sum() < 400
+
+
+def test_stack_with_fp8_activations_composes_the_fp8_layers():
+    # a two-layer stack (dense, then MoE top-1) with fp8 activations is the
+    # residual composition of the fp8-activation layers
+    rng = np.random.default_rng(38)
+    T, d, F = 12, 32, 64
+    dense = _rand_layer(rng, T, d, 1, F)
+    moe = _rand_layer(rng, T, d, 3, F)
+    H = rng.standard_normal((T, d))
+    st = O.stack_forward([dense, moe], H, [1, 1], 1e-6, fp8_act=True)
+    h1 = H + O.oracle_forward(dict(dense, hidden=H), k=1, eps=1e-6, fp8_act=True)["out"]
+    h2 = h1 + O.oracle_forward(dict(moe, hidden=h1), k=1, eps=1e-6, fp8_act=True)["out"]
+    np.testing.assert_array_equal(st["out"], h2)
+    plain = O.stack_forward([dense, moe], H, [1, 1], 1e-6)["out"]
+    assert np.max(np.abs(plain - st["out"])) > 0
