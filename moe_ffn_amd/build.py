@@ -73,6 +73,40 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
     return LIB
 
 
+# The host code with AddressSanitizer (every -fsanitize behind -Xarch_host:
+# the device code is built as usual, without it): the library's sources and a
+# C++ driver of the ABI's validation and error paths
+# (tests/asan/abi_host_check.cpp) linked into one executable.
+ASAN_FLAGS = ["-O1", "-g", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+              "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+              "-Wno-unused-command-line-argument",
+              "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def build_host_asan(out_dir: str | None = None, jobs: int | None = None) -> str:
+    out_dir = out_dir or os.path.join(BUILD, "host_asan")
+    os.makedirs(out_dir, exist_ok=True)
+    srcs = sources() + [os.path.join(ROOT, "tests", "asan", "abi_host_check.cpp")]
+
+    def one(src):
+        obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+        r = subprocess.run([_hipcc(), *ASAN_FLAGS, "-x", "hip", "-c", src, "-o", obj],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"host ASan compile failed: {src}\n{r.stdout}{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=jobs or min(len(srcs), os.cpu_count() or 4, 16)) as ex:
+        objs = list(ex.map(one, srcs))
+    exe = os.path.join(out_dir, "abi_host_check")
+    r = subprocess.run([_hipcc(), "--offload-arch=" + ARCH, "-Xarch_host", "-fsanitize=address",
+                        "-o", exe, *objs], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("host ASan link failed:\n" + r.stdout + r.stderr)
+    return exe
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
