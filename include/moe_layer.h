@@ -200,7 +200,8 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const void* hidden, int32_t T
  * start at zero are cleared by a kernel at the start of each call, and calls
  * that overlap on one device (on two streams, or with two host threads) race.
  * Sizes: the buffers needed for T tokens must fit in 16 MiB (at d_model 2048,
- * d_ff 3072 and 16 experts: T up to 815 with top-1, 286 with top-2); larger T
+ * d_ff 3072 and 16 experts: T up to 815 with top-1, 286 with top-2; layers
+ * with fp8 activations carve other buffers: 699 and 249); larger T
  * is rejected with INVALID_ARG and a message giving the bytes needed.  Outputs and routing are
  * those moe_layer_forward gives for the same arguments.
  * Errors: as moe_layer_forward; INVALID_ARG also when T needs more scratch. */
