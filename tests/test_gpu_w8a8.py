@@ -156,3 +156,25 @@ def test_w8a8_small_shapes(E, k, T):
     st = check_parity(inp, w8a8_layer(inp, T), vals=fp8_vals(inp), fp8_act=True, label=cfg.name)
     assert st["rows_compared"] == T
     assert st["rms_err_rel"] < 5e-3
+
+
+@pytest.mark.parametrize("T", [1, 40, 300])
+def test_w8a8_edge_cases(T):
+    """Zero hidden rows (scale 0, codes 0 all the way through), every token
+    routed to one expert by a large bias, and single tokens, on the weight
+    streams (T * k <= 64) and on the fp8 MFMA GEMMs."""
+    base = make_inputs(WORKLOADS[2], T=T)
+    h = base["hidden"].copy()
+    h[::7] = 0                                  # rows 0, 7, 14, ... all bf16 +0
+    zero_rows = dict(base, hidden=h)
+    b = np.array(base["bias"], np.float32).copy()
+    b[5] += 1e4
+    one_expert = dict(base, bias=b)
+    for label, inp in (("zero rows", zero_rows), ("one expert", one_expert)):
+        print(f"[case] w8a8 {label} T={T}", flush=True)
+        st = check_parity(inp, w8a8_layer(inp, T), vals=fp8_vals(inp), fp8_act=True,
+                          label=f"w8a8 {label} T={T}")
+        assert st["rows_compared"] == T
+    out = w8a8_layer(zero_rows, T).forward(to_torch(h, "bf16"))
+    torch.cuda.synchronize()
+    assert torch.all(out[::7] == 0)             # a zero row's output is exactly zero
