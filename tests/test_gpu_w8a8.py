@@ -52,7 +52,8 @@ def _bf16_rows(rng, R, K):
     return xb
 
 
-@pytest.mark.parametrize("R,K", [(64, 2048), (9, 8), (33, 3072)])
+# K up to 4096: each row held in registers; beyond, two passes over the row
+@pytest.mark.parametrize("R,K", [(64, 2048), (9, 8), (33, 3072), (5, 4096), (6, 5000)])
 def test_quantize_rows_bit_exact(R, K):
     from moe_ffn_amd import fp8_quantize_rows
     rng = np.random.default_rng(R * 7 + K)
