@@ -229,6 +229,21 @@ __global__ __launch_bounds__(64 * S, 1) void k_gateup_stream(
                            lane * 16) : nullptr;
   }
   const int col = lane & 31;
+  // fp8 weights: the row scales of this lane's epilogue elements, loaded
+  // before the stream so that their latency hides under it (the S waves take
+  // the NT * 8 (gate, up) pairs in turn)
+  constexpr int NPL = (NT * 8 + S - 1) / S;
+  float sgl[NPL], sul[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int p = wave + j * S;
+    sgl[j] = sul[j] = 1.f;
+    if (FP8 && p < NT * 8) {  // gate rows 0..15, up rows 16..31 of the tile
+      const float* sc = sgu + (size_t)e * 2 * F + 32 * (NT * ft + (p >> 3));
+      sgl[j] = sc[c32_row(p & 7, lane)];
+      sul[j] = sc[16 + c32_row(p & 7, lane)];
+    }
+  }
 
   for (int c0 = 0; c0 < cnt; c0 += 32) {
     const int ntok = min(32, cnt - c0);
@@ -249,14 +264,15 @@ __global__ __launch_bounds__(64 * S, 1) void k_gateup_stream(
     // c32_row(i, lane); the S waves take the NT * 8 (gate, up) pairs in turn
     uint16_t* dst = act + (size_t)(off + c0 + col) * F + ft * 16 * NT;
 #pragma unroll
-    for (int p = wave; p < NT * 8; p += S) {
+    for (int j = 0; j < NPL; ++j) {
+      const int p = wave + j * S;
+      if (p >= NT * 8) break;
       const int q = p >> 3, i = p & 7, f = c32_row(i, lane);
       float g = split_sum<NT, S>(red, q, i, lane);
       float u = split_sum<NT, S>(red, q, i + 8, lane);
-      if constexpr (FP8) {  // row scales: gate rows 0..15, up rows 16..31 of the tile
-        const float* sc = sgu + (size_t)e * 2 * F + 32 * (NT * ft + q);
-        g *= sc[f];
-        u *= sc[16 + f];
+      if constexpr (FP8) {
+        g *= sgl[j];
+        u *= sul[j];
       }
       if (valid) dst[16 * q + f] = (uint16_t)f32_to_bf16(silu(rs * g) * (rs * u));
     }
@@ -293,6 +309,16 @@ __global__ __launch_bounds__(64 * SD, 1) void k_down_stream(
       FP8 ? wd8 + ((size_t)e * (d / kTileRows) + mt) * (size_t)ksteps * kBlockElems + lane * 16
           : nullptr};
   const int col = lane & 31;
+  const int m0 = mt * kTileRows;
+  // fp8 weights: the row scales of this lane's epilogue rows (the SD waves
+  // take the 16 accumulator elements in turn), loaded before the stream
+  constexpr int NEL = (16 + SD - 1) / SD;
+  float sdl[NEL];
+#pragma unroll
+  for (int j = 0; j < NEL; ++j) {
+    const int i = wave + j * SD;
+    sdl[j] = FP8 && i < 16 ? sd[(size_t)e * d + m0 + c32_row(i, lane)] : 1.f;
+  }
 
   for (int c0 = 0; c0 < cnt; c0 += 32) {
     const int ntok = min(32, cnt - c0);
@@ -301,6 +327,7 @@ __global__ __launch_bounds__(64 * SD, 1) void k_down_stream(
     const uint16_t* arow = (valid ? act + (size_t)slot * F : zrow) + (lane >> 5) * 8;
     const int tok = (k == 1 && valid) ? list[c0 + col] : 0;
     const float gw = (k == 1 && valid) ? gate[tok] : 0.f;
+    const float as = FP8 && asc != nullptr ? asc[slot] : 1.f;  // fp8 activations: the row's scale
     f32x16 acc[1];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[0][i] = 0.f;
@@ -309,15 +336,13 @@ __global__ __launch_bounds__(64 * SD, 1) void k_down_stream(
     stash<1>(acc, red, wave, lane);
     __syncthreads();
     // the SD waves take the 16 accumulator elements (rows m0 + c32_row(i, lane)) in turn
-    const int m0 = mt * kTileRows;
 #pragma unroll
-    for (int i = wave; i < 16; i += SD) {
+    for (int j = 0; j < NEL; ++j) {
+      const int i = wave + j * SD;
+      if (i >= 16) break;
       const int r = c32_row(i, lane);
       float y = split_sum<1, SD>(red, 0, i, lane);
-      if constexpr (FP8) {
-        y *= sd[(size_t)e * d + m0 + r];
-        if (asc != nullptr) y *= asc[slot];  // fp8 activations: the row's scale
-      }
+      if constexpr (FP8) y = (y * sdl[j]) * as;
       if (valid) {
         if (k == 1) out[(size_t)tok * d + m0 + r] = (uint16_t)f32_to_bf16(gw * y);
         else ybuf[(size_t)slot * d + m0 + r] = y;

@@ -21,8 +21,8 @@
 // Layers with fp8 activations (xs != null) get the quantised expert input
 // instead of x': the row's scale a = max_i |u_i| / 448 of u = bf16(inv_rms *
 // x') is bf16(inv_rms * max_i |x'_i|) / 448 (both roundings are monotone), so
-// the first pass also tracks max |x'|; a second pass over the row (in cache)
-// writes the E4M3 values of u (quant4_e4m3, exact in bf16) and xs[t] = a.  The
+// the first pass also tracks max |x'|; a second pass over the row (its first
+// 2048 values from registers, the rest from cache) writes the E4M3 values of u (quant4_e4m3, exact in bf16) and xs[t] = a.  The
 // weight streams then multiply exact code values and scale the sums by a.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -55,13 +55,19 @@ __global__ __launch_bounds__(256) void k_router_token(
   for (int e = 0; e < NV; ++e) acc[e] = 0.f;
   float ss = 0.f, mx = 0.f;
   constexpr int G = EP < 16 ? EP : 16;  // router rows loaded together
+  u32x4 hv0 = {0u, 0u, 0u, 0u}, gv0 = {0u, 0u, 0u, 0u};  // this thread's first chunk
   for (int c = tid * 8; c < d; c += 256 * 8) {
     u32x4 wv[G];
 #pragma unroll
     for (int e = 0; e < G; ++e) wv[e] = ldg16(wrow[e] + c);
     float h[8], g[8], x[8];
-    unpack8(ldg16(hrow + c), h);
-    unpack8(ldg16(gain + c), g);
+    const u32x4 hv = ldg16(hrow + c), gv = ldg16(gain + c);
+    if (c == tid * 8) {
+      hv0 = hv;
+      gv0 = gv;
+    }
+    unpack8(hv, h);
+    unpack8(gv, g);
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -167,10 +173,12 @@ __global__ __launch_bounds__(256) void k_router_token(
   if (xs != nullptr) {  // second pass: the E4M3 values of u = bf16(inv * x')
     __syncthreads();
     const float inv = s_inv, r = s_r;
+    // the first chunk comes from registers (at d_model <= 2048 the whole row)
     for (int c = tid * 8; c < d; c += 256 * 8) {
       float h[8], g[8];
-      unpack8(ldg16(hrow + c), h);
-      unpack8(ldg16(gain + c), g);
+      const bool first = c == tid * 8;
+      unpack8(first ? hv0 : ldg16(hrow + c), h);
+      unpack8(first ? gv0 : ldg16(gain + c), g);
       uint32_t uw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
