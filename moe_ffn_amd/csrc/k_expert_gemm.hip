@@ -6,7 +6,8 @@
 //   MODE 0  act[slot, f] = bf16( SiLU(x W_gate^T) * (x W_up^T) )   K = d_model
 //           (x: the normalised rows, RMSNorm applied by the gather)
 //   MODE 1  y[slot, m]   = act[slot] W_down^T                                    K = d_ff
-//           k = 1: out[token] = bf16(gate * y); k > 1: y kept in fp32.
+//           k = 1: out[token] = bf16(gate * y) (in a stack, bf16(res + that));
+//           k > 1: y kept in fp32.
 //
 // Work unit: (expert, block of 128*RT weight rows, span of at most 32*cap of
 // the expert's slots; cap <= TTM, chosen per launch on the host, TTM = 5 for
@@ -380,7 +381,8 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
                                          const float* __restrict__ rsc,
                                          const float* __restrict__ asc, float* __restrict__ pmax,
                                          int k, const uint16_t* __restrict__ zrow,
-                                         uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
+                                         uint16_t* __restrict__ dst16,
+                                         const uint16_t* __restrict__ res, float* __restrict__ ybuf,
                                          int d, int F) {
   using G = Geo<RT>;
   const int K = MODE == 0 ? d : F;
@@ -521,11 +523,27 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const int mw = tile0 * kTileRows;  // the wave's first output row
       if (k == 1) {
+        // in a stack (res): out = bf16(res + bf16(gate * y)); the residual
+        // pieces are all loaded first (rows past the unit read token 0's)
+        u32x4 hv[4];
+        if (res != nullptr) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tr = __shfl(tok, (lane >> 3) + 8 * i, 64);
+            hv[i] = ldg16(res + (size_t)tr * d + mw + (lane & 7) * 8);
+          }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tl = (lane >> 3) + 8 * i, ch = lane & 7;
           const int tr = __shfl(tok, tl, 64);
-          const u32x4 v = *reinterpret_cast<const u32x4*>(wl + tl * 128 + ((ch ^ (tl & 7)) << 4));
+          u32x4 v = *reinterpret_cast<const u32x4*>(wl + tl * 128 + ((ch ^ (tl & 7)) << 4));
+          if (res != nullptr) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              v[q] = pack_bf16x2(bf16_lo(hv[i][q]) + bf16_lo(v[q]),
+                                 bf16_hi(hv[i][q]) + bf16_hi(v[q]));
+          }
           if (j * kSub + tl < u.nrows)
             *reinterpret_cast<u32x4*>(dst16 + (size_t)tr * d + mw + ch * 8) = v;
         }
@@ -557,17 +575,18 @@ __device__ __forceinline__ void run_any(const Unit& u, u32x4* lds, const uint16_
                                         const float* __restrict__ rsc,
                                         const float* __restrict__ asc, float* __restrict__ pmax,
                                         int k, const uint16_t* __restrict__ zrow,
-                                        uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
+                                        uint16_t* __restrict__ dst16,
+                                        const uint16_t* __restrict__ res, float* __restrict__ ybuf,
                                         int d, int F) {
   if constexpr (TT > 1) {
     if (u.nsub != TT) {
       run_any<MODE, RT, Q, TT - 1, SC, F8>(u, lds, wpk, src, gather, gate, rsc, asc, pmax, k,
-                                           zrow, dst16, ybuf, d, F);
+                                           zrow, dst16, res, ybuf, d, F);
       return;
     }
   }
   run_unit<MODE, RT, Q, TT, SC, F8>(u, lds, wpk, src, gather, gate, rsc, asc, pmax, k, zrow, dst16,
-                                    ybuf, d, F);
+                                    res, ybuf, d, F);
 }
 }  // namespace
 
@@ -579,8 +598,8 @@ __global__ __launch_bounds__(256, OCC) void k_expert_gemm(
     const int* __restrict__ gather, const float* __restrict__ gate,
     const float* __restrict__ rsc, const float* __restrict__ asc, float* __restrict__ pmax, int k,
     int E, int cap,
-    const uint16_t* __restrict__ zrow, uint16_t* __restrict__ dst16, float* __restrict__ ybuf,
-    int d, int F) {
+    const uint16_t* __restrict__ zrow, uint16_t* __restrict__ dst16,
+    const uint16_t* __restrict__ res, float* __restrict__ ybuf, int d, int F) {
   static_assert(TTM >= 1 && TTM <= 8, "token subtiles per unit");
   __shared__ u32x4 lds[kBStages * stage_ent<TTM>()];
   static_assert(MODE == 0 || sizeof(lds) >= 4 * 8192, "the down epilogue's per-wave LDS tiles");
@@ -598,7 +617,7 @@ __global__ __launch_bounds__(256, OCC) void k_expert_gemm(
     decode_unit(tab, nrb, L, u);
     __syncthreads();  // the previous unit's last LDS reads are done everywhere
     run_any<MODE, RT, Q, TTM, SC, F8>(u, lds, wpk, src, gather, gate, rsc, asc, pmax, k, zrow, dst16,
-                                      ybuf, d, F);
+                                      res, ybuf, d, F);
   }
 }
 
@@ -673,7 +692,8 @@ hipError_t launch_gemm(const FwdArgs& a) {
                 (const int*)a.offsets, (const int*)a.gather, (const float*)a.gate,
                 rsc, asc, F8 && MODE == 0 ? a.pmm : nullptr, a.dim.k, a.dim.E, cap,
                 (const uint16_t*)a.zrow,
-                (uint16_t*)(MODE == 0 ? a.act : a.out), a.ybuf, a.dim.d, a.dim.F);
+                (uint16_t*)(MODE == 0 ? a.act : a.out),
+                (const uint16_t*)(MODE == 0 ? nullptr : a.res), a.ybuf, a.dim.d, a.dim.F);
 }
 }  // namespace
 

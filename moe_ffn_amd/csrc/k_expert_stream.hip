@@ -281,7 +281,8 @@ __global__ __launch_bounds__(64 * S, 1) void k_gateup_stream(
 }
 
 // Down projection for one 32-row d_model tile; k = 1 writes gate * y into the
-// output row of the token, k > 1 writes y (fp32) for the combine kernel.
+// output row of the token (in a stack, bf16(res + bf16(gate * y))), k > 1
+// writes y (fp32) for the combine kernel.
 // SD waves split the reduction axis.
 template <int D, bool FP8, int SD>
 __global__ __launch_bounds__(64 * SD, 1) void k_down_stream(
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(64 * SD, 1) void k_down_stream(
     const float* __restrict__ sd, const uint16_t* __restrict__ act,
     const int* __restrict__ sel, int n, int k, int E, const float* __restrict__ gate,
     const float* __restrict__ asc, const uint16_t* __restrict__ zrow, uint16_t* __restrict__ out,
-    float* __restrict__ ybuf, int d, int F) {
+    const uint16_t* __restrict__ res, float* __restrict__ ybuf, int d, int F) {
   __shared__ float red[SD * 16 * 64];
   __shared__ int list[64];
   __shared__ int sh[2];
@@ -328,6 +329,15 @@ __global__ __launch_bounds__(64 * SD, 1) void k_down_stream(
     const int tok = (k == 1 && valid) ? list[c0 + col] : 0;
     const float gw = (k == 1 && valid) ? gate[tok] : 0.f;
     const float as = FP8 && asc != nullptr ? asc[slot] : 1.f;  // fp8 activations: the row's scale
+    // in a stack (res, k = 1): the residual stream's values of this lane's
+    // output elements, loaded before the stream (lanes without a token read zrow)
+    uint16_t hres[NEL];
+#pragma unroll
+    for (int j = 0; j < NEL; ++j) {
+      const int i = wave + j * SD;
+      const bool use = res != nullptr && k == 1 && valid && i < 16;
+      hres[j] = *(use ? res + (size_t)tok * d + m0 + c32_row(i, lane) : zrow);
+    }
     f32x16 acc[1];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[0][i] = 0.f;
@@ -344,8 +354,13 @@ __global__ __launch_bounds__(64 * SD, 1) void k_down_stream(
       float y = split_sum<1, SD>(red, 0, i, lane);
       if constexpr (FP8) y = (y * sdl[j]) * as;
       if (valid) {
-        if (k == 1) out[(size_t)tok * d + m0 + r] = (uint16_t)f32_to_bf16(gw * y);
-        else ybuf[(size_t)slot * d + m0 + r] = y;
+        if (k == 1) {
+          const uint32_t o = f32_to_bf16(gw * y);
+          out[(size_t)tok * d + m0 + r] =
+              (uint16_t)(res != nullptr ? f32_to_bf16(bf16_lo(hres[j]) + bf16_lo(o)) : o);
+        } else {
+          ybuf[(size_t)slot * d + m0 + r] = y;
+        }
       }
     }
     __syncthreads();  // red is reused by the next pass over the tokens
@@ -390,7 +405,7 @@ hipError_t launch_streams(const FwdArgs& a) {
                 (const uint16_t*)a.wd, (const uint8_t*)a.wd8, a.sd, (const uint16_t*)a.act,
                 (const int*)a.sel, a.n, a.dim.k, E, (const float*)a.gate,
                 (const float*)(a.dim.act8 ? a.sm : nullptr), (const uint16_t*)a.zrow,
-                (uint16_t*)a.out, a.ybuf, d, F);
+                (uint16_t*)a.out, (const uint16_t*)a.res, a.ybuf, d, F);
 }
 }  // namespace
 

@@ -1,4 +1,6 @@
-// Residual add between the layers of an FFN stack: h_next = h + ffn(h).
+// Residual add between the layers of an FFN stack: h_next = h + ffn(h)
+// (fp32 stacks; bf16 layers add their output to the residual stream in their
+// last kernel, with the same roundings as k_residual_bf16).
 //
 // The ZONOS2 backbone stacks 28 layers (digest item 5: the first three and
 // the last one dense, the middle ones MoE); each layer's FFN output is added

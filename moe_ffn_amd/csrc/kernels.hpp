@@ -57,6 +57,10 @@ struct FwdArgs {
   int T, n;            // tokens, assignments (T * k)
   const void* hidden;  // [T, d]
   void* out;           // [T, d]
+  // bf16 layers in a stack: the residual stream [T, d] that the layer's output
+  // is added to (out = bf16(res + bf16(y)), the layer output's rounding then
+  // the sum's, as a separate add of the two bf16 rows would); null otherwise
+  const void* res = nullptr;
   // layer-owned parameters
   const float* wrg;    // [EP, d] fp32: W_r[e][i] * g[i] (zero rows e >= E), fp32 layers
   const float* gain;   // [d] fp32

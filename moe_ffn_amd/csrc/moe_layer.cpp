@@ -491,11 +491,12 @@ namespace {
 // MOE_DEBUG_SYNC synchronisation must not run.
 // eda: a stack's depth-averaging state for this layer's router (bf16 MoE
 // layers only; null otherwise), eda_first: the stack's first MoE layer.
-// wk: the per-call buffers (null: the layer's workspace).
+// wk: the per-call buffers (null: the layer's workspace).  res: bf16 layers in
+// a stack, the residual stream that the output is added to (else null).
 moe_status_t forward_impl(moe_layer_t* L, const void* hidden, int32_t T, void* out, void* stream,
                           const moe_routing_out_t* routing, bool allow_sync,
                           float* eda = nullptr, float eda_alpha = 0.f, bool eda_first = false,
-                          const Work* wk = nullptr) {
+                          const Work* wk = nullptr, const void* res = nullptr) {
   if (L == nullptr || L->magic != kMagic) return fail(MOE_ERR_INVALID_ARG, "invalid layer handle");
   if (T < 0 || T > L->max_tokens)
     return fail(MOE_ERR_INVALID_ARG, "T must be in [0, max_tokens] (max_tokens = " +
@@ -528,6 +529,7 @@ moe_status_t forward_impl(moe_layer_t* L, const void* hidden, int32_t T, void* o
   a.n = T * L->dim.k;
   a.hidden = hidden;
   a.out = out;
+  a.res = res;
   a.wrg = L->wrg;
   a.gain = L->gain32;
   a.bias = L->bias;
@@ -754,8 +756,9 @@ void moe_layer_destroy(moe_layer_t* L) {
 // MoE layers top-1 except the last one, top-2), each followed by the residual
 // add, h_{l+1} = h_l + FFN_l(h_l).  The stack borrows layer handles created by
 // the caller (a dense layer is a one-expert layer) and owns two residual
-// buffers, one FFN output buffer and, once captured, a HIP graph of the
-// whole sequence.
+// buffers, one FFN output buffer (fp32 stacks; bf16 layers add their output
+// to the residual stream in their last kernel) and, once captured, a HIP
+// graph of the whole sequence.
 
 struct moe_stack {
   uint32_t magic;
@@ -826,17 +829,23 @@ moe_status_t stack_enqueue(moe_stack* S, const void* hin, int32_t T, void* hout,
   const void* cur = hin;
   const int nl = (int)S->layers.size();
   bool first_moe = true;
+  // bf16: each layer's last kernel adds its output to the residual stream
+  // (out = bf16(h + bf16(y)), the same two roundings as a separate add);
+  // fp32: a residual launch after each layer
+  const bool fused = S->dtype == MOE_DTYPE_BF16;
   for (int l = 0; l < nl; ++l) {
     const bool moe = S->layers[l]->dim.E > 1;
     float* eda = S->eda_on && moe ? S->eda : nullptr;
-    moe_status_t st = forward_impl(S->layers[l], cur, T, S->y, s,
+    void* nxt = l == nl - 1 ? hout : ((l & 1) ? S->hB : S->hA);
+    moe_status_t st = forward_impl(S->layers[l], cur, T, fused ? nxt : S->y, s,
                                    routing != nullptr ? &routing[l] : nullptr, allow_sync, eda,
-                                   S->eda_alpha, first_moe);
+                                   S->eda_alpha, first_moe, nullptr, fused ? cur : nullptr);
     if (moe) first_moe = false;
     if (st != MOE_OK) return st;
-    void* nxt = l == nl - 1 ? hout : ((l & 1) ? S->hB : S->hA);
-    hipError_t he = moe::launch_residual(cur, S->y, nxt, n, S->dtype, s);
-    if (he != hipSuccess) return hip_fail(he, "residual launch");
+    if (!fused) {
+      hipError_t he = moe::launch_residual(cur, S->y, nxt, n, S->dtype, s);
+      if (he != hipSuccess) return hip_fail(he, "residual launch");
+    }
     cur = nxt;
   }
   return MOE_OK;
