@@ -142,9 +142,10 @@ hipError_t launch_combine(const FwdArgs& a);
 constexpr int kPermuteMaxGroups = 256;  // workgroups of the permutation, at most
 hipError_t launch_bias_update(const int* counts, int E, float rate, float* bias, hipStream_t s);
 
-// residual add of an FFN stack: out = h + y (n elements, dtype 1 = bf16, 0 = fp32)
-hipError_t launch_residual(const void* h, const void* y, void* out, size_t n, int dtype,
-                           hipStream_t s);
+// residual add of an fp32 FFN stack: out = h + y (n elements; bf16 layers add
+// theirs in their last kernel, FwdArgs::res)
+hipError_t launch_residual_f32(const float* h, const float* y, float* out, size_t n,
+                               hipStream_t s);
 
 // zero fill by a kernel (graph-capturable): bytes a multiple of 16, p 16-byte aligned
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);

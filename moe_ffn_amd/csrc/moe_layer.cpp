@@ -843,7 +843,9 @@ moe_status_t stack_enqueue(moe_stack* S, const void* hin, int32_t T, void* hout,
     if (moe) first_moe = false;
     if (st != MOE_OK) return st;
     if (!fused) {
-      hipError_t he = moe::launch_residual(cur, S->y, nxt, n, S->dtype, s);
+      hipError_t he = moe::launch_residual_f32(static_cast<const float*>(cur),
+                                               static_cast<const float*>(S->y),
+                                               static_cast<float*>(nxt), n, s);
       if (he != hipSuccess) return hip_fail(he, "residual launch");
     }
     cur = nxt;

@@ -8,6 +8,8 @@ tolerance, at d_model = 256 and at the full width d_model = 2048; and its
 captured HIP graph must reproduce eager runs on every replay, also after the
 input buffer's contents change.  With the router logits depth-averaged (O11)
 every MoE layer's routing is compared with the oracle's, layer by layer.
+fp32 stacks (a separate residual launch after each layer) equal their layer
+loop with the fp32 add in torch.
 """
 
 from dataclasses import replace
@@ -326,6 +328,27 @@ def test_eda_rejects_bad_rates_and_fp32_stacks():
     with pytest.raises(MoELayerError):
         s32.set_eda(0.5)
     s32.close()
+
+
+@pytest.mark.parametrize("T", [16, 100])
+def test_fp32_stack_matches_layer_loop(T):
+    """fp32 layers keep a residual launch after each layer (bf16 layers add in
+    their last kernel): the stack equals the loop with the fp32 add in torch."""
+    from moe_ffn_amd import MoEStack
+    base = WORKLOADS[0]
+    plan = [replace(base, E=1, bias="zero"), base, replace(base, k=2)]
+    inps = [make_inputs(cfg, T=T, layer=l) for l, cfg in enumerate(plan)]
+    layers = [make_layer(inp, max_tokens=T) for inp in inps]
+    stack = MoEStack(layers, max_tokens=T)
+    h = to_torch(inps[0]["hidden"], "f32")
+    print(f"[case] fp32 stack T={T}", flush=True)
+    out = stack.forward(h)
+    ref = h
+    for L in layers:
+        ref = ref + L.forward(ref)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+    stack.close()
 
 
 @pytest.mark.parametrize("T", [40, 300])
