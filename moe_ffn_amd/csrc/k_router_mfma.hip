@@ -88,6 +88,16 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
   }
   const uint16_t* gp = gain + kgrp + k0;
 
+  // the 16-expert finish (16 lanes per token, lane e % 16 owns expert e):
+  // its bias and (depth averaging) the previous MoE layer's logit are loaded
+  // now, under the main loop's loads
+  float bias_e = 0.f, eda_prev = 0.f;
+  if (EPAD == 16 && NTOK == 16 && tid < 16 * NTOK) {
+    const int e = tid & 15, t = t0 + (tid >> 4);
+    bias_e = bias[e];  // bias is padded with zeros to 64 entries
+    if (eda != nullptr && !eda_first && e < E && t < T) eda_prev = eda[(size_t)t * 64 + e];
+  }
+
   f32x4 acc[TT][NA];
   float ss[TT], mx[TT];
 #pragma unroll
@@ -191,11 +201,10 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
       const bool live = e < E;
       float z = zs[tl][e] * inv;
       if (eda != nullptr && live && t < T) {  // depth-averaged logits across MoE layers
-        float* st = eda + (size_t)t * 64 + e;
-        if (!eda_first) z = eda_alpha * *st + (1.0f - eda_alpha) * z;
-        *st = z;
+        if (!eda_first) z = eda_alpha * eda_prev + (1.0f - eda_alpha) * z;
+        eda[(size_t)t * 64 + e] = z;
       }
-      const float sc = z + bias[e];  // bias is padded with zeros to 64 entries
+      const float sc = z + bias_e;
       const uint32_t u = sc == 0.f ? 0u : __float_as_uint(sc);  // -0 ranks as +0
       const uint32_t ord = sc != sc ? 0u : (u & 0x80000000u) ? ~u : (u | 0x80000000u);
       bool avail = live;

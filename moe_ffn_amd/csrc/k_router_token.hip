@@ -50,6 +50,14 @@ __global__ __launch_bounds__(256) void k_router_token(
 #pragma unroll
   for (int e = 0; e < EP; ++e) wrow[e] = e < E ? wr + (size_t)e * d : zrow;
 
+  // wave 0's lane e finishes expert e: its bias and (depth averaging) the
+  // previous MoE layer's logit are loaded now, under the main loop's loads
+  float bias_e = 0.f, eda_prev = 0.f;
+  if (wave == 0) {
+    bias_e = bias[lane];  // bias is zero-padded to 64 entries
+    if (eda != nullptr && !eda_first && lane < E) eda_prev = eda[(size_t)t * 64 + lane];
+  }
+
   float acc[NV];
 #pragma unroll
   for (int e = 0; e < NV; ++e) acc[e] = 0.f;
@@ -122,11 +130,10 @@ __global__ __launch_bounds__(256) void k_router_token(
     const int el = lane < EP ? lane : 0;
     float z = live ? (((red[0][el] + red[1][el]) + red[2][el]) + red[3][el]) * inv : 0.f;
     if (eda != nullptr && live) {  // depth-averaged logits across the stack's MoE layers
-      float* st = eda + (size_t)t * 64 + lane;
-      if (!eda_first) z = eda_alpha * *st + (1.0f - eda_alpha) * z;
-      *st = z;
+      if (!eda_first) z = eda_alpha * eda_prev + (1.0f - eda_alpha) * z;
+      eda[(size_t)t * 64 + lane] = z;
     }
-    const float sc = z + bias[lane < 64 ? lane : 0];  // bias is zero-padded to 64 entries
+    const float sc = z + bias_e;
     // top-k by descending score, exact ties to the lower index: each round
     // takes the wave maximum of a 64-bit key (available flag, the score's
     // order-preserving bits with NaN lowest, 63 - lane), unique per lane, so
