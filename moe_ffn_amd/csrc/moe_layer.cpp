@@ -508,7 +508,11 @@ moe_status_t forward_impl(moe_layer_t* L, const void* hidden, int32_t T, void* o
   const size_t es = L->dim.dtype == MOE_DTYPE_BF16 ? 2 : 4;
   const size_t bytes = (size_t)T * L->dim.d * es;
   const uintptr_t h0 = reinterpret_cast<uintptr_t>(hidden), o0 = reinterpret_cast<uintptr_t>(out);
-  if (h0 < o0 + bytes && o0 < h0 + bytes)
+  // a one-layer stack pass in place: out, hidden and res are the same rows,
+  // and every element is read and rewritten by one lane of the layer's last
+  // kernel, after every read of the hidden rows (router, gather) has ended
+  const bool in_place = res != nullptr && out == hidden && res == hidden;
+  if (!in_place && h0 < o0 + bytes && o0 < h0 + bytes)
     return fail(MOE_ERR_INVALID_ARG, "out overlaps hidden");
   if (routing != nullptr) {
     const void* rp[] = {routing->sel, routing->gate, routing->counts, routing->offsets,

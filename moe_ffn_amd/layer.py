@@ -56,6 +56,19 @@ class RoutingOut(ctypes.Structure):
                 ("scatter", ctypes.c_void_p)]
 
 
+def _out_like(hidden: torch.Tensor, out: torch.Tensor | None) -> torch.Tensor:
+    """A new output tensor like `hidden`, or `out` if it has hidden's shape,
+    dtype and device and is contiguous (the library writes T * d elements
+    through its pointer and cannot check its size)."""
+    if out is None:
+        return torch.empty_like(hidden)
+    if not (out.shape == hidden.shape and out.dtype == hidden.dtype
+            and out.device == hidden.device and out.is_contiguous()):
+        raise ValueError(f"out: need a contiguous {hidden.dtype} tensor of shape "
+                         f"{tuple(hidden.shape)} on {hidden.device}")
+    return out
+
+
 class MoELayerError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
@@ -240,8 +253,7 @@ class MoELayer:
                 and hidden.shape[1] == self.d and hidden.is_contiguous()):
             raise ValueError(f"hidden: need a contiguous CUDA {self.torch_dtype} tensor [T, {self.d}]")
         T = hidden.shape[0]
-        if out is None:
-            out = torch.empty_like(hidden)
+        out = _out_like(hidden, out)
         r = None
         rp = None
         if routing:
@@ -339,9 +351,7 @@ class MoEStack:
         if not (hidden.is_cuda and hidden.dtype == self.torch_dtype and hidden.dim() == 2
                 and hidden.shape[1] == self.d and hidden.is_contiguous()):
             raise ValueError(f"hidden: need a contiguous CUDA {self.torch_dtype} tensor [T, {self.d}]")
-        if out is None:
-            out = torch.empty_like(hidden)
-        return out
+        return _out_like(hidden, out)
 
     def forward(self, hidden: torch.Tensor, out: torch.Tensor | None = None, stream=None):
         out = self._io(hidden, out)

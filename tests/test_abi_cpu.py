@@ -157,3 +157,18 @@ def test_entry_points_reject_bad_handles_and_destroy_is_null_safe():
     assert lib.moe_layer_timing_stop(None, None, None) == layer.MOE_ERR_INVALID_ARG
     lib.moe_layer_destroy(None)
     lib.moe_layer_destroy(ctypes.addressof(bogus))  # wrong magic: ignored
+
+
+def test_binding_checks_caller_outputs():
+    """The binding refuses an `out` tensor the library would write past or
+    misread (it writes T * d elements through the pointer without a size)."""
+    import torch
+    from moe_ffn_amd.layer import _out_like
+    h = torch.zeros((8, 64), dtype=torch.bfloat16)
+    assert _out_like(h, None).shape == h.shape
+    ok = torch.empty_like(h)
+    assert _out_like(h, ok) is ok
+    for bad in (torch.zeros((7, 64), dtype=torch.bfloat16), torch.zeros((8, 64)),
+                torch.zeros((64, 8), dtype=torch.bfloat16).t()):
+        with pytest.raises(ValueError):
+            _out_like(h, bad)

@@ -283,3 +283,8 @@ def test_bad_arguments_raise():
     buf = torch.zeros(64 * 2048 + 8, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(MoELayerError):
         layer.forward(h, out=buf[1:1 + 64 * 2048].view(64, 2048))   # misaligned out
+    for bad in (torch.zeros((63, 2048), dtype=torch.bfloat16, device="cuda"),   # too few rows
+                torch.zeros((64, 2048), dtype=torch.float32, device="cuda"),    # wrong dtype
+                torch.zeros((2048, 64), dtype=torch.bfloat16, device="cuda").t()):  # strided
+        with pytest.raises(ValueError):
+            layer.forward(h, out=bad)

@@ -330,6 +330,28 @@ def test_eda_rejects_bad_rates_and_fp32_stacks():
     s32.close()
 
 
+@pytest.mark.parametrize("T", [32, 200])
+def test_stack_in_place(T):
+    """hidden_out may be hidden_in: in a one-layer stack the layer's last
+    kernel then reads each residual value and writes the sum in its place
+    (k = 1: the down projection; k = 2: the combine), on the weight streams
+    (T = 32) and on the tile path (T = 200); a longer stack ends in place."""
+    from moe_ffn_amd import MoEStack
+    inps = _small_stack_inputs(T)
+    layers = [make_layer(inp, max_tokens=T) for inp in inps]
+    h0 = to_torch(inps[0]["hidden"], "bf16")
+    for label, sub in (("k=1 layer", [layers[2]]), ("k=2 layer", [layers[4]]), ("six layers", layers)):
+        print(f"[case] in-place stack {label} T={T}", flush=True)
+        stack = MoEStack(sub, max_tokens=T)
+        want = stack.forward(h0)
+        h = h0.clone()
+        got = stack.forward(h, out=h)
+        torch.cuda.synchronize()
+        assert got.data_ptr() == h.data_ptr()
+        assert torch.equal(h.view(torch.int16), want.view(torch.int16)), label
+        stack.close()
+
+
 @pytest.mark.parametrize("T", [16, 100])
 def test_fp32_stack_matches_layer_loop(T):
     """fp32 layers keep a residual launch after each layer (bf16 layers add in
