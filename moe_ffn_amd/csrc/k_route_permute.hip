@@ -5,17 +5,20 @@
 // a = t*k + j are counting-sorted by expert so that every expert sees its rows
 // contiguously, with slots inside an expert in increasing a.
 //
-// Two launches over P groups of consecutive 64-wide chunks (P at most
-// kPermuteMaxGroups, each group one workgroup of four waves, each wave a
-// contiguous run of the group's chunks).  Ranks never come from the order of
-// atomics: within a chunk, the lanes holding the same expert are found with
-// log2(E) ballots (one per bit of the expert id), and a lane's rank is the
-// number of such peers below it.  The first launch counts each group's
-// assignments per expert; the second gives every group its bases: the
-// expert's offset (from the totals of all groups) plus the counts of the
-// groups before it, then of the waves before it in the group, then a running
-// base per wave across its chunks.  The result is deterministic and identical
-// to a stable sort by expert.
+// Ranks never come from the order of atomics: within a chunk of 64
+// assignments, the lanes holding the same expert are found with log2(E)
+// ballots (one per bit of the expert id), and a lane's rank is the number of
+// such peers below it.  Up to 8192 assignments one launch does it all
+// (k_route_fused: every workgroup counts all chunks itself and places four;
+// at 4096 assignments 5.0 us of event time against 10.0 for two launches, the
+// step 1.5-1.8 us shorter).  Larger batches take two launches over P groups of
+// consecutive chunks (P at most kPermuteMaxGroups, each group one workgroup of
+// four waves, each wave a contiguous run of the group's chunks): the first
+// counts each group's assignments per expert; the second gives every group
+// its bases: the expert's offset (from the totals of all groups) plus the
+// counts of the groups before it, then of the waves before it in the group,
+// then a running base per wave across its chunks.  Either way the result is
+// deterministic and identical to a stable sort by expert.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -23,6 +26,11 @@ namespace moe {
 
 namespace {
 constexpr int kPB = 16;  // 64-wide chunks whose expert ids are loaded together
+// one-launch form: waves per workgroup, chunks placed per workgroup, and the
+// most chunks it takes (8192 assignments: each wave counts at most 8 chunks;
+// at 16384 assignments the redundant counting made the step no faster than
+// the two launches)
+constexpr int kFusedWaves = 16, kFusedCpg = 4, kFusedMaxChunks = 128;
 
 // Expert ids of chunks cb .. cb+kPB-1 for this lane; indexes past the end are
 // clamped (their values are ignored), so every load stays in bounds.
@@ -85,6 +93,38 @@ __device__ __forceinline__ void count_part(const int* __restrict__ sel, int n, i
   }
 }
 
+// Slots of this wave's chunks from its running bases base[EP] (LDS).  All
+// lanes read their expert's base before the peer group's lowest lane advances
+// it (the write depends on the value read; one wave's LDS operations complete
+// in order).
+template <int EP>
+__device__ __forceinline__ void place_part(const int* __restrict__ sel, int n, int k, int E,
+                                           Part pt, int lane, int* base,
+                                           int* __restrict__ gather, int* __restrict__ scatter,
+                                           int* __restrict__ slot_expert) {
+  constexpr int NB = ilog2(EP);
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int cb = pt.c0; cb < pt.c1; cb += kPB) {
+    int v[kPB];
+    load_batch(sel, n, cb, lane, v);
+#pragma unroll
+    for (int j = 0; j < kPB; ++j) {
+      if (cb + j >= pt.c1) break;
+      const int a = (cb + j) * 64 + lane;
+      const int my = expert_of(v[j], cb + j, lane, n, E);
+      const uint64_t peers = peers_of<NB>(my);
+      if (my >= 0) {
+        const int b = base[my];
+        const int pos = b + __popcll(peers & below);
+        gather[pos] = a / k;
+        scatter[a] = pos;
+        slot_expert[pos] = my;
+        if ((peers & below) == 0) base[my] = b + __popcll(peers);
+      }
+    }
+  }
+}
+
 // Launch 1: hist[g][e] = assignments of group g routed to expert e.
 template <int EP>
 __global__ __launch_bounds__(256) void k_route_hist(const int* __restrict__ sel, int n, int E,
@@ -105,7 +145,6 @@ __global__ __launch_bounds__(256) void k_route_place(
     const int* __restrict__ sel, int n, int k, int E, int cpg, const int* __restrict__ hist,
     int* __restrict__ counts, int* __restrict__ offsets, int* __restrict__ gather,
     int* __restrict__ scatter, int* __restrict__ slot_expert) {
-  constexpr int NB = ilog2(EP);
   constexpr int G = 256 / EP;  // thread groups that split the group axis
   __shared__ int part_tot[G][EP], part_pre[G][EP];
   __shared__ int wc[4][EP];    // per-wave counts, then per-wave running bases
@@ -113,7 +152,6 @@ __global__ __launch_bounds__(256) void k_route_place(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nchunks = (n + 63) / 64;
   const int P = gridDim.x, g = blockIdx.x;
-  const uint64_t below = (1ull << lane) - 1ull;
 
   {  // totals over all groups and over the groups before this one
     const int e = tid % EP, gi = tid / EP;
@@ -159,35 +197,96 @@ __global__ __launch_bounds__(256) void k_route_place(
     }
   }
   __syncthreads();
-  // slots.  All lanes read their expert's base before the group's lowest
-  // lane advances it (the write depends on the value read; one wave's LDS
-  // operations complete in order).
-  for (int cb = pt.c0; cb < pt.c1; cb += kPB) {
-    int v[kPB];
-    load_batch(sel, n, cb, lane, v);
+  place_part<EP>(sel, n, k, E, pt, lane, wc[wave], gather, scatter, slot_expert);
+}
+
+// One launch for up to kFusedMaxChunks chunks: workgroup g places chunks
+// 4g .. 4g+3 (one per wave), and first counts every chunk itself, its 16
+// waves taking the chunks in turn: per wave the totals per expert, the counts
+// of the chunks before its group, and each own chunk's counts, so no
+// histogram of the other groups is needed.  (One workgroup placing every
+// chunk took 8.2 us at 4096 assignments and 18.9 us at 16384: its scattered
+// stores all go through one CU; here they spread over the groups.)
+template <int EP>
+__global__ __launch_bounds__(kFusedWaves * 64) void k_route_fused(
+    const int* __restrict__ sel, int n, int k, int E, int* __restrict__ counts,
+    int* __restrict__ offsets, int* __restrict__ gather, int* __restrict__ scatter,
+    int* __restrict__ slot_expert) {
+  constexpr int NB = ilog2(EP);
+  __shared__ int tot[kFusedWaves][EP], pre[kFusedWaves][EP];
+  __shared__ int own[kFusedCpg][EP];  // own chunks' counts, then their running bases
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nchunks = (n + 63) / 64;
+  const int c0 = blockIdx.x * kFusedCpg, c1 = min(nchunks, c0 + kFusedCpg);
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int i = tid; i < kFusedWaves * EP; i += kFusedWaves * 64) {
+    tot[i / EP][i % EP] = 0;
+    pre[i / EP][i % EP] = 0;
+  }
+  if (tid < kFusedCpg * EP) own[tid / EP][tid % EP] = 0;
+  __syncthreads();
+  for (int cb = wave; cb < nchunks; cb += kFusedWaves * kPB) {
+    int v[kPB];  // chunks cb + 16 j; indexes past the end are clamped and ignored
+#pragma unroll
+    for (int j = 0; j < kPB; ++j) v[j] = sel[min((cb + kFusedWaves * j) * 64 + lane, n - 1)];
 #pragma unroll
     for (int j = 0; j < kPB; ++j) {
-      if (cb + j >= pt.c1) break;
-      const int a = (cb + j) * 64 + lane;
-      const int my = expert_of(v[j], cb + j, lane, n, E);
+      const int c = cb + kFusedWaves * j;
+      if (c >= nchunks) break;
+      const int my = expert_of(v[j], c, lane, n, E);
       const uint64_t peers = peers_of<NB>(my);
-      if (my >= 0) {
-        const int b = wc[wave][my];
-        const int pos = b + __popcll(peers & below);
-        gather[pos] = a / k;
-        scatter[a] = pos;
-        slot_expert[pos] = my;
-        if ((peers & below) == 0) wc[wave][my] = b + __popcll(peers);
+      if (my >= 0 && (peers & below) == 0) {
+        const int pc = __popcll(peers);
+        atomicAdd(&tot[wave][my], pc);
+        if (c < c0) atomicAdd(&pre[wave][my], pc);
+        else if (c < c1) atomicAdd(&own[c - c0][my], pc);
       }
     }
   }
+  __syncthreads();
+  if (wave == 0) {  // offsets: exclusive scan of the totals over the experts (EP <= 64)
+    int t = 0, b = 0;
+    if (lane < EP)
+      for (int w = 0; w < kFusedWaves; ++w) {
+        t += tot[w][lane];
+        b += pre[w][lane];
+      }
+    int inc = t;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += u;
+    }
+    if (blockIdx.x == 0 && lane < E) {
+      counts[lane] = t;
+      offsets[lane] = inc - t;
+    }
+    if (blockIdx.x == 0 && lane == E - 1) offsets[E] = inc;
+    if (lane < EP) {  // each own chunk's first slot per expert
+      int base = inc - t + b;
+      for (int j = 0; j < kFusedCpg; ++j) {
+        const int v = own[j][lane];
+        own[j][lane] = base;
+        base += v;
+      }
+    }
+  }
+  __syncthreads();
+  if (wave < c1 - c0)
+    place_part<EP>(sel, n, k, E, Part{c0 + wave, c0 + wave + 1}, lane, own[wave], gather, scatter,
+                   slot_expert);
 }
 
 namespace {
-// Groups of at least four chunks (one per wave), at most kPermuteMaxGroups.
+// One launch up to kFusedMaxChunks chunks; beyond, groups of at least four
+// chunks (one per wave), at most kPermuteMaxGroups.
 template <int EP>
 hipError_t launch_ep(const FwdArgs& a) {
   const int nchunks = (a.n + 63) / 64;
+  if (nchunks <= kFusedMaxChunks)
+    return launch(k_route_fused<EP>, dim3((nchunks + kFusedCpg - 1) / kFusedCpg),
+                  dim3(kFusedWaves * 64), a.stream, a.ev[kSlotPermute], a.sel, a.n, a.dim.k,
+                  a.dim.E, a.counts, a.offsets, a.gather, a.scatter, a.slot_expert);
   int cpg = 4;
   if ((nchunks + cpg - 1) / cpg > kPermuteMaxGroups)
     cpg = (nchunks + kPermuteMaxGroups - 1) / kPermuteMaxGroups;
