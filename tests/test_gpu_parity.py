@@ -221,6 +221,24 @@ def test_permutation_over_many_groups(E, k, T):
     assert st["rows_compared"] == T
 
 
+@pytest.mark.parametrize("E,k,T", [
+    (64, 2, 4096),   # 8192 assignments: exactly 128 chunks, the largest one-launch batch
+    (40, 3, 2730),   # 8190: one launch, ragged last chunk, 40 experts (64 padded)
+    (5, 1, 389),     # 7 chunks: the second workgroup places three
+    (64, 1, 8193),   # one assignment past the one-launch limit: two launches
+])
+def test_permutation_one_launch_and_its_limit(E, k, T):
+    """The one-launch permutation (every workgroup counts all chunks, places
+    four) up to its limit and the two-launch form just past it: dispatch
+    arrays and output rows in full."""
+    cfg = LayerConfig(94, f"perm_bf16_E{E}_k{k}_T{T}", T=T, d=256, E=E, F=256, k=k,
+                      dtype="bf16", bias="normal", family=f"groups_bf16_d256_E{E}_F256")
+    inp = make_inputs(cfg)
+    print(f"[case] {cfg.name}", flush=True)
+    st = check_parity(inp, make_layer(inp, max_tokens=T), label=cfg.name)
+    assert st["rows_compared"] == T
+
+
 def test_deterministic_bytes():
     inp = make_inputs(3, T=1000)
     layer = family_layer(3)
