@@ -36,6 +36,7 @@ import json
 import os
 import sys
 import time
+import warnings
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -487,10 +488,15 @@ def make_layers(inp, n: int, fp8: bool, dev, act8: bool = False):
         from synth.gen import fp8_expert_weights
         q8 = fp8_expert_weights(inp)
 
+    def host(a):  # read-only cached inputs: the tensor is only read, for the copy
+        with warnings.catch_warnings():
+            warnings.filterwarnings("ignore", message="The given NumPy array is not writable")
+            return torch.from_numpy(a)
+
     def tt(a, bf16=True):
         if bf16 and a.dtype == np.uint16:
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+            return host(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return host(np.ascontiguousarray(a, np.float32)).to(dev)
 
     w = {"rms_gain": tt(inp["gain"]), "w_router": tt(inp["w_router"]),
          "b_router": tt(inp["bias"], False)}
@@ -498,7 +504,7 @@ def make_layers(inp, n: int, fp8: bool, dev, act8: bool = False):
     if q8 is None:
         w.update({n_: tt(inp[n_]) for n_ in ("w_gate", "w_up", "w_down")})
     else:
-        w.update({n_: torch.from_numpy(q8[n_]).to(dev) for n_ in ("w_gate", "w_up", "w_down")})
+        w.update({n_: host(q8[n_]).to(dev) for n_ in ("w_gate", "w_up", "w_down")})
         scales = {n_: tt(q8["s_" + n_], False) for n_ in ("gate", "up", "down")}
     layers = [MoELayer(cfg.d, cfg.F, cfg.E, cfg.k, cfg.dtype, w, cfg.T, rms_eps=cfg.eps,
                        fp8_scales=scales, fp8_act=act8)

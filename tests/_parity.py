@@ -15,6 +15,8 @@ protocol:
 
 from __future__ import annotations
 
+import warnings
+
 import numpy as np
 import torch
 
@@ -25,10 +27,18 @@ TOL = {"bf16": 2e-2, "f32": 1e-5}
 GATE_TOL = 2e-5
 
 
+def _host(arr: np.ndarray) -> torch.Tensor:
+    """A CPU tensor over `arr` (read-only cached inputs included: the tensor is
+    only read, for the copy to the device)."""
+    with warnings.catch_warnings():
+        warnings.filterwarnings("ignore", message="The given NumPy array is not writable")
+        return torch.from_numpy(arr)
+
+
 def to_torch(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
     if dtype == "bf16" and arr.dtype == np.uint16:
-        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device).view(torch.bfloat16)
-    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+        return _host(np.ascontiguousarray(arr).view(np.int16)).to(device).view(torch.bfloat16)
+    return _host(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
 
 
 def device_weights(inputs: dict) -> dict:
