@@ -67,6 +67,10 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
   __shared__ float ssr[NW][TT][64];
   __shared__ float mxr[NW][TT][64];
   __shared__ float zs[NTOK][EPAD + 1];
+  // each wave's gain for its current batch of k-steps (kRBatch x 4 k-groups of
+  // 8 values): loaded once per batch and read back by the 16 lanes sharing a
+  // k-group, instead of one copy per lane from memory
+  __shared__ u32x4 gsh[NW][kRBatch * 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * NTOK;
@@ -136,20 +140,23 @@ __global__ __launch_bounds__(NW * 64) void k_router_mfma(
   };
 
   int s = 0;
+  const uint16_t* gw = gain + k0 + lane * 8;  // lanes 0 .. 4 kRBatch - 1: a batch's gain
   for (; s + kRBatch <= kper; s += kRBatch) {
-    u32x4 gv[kRBatch], av[kRBatch][NA], hv[kRBatch][TT];
+    u32x4 av[kRBatch][NA], hv[kRBatch][TT];
+    u32x4 gb = {0u, 0u, 0u, 0u};
+    if (lane < kRBatch * 4) gb = ldg16(gw + s * kRK);
 #pragma unroll
     for (int b = 0; b < kRBatch; ++b) {
       const int ko = (s + b) * kRK;
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) hv[b][tt] = ldg16(hp[tt] + ko);
-      gv[b] = ldg16(gp + ko);
 #pragma unroll
       for (int a = 0; a < NA; ++a) av[b][a] = ldg16(ap[a] + ko);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the whole batch of loads in flight together
+    if (lane < kRBatch * 4) gsh[wave][lane] = gb;  // one wave's LDS operations run in order
 #pragma unroll
-    for (int b = 0; b < kRBatch; ++b) step(gv[b], av[b], hv[b]);
+    for (int b = 0; b < kRBatch; ++b) step(gsh[wave][b * 4 + (lane >> 4)], av[b], hv[b]);
   }
   for (; s < kper; ++s) {
     const int ko = s * kRK;
