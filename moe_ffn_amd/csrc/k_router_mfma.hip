@@ -335,7 +335,9 @@ hipError_t go(const FwdArgs& a) {
 }  // namespace
 
 // One 16-token tile per workgroup: at 16384 tokens two tiles per workgroup
-// (half the workgroups) measured 6% slower.
+// (half the workgroups, each reading the router rows once for 32 tokens)
+// measured 6% slower, and again with the gain staged in LDS: 25.0 against
+// 21.8 us.
 hipError_t launch_router_mfma(const FwdArgs& a) {
   const int E = a.dim.E;
   return E > 32 ? go<4, 1>(a) : E > 16 ? go<2, 1>(a) : go<1, 1>(a);
