@@ -36,7 +36,6 @@ __global__ __launch_bounds__(256) void k_gather_tiles(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ gain,
                                                       const float* __restrict__ inv,
                                                       const int* __restrict__ counts,
-                                                      const int* __restrict__ offsets,
                                                       const int* __restrict__ gather, int E, int d,
                                                       uint16_t* __restrict__ xt,
                                                       const float* __restrict__ xs_tok,
@@ -45,14 +44,30 @@ __global__ __launch_bounds__(256) void k_gather_tiles(const uint16_t* __restrict
   const int groups = d / 64;
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);  // wave of the grid
   const int P = gw / groups, g = gw - (gw / groups) * groups;
-  int e = 0, base = 0;
-  for (; e < E; ++e) {
-    const int ns = (counts[e] + 31) >> 5;
-    if (P < base + ns) break;
-    base += ns;
+  // the subtile's expert: the experts' counts eight at a time (all eight
+  // scalar loads in flight together), with running sums of their subtiles and
+  // of their slots (the expert's first slot, so offsets is not read)
+  int e = -1, base = 0, off = 0, cnt = 0;
+  for (int e0 = 0; e0 < E && e < 0; e0 += 8) {
+    int c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = counts[min(e0 + j, E - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (e < 0 && e0 + j < E) {
+        const int ns = (c[j] + 31) >> 5;
+        if (P < base + ns) {
+          e = e0 + j;
+          cnt = c[j];
+        } else {
+          base += ns;
+          off += c[j];
+        }
+      }
+    }
   }
-  if (e >= E) return;  // past the last subtile (no barrier in this kernel)
-  const int r0 = (P - base) * 32, cnt = counts[e], off = offsets[e];
+  if (e < 0) return;  // past the last subtile (no barrier in this kernel)
+  const int r0 = (P - base) * 32;
   const int lane = threadIdx.x & 63;
   uint16_t* dst = Q8 ? nullptr : xt + (size_t)P * (d / kKStep) * kBlockElems;
   u32x4 v[4];
@@ -118,7 +133,7 @@ hipError_t launch_gather_tiles(const FwdArgs& a) {
   return launch(a.dim.act8 ? k_gather_tiles<true> : k_gather_tiles<false>, dim3((waves + 3) / 4),
                 dim3(256), a.stream, a.ev[kSlotGather], (const uint16_t*)a.hidden,
                 (const uint16_t*)a.gain16, (const float*)a.inv, (const int*)a.counts,
-                (const int*)a.offsets, (const int*)a.gather, a.dim.E, a.dim.d, (uint16_t*)a.xt,
+                (const int*)a.gather, a.dim.E, a.dim.d, (uint16_t*)a.xt,
                 (const float*)a.xs_tok, (uint8_t*)a.xq, a.sx);
 }
 
