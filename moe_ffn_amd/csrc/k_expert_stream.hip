@@ -117,6 +117,53 @@ __device__ __forceinline__ Route small_dispatch(const int* __restrict__ sel, int
   return {sh[0], sh[1]};
 }
 
+// Token operands of the fp8 weight streams: the lane's 16 bytes of k-step ks.
+// BGlobal reads them from the token's row in memory (zrow for lanes without a
+// token).  BLds reads the wave's LDS copy of its k-range of the pass's token
+// rows (stage_b); lanes without a token read the wave's zero piece at stride
+// 0, so no branch or select sits between an LDS read and its MFMA.  With half
+// the weight bytes per k-step, the fp8 gate/up stream is the one these loads
+// slow: a timing copy without any token loads ran it in 24.8 instead of 26.3
+// us; staging them in LDS, 25.9 (the fp8 down stream, whose waves stream
+// fewer k-steps, and the bf16 streams were no faster with it).
+struct BGlobal {
+  const uint16_t* xb;  // the lane's row, k-group offset applied
+  __device__ __forceinline__ u32x4 operator()(int ks) const { return ldg16(xb + ks * kKStep); }
+};
+struct BLds {
+  const u32x4* b;  // the lane's piece (token, k-step ks0, k-group), or the zero piece
+  int ks0, step;   // step: 2 pieces per k-step, 0 for the zero piece
+  __device__ __forceinline__ u32x4 operator()(int ks) const { return b[(ks - ks0) * step]; }
+};
+
+// LDS pieces a wave can stage for one pass (its slice of the split-K buffer,
+// idle during the stream): 256 x 16 bytes per accumulator tile.
+constexpr int kStagePieces = 256;
+
+// Copy the wave's k-range [ks0, ks0 + kper) of ntok token rows (row t starts at
+// rowp(t)) into bl: piece (t, s, g), the 8 values k = 16 (ks0 + s) + 8 g .. +7,
+// at bl[(t * kper + s) * 2 + g]; ntok * 2 * kper <= NP pieces.  Branch-free:
+// lanes past the last piece load and store the last piece again (the same
+// bytes), so all loads issue together behind the weights in flight.  The same
+// wave reads the pieces back (one wave's LDS operations run in order).
+template <int NP, class RowP>
+__device__ __forceinline__ void stage_b(u32x4* bl, const RowP& rowp, int ntok, int ks0, int kper,
+                                        int lane) {
+  const int per = 2 * kper, total = ntok * per;
+  int c[NP / 64];
+  const uint16_t* src[NP / 64];
+#pragma unroll
+  for (int it = 0; it < NP / 64; ++it) {
+    c[it] = min(lane + 64 * it, total - 1);
+    src[it] = rowp(c[it] / per) + (size_t)ks0 * kKStep + (c[it] % per) * 8;
+  }
+  u32x4 v[NP / 64];
+#pragma unroll
+  for (int it = 0; it < NP / 64; ++it) v[it] = ldg16(src[it]);
+#pragma unroll
+  for (int it = 0; it < NP / 64; ++it) bl[c[it]] = v[it];
+}
+
 // Rolling prefetch over `kper` k-steps (a multiple of D): D k-steps of
 // operands are always in flight while the oldest one is multiplied.
 // NW weight streams share one activation operand per k-step.
@@ -152,17 +199,21 @@ __device__ __forceinline__ void stream_mac(const uint16_t* const (&w)[NW], const
 // The same stream over an fp8 (E4M3) bank: each 16-byte load of a lane holds
 // its codes for two consecutive k-steps (k-step pairs p, 1 KiB per wave-wide
 // load), converted exactly to bf16 operands in registers; D2 pairs in flight.
-template <int D2, int NW>
-__device__ __forceinline__ void stream_mac_fp8(const uint8_t* const (&w)[NW], const uint16_t* xb,
-                                               int ks0, int kper, f32x16 (&acc)[NW]) {
+template <int D2, int NW, class BS, class Pre>
+__device__ __forceinline__ void stream_mac_fp8(const uint8_t* const (&w)[NW], const BS& xb,
+                                               int ks0, int kper, f32x16 (&acc)[NW],
+                                               const Pre& pre) {
   u32x4 qw[NW][D2], qx[D2][2];
   const int p0 = ks0 / 2;
 #pragma unroll
-  for (int i = 0; i < D2; ++i) {
+  for (int i = 0; i < D2; ++i)
 #pragma unroll
     for (int j = 0; j < NW; ++j) qw[j][i] = ldw8(w[j] + (size_t)(p0 + i) * 1024);
-    qx[i][0] = ldg16(xb + (ks0 + 2 * i) * kKStep);
-    qx[i][1] = ldg16(xb + (ks0 + 2 * i + 1) * kKStep);
+  pre();  // with the first weights in flight (the LDS form stages its token rows here)
+#pragma unroll
+  for (int i = 0; i < D2; ++i) {
+    qx[i][0] = xb(ks0 + 2 * i);
+    qx[i][1] = xb(ks0 + 2 * i + 1);
   }
   const int rounds = kper / (2 * D2);
   for (int r = 1; r < rounds; ++r) {
@@ -176,8 +227,9 @@ __device__ __forceinline__ void stream_mac_fp8(const uint8_t* const (&w)[NW], co
       }
 #pragma unroll
       for (int j = 0; j < NW; ++j) qw[j][i] = ldw8(w[j] + (size_t)(pn + i) * 1024);
-      qx[i][0] = ldg16(xb + 2 * (pn + i) * kKStep);
-      qx[i][1] = ldg16(xb + (2 * (pn + i) + 1) * kKStep);
+      qx[i][0] = xb(2 * (pn + i));
+      qx[i][1] = xb(2 * (pn + i) + 1);
+      __builtin_amdgcn_sched_barrier(0);  // refill each slot right after its multiplies
     }
   }
 #pragma unroll
@@ -205,8 +257,10 @@ __global__ __launch_bounds__(64 * S, 1) void k_gateup_stream(
   __shared__ float red[S * NT * 16 * 64];
   __shared__ int list[64];
   __shared__ int sh[2];
+  __shared__ u32x4 zp[S];  // fp8: each wave's zero token piece
   const int e = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (FP8 && lane == 0) zp[wave] = u32x4{0u, 0u, 0u, 0u};
   const Route rt = small_dispatch(sel, n, k, E, e, lane, wave, list, sh, blockIdx.x == 0, counts,
                                   offsets, gather, scatter);
   const int cnt = rt.cnt, off = rt.off;
@@ -256,8 +310,21 @@ __global__ __launch_bounds__(64 * S, 1) void k_gateup_stream(
     for (int q = 0; q < NT; ++q)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[q][i] = 0.f;
-    if constexpr (FP8) stream_mac_fp8<D, NT>(wp8, xrow, ks0, kper, acc);
-    else stream_mac<D, NT>(wp, xrow, ks0, kper, acc);
+    if constexpr (FP8) {
+      if (ntok * 2 * kper <= NT * kStagePieces) {  // token operands from LDS
+        u32x4* bl = reinterpret_cast<u32x4*>(red + wave * NT * 16 * 64);
+        const auto pre = [&] {
+          stage_b<NT * kStagePieces>(
+              bl, [&](int t) { return xn + (size_t)list[c0 + t] * d; }, ntok, ks0, kper, lane);
+        };
+        const BLds bs{valid ? bl + col * 2 * kper + (lane >> 5) : zp + wave, ks0, valid ? 2 : 0};
+        stream_mac_fp8<D, NT>(wp8, bs, ks0, kper, acc, pre);
+      } else {
+        stream_mac_fp8<D, NT>(wp8, BGlobal{xrow}, ks0, kper, acc, [] {});
+      }
+    } else {
+      stream_mac<D, NT>(wp, xrow, ks0, kper, acc);
+    }
     stash<NT>(acc, red, wave, lane);
     __syncthreads();
     // gate(f) is element i of tile q, up(f) element i + 8, f = 16 (NT ft + q) +
@@ -341,7 +408,7 @@ __global__ __launch_bounds__(64 * SD, 1) void k_down_stream(
     f32x16 acc[1];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[0][i] = 0.f;
-    if constexpr (FP8) stream_mac_fp8<D, 1>(wp8, arow, ks0, kper, acc);
+    if constexpr (FP8) stream_mac_fp8<D, 1>(wp8, BGlobal{arow}, ks0, kper, acc, [] {});
     else stream_mac<D, 1>(wp, arow, ks0, kper, acc);
     stash<1>(acc, red, wave, lane);
     __syncthreads();
