@@ -4,7 +4,8 @@
 unpadded), top-k 1 to 8, d_model 256 to 768, d_ff 128 to 512, batch sizes from
 one token through the weight streams (T*k <= 64) to the tile GEMMs, zero and
 normal router biases; bf16 layers, E4M3 weights (R18) and E4M3 weights with
-E4M3 activations (R20).  Each case runs the full parity protocol of
+E4M3 activations (R20); and 8 fp32 layers whose d_model and d_ff are any
+multiple of 4 (4 to 800).  Each case runs the full parity protocol of
 tests/_parity.py against the oracle: routing and dispatch arrays in full,
 every output row.
 """
@@ -36,6 +37,18 @@ def _cases(n=36, seed=20261204):
     return out
 
 
+def _f32_cases(n=8, seed=9):
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        E = rng.choice([1, 2, 3, 4, 7, 16, 33, 64])
+        k = 1 if E == 1 else rng.randint(1, min(8, E))
+        d, F = 4 * rng.randint(1, 200), 4 * rng.randint(1, 200)
+        T = rng.choice([1, 2, 7, 31, 64, 65, 200, 1000])
+        out.append((T, d, E, F, k, rng.choice(["normal", "zero"]), i))
+    return out
+
+
 @pytest.fixture(scope="module", autouse=True)
 def _need_gpu():
     if not torch.cuda.is_available():
@@ -59,5 +72,17 @@ def test_random_shape_parity(mode, T, d, E, F, k, bias, i):
     else:
         layer = w8a8_layer(inp, T)
         st = check_parity(inp, layer, vals=fp8_vals(inp), fp8_act=True, label=cfg.name)
+    assert st["rows_compared"] == T
+    layer.close()
+
+
+@pytest.mark.parametrize("T,d,E,F,k,bias,i", _f32_cases())
+def test_random_fp32_shape_parity(T, d, E, F, k, bias, i):
+    cfg = LayerConfig(980 + i, f"random_f32_{i}_T{T}_d{d}_E{E}_F{F}_k{k}", T=T, d=d, E=E, F=F,
+                      k=k, dtype="f32", bias=bias, family=f"random_f32_{i}")
+    print(f"[case] {cfg.name} bias={bias}", flush=True)
+    inp = make_inputs(cfg)
+    layer = make_layer(inp, max_tokens=T)
+    st = check_parity(inp, layer, label=cfg.name)
     assert st["rows_compared"] == T
     layer.close()
