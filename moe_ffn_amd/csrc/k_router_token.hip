@@ -22,8 +22,9 @@
 // instead of x': the row's scale a = max_i |u_i| / 448 of u = bf16(inv_rms *
 // x') is bf16(inv_rms * max_i |x'_i|) / 448 (both roundings are monotone), so
 // the first pass also tracks max |x'|; a second pass over the row (its first
-// 2048 values from registers, the rest from cache) writes the E4M3 values of u (quant4_e4m3, exact in bf16) and xs[t] = a.  The
-// weight streams then multiply exact code values and scale the sums by a.
+// 2048 values from registers, the rest from cache) writes the E4M3 values of
+// u (quant4_e4m3, exact in bf16) and xs[t] = a.  The weight streams then
+// multiply exact code values and scale the sums by a.
 #include "common.hpp"
 #include "kernels.hpp"
 
