@@ -12,9 +12,9 @@
 // Work unit: (expert, block of 128*RT weight rows, span of at most 32*cap of
 // the expert's slots; cap <= TTM, chosen per launch on the host, TTM = 5 for
 // gate/up and 6 for down).  An expert's slots are cut into the fewest spans of
-// at most cap 32-token subtiles, split evenly; the spans of one weight block
-// are adjacent in the unit order, so they run together under one L2 and the
-// block comes from HBM once.
+// at most cap 32-token subtiles, split evenly; units are ordered so that the
+// ones running together on an XCD share a few weight blocks and a few token
+// spans, each brought into that XCD's L2 once.
 //
 // Workgroup (OCC per CU, 1 by default): four waves, one per SIMD, stacked
 // along the weight rows; a wave
@@ -68,6 +68,8 @@ namespace {
 constexpr int kSub = 32;      // tokens per MFMA subtile
 constexpr int kBK = 4;        // k-steps (of 16) per token stage
 constexpr int kBStages = 3;   // LDS token stages
+// Weight blocks per group of the unit order, for an expert with ns spans.
+__host__ __device__ constexpr int grp_width(int ns) { return ns >= 8 ? 4 : 1; }
 // 16-byte LDS entries of one token stage of a unit with TT subtiles
 template <int TT>
 constexpr int stage_ent() { return TT * kBK * 64; }
@@ -297,8 +299,14 @@ __device__ __forceinline__ void mainloop(const Ctx<RT, TT>& c, u32x4* lds, f32x1
   }
 }
 
-// Work units.  Units are numbered expert-major, then weight block, then span
-// (the spans sharing a weight block are adjacent).  The grid is persistent,
+// Work units.  Units are numbered expert-major; inside an expert, its weight
+// blocks are taken in groups of kGrp, and a group's units are numbered
+// span-major (span 0 of the group's blocks, then span 1, ...).  A round of an
+// XCD's workgroups, which walk K nearly in lockstep, then covers a few weight
+// blocks against several token spans, so that each block and each span is
+// pulled into the XCD's L2 once per round: 32 units of the hottest expert of
+// a skewed batch touch 4 blocks and 8 spans rather than 1 block and 32 spans
+// (half the bytes from beyond L2).  The grid is persistent,
 // one workgroup per CU: the unit list is cut into 8 contiguous ranges, one per
 // XCD (workgroup b runs on XCD b % 8), so that units sharing weights or token
 // rows run at the same time under one L2; inside a range the XCD's workgroups
@@ -361,10 +369,13 @@ __device__ __forceinline__ void decode_unit(const ExpTab& tab, int nrb, int L, U
   const int ns = __builtin_amdgcn_readfirstlane(tab.sp[e]);
   const int nsub = __builtin_amdgcn_readfirstlane(tab.ns[e]);
   const int r = L - __builtin_amdgcn_readfirstlane(tab.ubase[e]);
-  const int sp = r % ns;
+  const int G = grp_width(ns);
+  const int g = r / (G * ns), i = r - g * G * ns;  // block group, unit inside it
+  const int gw = min(G, nrb - g * G);              // blocks in the group
+  const int sp = i / gw;
   const int s0 = sp * nsub / ns, s1 = (sp + 1) * nsub / ns;
   u.e = e;
-  u.rb = r / ns;
+  u.rb = g * G + i % gw;
   u.slot0 = __builtin_amdgcn_readfirstlane(tab.off[e]) + s0 * kSub;
   u.nrows = min(__builtin_amdgcn_readfirstlane(tab.cnt[e]), s1 * kSub) - s0 * kSub;
   u.nsub = s1 - s0;
@@ -647,9 +658,11 @@ int span_cap(int n, int E, int nrb, int grid, int TTM) {
     cost.clear();
     for (int e = 0; e < E; ++e) {
       const int sp = (ns[e] + t - 1) / t;
-      for (int rb = 0; rb < nrb; ++rb)
+      const int G = grp_width(sp);
+      for (int g = 0; g < nrb; g += G)  // the kernel's order: block groups, span-major
         for (int q = 0; q < sp; ++q)
-          cost.push_back((uint8_t)(2 + (q + 1) * ns[e] / sp - q * ns[e] / sp));
+          for (int rb = g; rb < std::min(nrb, g + G); ++rb)
+            cost.push_back((uint8_t)(2 + (q + 1) * ns[e] / sp - q * ns[e] / sp));
     }
     const int U = (int)cost.size(), per = (U + 7) / 8;
     long long mx = 0;
