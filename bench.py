@@ -119,7 +119,7 @@ def ingest_counters(pmc_dir: str) -> None:
     --copy-calibration 1024 under --pmc FETCH_SIZE, resp. WRITE_SIZE) and
     pmc_dir/c<N>_fetch, pmc_dir/c<N>_write for each --config N profiled
     (c<N>fp8_fetch, c<N>fp8_write for --config N --fp8; c<N>w8a8_* for
-    --w8a8).  Each
+    --w8a8); the entries of workloads it does not hold are kept.  Each
     counter is scaled by the bytes the copy kernel really moves over what the
     same counter reads for it."""
     from synth.configs import WORKLOADS
@@ -127,9 +127,14 @@ def ingest_counters(pmc_dir: str) -> None:
     cf = _counter_means(os.path.join(pmc_dir, "copy_fetch"))["torch_neg"] * 1024
     cw = _counter_means(os.path.join(pmc_dir, "copy_write"))["torch_neg"] * 1024
     ffac, wfac = copy_bytes / cf, copy_bytes / cw
-    out = {"_calibration": {"copy_bytes_each_way": copy_bytes, "fetch_counter_bytes": cf,
-                            "write_counter_bytes": cw, "fetch_factor": round(ffac, 5),
-                            "write_factor": round(wfac, 5)}}
+    # workloads not profiled in this directory keep their earlier entries
+    out = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            out = json.load(f)
+    out["_calibration"] = {"copy_bytes_each_way": copy_bytes, "fetch_counter_bytes": cf,
+                           "write_counter_bytes": cw, "fetch_factor": round(ffac, 5),
+                           "write_factor": round(wfac, 5)}
     for cid, tag in [(c, t) for c in (0, 1, 2, 3, 4) for t in ("", "fp8", "w8a8")]:
         fd, wd = (os.path.join(pmc_dir, f"c{cid}{tag}_{x}") for x in ("fetch", "write"))
         if not (os.path.isdir(fd) and os.path.isdir(wd)):
@@ -183,10 +188,16 @@ def dominant_kernel(cfg, counts, fp8: bool = False, act8: bool = False):
                 "work_unit": "bytes"}
     per_assign = 2 * 2 * F * d                      # gate and up: 2 flops x F x d each
     work = n * per_assign
+    # the same launch's algorithmic HBM bytes: the touched experts' gate and up
+    # rows (fp8 banks: codes + row scales), each routed row's operand tile read
+    # once (E4M3 with fp8 activations) and its bf16 activations written once
+    wgu = 2 * F * d + 2 * F * 4 if act8 else 2 * F * d * 2
+    hbm = touched * wgu + n * d * (1 if act8 else 2) + n * F * 2
     return {"slot": "experts_gate_up", "kernel": "k_expert_gemm<0>", "bound": "mfma",
             "peak": PEAK_FP8_TFLOPS if act8 else PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "units": n, "per_unit": per_assign,
-            "unit_name": "routed assignment (gate+up flops)", "work": work, "work_unit": "flops"}
+            "unit_name": "routed assignment (gate+up flops)", "work": work, "work_unit": "flops",
+            "hbm_bytes": hbm}
 
 
 def layer_work(cfg, counts, fp8: bool = False):
@@ -551,11 +562,23 @@ def roofline_entry(dom: dict, dom_ms: float, traffic) -> dict:
         achieved, peak = dom["work"] / (dom_ms * 1e-3) / 1e9, PEAK_HBM_GBPS
     else:
         achieved, peak = dom["work"] / (dom_ms * 1e-3) / 1e12, dom.get("peak", PEAK_BF16_TFLOPS)
-    return {"bound": dom["bound"], "achieved": round(achieved, 2), "peak": peak,
-            "unit": dom["unit"], "frac": round(achieved / peak, 4), "traffic": traffic,
-            "kernel": dom["kernel"], "avg_launch_us": round(dom_ms * 1e3, 3),
-            "per_unit": dom["per_unit"], "units_per_launch": dom["units"],
-            "unit_name": dom["unit_name"]}
+    out = {"bound": dom["bound"], "achieved": round(achieved, 2), "peak": peak,
+           "unit": dom["unit"], "frac": round(achieved / peak, 4), "traffic": traffic,
+           "kernel": dom["kernel"], "avg_launch_us": round(dom_ms * 1e3, 3),
+           "per_unit": dom["per_unit"], "units_per_launch": dom["units"],
+           "unit_name": dom["unit_name"]}
+    if "hbm_bytes" in dom:
+        # a grouped GEMM with few tokens per expert can take longer to read its
+        # weights at the HBM peak than to do its flops at the MFMA peak: the
+        # roofline's bound is then HBM, and both sides are reported
+        gbps = dom["hbm_bytes"] / (dom_ms * 1e-3) / 1e9
+        t_mfma = dom["work"] / (peak * 1e12)
+        t_hbm = dom["hbm_bytes"] / (PEAK_HBM_GBPS * 1e9)
+        out["hbm_side"] = {"algorithmic_bytes": dom["hbm_bytes"], "achieved_GBps": round(gbps, 1),
+                           "peak_GBps": PEAK_HBM_GBPS, "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+        out["roofline_bound"] = "hbm" if t_hbm > t_mfma else "mfma"
+        out["roofline_frac"] = round(max(t_mfma, t_hbm) / (dom_ms * 1e-3), 4)
+    return out
 
 
 def counter_traffic(wname: str, kernel: str):
@@ -608,7 +631,9 @@ def prefill_summary(cid: int, args, dev, w8a8: bool = False) -> tuple[dict, dict
            "experts_touched": touched,
            "gemm_gate_up": {"kernel": dom["kernel"], "us": rl["avg_launch_us"],
                             "achieved": rl["achieved"], "unit": rl["unit"], "frac": rl["frac"],
-                            "traffic": rl["traffic"]},
+                            "traffic": rl["traffic"],
+                            **{k_: rl[k_] for k_ in ("hbm_side", "roofline_bound",
+                                                      "roofline_frac") if k_ in rl}},
            "kernel_us": {k_: round(v * 1e3, 3) for k_, v in slots.items()},
            "us_per_step_with_kernel_events": round(ms_ev * 1e3, 3)}
     log(f"[bench] {wname}: {out['us_per_step']:.1f} us/step, {out['tokens_per_s'] / 1e6:.2f} M "

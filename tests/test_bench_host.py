@@ -100,6 +100,9 @@ def test_counter_ingestion_scales_by_the_copy(tmp_path, monkeypatch):
     _write_run(tmp_path / "c1_fetch", [(gu, "FETCH_SIZE", 1000.0), (gu, "FETCH_SIZE", 1200.0)])
     _write_run(tmp_path / "c1_write", [(gu, "WRITE_SIZE", 10.0), (gu, "WRITE_SIZE", 10.0)])
     out = tmp_path / "traffic.json"
+    # an entry of a workload this directory does not profile is kept
+    out.write_text(json.dumps({WORKLOADS[4].name: {"kernel": "k_expert_gemm<0>",
+                                                   "bytes_per_launch": 7}}))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
     bench.ingest_counters(str(tmp_path))
     t = json.loads(out.read_text())
@@ -110,3 +113,4 @@ def test_counter_ingestion_scales_by_the_copy(tmp_path, monkeypatch):
     assert rec["source_hash"] == bench.kernel_source_hash("k_gateup_stream")
     # mean 1100 KiB read x 2 + 10 KiB written x 1
     assert rec["bytes_per_launch"] == round(1100 * 1024 * 2) + round(10 * 1024)
+    assert t[WORKLOADS[4].name]["bytes_per_launch"] == 7
