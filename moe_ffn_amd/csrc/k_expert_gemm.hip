@@ -80,13 +80,29 @@ struct Geo {
   static constexpr int kRows = kTiles * 32;
 };
 
+// Operand loads are raw buffer loads: a wave-uniform resource (base and byte
+// range in scalar registers) per operand, the k-step's byte offset as a
+// scalar offset and the lane's 16 bytes as the one vector offset all loads
+// share, so no load needs a 64-bit vector address.  The range is the unit's
+// own operand extent.
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer of 32-bit elements (gfx9 family)
+constexpr int kBlockBytes = kBlockElems * 2;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 ldb16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
 template <int RT, int TT>
 struct Ctx {
-  const uint16_t* wa;     // this wave's first weight tile (lane offset applied)
-  size_t tile_elems;      // elements of one packed 32-row tile
-  int ksteps;             // K / 16
-  const uint16_t* bsrc[TT];  // token blocks copied by this wave (stage 0, lane offset applied)
-  int bstep[TT];          // elements from one token stage to the next (0: zero block)
+  __amdgpu_buffer_rsrc_t wr;  // this wave's RT weight tiles
+  int tile_bytes;             // bytes of one packed 32-row tile
+  int ksteps;                 // 1 KiB blocks along K
+  __amdgpu_buffer_rsrc_t tr;  // the unit's token subtiles
+  int boff[TT];               // bytes from tr's base to this wave's stage-0 blocks
+  int voff;                   // the lane's 16 bytes of a block
   int wave, lane;
 };
 
@@ -94,16 +110,16 @@ template <int RT, int TT>
 __device__ __forceinline__ void load_a(const Ctx<RT, TT>& c, int ks, u32x4 (&q)[RT]) {
   const int s = ks < c.ksteps ? ks : c.ksteps - 1;  // clamp: surplus loads stay in bounds
 #pragma unroll
-  for (int r = 0; r < RT; ++r) q[r] = ldg16(c.wa + r * c.tile_elems + (size_t)s * kBlockElems);
+  for (int r = 0; r < RT; ++r) q[r] = ldb16(c.wr, c.voff, r * c.tile_bytes + s * kBlockBytes);
 }
 
-// Token stage st: blocks j = wave + 4q (subtile j / 4, k-step j % 4) of the
-// stage, at LDS entries j * 64 .. j * 64 + 63 of the stage buffer.
+// Token stage st: blocks j = wave + 4q (subtile q, k-step wave of the stage),
+// at LDS entries j * 64 .. j * 64 + 63 of the stage buffer.
 template <int RT, int TT>
 __device__ __forceinline__ void load_b(const Ctx<RT, TT>& c, int st, int nst, u32x4 (&p)[TT]) {
   const int s = st < nst ? st : nst - 1;
 #pragma unroll
-  for (int q = 0; q < TT; ++q) p[q] = ldg16(c.bsrc[q] + s * c.bstep[q]);
+  for (int q = 0; q < TT; ++q) p[q] = ldb16(c.tr, c.voff, c.boff[q] + s * kBK * kBlockBytes);
 }
 template <int RT, int TT>
 __device__ __forceinline__ void store_b(const Ctx<RT, TT>& c, u32x4* buf, const u32x4 (&p)[TT]) {
@@ -404,18 +420,19 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
   Ctx<RT, TT> c;
   c.wave = wave;
   c.lane = lane;
+  c.voff = lane * 16;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   c.ksteps = K / (F8 ? 2 * kKStep : kKStep);  // 1 KiB blocks along K
-  c.tile_elems = (size_t)c.ksteps * kBlockElems;
-  c.wa = wpk + ((size_t)u.e * (rows_e / kTileRows) + tile0) * c.tile_elems + lane * 8;
+  c.tile_bytes = c.ksteps * kBlockBytes;
+  c.wr = rsrc(reinterpret_cast<const char*>(wpk) +
+                  ((size_t)u.e * (rows_e / kTileRows) + u.rb * G::kTiles + wv * RT) *
+                      c.tile_bytes,
+              RT * c.tile_bytes);
+  // subtiles sub0 .. sub0 + TT - 1 of the unit (run_any gives TT == u.nsub)
+  c.tr = rsrc(reinterpret_cast<const char*>(src) + (size_t)u.sub0 * c.tile_bytes,
+              TT * c.tile_bytes);
 #pragma unroll
-  for (int q = 0; q < TT; ++q) {
-    const int j = wave + 4 * q;  // token block of the stage: subtile j / 4, k-step j % 4
-    const bool valid = (j >> 2) < u.nsub;
-    c.bsrc[q] = valid ? src + ((size_t)(u.sub0 + (j >> 2)) * c.ksteps + (j & 3)) * kBlockElems +
-                            lane * 8
-                      : zrow + lane * 8;
-    c.bstep[q] = valid ? kBK * kBlockElems : 0;
-  }
+  for (int q = 0; q < TT; ++q) c.boff[q] = q * c.tile_bytes + wv * kBlockBytes;
 
   f32x16 acc[RT][TT];
 #pragma unroll
