@@ -21,8 +21,12 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
+// Two fp32 -> one word of two bf16 (lo in the low half), round to nearest even:
+// one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // Unpack 8 bf16 held in a 16-byte vector into fp32.
