@@ -33,6 +33,7 @@ namespace {
 thread_local std::string g_err;
 constexpr uint32_t kMagic = 0x314d6f45u;  // "EoM1"
 constexpr int kMaxTokensLimit = 1 << 20;
+constexpr int kMaxWidth = 1 << 16;  // bf16 d_model and d_ff
 
 moe_status_t fail(moe_status_t st, const std::string& msg) {
   g_err = msg;
@@ -262,6 +263,9 @@ moe_status_t check_config(const moe_layer_config_t* c) {
   if (c->dtype == MOE_DTYPE_BF16) {
     if (c->d_model % 256 != 0 || c->d_ff % 128 != 0)
       return fail(MOE_ERR_UNSUPPORTED, "bf16 layers need d_model % 256 == 0 and d_ff % 128 == 0");
+    // the grouped GEMMs address a unit's operands with 32-bit byte offsets
+    if (c->d_model > kMaxWidth || c->d_ff > kMaxWidth)
+      return fail(MOE_ERR_UNSUPPORTED, "bf16 layers need d_model and d_ff <= 65536");
   } else {
     if (c->d_model % 4 != 0 || c->d_ff % 4 != 0)
       return fail(MOE_ERR_UNSUPPORTED, "fp32 layers need d_model and d_ff multiples of 4");

@@ -67,6 +67,7 @@ def _cfg(layer, **kw):
     (dict(max_tokens=0), 1), (dict(rms_eps=-1.0), 1), (dict(rms_eps=float("nan")), 1),
     (dict(n_experts=65, top_k=1), 4), (dict(n_experts=16, top_k=9), 4),
     (dict(d_model=2000), 4), (dict(d_ff=3000), 4), (dict(max_tokens=(1 << 20) + 1), 4),
+    (dict(d_model=65536 + 256), 4), (dict(d_ff=65536 + 128), 4),
     (dict(dtype=0, d_model=6), 4),
 ])
 def test_create_rejects_bad_configs_on_host(kw, status):
