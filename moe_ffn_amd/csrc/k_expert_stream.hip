@@ -53,8 +53,32 @@ constexpr int kSplitD8 = 8;
 constexpr int kStreamDepth = 4;
 constexpr int kStreamDepth8 = 4;
 
-__device__ __forceinline__ u32x4 ldw8(const uint8_t* p) { return ldg16_stream(p); }
-__device__ __forceinline__ u32x4 ldw(const uint16_t* p) { return ldg16_stream(p); }
+// A workgroup's weight tiles read as one raw buffer: the base and range in
+// scalar registers, the tile and 1 KiB block as the scalar offset and the
+// lane's 16 bytes as the one vector offset all loads share (no 64-bit vector
+// address per load); non-temporal, as each byte is read once.
+struct WTiles {
+  __amdgpu_buffer_rsrc_t r;
+  int voff, tile_bytes;
+  __device__ __forceinline__ u32x4 operator()(int j, int blk) const {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, j * tile_bytes + blk * 1024, 2);
+  }
+};
+__device__ __forceinline__ WTiles wtiles(const void* base, int ntiles, int tile_bytes, int lane) {
+  return {__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, ntiles * tile_bytes,
+                                            0x00020000),
+          lane * 16, tile_bytes};
+}
+// The same tiles through plain non-temporal global loads (the lane's 16 bytes
+// applied to the pointer): the down streams, which timed no faster through
+// the buffer form.
+struct WPtr {
+  const char* p;
+  int tile_bytes;
+  __device__ __forceinline__ u32x4 operator()(int j, int blk) const {
+    return ldg16_stream(p + (size_t)j * tile_bytes + (size_t)blk * 1024);
+  }
+};
 
 // Split-K reduction spread over the waves: every wave parks its NACC
 // accumulator tiles in LDS; after a barrier, element i of tile q summed over
@@ -169,14 +193,14 @@ __device__ __forceinline__ void stage_b(u32x4* bl, const RowP& rowp, int ntok, i
 // NW weight streams share one activation operand per k-step.
 // Lanes without a token read a row of zeros, so every load is unconditional
 // (a branch around a load would make the compiler drain the queue).
-template <int D, int NW>
-__device__ __forceinline__ void stream_mac(const uint16_t* const (&w)[NW], const uint16_t* xb,
+template <int D, int NW, class W>
+__device__ __forceinline__ void stream_mac(const W& w, const uint16_t* xb,
                                            int ks0, int kper, f32x16 (&acc)[NW]) {
   u32x4 qw[NW][D], qx[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
 #pragma unroll
-    for (int j = 0; j < NW; ++j) qw[j][i] = ldw(w[j] + (size_t)(ks0 + i) * kBlockElems);
+    for (int j = 0; j < NW; ++j) qw[j][i] = w(j, ks0 + i);
     qx[i] = ldg16(xb + (ks0 + i) * kKStep);
   }
   const int rounds = kper / D;
@@ -187,7 +211,7 @@ __device__ __forceinline__ void stream_mac(const uint16_t* const (&w)[NW], const
 #pragma unroll
       for (int j = 0; j < NW; ++j) acc[j] = mfma_32x32x16(qw[j][i], qx[i], acc[j]);
 #pragma unroll
-      for (int j = 0; j < NW; ++j) qw[j][i] = ldw(w[j] + (size_t)(sn + i) * kBlockElems);
+      for (int j = 0; j < NW; ++j) qw[j][i] = w(j, sn + i);
       qx[i] = ldg16(xb + (sn + i) * kKStep);
     }
   }
@@ -199,8 +223,8 @@ __device__ __forceinline__ void stream_mac(const uint16_t* const (&w)[NW], const
 // The same stream over an fp8 (E4M3) bank: each 16-byte load of a lane holds
 // its codes for two consecutive k-steps (k-step pairs p, 1 KiB per wave-wide
 // load), converted exactly to bf16 operands in registers; D2 pairs in flight.
-template <int D2, int NW, class BS, class Pre>
-__device__ __forceinline__ void stream_mac_fp8(const uint8_t* const (&w)[NW], const BS& xb,
+template <int D2, int NW, class W, class BS, class Pre>
+__device__ __forceinline__ void stream_mac_fp8(const W& w, const BS& xb,
                                                int ks0, int kper, f32x16 (&acc)[NW],
                                                const Pre& pre) {
   u32x4 qw[NW][D2], qx[D2][2];
@@ -208,7 +232,7 @@ __device__ __forceinline__ void stream_mac_fp8(const uint8_t* const (&w)[NW], co
 #pragma unroll
   for (int i = 0; i < D2; ++i)
 #pragma unroll
-    for (int j = 0; j < NW; ++j) qw[j][i] = ldw8(w[j] + (size_t)(p0 + i) * 1024);
+    for (int j = 0; j < NW; ++j) qw[j][i] = w(j, p0 + i);
   pre();  // with the first weights in flight (the LDS form stages its token rows here)
 #pragma unroll
   for (int i = 0; i < D2; ++i) {
@@ -226,7 +250,7 @@ __device__ __forceinline__ void stream_mac_fp8(const uint8_t* const (&w)[NW], co
         acc[j] = mfma_32x32x16(e4m3x8_to_bf16x8(qw[j][i][2], qw[j][i][3]), qx[i][1], acc[j]);
       }
 #pragma unroll
-      for (int j = 0; j < NW; ++j) qw[j][i] = ldw8(w[j] + (size_t)(pn + i) * 1024);
+      for (int j = 0; j < NW; ++j) qw[j][i] = w(j, pn + i);
       qx[i][0] = xb(2 * (pn + i));
       qx[i][1] = xb(2 * (pn + i) + 1);
       __builtin_amdgcn_sched_barrier(0);  // refill each slot right after its multiplies
@@ -270,18 +294,11 @@ __global__ __launch_bounds__(64 * S, 1) void k_gateup_stream(
   const int kper = ksteps / S;
   const int ks0 = wave * kper;
   const size_t tile_elems = (size_t)ksteps * kBlockElems;
-  // the NT interleaved gate/up tiles of columns 16*NT*ft ..
-  const uint16_t* wg =
-      wgu + ((size_t)e * (2 * F / kTileRows) + NT * ft) * tile_elems + lane * 8;
-  const uint16_t* wp[NT];
-  const uint8_t* wp8[NT];
-#pragma unroll
-  for (int q = 0; q < NT; ++q) {
-    wp[q] = wg + q * tile_elems;
-    // fp8 bank: same tile order, half the bytes per tile
-    wp8[q] = FP8 ? wgu8 + (((size_t)e * (2 * F / kTileRows) + NT * ft + q) * tile_elems +
-                           lane * 16) : nullptr;
-  }
+  // the NT interleaved gate/up tiles of columns 16*NT*ft .. (fp8 bank: same
+  // tile order, half the bytes per tile)
+  const size_t t0 = (size_t)e * (2 * F / kTileRows) + NT * ft;
+  const WTiles wt = FP8 ? wtiles(wgu8 + t0 * tile_elems, NT, (int)tile_elems, lane)
+                        : wtiles(wgu + t0 * tile_elems, NT, (int)tile_elems * 2, lane);
   const int col = lane & 31;
   // fp8 weights: the row scales of this lane's epilogue elements, loaded
   // before the stream so that their latency hides under it (the S waves take
@@ -318,12 +335,12 @@ __global__ __launch_bounds__(64 * S, 1) void k_gateup_stream(
               bl, [&](int t) { return xn + (size_t)list[c0 + t] * d; }, ntok, ks0, kper, lane);
         };
         const BLds bs{valid ? bl + col * 2 * kper + (lane >> 5) : zp + wave, ks0, valid ? 2 : 0};
-        stream_mac_fp8<D, NT>(wp8, bs, ks0, kper, acc, pre);
+        stream_mac_fp8<D, NT>(wt, bs, ks0, kper, acc, pre);
       } else {
-        stream_mac_fp8<D, NT>(wp8, BGlobal{xrow}, ks0, kper, acc, [] {});
+        stream_mac_fp8<D, NT>(wt, BGlobal{xrow}, ks0, kper, acc, [] {});
       }
     } else {
-      stream_mac<D, NT>(wp, xrow, ks0, kper, acc);
+      stream_mac<D, NT>(wt, xrow, ks0, kper, acc);
     }
     stash<NT>(acc, red, wave, lane);
     __syncthreads();
@@ -371,11 +388,11 @@ __global__ __launch_bounds__(64 * SD, 1) void k_down_stream(
   const int ksteps = F / kKStep;
   const int kper = ksteps / SD;
   const int ks0 = wave * kper;
-  const uint16_t* const wp[1] = {
-      wd + ((size_t)e * (d / kTileRows) + mt) * (size_t)ksteps * kBlockElems + lane * 8};
-  const uint8_t* const wp8[1] = {
-      FP8 ? wd8 + ((size_t)e * (d / kTileRows) + mt) * (size_t)ksteps * kBlockElems + lane * 16
-          : nullptr};
+  const size_t tile_elems = (size_t)ksteps * kBlockElems, t0 = (size_t)e * (d / kTileRows) + mt;
+  const WPtr wt = FP8 ? WPtr{reinterpret_cast<const char*>(wd8 + t0 * tile_elems) + lane * 16,
+                             (int)tile_elems}
+                      : WPtr{reinterpret_cast<const char*>(wd + t0 * tile_elems) + lane * 16,
+                             (int)tile_elems * 2};
   const int col = lane & 31;
   const int m0 = mt * kTileRows;
   // fp8 weights: the row scales of this lane's epilogue rows (the SD waves
@@ -408,8 +425,8 @@ __global__ __launch_bounds__(64 * SD, 1) void k_down_stream(
     f32x16 acc[1];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[0][i] = 0.f;
-    if constexpr (FP8) stream_mac_fp8<D, 1>(wp8, BGlobal{arow}, ks0, kper, acc, [] {});
-    else stream_mac<D, 1>(wp, arow, ks0, kper, acc);
+    if constexpr (FP8) stream_mac_fp8<D, 1>(wt, BGlobal{arow}, ks0, kper, acc, [] {});
+    else stream_mac<D, 1>(wt, arow, ks0, kper, acc);
     stash<1>(acc, red, wave, lane);
     __syncthreads();
     // the SD waves take the 16 accumulator elements (rows m0 + c32_row(i, lane)) in turn
