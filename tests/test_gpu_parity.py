@@ -306,3 +306,29 @@ def test_bad_arguments_raise():
                 torch.zeros((2048, 64), dtype=torch.bfloat16, device="cuda").t()):  # strided
         with pytest.raises(ValueError):
             layer.forward(h, out=bad)
+
+
+
+@pytest.mark.parametrize("w8a8,F", [(False, 1152), (True, 1280)])
+def test_grouped_unit_order_with_a_partial_group(w8a8, F):
+    """Experts with eight or more token spans take their weight blocks in
+    groups of four, span-major.  bf16 d_ff 1152: six 384-row gate/up blocks
+    (a group of four, then one of two); fp8 activations d_ff 1280: ten 256-row
+    blocks (4, 4, 2).  A bias steers most of the 3000 tokens to expert 0 (some
+    80 subtiles, 16 or more spans), the rest over three others: output rows
+    and dispatch arrays in full."""
+    cfg = LayerConfig(95, f"grouped_bf16_T3000_d2048_E4_F{F}", T=3000, d=2048, E=4, F=F, k=1,
+                      dtype="bf16", bias="normal", family=f"grouped_bf16_d2048_E4_F{F}")
+    inp = dict(make_inputs(cfg), bias=np.array([2.0, 0.0, 0.0, 0.0], np.float32))
+    print(f"[case] {cfg.name} w8a8={w8a8}", flush=True)
+    if w8a8:
+        from tests.test_gpu_w8a8 import fp8_vals, w8a8_layer
+        layer = w8a8_layer(inp, cfg.T)
+        st = check_parity(inp, layer, vals=fp8_vals(inp), fp8_act=True, label=cfg.name)
+    else:
+        layer = make_layer(inp, max_tokens=cfg.T)
+        st = check_parity(inp, layer, label=cfg.name)
+    assert st["rows_compared"] == cfg.T
+    _, r = layer.forward(to_torch(inp["hidden"], "bf16"), routing=True)
+    c = r["counts"].cpu().numpy()
+    assert c[0] >= 8 * 5 * 32, c  # expert 0 holds at least 8 spans of 5 subtiles
