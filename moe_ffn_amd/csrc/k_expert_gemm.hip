@@ -442,6 +442,20 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[r][j][q] = 0.f;
 
+  // down, k = 1: the token of each of the lane's output rows, loaded before
+  // the main loop so that the epilogue's gate loads find them in registers
+  // (one memory round trip at the end of the unit instead of two; the fp8
+  // form has no registers to spare for them)
+  constexpr bool kTokPre = MODE == 1 && !F8;
+  int tokp[kTokPre ? TT : 1];
+  if constexpr (kTokPre) {
+#pragma unroll
+    for (int j = 0; j < TT; ++j) {
+      const int r = j * kSub + (lane & 31);
+      tokp[j] = k == 1 && r < u.nrows ? gather[u.slot0 + r] : 0;
+    }
+  }
+
   mainloop<RT, TT, Q, F8>(c, lds, acc);
 
   // epilogue
@@ -512,7 +526,9 @@ __device__ __forceinline__ void run_unit(const Unit& u, u32x4* lds, const uint16
       static_assert(MODE == 0 || RT == 2, "the down epilogue's LDS tile holds 64 rows");
       char* wl = reinterpret_cast<char*>(lds) + wave * 8192;
       const bool ok = r < u.nrows;
-      const int tok = k == 1 && ok ? gather[u.slot0 + r] : 0;
+      int tok;
+      if constexpr (kTokPre) tok = tokp[j];
+      else tok = k == 1 && ok ? gather[u.slot0 + r] : 0;
       const float gw = k == 1 && ok ? gate[tok] : 0.f;
       float ms = 1.f;  // F8: the token row's activation scale
       if constexpr (F8) ms = asc[(size_t)(u.sub0 + j) * kSub + col];
